@@ -1,0 +1,174 @@
+"""Pins of the oracle's quantizers against what the pages and the mathematics
+fix: hand-derived packed rows (golden fixtures), brute-force nearest codes,
+the half-step error bound, endpoint and constant-group special cases,
+grid-aligned lossless round trips, and the append invariant."""
+import numpy as np
+import pytest
+
+from tests import _golden
+from quantized_kv_cache_amd import workloads as W
+
+NP = {"f32": np.float32, "f16": np.float16}
+
+
+def _as_storage(vals, dtype):
+    x = np.asarray(vals, np.float32)
+    return W.cast(x, dtype)
+
+
+def _f32(orc, a, dtype):
+    return orc.to_f32(a, dtype).astype(np.float64)
+
+
+# --------------------------------------------------------------------------- golden rows
+@pytest.mark.parametrize("name", ["affine_pack_4bit_g32.txt", "affine_pack_8bit_g32.txt"])
+def test_golden_affine_rows(orc, name):
+    g = _golden.load(name)
+    x = _as_storage(g["x"], g["dtype"])[None, :]
+    codes, s, b = orc.quantize_affine(x, g["dtype"], g["bits"], g["group_size"])
+    assert [int(w) for w in codes[0]] == g["codes"]
+    sc = g["scales"] if isinstance(g["scales"], list) else [g["scales"]]
+    bi = g["biases"] if isinstance(g["biases"], list) else [g["biases"]]
+    assert _f32(orc, s, g["dtype"])[0].tolist() == sc
+    assert _f32(orc, b, g["dtype"])[0].tolist() == bi
+    xh = orc.dequant_affine(codes, s, b, g["dtype"], g["bits"], g["group_size"])
+    assert np.array_equal(xh, x.astype(np.float32))
+
+
+def test_golden_q8_0_block(orc):
+    g = _golden.load("q8_0_block.txt")
+    x = _as_storage(g["x"], g["dtype"])[None, :]
+    codes, d = orc.quantize_q8_0(x, g["dtype"])
+    assert codes[0].tolist() == g["codes"]
+    assert int(d[0, 0]) == g["d_bits"]
+    assert np.array_equal(orc.dequant_q8_0(codes, d), x.astype(np.float32))
+
+
+# --------------------------------------------------------------------------- affine invariants
+def _unpack(codes, bits, D):
+    per = 32 // bits
+    j = np.arange(D)
+    return (codes[..., j // per] >> ((j % per) * bits).astype(np.uint32)) & ((1 << bits) - 1)
+
+
+CASES = [(4, 64, "f16", "uniform"), (4, 32, "f16", "normal"), (8, 64, "f16", "normal"),
+         (8, 128, "f32", "uniform"), (4, 128, "f32", "normal"), (8, 32, "bf16", "normal"),
+         (4, 64, "bf16", "uniform")]
+
+
+@pytest.mark.parametrize("bits,gs,dt,dist", CASES)
+def test_affine_codes_are_nearest_and_bounded(orc, bits, gs, dt, dist):
+    D = 256
+    x = W.random_case(1000 + bits + gs, (3, 17, D), dist, dt)
+    codes, s, b = orc.quantize_affine(x, dt, bits, gs)
+    n = (1 << bits) - 1
+    c = _unpack(codes, bits, D).astype(np.int64)
+    assert c.min() >= 0 and c.max() <= n
+    xf = _f32(orc, x, dt).reshape(-1, D // gs, gs)
+    sf = _f32(orc, s, dt).reshape(-1, D // gs, 1)
+    bf = _f32(orc, b, dt).reshape(-1, D // gs, 1)
+    c = c.reshape(-1, D // gs, gs)
+    # brute force: every code is (up to a rounding-level tie) the nearest grid point
+    grid = np.arange(n + 1, dtype=np.float64)
+    err_all = np.abs(xf[..., None] - (sf[..., None] * grid + bf[..., None]))
+    best = err_all.min(axis=-1)
+    mine = np.take_along_axis(err_all, c[..., None], axis=-1)[..., 0]
+    assert np.all(mine <= best + 1e-5 * sf)
+    # the half-step bound on the reconstruction; when the stored scale rounds
+    # below the exact range/n the top of the grid falls short of the maximum by
+    # n * (range/n - s), which only matters for coarse scale dtypes (bfloat16)
+    xh = orc.dequant_affine(codes, s, b, dt, bits, gs).astype(np.float64).reshape(xf.shape)
+    ulp = np.spacing(np.abs(xf).astype(np.float32) + np.abs(bf).astype(np.float32)).astype(np.float64)
+    short = n * np.maximum(0.0, (xf.max(-1, keepdims=True) - xf.min(-1, keepdims=True)) / n - sf)
+    assert np.all(np.abs(xf - xh) <= np.maximum(sf / 2, short) + 2 * ulp)
+    if dt != "bf16":
+        assert np.all(np.abs(xf - xh) <= sf / 2 + 2 * ulp)
+    # group minimum -> code 0 and reconstruction equal to the bias; maximum -> top code
+    imin = xf.argmin(-1)[..., None]
+    imax = xf.argmax(-1)[..., None]
+    assert np.all(np.take_along_axis(c, imin, -1) == 0)
+    if dt != "bf16":   # bias is the exact minimum when the dtype holds it
+        assert np.array_equal(np.take_along_axis(xh, imin, -1), np.take_along_axis(xf, imin, -1))
+    nonconst = (xf.max(-1) > xf.min(-1))[..., None]
+    top = np.take_along_axis(c, imax, -1)[nonconst]
+    # a bfloat16 scale can round up by 2^-8, moving the maximum down one code
+    assert np.all(top == n) if dt != "bf16" else np.all(top >= n - 1)
+
+
+@pytest.mark.parametrize("dt", ["f16", "f32", "bf16"])
+def test_affine_constant_group(orc, dt):
+    x = _as_storage(np.full((2, 64), 0.3125, np.float32), dt)
+    x[1] = _as_storage(np.full(64, -7.0, np.float32), dt)
+    codes, s, b = orc.quantize_affine(x, dt, 4, 32)
+    assert np.all(codes == 0)
+    assert np.all(_f32(orc, s, dt) == orc.affine_eps(dt))
+    assert np.array_equal(_f32(orc, b, dt), _f32(orc, x[:, ::32], dt))
+    xh = orc.dequant_affine(codes, s, b, dt, 4, 32)
+    assert np.array_equal(xh, _f32(orc, x, dt).astype(np.float32))
+
+
+@pytest.mark.parametrize("bits,gs", [(4, 32), (4, 64), (8, 64), (8, 128)])
+def test_affine_grid_aligned_lossless(orc, bits, gs):
+    rng = np.random.default_rng(bits * 1000 + gs)
+    rows, D, n = 40, 256, (1 << bits) - 1
+    c = rng.integers(0, n + 1, (rows, D // gs, gs))
+    c[..., 0] = 0
+    c[..., 1] = n
+    for g in range(D // gs):          # shuffle so the endpoints move around
+        for r in range(rows):
+            rng.shuffle(c[r, g])
+    k = rng.integers(-64, 65, (rows, D // gs, 1))
+    x = ((k + c) / 16.0).reshape(rows, D).astype(np.float16)   # exact: s = 1/16
+    codes, s, b = orc.quantize_affine(x, "f16", bits, gs)
+    assert np.array_equal(_unpack(codes, bits, D).reshape(c.shape), c)
+    assert np.all(_f32(orc, s, "f16") == 1 / 16)
+    assert np.array_equal(_f32(orc, b, "f16"), (k[..., 0] / 16.0))
+    assert np.array_equal(orc.dequant_affine(codes, s, b, "f16", bits, gs), x.astype(np.float32))
+
+
+# --------------------------------------------------------------------------- Q8_0
+@pytest.mark.parametrize("dt,dist", [("f16", "normal"), ("f16", "uniform"), ("f32", "normal"),
+                                     ("bf16", "normal")])
+def test_q8_0_invariants(orc, dt, dist):
+    D = 256
+    x = W.random_case(77, (5, 9, D), dist, dt)
+    x[0, 0, :32] = 0                       # an all-zero block
+    codes, d = orc.quantize_q8_0(x, dt)
+    c = codes.astype(np.int64).reshape(-1, D // 32, 32)
+    df = orc.to_f32(d, "f16").astype(np.float64).reshape(-1, D // 32, 1)
+    xf = _f32(orc, x, dt).reshape(c.shape)
+    assert c.min() >= -127 and c.max() <= 127
+    assert df[0, 0, 0] == 0 and np.all(c[0, 0] == 0)
+    amax = np.abs(xf).max(-1)
+    assert np.all(np.abs(df[..., 0] - amax / 127) <= np.spacing((amax / 127).astype(np.float16)).astype(np.float64))
+    nz = df[..., 0] > 0
+    ia = np.abs(xf).argmax(-1)[..., None]
+    assert np.all(np.abs(np.take_along_axis(c, ia, -1)[..., 0][nz]) == 127)
+    grid = np.arange(-127, 128, dtype=np.float64)
+    err_all = np.abs(xf[..., None] - df[..., None] * grid)
+    best = err_all.min(-1)
+    mine = np.take_along_axis(err_all, (c + 127)[..., None], -1)[..., 0]
+    assert np.all(mine <= best + 1e-5 * df)
+    xh = orc.dequant_q8_0(codes, d).astype(np.float64).reshape(xf.shape)
+    assert np.all(np.abs(xf - xh) <= df / 2 + 2 * np.spacing(np.abs(xf).astype(np.float32)))
+
+
+# --------------------------------------------------------------------------- append
+@pytest.mark.parametrize("mode,bits,gs", [("affine", 4, 64), ("affine", 8, 32), ("q8_0", 8, 32)])
+def test_append_rowwise_equals_whole_quantize(orc, mode, bits, gs):
+    B, H, L, D = 2, 3, 9, 128
+    x = W.random_case(5, (B, H, L, D), "normal", "f16")
+    whole = orc.quantize(x, "f16", mode, bits, gs)
+    # start from a cache filled with a byte pattern; append token by token
+    cache = {k: (None if v is None else np.full_like(v, 0x5A if v.dtype != np.float16 else 3.0))
+             for k, v in whole.items()}
+    before = {k: (None if v is None else v.copy()) for k, v in cache.items()}
+    for t in range(L):
+        cache = orc.append_rows(cache, x[:, :, t:t + 1], "f16", t, mode, bits, gs)
+        for k, v in cache.items():
+            if v is None:
+                continue
+            assert np.array_equal(v[:, :, t + 1:].view(np.uint8), before[k][:, :, t + 1:].view(np.uint8))
+    for k, v in whole.items():
+        if v is not None:
+            assert np.array_equal(cache[k].view(np.uint8), v.view(np.uint8))
