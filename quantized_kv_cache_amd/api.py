@@ -1,0 +1,234 @@
+"""Torch-facing binding of libqkv.so.
+
+Argument marshalling only: tensors become device pointers, the current torch
+stream becomes the HIP stream, and a status other than QKV_OK raises
+:class:`QKVError`.  Every step of quantization and attention runs in the HIP
+kernels behind the C ABI; there is no CPU path.
+
+The function names are those of the C ABI (include/qkv.h):
+``qkv_quantize``, ``qkv_update_append``, ``qsdpa_workspace_bytes``,
+``qsdpa_decode``, ``qsdpa_prefill``.
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+
+import torch
+
+from . import _lib
+from ._lib import QKVError  # noqa: F401
+
+_DT = {torch.float32: _lib.QKV_F32, torch.float16: _lib.QKV_F16, torch.bfloat16: _lib.QKV_BF16}
+_DT_NAME = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+_ALGO = {"auto": _lib.QKV_ALGO_AUTO, "generic": _lib.QKV_ALGO_GENERIC,
+         "matrix": _lib.QKV_ALGO_MATRIX}
+
+
+def torch_dtype(name_or_dtype) -> torch.dtype:
+    if isinstance(name_or_dtype, torch.dtype):
+        return name_or_dtype
+    return _DT_NAME[name_or_dtype]
+
+
+def _dt(t: torch.Tensor) -> int:
+    try:
+        return _DT[t.dtype]
+    except KeyError:
+        raise TypeError(f"unsupported dtype {t.dtype}") from None
+
+
+def _stream(device: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _ptr(t: torch.Tensor | None):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+@dataclasses.dataclass
+class Pack:
+    """A quantized K or V cache: codes, scales and (affine) biases, each
+    [B, H, L_cap, *] with rows of one token of one head."""
+    mode: str                      # "affine" | "q8_0"
+    bits: int
+    group_size: int
+    D: int
+    codes: torch.Tensor            # affine: int32 words [B,H,L_cap,D*bits/32]; q8_0: int8 [B,H,L_cap,D]
+    scales: torch.Tensor           # [B,H,L_cap,D/group_size]
+    biases: torch.Tensor | None    # affine only
+
+    @property
+    def B(self) -> int:
+        return self.codes.shape[0]
+
+    @property
+    def H(self) -> int:
+        return self.codes.shape[1]
+
+    @property
+    def L_cap(self) -> int:
+        return self.codes.shape[2]
+
+    @property
+    def scale_dtype(self) -> torch.dtype:
+        return self.scales.dtype
+
+    def c_struct(self) -> _lib.QkvPack:
+        c, s = self.codes, self.scales
+        if c.stride(3) != 1 or s.stride(3) != 1:
+            raise ValueError("pack rows must be contiguous")
+        if self.biases is not None and self.biases.stride() != s.stride():
+            raise ValueError("biases must have the layout of scales")
+        if any(c.stride(i) % c.shape[3] or s.stride(i) % s.shape[3] for i in range(3)):
+            raise ValueError("pack strides must be whole rows")
+        rs = [c.stride(i) // c.shape[3] for i in range(3)]
+        ss = [s.stride(i) // s.shape[3] for i in range(3)]
+        if rs != ss:
+            raise ValueError("codes and scales must share row strides")
+        return _lib.QkvPack(
+            mode=_lib.QKV_AFFINE if self.mode == "affine" else _lib.QKV_Q8_0,
+            bits=self.bits, group_size=self.group_size, scale_dtype=_dt(s),
+            B=c.shape[0], H=c.shape[1], L_cap=c.shape[2], D=self.D,
+            codes=c.data_ptr(), scales=s.data_ptr(),
+            biases=None if self.biases is None else self.biases.data_ptr(),
+            stride_b=rs[0], stride_h=rs[1], stride_l=rs[2])
+
+
+def empty_pack(B: int, H: int, L_cap: int, D: int, mode: str = "affine", bits: int = 4,
+               group_size: int = 64, dtype=torch.float16, device="cuda") -> Pack:
+    """Allocate a zero-filled dense pack (the caller owns the memory)."""
+    dtype = torch_dtype(dtype)
+    if mode == "q8_0":
+        return Pack("q8_0", 8, 32, D,
+                    torch.zeros((B, H, L_cap, D), dtype=torch.int8, device=device),
+                    torch.zeros((B, H, L_cap, D // 32), dtype=torch.float16, device=device), None)
+    if mode != "affine":
+        raise ValueError(mode)
+    return Pack("affine", bits, group_size, D,
+                torch.zeros((B, H, L_cap, D * bits // 32), dtype=torch.int32, device=device),
+                torch.zeros((B, H, L_cap, D // group_size), dtype=dtype, device=device),
+                torch.zeros((B, H, L_cap, D // group_size), dtype=dtype, device=device))
+
+
+def _src_strides(x: torch.Tensor):
+    if x.dim() != 4 or x.stride(3) != 1:
+        raise ValueError("source must be [B,H,L,D] with D contiguous")
+    return _lib.i64_array([x.stride(0), x.stride(1), x.stride(2)])
+
+
+def qkv_quantize(x: torch.Tensor, mode: str = "affine", bits: int = 4, group_size: int = 64,
+                 L_cap: int | None = None, out: Pack | None = None) -> Pack:
+    """Quantize x[B,H,L,D] into rows [0, L) of a pack (a new one of capacity
+    L_cap unless ``out`` is given)."""
+    B, H, L, D = x.shape
+    if out is None:
+        out = empty_pack(B, H, L_cap or L, D, mode, bits, group_size, x.dtype, x.device)
+    st = _lib.load().qkv_quantize(_ptr(x), _dt(x), _src_strides(x), L,
+                                  ctypes.byref(out.c_struct()), _stream(x.device))
+    _lib.check(st)
+    return out
+
+
+def qkv_update_append(k_cache: Pack, v_cache: Pack, k_new: torch.Tensor, v_new: torch.Tensor,
+                      offset: int) -> None:
+    """Quantize k_new/v_new [B,H,T,D] into rows [offset, offset+T) in place."""
+    if k_new.shape != v_new.shape or k_new.stride() != v_new.stride() or k_new.dtype != v_new.dtype:
+        raise ValueError("k_new and v_new must share shape, strides and dtype")
+    st = _lib.load().qkv_update_append(_ptr(k_new), _ptr(v_new), _dt(k_new), _src_strides(k_new),
+                                       k_new.shape[2], offset, ctypes.byref(k_cache.c_struct()),
+                                       ctypes.byref(v_cache.c_struct()), _stream(k_new.device))
+    _lib.check(st)
+
+
+def _opts(num_splits: int, algo: str):
+    return _lib.QkvAttnOpts(num_splits=int(num_splits), algo=_ALGO[algo])
+
+
+def qsdpa_workspace_bytes(q: torch.Tensor, k: Pack, L: int, num_splits: int = 0,
+                          algo: str = "auto") -> int:
+    B, Hq, Lq, D = q.shape
+    return int(_lib.load().qsdpa_workspace_bytes(B, Hq, Lq, D, L, ctypes.byref(k.c_struct()),
+                                                 _dt(q), ctypes.byref(_opts(num_splits, algo))))
+
+
+class Workspace:
+    """Zero-initialised, reusable attention workspace (grows on demand).  The
+    kernels return its counters to zero after each call, so it stays valid
+    for later calls on the same stream."""
+
+    def __init__(self):
+        self._buf: dict[torch.device, torch.Tensor] = {}
+
+    def get(self, nbytes: int, device) -> torch.Tensor | None:
+        if nbytes == 0:
+            return None
+        device = torch.device(device)
+        buf = self._buf.get(device)
+        if buf is None or buf.numel() < nbytes:
+            buf = torch.zeros(((nbytes + 255) // 256) * 256, dtype=torch.uint8, device=device)
+            self._buf[device] = buf
+        return buf
+
+
+_default_ws = Workspace()
+
+
+def _mask_args(mask: torch.Tensor | None, shape4):
+    if mask is None:
+        return None, 0, None
+    m = mask
+    while m.dim() < 4:
+        m = m.unsqueeze(0)
+    m = m.expand(*shape4)
+    strides = [0 if n == 1 else s for s, n in zip(m.stride(), m.shape)]
+    return _ptr(m), _dt(m), _lib.i64_array(strides)
+
+
+def _attn_common(q, k, v, num_splits, algo, workspace, L):
+    if q.dim() != 4 or not q.is_contiguous():
+        raise ValueError("q must be a contiguous [B,Hq,Lq,D] tensor")
+    ws = workspace or _default_ws
+    nbytes = qsdpa_workspace_bytes(q, k, L, num_splits, algo)
+    buf = ws.get(nbytes, q.device)
+    return buf, nbytes
+
+
+def qsdpa_decode(q: torch.Tensor, k: Pack, v: Pack, L: int, scale: float,
+                 mask: torch.Tensor | None = None, num_splits: int = 0, algo: str = "auto",
+                 out: torch.Tensor | None = None, workspace: Workspace | None = None) -> torch.Tensor:
+    """softmax(scale q K^T + mask) V for q[B,Hq,1,D] over keys [0, L)."""
+    B, Hq, Lq, D = q.shape
+    if Lq != 1:
+        raise ValueError("decode takes one query per head")
+    out = torch.empty_like(q) if out is None else out
+    buf, nbytes = _attn_common(q, k, v, num_splits, algo, workspace, L)
+    mp, mdt, ms = _mask_args(mask, (B, Hq, 1, L))
+    st = _lib.load().qsdpa_decode(_ptr(q), _dt(q), B, Hq, D, ctypes.byref(k.c_struct()),
+                                  ctypes.byref(v.c_struct()), L, float(scale), mp, mdt, ms,
+                                  _ptr(out), _ptr(buf), nbytes,
+                                  ctypes.byref(_opts(num_splits, algo)), _stream(q.device))
+    _lib.check(st)
+    return out
+
+
+def qsdpa_prefill(q: torch.Tensor, k: Pack, v: Pack, L: int, scale: float, causal: bool = False,
+                  mask: torch.Tensor | None = None, num_splits: int = 0, algo: str = "auto",
+                  out: torch.Tensor | None = None,
+                  workspace: Workspace | None = None) -> torch.Tensor:
+    """softmax(scale q K^T + mask) V for q[B,Hq,Lq,D] over keys [0, L); causal
+    hides key j from query i when j > L - Lq + i."""
+    B, Hq, Lq, D = q.shape
+    if causal and mask is not None:
+        raise ValueError("pass either causal=True or an additive mask")
+    out = torch.empty_like(q) if out is None else out
+    buf, nbytes = _attn_common(q, k, v, num_splits, algo, workspace, L)
+    kind = _lib.QKV_MASK_CAUSAL if causal else (_lib.QKV_MASK_ADDITIVE if mask is not None
+                                                else _lib.QKV_MASK_NONE)
+    mp, mdt, ms = _mask_args(mask, (B, Hq, Lq, L))
+    st = _lib.load().qsdpa_prefill(_ptr(q), _dt(q), B, Hq, Lq, D, ctypes.byref(k.c_struct()),
+                                   ctypes.byref(v.c_struct()), L, float(scale), kind, mp, mdt, ms,
+                                   _ptr(out), _ptr(buf), nbytes,
+                                   ctypes.byref(_opts(num_splits, algo)), _stream(q.device))
+    _lib.check(st)
+    return out

@@ -1,0 +1,297 @@
+// Generic attention over a quantized KV cache: every supported combination of
+// query dtype (fp32 / fp16 / bf16), cache format (affine 4/8-bit, Q8_0), head
+// size and GQA factor, for decode (Lq = 1) and prefill (Lq > 1).
+//
+//   out[b,h,i,:] = softmax_j(scale * q[b,h,i,:] . K^[b,h/G,j,:] + m_ij) V^[b,h/G,j,:]
+//
+// (MLX page "add fast::quantized_kv_update": fast.cpp
+// quantized_scaled_dot_product_attention -- q reshaped to
+// [B, Hk, Hq/Hk, L, D] so each kv head serves G query heads -- and
+// sdpa_vector.h quant_sdpa_vector for the online softmax and the merge of
+// partial softmax states.)
+//
+// Work decomposition: one workgroup per (key split, row tile, batch x kv head).
+// The rows of a kv head are its G query heads times Lq queries, packed as
+// row p = i*G + g, so one tile shares every K/V load among the GQA heads (as
+// the llama.cpp page "Metal: Optimize q8_0 KV - #25556" does for two heads)
+// and, for prefill, among neighbouring queries.  Keys are consumed in blocks
+// of 32: scores (8 lanes per key, butterfly sum), an online-softmax update per
+// row, the V block dequantized once into LDS, then o = o*alpha + P V.
+// With several splits each workgroup writes its (m, l, o) state to the
+// workspace and the last one to finish (atomic ticket) merges them with the
+// log-sum-exp rule and writes the output.  This kernel favours generality over
+// speed; the matrix-core kernels cover the fp16 hot shapes.
+#include "qkv_device.hpp"
+#include "qkv_internal.hpp"
+
+namespace qkv {
+
+namespace {
+
+constexpr int KB = 32;      // keys per block
+constexpr int RTG = 16;     // rows per tile
+
+// Dequantize element d of a cache row (row index r in the pack).
+template <int MODE, int BITS, int ST>
+__device__ __forceinline__ float dequant_elem(const uint8_t* codes, const void* scales,
+                                              const void* biases, int64_t r, int d, int D,
+                                              int gs_log2) {
+    const int NG = D >> gs_log2;
+    const int g = d >> gs_log2;
+    if constexpr (MODE == MODE_Q8_0) {
+        const int8_t c = ((const int8_t*)codes)[r * D + d];
+        return f16_to_f32(((const uint16_t*)scales)[r * NG + g]) * (float)c;
+    } else {
+        const uint32_t* w = (const uint32_t*)(codes + r * (int64_t)(D * BITS / 8));
+        constexpr int PER = 32 / BITS;
+        const uint32_t c = (w[d / PER] >> ((d % PER) * BITS)) & ((1u << BITS) - 1u);
+        const float s = load_as_f32<ST>(scales, r * NG + g);
+        const float b = load_as_f32<ST>(biases, r * NG + g);
+        return s * (float)c + b;
+    }
+}
+
+template <int QT, int MODE, int BITS, int D>
+__global__ __launch_bounds__(256) void attn_generic_kernel(AttnLaunch p) {
+    constexpr int ST = (MODE == MODE_Q8_0) ? DT_F16 : QT;   // scale dtype
+    constexpr int DPK = D / 8;                               // d per lane (scores)
+    constexpr int DPO = D / 16;                              // d per lane (output)
+    __shared__ float qs[RTG][D];
+    __shared__ float sc[RTG][KB];
+    __shared__ float vt[KB][D];
+    __shared__ float m_s[RTG], l_s[RTG], a_s[RTG];
+    __shared__ int last_flag;
+
+    const int tid = threadIdx.x;
+    const int split = blockIdx.x;
+    const int rt = blockIdx.y;
+    const int64_t bk = blockIdx.z;
+    const int64_t b = bk / p.Hk;
+    const int64_t kvh = bk % p.Hk;
+    const int r0 = rt * RTG;
+    const int nr = min(RTG, p.n_rows - r0);
+
+    // queries of the tile, pre-multiplied by the softmax scale (fp32)
+    for (int idx = tid; idx < RTG * D; idx += 256) {
+        const int r = idx / D, d = idx % D;
+        float val = 0.0f;
+        if (r < nr) {
+            const int pr = r0 + r;
+            const int64_t i = pr / p.G, h = kvh * p.G + pr % p.G;
+            val = load_as_f32<QT>(p.q, ((b * p.Hq + h) * p.Lq + i) * D + d) * p.scale;
+        }
+        qs[r][d] = val;
+    }
+    if (tid < RTG) { m_s[tid] = -INFINITY; l_s[tid] = 0.0f; }
+
+    // key range of this split, cut at the last key any row of the tile sees
+    int64_t j_begin = (int64_t)split * p.chunk;
+    int64_t j_end = min(p.L, j_begin + p.chunk);
+    if (p.mask_kind == MASK_CAUSAL) {
+        const int64_t i_max = (r0 + nr - 1) / p.G;
+        j_end = min(j_end, p.L - p.Lq + i_max + 1);
+    }
+
+    const int64_t krow0 = b * p.k.sb + kvh * p.k.sh;
+    const int64_t vrow0 = b * p.v.sb + kvh * p.v.sh;
+    const uint8_t* kc = (const uint8_t*)p.k.codes;
+    const uint8_t* vc = (const uint8_t*)p.v.codes;
+
+    const int orow = tid / 16, ochunk = tid % 16;
+    float o[DPO];
+#pragma unroll
+    for (int i = 0; i < DPO; ++i) o[i] = 0.0f;
+    __syncthreads();
+
+    for (int64_t jb = j_begin; jb < j_end; jb += KB) {
+        // ---- scores: 8 lanes per key
+        {
+            const int kk = tid / 8, part = tid % 8;
+            const int64_t j = jb + kk;
+            const bool valid = j < j_end;
+            float acc[RTG];
+#pragma unroll
+            for (int r = 0; r < RTG; ++r) acc[r] = 0.0f;
+            if (valid) {
+                const int64_t kr = krow0 + j * p.k.sl;
+#pragma unroll 4
+                for (int e = 0; e < DPK; ++e) {
+                    const int d = part * DPK + e;
+                    const float kv = dequant_elem<MODE, BITS, ST>(kc, p.k.scales, p.k.biases, kr,
+                                                                  d, D, p.gs_log2);
+#pragma unroll
+                    for (int r = 0; r < RTG; ++r) acc[r] += qs[r][d] * kv;
+                }
+            }
+#pragma unroll
+            for (int r = 0; r < RTG; ++r) {
+                float a = acc[r];
+                a += __shfl_xor(a, 1, 64);
+                a += __shfl_xor(a, 2, 64);
+                a += __shfl_xor(a, 4, 64);
+                acc[r] = a;
+            }
+            if (part == 0) {
+#pragma unroll
+                for (int r = 0; r < RTG; ++r) {
+                    float z = -INFINITY;
+                    if (valid && r < nr) {
+                        const int pr = r0 + r;
+                        const int64_t i = pr / p.G, h = kvh * p.G + pr % p.G;
+                        z = acc[r];
+                        if (p.mask_kind == MASK_CAUSAL && j > p.L - p.Lq + i) z = -INFINITY;
+                        if (p.mask_kind == MASK_ADDITIVE)
+                            z += load_mask(p.mask, p.mask_dtype,
+                                           b * p.ms0 + h * p.ms1 + i * p.ms2 + j * p.ms3);
+                    }
+                    sc[r][kk] = z;
+                }
+            }
+        }
+        __syncthreads();
+        // ---- online softmax update: 16 lanes per row, 2 keys per lane
+        {
+            const int r = tid / 16, l16 = tid % 16;
+            const float z0 = sc[r][l16], z1 = sc[r][l16 + 16];
+            float mb = fmaxf(z0, z1);
+#pragma unroll
+            for (int o2 = 1; o2 < 16; o2 <<= 1) mb = fmaxf(mb, __shfl_xor(mb, o2, 64));
+            const float m_old = m_s[r];
+            const float m_new = fmaxf(m_old, mb);
+            float p0 = 0.0f, p1 = 0.0f, alpha = 1.0f;
+            if (m_new != -INFINITY) {
+                alpha = (m_old == -INFINITY) ? 0.0f : fast_exp2((m_old - m_new) * kLog2e);
+                p0 = (z0 == -INFINITY) ? 0.0f : fast_exp2((z0 - m_new) * kLog2e);
+                p1 = (z1 == -INFINITY) ? 0.0f : fast_exp2((z1 - m_new) * kLog2e);
+            }
+            float ps = p0 + p1;
+#pragma unroll
+            for (int o2 = 1; o2 < 16; o2 <<= 1) ps += __shfl_xor(ps, o2, 64);
+            sc[r][l16] = p0;
+            sc[r][l16 + 16] = p1;
+            if (l16 == 0) {
+                m_s[r] = m_new;
+                l_s[r] = l_s[r] * alpha + ps;
+                a_s[r] = alpha;
+            }
+        }
+        // ---- V block -> LDS (fp32)
+        for (int idx = tid; idx < KB * D; idx += 256) {
+            const int kk = idx / D, d = idx % D;
+            const int64_t j = jb + kk;
+            vt[kk][d] = (j < j_end) ? dequant_elem<MODE, BITS, ST>(vc, p.v.scales, p.v.biases,
+                                                                   vrow0 + j * p.v.sl, d, D,
+                                                                   p.gs_log2)
+                                    : 0.0f;
+        }
+        __syncthreads();
+        // ---- o = o * alpha + P V
+        {
+            const float alpha = a_s[orow];
+#pragma unroll
+            for (int i = 0; i < DPO; ++i) o[i] *= alpha;
+            for (int kk = 0; kk < KB; ++kk) {
+                const float pk = sc[orow][kk];
+#pragma unroll
+                for (int i = 0; i < DPO; ++i) o[i] += pk * vt[kk][ochunk * DPO + i];
+            }
+        }
+        __syncthreads();
+    }
+
+    const bool row_ok = orow < nr;
+    const int pr = r0 + orow;
+    const int64_t oi = row_ok ? (int64_t)(pr / p.G) : 0;
+    const int64_t oh = row_ok ? kvh * p.G + pr % p.G : 0;
+    const int64_t obase = ((b * p.Hq + oh) * p.Lq + oi) * D + ochunk * DPO;
+
+    if (p.S == 1) {
+        if (row_ok) {
+            const float l = l_s[orow];
+            const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+#pragma unroll
+            for (int i = 0; i < DPO; ++i) store_from_f32<QT>(p.out, obase + i, o[i] * inv);
+        }
+        return;
+    }
+
+    // ---- partial state -> workspace, then the last workgroup merges
+    const int64_t tile = bk * p.n_rt + rt;
+    const int W = D + 2;
+    float* mine = p.partials + ((tile * p.S + split) * RTG + orow) * W;
+#pragma unroll
+    for (int i = 0; i < DPO; ++i) mine[2 + ochunk * DPO + i] = o[i];
+    if (ochunk == 0) { mine[0] = m_s[orow]; mine[1] = l_s[orow]; }
+    __threadfence();
+    __syncthreads();
+    if (tid == 0) {
+        const uint32_t prev = atomicAdd(&p.tickets[tile], 1u);
+        last_flag = (prev == (uint32_t)(p.S - 1));
+    }
+    __syncthreads();
+    if (!last_flag) return;
+    __threadfence();
+    if (tid == 0) p.tickets[tile] = 0u;        // leave the counter ready for the next call
+    if (!row_ok) return;
+    const float* base = p.partials + (tile * p.S * RTG + orow) * W;
+    float M = -INFINITY;
+    for (int s = 0; s < p.S; ++s) M = fmaxf(M, base[(int64_t)s * RTG * W]);
+    float acc[DPO];
+#pragma unroll
+    for (int i = 0; i < DPO; ++i) acc[i] = 0.0f;
+    float den = 0.0f;
+    if (M != -INFINITY) {
+        for (int s = 0; s < p.S; ++s) {
+            const float* ps = base + (int64_t)s * RTG * W;
+            const float ms = ps[0];
+            if (ms == -INFINITY) continue;
+            const float w = fast_exp2((ms - M) * kLog2e);
+            den += w * ps[1];
+#pragma unroll
+            for (int i = 0; i < DPO; ++i) acc[i] += w * ps[2 + ochunk * DPO + i];
+        }
+    }
+    const float inv = den > 0.0f ? 1.0f / den : 0.0f;
+#pragma unroll
+    for (int i = 0; i < DPO; ++i) store_from_f32<QT>(p.out, obase + i, acc[i] * inv);
+}
+
+template <int QT, int MODE, int BITS, int D>
+hipError_t launch_g(int64_t B, const AttnLaunch& p, hipStream_t stream) {
+    dim3 grid(p.S, p.n_rt, (unsigned)(B * p.Hk));
+    hipLaunchKernelGGL((attn_generic_kernel<QT, MODE, BITS, D>), grid, dim3(256), 0, stream, p);
+    return hipGetLastError();
+}
+
+template <int QT, int MODE, int BITS>
+hipError_t dispatch_d(int D, int64_t B, const AttnLaunch& p, hipStream_t s) {
+    switch (D) {
+        case 64: return launch_g<QT, MODE, BITS, 64>(B, p, s);
+        case 128: return launch_g<QT, MODE, BITS, 128>(B, p, s);
+        case 256: return launch_g<QT, MODE, BITS, 256>(B, p, s);
+    }
+    return hipErrorNotSupported;
+}
+
+template <int QT>
+hipError_t dispatch_fmt(int mode, int bits, int D, int64_t B, const AttnLaunch& p,
+                        hipStream_t s) {
+    if (mode == MODE_Q8_0) return dispatch_d<QT, MODE_Q8_0, 8>(D, B, p, s);
+    if (bits == 4) return dispatch_d<QT, MODE_AFFINE, 4>(D, B, p, s);
+    if (bits == 8) return dispatch_d<QT, MODE_AFFINE, 8>(D, B, p, s);
+    return hipErrorNotSupported;
+}
+
+}  // namespace
+
+hipError_t launch_attn_generic(int q_dtype, int mode, int bits, int D, int64_t B,
+                               const AttnLaunch& p, hipStream_t stream) {
+    switch (q_dtype) {
+        case DT_F32: return dispatch_fmt<DT_F32>(mode, bits, D, B, p, stream);
+        case DT_F16: return dispatch_fmt<DT_F16>(mode, bits, D, B, p, stream);
+        case DT_BF16: return dispatch_fmt<DT_BF16>(mode, bits, D, B, p, stream);
+    }
+    return hipErrorNotSupported;
+}
+
+}  // namespace qkv

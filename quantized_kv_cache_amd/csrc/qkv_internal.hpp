@@ -1,0 +1,75 @@
+// Internal interface between the C-ABI host layer (qkv_api.cpp) and the HIP
+// kernels.  Plain pointers and sizes only; every argument has already been
+// validated by the host layer when a launcher is called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qkv {
+
+enum DType { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2 };
+enum Mode { MODE_AFFINE = 0, MODE_Q8_0 = 1 };
+enum MaskKind { MASK_NONE = 0, MASK_CAUSAL = 1, MASK_ADDITIVE = 2 };
+
+// One tensor's worth of rows to quantize: source rows [B,H,T,D] with element
+// strides, destination pack rows offset+t.
+struct QuantJob {
+    const void* x;
+    int64_t xs0, xs1, xs2;          // element strides of b, h, t
+    void* codes;
+    void* scales;
+    void* biases;                   // nullptr for Q8_0
+    int64_t sb, sh, sl;             // pack strides in rows
+};
+
+struct QuantLaunch {
+    QuantJob job[2];                // K (and V for append)
+    int64_t H, T, offset;
+    int64_t rows;                   // B*H*T
+};
+
+// Read-only view of a pack for attention.
+struct PackView {
+    const void* codes;
+    const void* scales;
+    const void* biases;
+    int64_t sb, sh, sl;             // strides in rows
+};
+
+struct AttnLaunch {
+    const void* q;
+    void* out;
+    PackView k, v;
+    int64_t Hq, Hk, Lq, L;
+    int32_t G;                      // Hq / Hk
+    int32_t gs_log2;                // log2(group_size) (5 for Q8_0)
+    float scale;
+    int32_t mask_kind;
+    const void* mask;
+    int32_t mask_dtype;
+    int64_t ms0, ms1, ms2, ms3;     // mask element strides
+    int32_t S;                      // splits of the key range
+    int64_t chunk;                  // keys per split
+    int32_t n_rows;                 // G * Lq rows per (b, kv head)
+    int32_t n_rt;                   // row tiles per (b, kv head)
+    int32_t RT;                     // rows per tile
+    float* partials;                // [B*Hk*n_rt][S][RT][D+2] (m, l, o)
+    uint32_t* tickets;              // [B*Hk*n_rt]
+};
+
+// Launchers (return hipGetLastError() of the launch).
+hipError_t launch_quantize(int x_dtype, int mode, int bits, int group_size, int D,
+                           const QuantLaunch& p, int njobs, hipStream_t stream);
+
+hipError_t launch_attn_generic(int q_dtype, int mode, int bits, int D, int64_t B,
+                               const AttnLaunch& p, hipStream_t stream);
+
+// Matrix-core decode/prefill for fp16 queries; returns hipErrorNotSupported
+// when no instantiation covers the arguments.
+bool matrix_supported(int q_dtype, int mode, int bits, int group_size, int D, int G,
+                      int64_t Lq);
+hipError_t launch_attn_matrix(int mode, int bits, int D, int64_t B, const AttnLaunch& p,
+                              hipStream_t stream);
+
+}  // namespace qkv

@@ -1,0 +1,137 @@
+"""The C ABI on the host: the library loads, exports every function that
+include/qkv.h declares, and rejects bad arguments before any HIP call (these
+checks run without a GPU; no call here reaches a kernel launch)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from quantized_kv_cache_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 0x10000000        # aligned, never dereferenced: validation fails first
+
+
+def header_functions():
+    src = open(os.path.join(ROOT, "include", "qkv.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\**(\w+)\s*\(", src, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    return _lib.load()
+
+
+def test_exports_every_declared_function(L):
+    names = header_functions()
+    assert set(names) == set(_lib.EXPORTS), names
+    for n in names:
+        assert hasattr(L, n), n
+    assert L.qkv_abi_version() == 1
+
+
+def _pack(**kw):
+    d = dict(mode=_lib.QKV_AFFINE, bits=4, group_size=64, scale_dtype=_lib.QKV_F16, B=1, H=2,
+             L_cap=64, D=128, codes=FAKE, scales=FAKE + 0x100000, biases=FAKE + 0x200000,
+             stride_b=128, stride_h=64, stride_l=1)
+    d.update(kw)
+    return _lib.QkvPack(**d)
+
+
+def _quant(L, pk, x=FAKE + 0x400000, dt=_lib.QKV_F16, strides=(16384, 8192, 128), n=64):
+    st = L.qkv_quantize(ctypes.c_void_p(x) if x else None, dt, _lib.i64_array(strides), n,
+                        ctypes.byref(pk), None)
+    return st, L.qkv_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(bits=3), _lib.QKV_EUNSUPPORTED, "bits"),
+    (dict(group_size=48), _lib.QKV_EUNSUPPORTED, "group_size"),
+    (dict(D=96, group_size=32), _lib.QKV_EUNSUPPORTED, "head size"),
+    (dict(D=160, group_size=64), _lib.QKV_EINVAL, "multiple"),
+    (dict(codes=FAKE + 4), _lib.QKV_EINVAL, "aligned"),
+    (dict(scales=FAKE + 0x100001), _lib.QKV_EINVAL, "misaligned"),
+    (dict(biases=None), _lib.QKV_EINVAL, "biases"),
+    (dict(codes=None), _lib.QKV_EINVAL, "null"),
+    (dict(mode=_lib.QKV_Q8_0, bits=8, group_size=32), _lib.QKV_EINVAL, "biases"),
+    (dict(mode=_lib.QKV_Q8_0, bits=8, group_size=32, biases=None, scale_dtype=_lib.QKV_F32),
+     _lib.QKV_EINVAL, "fp16"),
+    (dict(stride_l=-1), _lib.QKV_EINVAL, "stride"),
+    (dict(mode=7), _lib.QKV_EINVAL, "mode"),
+])
+def test_quantize_rejects_bad_packs(L, kw, status, msg):
+    st, err = _quant(L, _pack(**kw))
+    assert st == status and msg in err, (st, err)
+
+
+def test_quantize_rejects_bad_sources(L):
+    assert _quant(L, _pack(), x=0)[0] == _lib.QKV_EINVAL
+    assert _quant(L, _pack(), x=FAKE + 0x400008)[0] == _lib.QKV_EINVAL          # misaligned
+    assert _quant(L, _pack(), strides=(16384, 8192, 100))[0] == _lib.QKV_EINVAL  # not /8
+    assert _quant(L, _pack(), n=65)[0] == _lib.QKV_EINVAL                       # > L_cap
+    assert _quant(L, _pack(), dt=_lib.QKV_F32)[0] == _lib.QKV_EUNSUPPORTED      # scale != src
+    st, _ = _quant(L, _pack(), n=0)                                             # nothing to do
+    assert st == _lib.QKV_OK
+
+
+def _append(L, kp, vp, T=1, offset=0, k=FAKE + 0x400000, v=FAKE + 0x500000):
+    return L.qkv_update_append(ctypes.c_void_p(k), ctypes.c_void_p(v), _lib.QKV_F16,
+                               _lib.i64_array((256, 128, 128)), T, offset, ctypes.byref(kp),
+                               ctypes.byref(vp), None)
+
+
+def test_append_rejects(L):
+    kp = _pack()
+    vp = _pack(codes=FAKE + 0x800000, scales=FAKE + 0x900000, biases=FAKE + 0xa00000)
+    assert _append(L, kp, vp, offset=64) == _lib.QKV_EINVAL          # past capacity
+    assert _append(L, kp, vp, offset=-1) == _lib.QKV_EINVAL
+    assert _append(L, kp, vp, T=0) == _lib.QKV_EINVAL
+    assert _append(L, kp, kp) == _lib.QKV_EINVAL                      # K and V alias
+    assert _append(L, kp, _pack(bits=8)) == _lib.QKV_EINVAL           # formats differ
+    assert _append(L, kp, vp, T=2, offset=63) == _lib.QKV_EINVAL
+    assert "capacity" in L.qkv_last_error().decode()
+
+
+def _decode(L, q=FAKE + 0x1000000, out=FAKE + 0x2000000, kp=None, vp=None, Hq=4, Ln=64,
+            mask=None, ms=None, ws=None, wsb=0, opts=None, qdt=_lib.QKV_F16):
+    kp = kp or _pack()
+    vp = vp or _pack(codes=FAKE + 0x800000, scales=FAKE + 0x900000, biases=FAKE + 0xa00000)
+    return L.qsdpa_decode(ctypes.c_void_p(q) if q else None, qdt, 1, Hq, 128, ctypes.byref(kp),
+                          ctypes.byref(vp), Ln, 1.0, ctypes.c_void_p(mask) if mask else None,
+                          _lib.QKV_F32, _lib.i64_array(ms) if ms else None,
+                          ctypes.c_void_p(out) if out else None,
+                          ctypes.c_void_p(ws) if ws else None, wsb,
+                          ctypes.byref(opts) if opts else None, None)
+
+
+def test_decode_rejects(L):
+    assert _decode(L, Hq=3) == _lib.QKV_EINVAL                        # Hq % Hk
+    assert _decode(L, Ln=0) == _lib.QKV_EINVAL
+    assert _decode(L, Ln=65) == _lib.QKV_EINVAL                       # > L_cap
+    assert _decode(L, q=0) == _lib.QKV_EINVAL
+    assert _decode(L, out=FAKE + 0x1000000) == _lib.QKV_EINVAL        # out aliases q
+    assert _decode(L, out=FAKE + 0x100) == _lib.QKV_EINVAL            # out overlaps codes
+    assert _decode(L, qdt=_lib.QKV_F32) == _lib.QKV_EUNSUPPORTED      # scale dtype != q
+    assert _decode(L, vp=_pack(bits=8, codes=FAKE + 0x800000, scales=FAKE + 0x900000,
+                               biases=FAKE + 0xa00000)) == _lib.QKV_EINVAL
+    assert _decode(L, mask=FAKE + 0x3000000, ms=(0, 0, 0, -1)) == _lib.QKV_EINVAL
+    # partitioned plans need a workspace
+    opts = _lib.QkvAttnOpts(num_splits=4, algo=_lib.QKV_ALGO_GENERIC)
+    assert _decode(L, opts=opts) == _lib.QKV_EWORKSPACE
+    assert "workspace" in L.qkv_last_error().decode()
+    assert _decode(L, opts=_lib.QkvAttnOpts(num_splits=-1, algo=0)) == _lib.QKV_EINVAL
+
+
+def test_workspace_bytes(L):
+    kp = _pack()
+    one = _lib.QkvAttnOpts(num_splits=1, algo=_lib.QKV_ALGO_GENERIC)
+    four = _lib.QkvAttnOpts(num_splits=4, algo=_lib.QKV_ALGO_GENERIC)
+    assert L.qsdpa_workspace_bytes(1, 4, 1, 128, 64, ctypes.byref(kp), _lib.QKV_F16,
+                                   ctypes.byref(one)) == 0
+    n = L.qsdpa_workspace_bytes(1, 4, 1, 128, 64, ctypes.byref(kp), _lib.QKV_F16,
+                                ctypes.byref(four))
+    # tickets padded to 256 B, then splits x 16 rows x (D + 2) floats per (b, kv head, tile)
+    assert n == 256 + 2 * 2 * 16 * 130 * 4
+    assert L.qsdpa_workspace_bytes(1, 3, 1, 128, 64, ctypes.byref(kp), _lib.QKV_F16, None) == 0

@@ -1,0 +1,215 @@
+"""GPU parity of qsdpa_decode / qsdpa_prefill against the oracle on the same
+seeded inputs: |gpu - ref| <= 2e-3 + 1e-2 |ref| element-wise, where ref is
+the oracle's fp64 attention over its own dequantized packs."""
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import quantized_kv_cache_amd as qkv
+from tests._cases import (W, assert_close, assert_pack_equal, oracle_attention, oracle_pack,
+                          orc, pack_numpy, to_dev)
+
+pytestmark = pytest.mark.gpu
+
+
+def _seed(*a):
+    return zlib.crc32(repr(a).encode()) % 100000
+
+
+def _case(dtype, mode, bits, gs, B, Hq, Hk, Lq, L, D, dist="normal", Lcap=None):
+    s = _seed(dtype, mode, bits, gs, B, Hq, Hk, Lq, L, D)
+    q = W.random_case(s, (B, Hq, Lq, D), dist, dtype)
+    k = W.random_case(s + 1, (B, Hk, Lcap or L, D), dist, dtype)
+    v = W.random_case(s + 2, (B, Hk, Lcap or L, D), dist, dtype)
+    kp = qkv.qkv_quantize(to_dev(k, dtype), mode, bits, gs)
+    vp = qkv.qkv_quantize(to_dev(v, dtype), mode, bits, gs)
+    kr, vr = oracle_pack(k, dtype, mode, bits, gs), oracle_pack(v, dtype, mode, bits, gs)
+    assert_pack_equal(pack_numpy(kp), kr)
+    assert_pack_equal(pack_numpy(vp), vr)
+    return q, kp, vp, kr, vr
+
+
+DECODE_CASES = [
+    # dtype, mode, bits, gs, B, Hq, Hk, L, D
+    ("f32", "affine", 8, 64, 1, 4, 1, 256, 64),
+    ("f32", "affine", 4, 32, 2, 6, 3, 77, 128),
+    ("f16", "affine", 4, 64, 1, 32, 8, 1000, 128),
+    ("f16", "affine", 8, 64, 2, 8, 2, 333, 128),
+    ("f16", "affine", 4, 128, 1, 16, 16, 65, 128),
+    ("f16", "q8_0", 8, 32, 1, 32, 2, 700, 256),
+    ("f16", "q8_0", 8, 32, 2, 4, 4, 129, 64),
+    ("bf16", "affine", 4, 64, 1, 8, 2, 300, 256),
+    ("bf16", "q8_0", 8, 32, 1, 8, 1, 95, 128),
+    ("f16", "affine", 8, 32, 1, 2, 1, 1, 64),          # a single key
+]
+
+
+@pytest.mark.parametrize("algo", ["generic", "auto"])
+@pytest.mark.parametrize("case", DECODE_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_decode_small(case, algo):
+    dtype, mode, bits, gs, B, Hq, Hk, L, D = case
+    q, kp, vp, kr, vr = _case(dtype, mode, bits, gs, B, Hq, Hk, 1, L, D)
+    scale = 1.0 / np.sqrt(D)
+    out = qkv.qsdpa_decode(to_dev(q, dtype), kp, vp, L, scale, algo=algo)
+    ref = oracle_attention(q, dtype, kr, vr, L, mode, bits, gs, scale)
+    assert_close(out, ref, f"decode {case} {algo}")
+
+
+@pytest.mark.parametrize("splits", [1, 2, 7, 64, 512])
+def test_decode_split_count_invariance(splits):
+    """Any number of key splits (including 1 and odd counts) gives the
+    oracle's result; the merge ticket returns to zero between calls."""
+    dtype, mode, bits, gs = "f16", "affine", 4, 64
+    q, kp, vp, kr, vr = _case(dtype, mode, bits, gs, 1, 8, 2, 1, 4097, 128, dist="uniform")
+    ref = oracle_attention(q, dtype, kr, vr, 4097, mode, bits, gs, 1.0)
+    qd = to_dev(q, dtype)
+    ws = qkv.Workspace()
+    for algo in ("generic", "auto"):
+        for _ in range(3):
+            out = qkv.qsdpa_decode(qd, kp, vp, 4097, 1.0, num_splits=splits, algo=algo,
+                                   workspace=ws)
+            assert_close(out, ref, f"splits={splits} {algo}")
+
+
+def test_decode_attends_only_first_L_rows():
+    """Rows beyond L (garbage in the cache) never influence the result."""
+    dtype, mode, bits, gs = "f16", "affine", 8, 64
+    q, kp, vp, kr, vr = _case(dtype, mode, bits, gs, 2, 8, 4, 1, 160, 128, Lcap=200)
+    kp.codes[:, :, 160:] = 0x7fffffff
+    vp.scales[:, :, 160:] = 1000.0
+    for L in (1, 100, 160):
+        out = qkv.qsdpa_decode(to_dev(q, dtype), kp, vp, L, 0.1)
+        assert_close(out, oracle_attention(q, dtype, kr, vr, L, mode, bits, gs, 0.1), f"L={L}")
+
+
+@pytest.mark.parametrize("mdt", ["f32", "f16"])
+def test_decode_additive_mask(mdt):
+    dtype, mode, bits, gs = "f16", "q8_0", 8, 32
+    B, Hq, Hk, L, D = 2, 8, 2, 301, 128
+    q, kp, vp, kr, vr = _case(dtype, mode, bits, gs, B, Hq, Hk, 1, L, D)
+    rng = np.random.default_rng(5)
+    mask = (rng.standard_normal((B, Hq, 1, L)) * 2).astype(np.float32)
+    mask[rng.random(mask.shape) < 0.3] = -np.inf
+    mask[1, 3, 0, :] = -np.inf                        # a fully masked row -> zeros
+    mask_dev = to_dev(mask.astype(np.float16) if mdt == "f16" else mask, mdt)
+    out = qkv.qsdpa_decode(to_dev(q, dtype), kp, vp, L, 0.125, mask=mask_dev)
+    mref = mask_dev.float().cpu().numpy()
+    ref = oracle_attention(q, dtype, kr, vr, L, mode, bits, gs, 0.125, mask=mref)
+    assert_close(out, ref, "masked decode")
+    assert torch.all(out[1, 3] == 0)
+    # a broadcast [L] mask
+    m1 = mask_dev[0, 0, 0]
+    out = qkv.qsdpa_decode(to_dev(q, dtype), kp, vp, L, 0.125, mask=m1)
+    ref = oracle_attention(q, dtype, kr, vr, L, mode, bits, gs, 0.125,
+                           mask=m1.float().cpu().numpy()[None, None, None])
+    assert_close(out, ref, "broadcast mask")
+
+
+PREFILL_CASES = [
+    # dtype, mode, bits, gs, B, Hq, Hk, Lq, L, D, causal
+    ("f16", "q8_0", 8, 32, 1, 32, 2, 40, 300, 256, True),
+    ("f16", "q8_0", 8, 32, 1, 8, 2, 17, 17, 128, True),
+    ("f16", "affine", 4, 64, 2, 8, 2, 5, 90, 128, False),
+    ("f32", "affine", 8, 32, 1, 4, 1, 33, 64, 64, True),
+    ("bf16", "q8_0", 8, 32, 1, 4, 2, 9, 70, 256, True),
+    ("f16", "affine", 8, 64, 1, 4, 4, 70, 200, 128, True),
+]
+
+
+@pytest.mark.parametrize("algo", ["generic", "auto"])
+@pytest.mark.parametrize("case", PREFILL_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_prefill_small(case, algo):
+    dtype, mode, bits, gs, B, Hq, Hk, Lq, L, D, causal = case
+    q, kp, vp, kr, vr = _case(dtype, mode, bits, gs, B, Hq, Hk, Lq, L, D)
+    scale = 1.0 / np.sqrt(D)
+    out = qkv.qsdpa_prefill(to_dev(q, dtype), kp, vp, L, scale, causal=causal, algo=algo)
+    ref = oracle_attention(q, dtype, kr, vr, L, mode, bits, gs, scale, causal=causal)
+    assert_close(out, ref, f"prefill {case} {algo}")
+
+
+def test_prefill_additive_mask_and_single_query_equals_decode():
+    dtype, mode, bits, gs = "f16", "affine", 4, 32
+    B, Hq, Hk, Lq, L, D = 1, 4, 2, 6, 50, 64
+    q, kp, vp, kr, vr = _case(dtype, mode, bits, gs, B, Hq, Hk, Lq, L, D)
+    mask = np.random.default_rng(3).standard_normal((B, Hq, Lq, L)).astype(np.float32)
+    mask[0, 1, 2, ::3] = -np.inf
+    out = qkv.qsdpa_prefill(to_dev(q, dtype), kp, vp, L, 0.3, mask=to_dev(mask, "f32"))
+    assert_close(out, oracle_attention(q, dtype, kr, vr, L, mode, bits, gs, 0.3, mask=mask),
+                 "prefill additive")
+    q1 = to_dev(q[:, :, :1].copy(), dtype)
+    a = qkv.qsdpa_prefill(q1, kp, vp, L, 0.3)
+    b = qkv.qsdpa_decode(q1, kp, vp, L, 0.3)
+    assert_close(a, b.double().cpu().numpy(), "Lq=1 prefill vs decode")
+
+
+# ------------------------------------------------------------------ full-size workloads
+def _workload_packs(w, L=None):
+    inp = W.make_inputs(w, L=L)
+    kp = qkv.qkv_quantize(to_dev(inp["k"], w.dtype), w.mode, w.bits, w.group_size,
+                          L_cap=w.cap if L is None else None)
+    vp = qkv.qkv_quantize(to_dev(inp["v"], w.dtype), w.mode, w.bits, w.group_size,
+                          L_cap=w.cap if L is None else None)
+    kr = oracle_pack(inp["k"], w.dtype, w.mode, w.bits, w.group_size)
+    vr = oracle_pack(inp["v"], w.dtype, w.mode, w.bits, w.group_size)
+    return inp, kp, vp, kr, vr
+
+
+@pytest.mark.parametrize("name", ["tiny_decode", "decode_64k_4bit_gqa4", "q8_0_decode_gqa16"])
+def test_decode_workload_full(name):
+    w = W.WORKLOADS[name]
+    print(f"[decode] {name}", flush=True)
+    inp, kp, vp, kr, vr = _workload_packs(w)
+    out = qkv.qsdpa_decode(to_dev(inp["q"], w.dtype), kp, vp, w.L, w.scale)
+    ref = oracle_attention(inp["q"], w.dtype, kr, vr, w.L, w.mode, w.bits, w.group_size, w.scale)
+    assert_close(out, ref, name)
+
+
+def test_append_decode_workload_steps():
+    """The batched append+decode workload at full size for its first and a
+    later step (B=8, Hq=32, Hk=8, D=128, cache 16384 + t, 8-bit)."""
+    w = W.WORKLOADS["append_decode_b8_8bit"]
+    print("[append+decode] full size", flush=True)
+    inp = W.make_inputs(w)
+    rng = inp["rng"]
+    kp = qkv.empty_pack(w.B, w.Hk, w.cap, w.D, w.mode, w.bits, w.group_size, torch.float16)
+    vp = qkv.empty_pack(w.B, w.Hk, w.cap, w.D, w.mode, w.bits, w.group_size, torch.float16)
+    qkv.qkv_quantize(to_dev(inp["k"], "f16"), out=kp)
+    qkv.qkv_quantize(to_dev(inp["v"], "f16"), out=vp)
+    kr = oracle_pack(inp["k"], "f16", w.mode, w.bits, w.group_size)
+    vr = oracle_pack(inp["v"], "f16", w.mode, w.bits, w.group_size)
+    for t in range(3):
+        s = W.append_step_inputs(w, rng)
+        qkv.qkv_update_append(kp, vp, to_dev(s["k_new"], "f16"), to_dev(s["v_new"], "f16"),
+                              w.L + t)
+        kr = {k: np.concatenate([a, b], axis=2) for (k, a), b in
+              zip(kr.items(), oracle_pack(s["k_new"], "f16", w.mode, w.bits, w.group_size).values())}
+        vr = {k: np.concatenate([a, b], axis=2) for (k, a), b in
+              zip(vr.items(), oracle_pack(s["v_new"], "f16", w.mode, w.bits, w.group_size).values())}
+        L = w.L + t + 1
+        out = qkv.qsdpa_decode(to_dev(s["q"], "f16"), kp, vp, L, w.scale)
+        if t in (0, 2):
+            ref = oracle_attention(s["q"], "f16", kr, vr, L, w.mode, w.bits, w.group_size, w.scale)
+            assert_close(out, ref, f"step {t}")
+
+
+def test_prefill_workload_sampled_rows():
+    """The 512-query causal prefill at full size (L=20480, GQA-16, D=256,
+    Q8_0), checked on sampled query positions that the oracle computes one by
+    one with the bottom-right causal rule written as an explicit mask."""
+    w = W.WORKLOADS["q8_0_prefill_512"]
+    print("[prefill] full size", flush=True)
+    inp, kp, vp, kr, vr = _workload_packs(w)
+    out = qkv.qsdpa_prefill(to_dev(inp["q"], w.dtype), kp, vp, w.L, w.scale, causal=True)
+    idx = np.array([0, 1, 7, 100, 255, 256, 300, 459, 510, 511])
+    qs = np.ascontiguousarray(inp["q"][:, :, idx])
+    j = np.arange(w.L)[None, :]
+    mask = np.where(j > (w.L - w.Lq + idx)[:, None], -np.inf, 0.0).astype(np.float32)
+    ref = oracle_attention(qs, w.dtype, kr, vr, w.L, w.mode, w.bits, w.group_size, w.scale,
+                           mask=mask[None, None])
+    assert_close(out[:, :, idx], ref, "prefill sampled rows")
+    # rows of the last query equal a decode of that query over every key
+    dec = qkv.qsdpa_decode(to_dev(np.ascontiguousarray(inp["q"][:, :, -1:]), w.dtype), kp, vp,
+                           w.L, w.scale)
+    assert_close(out[:, :, -1:], dec.double().cpu().numpy(), "last row vs decode")

@@ -1,0 +1,109 @@
+"""GPU parity of qkv_quantize and qkv_update_append: packed codes, scales and
+biases must equal the oracle's bit for bit."""
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import quantized_kv_cache_amd as qkv
+from tests._cases import (W, assert_pack_equal, oracle_pack, pack_numpy, to_dev)
+
+pytestmark = pytest.mark.gpu
+
+FORMATS = [("affine", 4, 32), ("affine", 4, 64), ("affine", 4, 128), ("affine", 8, 32),
+           ("affine", 8, 64), ("affine", 8, 128), ("q8_0", 8, 32)]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("mode,bits,gs", FORMATS)
+@pytest.mark.parametrize("D", [64, 128, 256])
+def test_quantize_fuzz_bitexact(dtype, mode, bits, gs, D):
+    if mode == "affine" and D % gs:
+        pytest.skip("group does not divide D")
+    seed = zlib.crc32(f"{dtype}{mode}{bits}{gs}{D}".encode()) % 10000
+    x = W.random_case(seed, (2, 3, 37, D), "normal" if seed % 2 else "uniform", dtype)
+    x[0, 0, 3] = x[0, 0, 3, 0]                  # a constant row (eps scale)
+    x[1, 2, 5, :32] = 0                         # a zero block
+    pk = qkv.qkv_quantize(to_dev(x, dtype), mode, bits, gs)
+    assert_pack_equal(pack_numpy(pk), oracle_pack(x, dtype, mode, bits, gs))
+
+
+@pytest.mark.parametrize("name", list(W.WORKLOADS))
+def test_quantize_workload_bitexact(name):
+    w = W.WORKLOADS[name]
+    inp = W.make_inputs(w)
+    print(f"[quantize] {name} K,V {inp['k'].shape} {w.dtype}", flush=True)
+    for t in ("k", "v"):
+        pk = qkv.qkv_quantize(to_dev(inp[t], w.dtype), w.mode, w.bits, w.group_size)
+        assert_pack_equal(pack_numpy(pk), oracle_pack(inp[t], w.dtype, w.mode, w.bits,
+                                                      w.group_size))
+        del pk
+        torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("mode,bits,gs", [("affine", 4, 64), ("affine", 8, 64), ("q8_0", 8, 32)])
+def test_quantize_strided_source_and_pack(mode, bits, gs):
+    """A non-contiguous source (every other token) into a pack laid out as
+    [B, L_cap, H] rows viewed as [B, H, L_cap]."""
+    B, H, L, D = 2, 4, 24, 128
+    full = W.random_case(9, (B, H, 2 * L, D), "normal", "f16")
+    xs = full[:, :, ::2]
+    xt = to_dev(full, "f16")[:, :, ::2]
+    dense = qkv.empty_pack(B, L, H, D, mode, bits, gs, torch.float16)   # [B, L, H, .]
+    perm = qkv.Pack(mode, bits, gs, D, dense.codes.transpose(1, 2), dense.scales.transpose(1, 2),
+                    None if dense.biases is None else dense.biases.transpose(1, 2))
+    qkv.qkv_quantize(xt, out=perm)
+    assert_pack_equal(pack_numpy(perm), oracle_pack(np.ascontiguousarray(xs), "f16", mode, bits, gs))
+
+
+@pytest.mark.parametrize("mode,bits,gs", [("affine", 4, 64), ("affine", 8, 32), ("q8_0", 8, 32)])
+@pytest.mark.parametrize("T,offset", [(1, 0), (1, 40), (3, 17), (48, 0)])
+def test_append_bitexact_untouched_rows(mode, bits, gs, T, offset):
+    B, H, Lcap, D = 2, 3, 48, 128
+    base = W.random_case(21, (B, H, Lcap, D), "normal", "f16")
+    new = W.random_case(22, (2, B, H, T, D), "normal", "f16")
+    kc = qkv.qkv_quantize(to_dev(base, "f16"), mode, bits, gs)
+    vc = qkv.qkv_quantize(to_dev(base[:, :, ::-1].copy(), "f16"), mode, bits, gs)
+    k_before, v_before = pack_numpy(kc), pack_numpy(vc)
+    qkv.qkv_update_append(kc, vc, to_dev(new[0], "f16"), to_dev(new[1], "f16"), offset)
+    kref = oracle_pack(new[0], "f16", mode, bits, gs)
+    vref = oracle_pack(new[1], "f16", mode, bits, gs)
+    rows = slice(offset, offset + T)
+    k_after, v_after = pack_numpy(kc), pack_numpy(vc)
+    assert_pack_equal({k: None if a is None else a[:, :, rows] for k, a in k_after.items()}, kref)
+    assert_pack_equal({k: None if a is None else a[:, :, rows] for k, a in v_after.items()}, vref)
+    others = np.r_[0:offset, offset + T:Lcap]
+    assert_pack_equal(k_after, k_before, rows=others)
+    assert_pack_equal(v_after, v_before, rows=others)
+
+
+def test_append_workload_steps():
+    """The batched append workload: a few steps of appending one token per
+    sequence at rows 16384 + t (B=8, Hk=8, D=128, 8-bit, group 64)."""
+    w = W.WORKLOADS["append_decode_b8_8bit"]
+    B, Hk, D = w.B, w.Hk, w.D
+    kc = qkv.empty_pack(B, Hk, w.cap, D, w.mode, w.bits, w.group_size, torch.float16)
+    vc = qkv.empty_pack(B, Hk, w.cap, D, w.mode, w.bits, w.group_size, torch.float16)
+    rng = np.random.default_rng(w.seed)
+    for t in range(4):
+        s = W.append_step_inputs(w, rng)
+        qkv.qkv_update_append(kc, vc, to_dev(s["k_new"], "f16"), to_dev(s["v_new"], "f16"),
+                              w.L + t)
+        got_k = {k: None if a is None else a[:, :, w.L + t:w.L + t + 1]
+                 for k, a in pack_numpy(kc).items()}
+        got_v = {k: None if a is None else a[:, :, w.L + t:w.L + t + 1]
+                 for k, a in pack_numpy(vc).items()}
+        assert_pack_equal(got_k, oracle_pack(s["k_new"], "f16", w.mode, w.bits, w.group_size))
+        assert_pack_equal(got_v, oracle_pack(s["v_new"], "f16", w.mode, w.bits, w.group_size))
+
+
+def test_quantize_rejects_bad_arguments():
+    x = torch.zeros((1, 1, 8, 128), dtype=torch.float16, device="cuda")
+    pk = qkv.empty_pack(1, 1, 4, 128)
+    with pytest.raises(qkv.QKVError, match="QKV_EINVAL"):
+        qkv.qkv_quantize(x, out=pk)           # L=8 > L_cap=4
+    before = pack_numpy(pk)
+    with pytest.raises(qkv.QKVError):
+        qkv.qkv_update_append(pk, pk, x[:, :, :2], x[:, :, :2], 3)   # rows 3..5 > cap
+    assert_pack_equal(pack_numpy(pk), before)
