@@ -119,12 +119,30 @@ qkv_status qkv_update_append(const void* k_new, const void* v_new, int32_t dtype
                              const qkv_pack* k_cache, const qkv_pack* v_cache, void* stream);
 
 /* Bytes of workspace the attention calls need for these sizes (0 when no
- * partitioning is used).  The workspace must be zero-filled before its first
- * use; every call returns its counters to zero when it completes, so a
- * workspace can be reused by later calls on the same stream.  Calls that may
- * overlap (different streams) need separate workspaces. */
+ * key partitioning is used): per row tile and split, the partial softmax
+ * state (m, l) and an unnormalised output row.  The workspace needs no
+ * initialisation; a call writes it with its first kernel and reads it with
+ * the split merge kernel it launches next on the same stream.  Calls that may
+ * overlap (different streams) need separate workspaces.  It must be 256-byte
+ * aligned. */
 size_t qsdpa_workspace_bytes(int64_t B, int64_t Hq, int64_t Lq, int64_t D, int64_t L,
                              const qkv_pack* k, int32_t q_dtype, const qkv_attn_opts* opts);
+
+/* The launch plan an attention call with these arguments would use:
+ * the kernel (QKV_ALGO_GENERIC or QKV_ALGO_MATRIX), the key splits, the rows
+ * per tile and the workspace size.  Errors: EINVAL for null pointers or
+ * shapes that the attention calls would reject as such. */
+typedef struct {
+    int32_t algo;
+    int32_t num_splits;
+    int32_t row_tile;
+    int32_t reserved;
+    int64_t keys_per_split;
+    size_t workspace_bytes;
+} qkv_attn_plan;
+
+qkv_status qsdpa_plan(int64_t B, int64_t Hq, int64_t Lq, int64_t D, int64_t L, const qkv_pack* k,
+                      int32_t q_dtype, const qkv_attn_opts* opts, qkv_attn_plan* plan);
 
 /* Decode: q, out [B,Hq,1,D] contiguous in q_dtype; attends keys [0, L) of
  * the packs (L <= L_cap); query head h uses kv head h / (Hq/Hk).

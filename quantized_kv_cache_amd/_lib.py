@@ -16,8 +16,8 @@ QKV_MASK_NONE, QKV_MASK_CAUSAL, QKV_MASK_ADDITIVE = 0, 1, 2
 QKV_ALGO_AUTO, QKV_ALGO_GENERIC, QKV_ALGO_MATRIX = 0, 1, 2
 
 # every symbol include/qkv.h declares
-EXPORTS = ["qkv_quantize", "qkv_update_append", "qsdpa_workspace_bytes", "qsdpa_decode",
-           "qsdpa_prefill", "qkv_last_error", "qkv_abi_version"]
+EXPORTS = ["qkv_quantize", "qkv_update_append", "qsdpa_workspace_bytes", "qsdpa_plan",
+           "qsdpa_decode", "qsdpa_prefill", "qkv_last_error", "qkv_abi_version"]
 
 
 class QkvPack(ctypes.Structure):
@@ -33,6 +33,12 @@ class QkvPack(ctypes.Structure):
 
 class QkvAttnOpts(ctypes.Structure):
     _fields_ = [("num_splits", ctypes.c_int32), ("algo", ctypes.c_int32)]
+
+
+class QkvAttnPlan(ctypes.Structure):
+    _fields_ = [("algo", ctypes.c_int32), ("num_splits", ctypes.c_int32),
+                ("row_tile", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("keys_per_split", ctypes.c_int64), ("workspace_bytes", ctypes.c_size_t)]
 
 
 class QKVError(RuntimeError):
@@ -63,6 +69,8 @@ def load():
     L.qkv_update_append.restype = I32
     L.qsdpa_workspace_bytes.argtypes = [I64, I64, I64, I64, I64, PK, I32, OP]
     L.qsdpa_workspace_bytes.restype = SZ
+    L.qsdpa_plan.argtypes = [I64, I64, I64, I64, I64, PK, I32, OP, ctypes.POINTER(QkvAttnPlan)]
+    L.qsdpa_plan.restype = I32
     L.qsdpa_decode.argtypes = [P, I32, I64, I64, I64, PK, PK, I64, ctypes.c_float, P, I32, I64P,
                                P, P, SZ, OP, P]
     L.qsdpa_decode.restype = I32

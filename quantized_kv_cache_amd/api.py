@@ -7,7 +7,7 @@ kernels behind the C ABI; there is no CPU path.
 
 The function names are those of the C ABI (include/qkv.h):
 ``qkv_quantize``, ``qkv_update_append``, ``qsdpa_workspace_bytes``,
-``qsdpa_decode``, ``qsdpa_prefill``.
+``qsdpa_plan``, ``qsdpa_decode``, ``qsdpa_prefill``.
 """
 from __future__ import annotations
 
@@ -152,10 +152,22 @@ def qsdpa_workspace_bytes(q: torch.Tensor, k: Pack, L: int, num_splits: int = 0,
                                                  _dt(q), ctypes.byref(_opts(num_splits, algo))))
 
 
+def qsdpa_plan(q: torch.Tensor, k: Pack, L: int, num_splits: int = 0,
+               algo: str = "auto") -> dict:
+    """The launch plan of an attention call: kernel, splits, row tile, workspace."""
+    B, Hq, Lq, D = q.shape
+    pl = _lib.QkvAttnPlan()
+    st = _lib.load().qsdpa_plan(B, Hq, Lq, D, L, ctypes.byref(k.c_struct()), _dt(q),
+                                ctypes.byref(_opts(num_splits, algo)), ctypes.byref(pl))
+    _lib.check(st)
+    return {"algo": {1: "generic", 2: "matrix"}[pl.algo], "num_splits": pl.num_splits,
+            "row_tile": pl.row_tile, "keys_per_split": pl.keys_per_split,
+            "workspace_bytes": pl.workspace_bytes}
+
+
 class Workspace:
-    """Zero-initialised, reusable attention workspace (grows on demand).  The
-    kernels return its counters to zero after each call, so it stays valid
-    for later calls on the same stream."""
+    """Reusable attention workspace (grows on demand), one buffer per device,
+    for calls on one stream."""
 
     def __init__(self):
         self._buf: dict[torch.device, torch.Tensor] = {}
@@ -166,7 +178,7 @@ class Workspace:
         device = torch.device(device)
         buf = self._buf.get(device)
         if buf is None or buf.numel() < nbytes:
-            buf = torch.zeros(((nbytes + 255) // 256) * 256, dtype=torch.uint8, device=device)
+            buf = torch.empty(((nbytes + 255) // 256) * 256, dtype=torch.uint8, device=device)
             self._buf[device] = buf
         return buf
 
@@ -232,3 +244,34 @@ def qsdpa_prefill(q: torch.Tensor, k: Pack, v: Pack, L: int, scale: float, causa
                                    ctypes.byref(_opts(num_splits, algo)), _stream(q.device))
     _lib.check(st)
     return out
+
+
+class PreparedDecode:
+    """A qsdpa_decode call with its arguments marshalled once.
+
+    Calling the object re-issues the same launch (same tensors, same stream)
+    with only the ctypes call on the host path -- the form a serving loop or
+    a benchmark uses.  The tensors must stay alive and keep their storage."""
+
+    def __init__(self, q: torch.Tensor, k: Pack, v: Pack, L: int, scale: float,
+                 out: torch.Tensor, mask: torch.Tensor | None = None, num_splits: int = 0,
+                 algo: str = "auto", workspace: Workspace | None = None):
+        B, Hq, Lq, D = q.shape
+        if Lq != 1 or not q.is_contiguous() or out.shape != q.shape:
+            raise ValueError("decode takes contiguous q, out of shape [B,Hq,1,D]")
+        buf, nbytes = _attn_common(q, k, v, num_splits, algo, workspace, L)
+        mp, mdt, ms = _mask_args(mask, (B, Hq, 1, L))
+        self._keep = (q, k, v, out, buf, mask)
+        self._kc, self._vc = k.c_struct(), v.c_struct()
+        self._opts = _opts(num_splits, algo)
+        self._fn = _lib.load().qsdpa_decode
+        self._args = (_ptr(q), _dt(q), B, Hq, D, ctypes.byref(self._kc), ctypes.byref(self._vc),
+                      L, float(scale), mp, mdt, ms, _ptr(out), _ptr(buf), nbytes,
+                      ctypes.byref(self._opts), _stream(q.device))
+        self.out = out
+
+    def __call__(self) -> torch.Tensor:
+        st = self._fn(*self._args)
+        if st:
+            _lib.check(st)
+        return self.out

@@ -12,6 +12,7 @@
 
 #include "../../include/qkv.h"
 #include "qkv_internal.hpp"
+#include "qkv_merge.hpp"
 
 namespace {
 
@@ -144,21 +145,18 @@ struct Plan {
     size_t ws_bytes;
 };
 
-constexpr size_t kTicketAlign = 256;
-
 size_t ws_for(int64_t B, int64_t Hk, int n_rt, int S, int RT, int64_t D) {
     if (S <= 1) return 0;
-    size_t tickets = (size_t)(B * Hk * n_rt) * 4;
-    tickets = (tickets + kTicketAlign - 1) / kTicketAlign * kTicketAlign;
-    return tickets + (size_t)(B * Hk * n_rt) * (size_t)S * (size_t)RT * (size_t)(D + 2) * 4;
+    return (size_t)(B * Hk * n_rt) * (size_t)S * (size_t)RT * (size_t)(D + 2) * 4;  // ml + o
 }
 
-// Split count: aim for about 2048 workgroups (8 per CU) with at least one
-// 64-key block per split.
-int auto_splits(int64_t base_wgs, int64_t L, int64_t min_keys) {
-    int64_t want = (2048 + base_wgs - 1) / base_wgs;
-    int64_t cap = std::max<int64_t>(1, (L + min_keys - 1) / min_keys);
-    return (int)std::max<int64_t>(1, std::min<int64_t>({want, cap, 1024}));
+// Split count: enough workgroups to cover the CUs about twice, each split at
+// least min_keys long, and at most kMaxSplits (the merge keeps per-split
+// weights in LDS).
+int auto_splits(int64_t base_wgs, int64_t L, int64_t min_keys, int64_t target) {
+    int64_t want = (target + base_wgs - 1) / base_wgs;
+    int64_t cap = std::max<int64_t>(1, L / min_keys);
+    return (int)std::max<int64_t>(1, std::min<int64_t>({want, cap, 256}));
 }
 
 Plan make_plan(int64_t B, int64_t Hq, int64_t Lq, int64_t D, int64_t L, const qkv_pack* k,
@@ -169,14 +167,18 @@ Plan make_plan(int64_t B, int64_t Hq, int64_t Lq, int64_t D, int64_t L, const qk
     const int algo = opts ? opts->algo : QKV_ALGO_AUTO;
     const int bits = k->bits;
     pl.matrix = false;
-    if (algo != QKV_ALGO_GENERIC &&
+    // the matrix kernel addresses a kv head's rows with 32-bit offsets
+    const int64_t span = (k->L_cap - 1) * k->stride_l * row_bytes(k) + row_bytes(k);
+    if (algo != QKV_ALGO_GENERIC && span < (int64_t(1) << 31) &&
         qkv::matrix_supported(q_dtype, k->mode, bits, k->group_size, (int)D, G, Lq))
         pl.matrix = true;
     const int64_t n_rows = (int64_t)G * Lq;
     pl.RT = pl.matrix ? 16 : 16;
     pl.n_rt = (int)((n_rows + pl.RT - 1) / pl.RT);
     const int64_t base = B * Hk * pl.n_rt;
-    int S = (opts && opts->num_splits > 0) ? opts->num_splits : auto_splits(base, L, 64);
+    int S = (opts && opts->num_splits > 0)
+                ? std::min(opts->num_splits, 256)
+                : (pl.matrix ? auto_splits(base, L, 512, 256) : auto_splits(base, L, 256, 512));
     int64_t chunk = (L + S - 1) / S;
     const int64_t gran = pl.matrix ? 64 : 32;
     chunk = (chunk + gran - 1) / gran * gran;
@@ -271,14 +273,13 @@ qkv_status attention(const char* name, const void* q, int32_t q_dtype, int64_t B
     a.n_rt = pl.n_rt;
     a.RT = pl.RT;
     if (pl.ws_bytes > 0) {
-        size_t tickets = (size_t)(B * k->H * pl.n_rt) * 4;
-        tickets = (tickets + kTicketAlign - 1) / kTicketAlign * kTicketAlign;
-        a.tickets = static_cast<uint32_t*>(workspace);
-        a.partials = reinterpret_cast<float*>(static_cast<char*>(workspace) + tickets);
+        a.part_ml = static_cast<float*>(workspace);
+        a.part_o = a.part_ml + (size_t)(B * k->H * pl.n_rt) * (size_t)pl.S * 16 * 2;
     }
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e = pl.matrix ? qkv::launch_attn_matrix(k->mode, k->bits, (int)D, B, a, s)
                              : qkv::launch_attn_generic(q_dtype, k->mode, k->bits, (int)D, B, a, s);
+    if (e == hipSuccess && pl.S > 1) e = qkv::launch_merge(q_dtype, (int)D, B, a, s);
     return hip_status(e, name);
 }
 
@@ -337,6 +338,21 @@ size_t qsdpa_workspace_bytes(int64_t B, int64_t Hq, int64_t Lq, int64_t D, int64
                              const qkv_pack* k, int32_t q_dtype, const qkv_attn_opts* opts) {
     if (!k || k->H < 1 || B < 1 || Hq < 1 || Lq < 1 || L < 1 || Hq % k->H) return 0;
     return make_plan(B, Hq, Lq, D, L, k, q_dtype, opts).ws_bytes;
+}
+
+qkv_status qsdpa_plan(int64_t B, int64_t Hq, int64_t Lq, int64_t D, int64_t L, const qkv_pack* k,
+                      int32_t q_dtype, const qkv_attn_opts* opts, qkv_attn_plan* plan) {
+    if (!k || !plan) return fail(QKV_EINVAL, "qsdpa_plan: null pack or plan");
+    if (k->H < 1 || B < 1 || Hq < 1 || Lq < 1 || L < 1 || Hq % k->H)
+        return fail(QKV_EINVAL, "qsdpa_plan: bad sizes");
+    Plan pl = make_plan(B, Hq, Lq, D, L, k, q_dtype, opts);
+    plan->algo = pl.matrix ? QKV_ALGO_MATRIX : QKV_ALGO_GENERIC;
+    plan->num_splits = pl.S;
+    plan->row_tile = pl.RT;
+    plan->reserved = 0;
+    plan->keys_per_split = pl.chunk;
+    plan->workspace_bytes = pl.ws_bytes;
+    return ok();
 }
 
 qkv_status qsdpa_decode(const void* q, int32_t q_dtype, int64_t B, int64_t Hq, int64_t D,

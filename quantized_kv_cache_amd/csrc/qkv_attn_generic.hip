@@ -18,11 +18,12 @@
 // of 32: scores (8 lanes per key, butterfly sum), an online-softmax update per
 // row, the V block dequantized once into LDS, then o = o*alpha + P V.
 // With several splits each workgroup writes its (m, l, o) state to the
-// workspace and the last one to finish (atomic ticket) merges them with the
-// log-sum-exp rule and writes the output.  This kernel favours generality over
+// workspace and the split merge kernel combines them with the log-sum-exp
+// rule and writes the output.  This kernel favours generality over
 // speed; the matrix-core kernels cover the fp16 hot shapes.
 #include "qkv_device.hpp"
 #include "qkv_internal.hpp"
+#include "qkv_merge.hpp"
 
 namespace qkv {
 
@@ -60,7 +61,6 @@ __global__ __launch_bounds__(256) void attn_generic_kernel(AttnLaunch p) {
     __shared__ float sc[RTG][KB];
     __shared__ float vt[KB][D];
     __shared__ float m_s[RTG], l_s[RTG], a_s[RTG];
-    __shared__ int last_flag;
 
     const int tid = threadIdx.x;
     const int split = blockIdx.x;
@@ -217,43 +217,16 @@ __global__ __launch_bounds__(256) void attn_generic_kernel(AttnLaunch p) {
 
     // ---- partial state -> workspace, then the last workgroup merges
     const int64_t tile = bk * p.n_rt + rt;
-    const int W = D + 2;
-    float* mine = p.partials + ((tile * p.S + split) * RTG + orow) * W;
+    float* ml = p.part_ml + (tile * p.S + split) * RTG * 2;
+    float* po = p.part_o + (tile * p.S + split) * RTG * D;
+    if (row_ok) {
 #pragma unroll
-    for (int i = 0; i < DPO; ++i) mine[2 + ochunk * DPO + i] = o[i];
-    if (ochunk == 0) { mine[0] = m_s[orow]; mine[1] = l_s[orow]; }
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) {
-        const uint32_t prev = atomicAdd(&p.tickets[tile], 1u);
-        last_flag = (prev == (uint32_t)(p.S - 1));
+        for (int i = 0; i < DPO; ++i) po[orow * D + ochunk * DPO + i] = o[i];
     }
-    __syncthreads();
-    if (!last_flag) return;
-    __threadfence();
-    if (tid == 0) p.tickets[tile] = 0u;        // leave the counter ready for the next call
-    if (!row_ok) return;
-    const float* base = p.partials + (tile * p.S * RTG + orow) * W;
-    float M = -INFINITY;
-    for (int s = 0; s < p.S; ++s) M = fmaxf(M, base[(int64_t)s * RTG * W]);
-    float acc[DPO];
-#pragma unroll
-    for (int i = 0; i < DPO; ++i) acc[i] = 0.0f;
-    float den = 0.0f;
-    if (M != -INFINITY) {
-        for (int s = 0; s < p.S; ++s) {
-            const float* ps = base + (int64_t)s * RTG * W;
-            const float ms = ps[0];
-            if (ms == -INFINITY) continue;
-            const float w = fast_exp2((ms - M) * kLog2e);
-            den += w * ps[1];
-#pragma unroll
-            for (int i = 0; i < DPO; ++i) acc[i] += w * ps[2 + ochunk * DPO + i];
-        }
+    if (row_ok && ochunk == 0) {           // the merge works in log2 units
+        ml[2 * orow] = m_s[orow] * kLog2e;
+        ml[2 * orow + 1] = l_s[orow];
     }
-    const float inv = den > 0.0f ? 1.0f / den : 0.0f;
-#pragma unroll
-    for (int i = 0; i < DPO; ++i) store_from_f32<QT>(p.out, obase + i, acc[i] * inv);
 }
 
 template <int QT, int MODE, int BITS, int D>

@@ -1,12 +1,663 @@
-// Matrix-core (MFMA) attention kernels for fp16 queries on gfx950.
+// Matrix-core decode for fp16 queries on gfx950: scaled-dot-product attention
+// of one query per head over a group-quantized KV cache, with both
+// contractions (q K^T and P V) on v_mfma_f32_16x16x32_f16.
+//
+// What is computed follows the MLX page "add fast::quantized_kv_update"
+// (sdpa_vector.h quant_sdpa_vector: scores from packed codes through the
+// per-group factorisation  q . (s c + b) = s (q . c) + b (sum q), online
+// softmax, merge of partial softmax states) and the llama.cpp page "Metal:
+// Optimize q8_0 KV - #25556" (Q8_0 blocks; the query heads of a GQA group
+// share every K/V load).  The kernel design is MI355X-specific:
+//
+//  * One workgroup (8 waves) per (key split, batch x kv head) streams its
+//    chunk of packed K/V exactly once; the G query heads of the kv head are
+//    the 16 rows of the matrix tiles (rows >= G are zero).  Each wave takes
+//    every 8th tile of 32 keys and keeps the next tile's loads in flight.
+//  * q K^T: A = queries [16 heads x 32 d], B = key codes [32 d x 16 keys].
+//    Codes enter the matrix core unconverted: masking a packed word leaves
+//    fp16 subnormals c * 2^-24 (4-bit: the odd nibble of a byte becomes
+//    16 c * 2^-24, compensated by a query pre-divided by 16; Q8_0: the sign
+//    bit is flipped so c + 128 is unsigned).  Each K-step of 32 d lies in one
+//    quantization group, so every group has its own accumulator and the
+//    per-key scale/bias (and the Q8_0 -128 offset) are applied afterwards in
+//    fp32:  z = sum_g s_g * 2^24 * acc_g + b_g * sum_{d in g} q_d.
+//  * The 16x16 score tiles go through a per-wave LDS scratch to the layout
+//    of the P operand: each lane owns one head and 8 keys, so the running
+//    max, the rescale of its accumulators and exp2 are lane-local (the 4
+//    lanes of a head agree after two xor-shuffles).  Rescales happen only
+//    when a tile raises the running max.
+//  * P V, folded form (affine caches with G * groups <= 16): the value codes
+//    also enter as fp16 subnormals; the value scale moves into the P operand,
+//    whose 16 columns are (head, group) pairs: P'[key][(h, g)] = p_h s_g, so
+//    o[h][d] = 2^24 sum_key P'[key][(h, g(d))] c[key][d] + sum_key p_h b_g.
+//    Only the (h, group of d) column of each output row is kept.
+//  * P V, dequantized form (Q8_0 and wide groups): A = V^ [16 d x 32 keys]
+//    (fp16, rounded once by v_pk_fma_f16 / v_pk_mul_f16), B = P [32 keys x
+//    16 heads].
+//  * The waves merge their softmax states through LDS; with several splits
+//    the workgroup writes (m, l, o) to the workspace for the split merge
+//    kernel that runs next on the stream.
+//  * Every cache access is a 32-bit offset from a wave-uniform base (the
+//    host checks that a kv head's rows span less than 2 GiB).
 #include "qkv_device.hpp"
 #include "qkv_internal.hpp"
+#include "qkv_merge.hpp"
 
 namespace qkv {
 
-bool matrix_supported(int, int, int, int, int, int, int64_t) { return false; }
+namespace {
 
-hipError_t launch_attn_matrix(int, int, int, int64_t, const AttnLaunch&, hipStream_t) {
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+
+constexpr int TK = 32;          // keys per tile
+constexpr int NWAVE = 8;
+constexpr int NTHR = NWAVE * 64;
+constexpr int SROW = 36;        // LDS score row stride (floats)
+
+__device__ __forceinline__ uint32_t perm_b(uint32_t hi, uint32_t lo, uint32_t sel) {
+    return __builtin_amdgcn_perm(hi, lo, sel);
+}
+__device__ __forceinline__ h8 to_h8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+    u4 v = {a, b, c, d};
+    return __builtin_bit_cast(h8, v);
+}
+__device__ __forceinline__ h2 as_h2(uint32_t u) { return __builtin_bit_cast(h2, u); }
+__device__ __forceinline__ uint32_t as_u(h2 h) { return __builtin_bit_cast(uint32_t, h); }
+__device__ __forceinline__ float lo_f16(uint32_t u) { return f16_to_f32((uint16_t)(u & 0xffffu)); }
+__device__ __forceinline__ float hi_f16(uint32_t u) { return f16_to_f32((uint16_t)(u >> 16)); }
+
+__device__ __forceinline__ f4 mfma(h8 a, h8 b, f4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+template <typename T>
+__device__ __forceinline__ T ldg(const uint8_t* base, uint32_t off) {
+    return *(const T*)(base + off);
+}
+
+// Format traits -------------------------------------------------------------
+template <int MODE, int BITS, int GS, int D>
+struct Fmt {
+    static constexpr int NG = D / GS;                 // groups per row
+    static constexpr int ROWB = D * BITS / 8;         // code bytes per row
+    static constexpr int STEPS = D / 32;              // K-steps of q K^T
+    static constexpr int SPG = GS / 32;               // K-steps per group
+    static constexpr int KCH = GS / 4 * BITS / 8;     // bytes per lane per group (q K^T)
+    static constexpr int KW = KCH >= 4 ? KCH / 4 : 1;
+    static constexpr int VCODES = D / 16;             // codes per lane per key (P V)
+    static constexpr int VBYTES = VCODES * BITS / 8;
+    static constexpr int VW = VBYTES >= 4 ? VBYTES / 4 : 1;
+    static constexpr int SROWB = NG * 2;              // bytes of one row's scales
+    static constexpr int NSW = NG >= 2 ? NG / 2 : 1;  // dwords holding one row's scales
+};
+
+// Query half order inside one 8-code K-step chunk of a lane, matching the
+// halves produced by unpack_k (position e of the 8 consecutive d values).
+template <int BITS>
+__device__ __forceinline__ int qpos(int h) {
+    if constexpr (BITS == 4) {
+        constexpr int p[8] = {0, 4, 1, 5, 2, 6, 3, 7};
+        return p[h];
+    } else {
+        constexpr int p[8] = {0, 2, 1, 3, 4, 6, 5, 7};
+        return p[h];
+    }
+}
+
+// 8 codes of one key (one K-step chunk) -> B operand halves (fp16 subnormals).
+template <int MODE, int BITS>
+__device__ __forceinline__ h8 unpack_k(const uint32_t* w) {
+    if constexpr (BITS == 4) {
+        const uint32_t x = w[0];
+        const uint32_t t = perm_b(0u, x, 0x0C030C01u);           // bytes 1, 3 -> halves
+        return to_h8(x & 0x000F000Fu, x & 0x00F000F0u, t & 0x000F000Fu, t & 0x00F000F0u);
+    } else {
+        const uint32_t f = (MODE == MODE_Q8_0) ? 0x00800080u : 0u;
+        const uint32_t a0 = (w[0] & 0x00FF00FFu) ^ f;
+        const uint32_t a1 = perm_b(0u, w[0], 0x0C030C01u) ^ f;
+        const uint32_t a2 = (w[1] & 0x00FF00FFu) ^ f;
+        const uint32_t a3 = perm_b(0u, w[1], 0x0C030C01u) ^ f;
+        return to_h8(a0, a1, a2, a3);
+    }
+}
+
+// Byte 'byte' of the chunks of two keys -> [key a byte, 0, key b byte, 0].
+__device__ __forceinline__ uint32_t pair_bytes(const uint32_t* wa, const uint32_t* wb, int byte) {
+    const uint32_t sel = (uint32_t)(byte & 3) | 0x0C00u | ((uint32_t)(4 + (byte & 3)) << 16) |
+                         0x0C000000u;
+    return perm_b(wb[byte >> 2], wa[byte >> 2], sel);
+}
+
+// Code t of the lane's chunk for a pair of keys, as fp16 subnormal halves
+// (4-bit odd codes arrive as 16 c).
+template <int BITS>
+__device__ __forceinline__ uint32_t pair_sub(const uint32_t* wa, const uint32_t* wb, int t) {
+    if constexpr (BITS == 4) {
+        const uint32_t x = pair_bytes(wa, wb, t >> 1);
+        return (t & 1) ? (x & 0x00F000F0u) : (x & 0x000F000Fu);
+    } else {
+        return pair_bytes(wa, wb, t);
+    }
+}
+
+// Code t for a pair of keys as (1024 + c) halves (dequantized form).
+template <int MODE, int BITS>
+__device__ __forceinline__ uint32_t pair_int(const uint32_t* wa, const uint32_t* wb, int t) {
+    if constexpr (BITS == 4) {
+        return pair_sub<4>(wa, wb, t) | 0x64006400u;
+    } else {
+        uint32_t x = pair_bytes(wa, wb, t);
+        if constexpr (MODE == MODE_Q8_0) x ^= 0x00800080u;
+        return x | 0x64006400u;
+    }
+}
+
+// Compiler-only ordering of the per-wave LDS scratch: LDS instructions of one
+// wave execute in order, so no wait on outstanding global loads is needed.
+__device__ __forceinline__ void lds_order() { __asm__ __volatile__("" ::: "memory"); }
+
+template <int MODE, int BITS, int GS, int D, bool MASK, bool FOLD>
+__global__ __launch_bounds__(NTHR) void attn_matrix_decode(AttnLaunch p) {
+    using F = Fmt<MODE, BITS, GS, D>;
+    constexpr int NG = F::NG;
+    constexpr int STEPS = F::STEPS;
+    constexpr int NT = D / 16;                    // P V tiles (16 d each)
+    constexpr int KW = F::KW;
+    constexpr int VW = F::VW;
+    constexpr int NSW = F::NSW;
+    static_assert(!FOLD || (MODE == MODE_AFFINE && NG <= 2), "folded P V needs <= 2 groups");
+
+    __shared__ float s_scores[NWAVE][16 * SROW];
+    __shared__ float s_qsum[16][NG];
+    __shared__ float s_ml[NWAVE][2][16];
+    __shared__ float s_bias[NWAVE][16][2];
+    __shared__ float s_o[64 * (D / 4)];
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
+    const int lane = tid & 63;
+    const int n = lane & 15;          // A/B row or column index
+    const int kb = lane >> 4;         // K-block of the lane (0..3)
+    const int split = blockIdx.x;
+    const int64_t bk = blockIdx.z;
+    const int64_t b = bk / p.Hk;
+    const int64_t kvh = bk % p.Hk;
+    const int G = p.G;
+    const float sl = p.scale * kLog2e;            // scores kept in log2 units
+
+    // ---------------------------------------------------------------- queries
+    // A operand of q K^T for every K-step, and per-(head, group) sums of q.
+    h8 qa[STEPS];
+    {
+        const uint16_t* qrow = (const uint16_t*)p.q + ((b * p.Hq + kvh * G + n) * D);
+        float part[NG];
+#pragma unroll
+        for (int g = 0; g < NG; ++g) part[g] = 0.0f;
+#pragma unroll
+        for (int st = 0; st < STEPS; ++st) {
+            const int g = st / F::SPG, u = st % F::SPG;
+            const int d0 = g * GS + kb * (GS / 4) + 8 * u;
+            uint32_t w[4];
+#pragma unroll
+            for (int hh = 0; hh < 4; ++hh) {
+                uint16_t lo = 0, hi = 0;
+                if (n < G) {
+                    const int e0 = qpos<BITS>(2 * hh), e1 = qpos<BITS>(2 * hh + 1);
+                    _Float16 v0 = __builtin_bit_cast(_Float16, qrow[d0 + e0]);
+                    _Float16 v1 = __builtin_bit_cast(_Float16, qrow[d0 + e1]);
+                    part[g] += (float)v0 + (float)v1;
+                    if constexpr (BITS == 4) {       // odd nibbles arrive as 16 c
+                        if (hh & 1) { v0 = v0 * (_Float16)0.0625f; v1 = v1 * (_Float16)0.0625f; }
+                    }
+                    lo = __builtin_bit_cast(uint16_t, v0);
+                    hi = __builtin_bit_cast(uint16_t, v1);
+                }
+                w[hh] = (uint32_t)lo | ((uint32_t)hi << 16);
+            }
+            qa[st] = to_h8(w[0], w[1], w[2], w[3]);
+        }
+#pragma unroll
+        for (int g = 0; g < NG; ++g) {
+            float s = part[g];
+            s += __shfl_xor(s, 16, 64);
+            s += __shfl_xor(s, 32, 64);
+            if (wave == 0 && kb == 0) s_qsum[n][g] = s * sl;
+        }
+    }
+    __syncthreads();
+    float qs[4][NG];                    // (scale log2e) sum q of output rows 4kb + j
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int g = 0; g < NG; ++g) qs[j][g] = s_qsum[4 * kb + j][g];
+
+    // ---------------------------------------------------------------- key range
+    const int64_t j0 = (int64_t)split * p.chunk;
+    const int64_t j1 = min(p.L, j0 + p.chunk);
+    const int ntiles = (int)((j1 - j0 + TK - 1) / TK);
+
+    // wave-uniform bases of this (batch, kv head); rows are 32-bit offsets
+    const int64_t krow0 = b * p.k.sb + kvh * p.k.sh;
+    const int64_t vrow0 = b * p.v.sb + kvh * p.v.sh;
+    const uint8_t* kc = (const uint8_t*)p.k.codes + krow0 * F::ROWB;
+    const uint8_t* vc = (const uint8_t*)p.v.codes + vrow0 * F::ROWB;
+    const uint8_t* ksc = (const uint8_t*)p.k.scales + krow0 * F::SROWB;
+    const uint8_t* kbi = (const uint8_t*)p.k.biases + krow0 * F::SROWB;
+    const uint8_t* vsc = (const uint8_t*)p.v.scales + vrow0 * F::SROWB;
+    const uint8_t* vbi = (const uint8_t*)p.v.biases + vrow0 * F::SROWB;
+    const uint32_t kcs = (uint32_t)(p.k.sl * F::ROWB), vcs = (uint32_t)(p.v.sl * F::ROWB);
+    const uint32_t kss = (uint32_t)(p.k.sl * F::SROWB), vss = (uint32_t)(p.v.sl * F::SROWB);
+    const uint32_t jmax = (uint32_t)(j1 - 1);
+
+    // folded P V: this lane's P' column is (head ch, group cg)
+    const int ch = FOLD ? n % G : n;
+    const int cg = FOLD ? n / G : 0;
+    const bool cvalid = FOLD ? (n < G * NG) : true;
+    const int vg = (F::VCODES * n) / GS;          // group of the lane's dequantized P V chunk
+
+    // Registers of one tile.  Only loads write them; every use waits in
+    // process(), so the loads of the next tile stay in flight meanwhile.
+    struct Tile {
+        uint32_t kw[2][NG][KW];       // q K^T codes: key (16 hf + n), per group
+        uint32_t ks[2][NSW];          // key scales (fp16)
+        uint32_t kbias[2][NSW];
+        uint32_t vw[8][VW];           // P V codes: keys 8 kb + e
+        uint32_t vs[8];               // folded: scale row of key 8 kb + e; else the lane's scale
+        uint32_t vb[8];               // folded: bias row of key 8 kb + e (softmax lane); else bias
+    };
+    auto load_scales = [&](const uint8_t* base, uint32_t off, uint32_t* dst) {
+        if constexpr (NG == 1) dst[0] = ldg<uint16_t>(base, off);
+        else if constexpr (NG == 2) dst[0] = ldg<uint32_t>(base, off);
+        else if constexpr (NG == 4) { uint2 x = ldg<uint2>(base, off); dst[0] = x.x; dst[1] = x.y; }
+        else { uint4 x = ldg<uint4>(base, off); dst[0] = x.x; dst[1] = x.y; dst[2] = x.z; dst[3] = x.w; }
+    };
+
+    auto load_tile = [&](int tt, Tile& T) {
+        const uint32_t base = (uint32_t)(j0 + (int64_t)tt * TK);
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+            const uint32_t j = min(base + 16 * hf + n, jmax);
+            const uint32_t off = j * kcs + kb * F::KCH;
+#pragma unroll
+            for (int g = 0; g < NG; ++g) {
+                const uint32_t o = off + g * (GS * BITS / 8);
+                if constexpr (KW == 1) {
+                    T.kw[hf][g][0] = ldg<uint32_t>(kc, o);
+                } else if constexpr (KW == 2) {
+                    uint2 x = ldg<uint2>(kc, o);
+                    T.kw[hf][g][0] = x.x; T.kw[hf][g][1] = x.y;
+                } else {
+#pragma unroll
+                    for (int q4 = 0; q4 < KW; q4 += 4) {
+                        uint4 x = ldg<uint4>(kc, o + 4 * q4);
+                        T.kw[hf][g][q4] = x.x; T.kw[hf][g][q4 + 1] = x.y;
+                        T.kw[hf][g][q4 + 2] = x.z; T.kw[hf][g][q4 + 3] = x.w;
+                    }
+                }
+            }
+            load_scales(ksc, j * kss, T.ks[hf]);
+            if constexpr (MODE == MODE_AFFINE) load_scales(kbi, j * kss, T.kbias[hf]);
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const uint32_t j = min(base + 8 * kb + e, jmax);
+            const uint32_t o = j * vcs + n * F::VBYTES;
+            if constexpr (F::VBYTES == 2) {
+                T.vw[e][0] = ldg<uint16_t>(vc, o);
+            } else if constexpr (F::VBYTES == 4) {
+                T.vw[e][0] = ldg<uint32_t>(vc, o);
+            } else if constexpr (F::VBYTES == 8) {
+                uint2 x = ldg<uint2>(vc, o);
+                T.vw[e][0] = x.x; T.vw[e][1] = x.y;
+            } else {
+                uint4 x = ldg<uint4>(vc, o);
+                T.vw[e][0] = x.x; T.vw[e][1] = x.y; T.vw[e][2] = x.z; T.vw[e][3] = x.w;
+            }
+            if constexpr (FOLD) {
+                // scale row (column group cg is picked later) and bias row
+                if constexpr (NG == 1) {
+                    T.vs[e] = ldg<uint16_t>(vsc, j * vss);
+                    T.vb[e] = ldg<uint16_t>(vbi, j * vss);
+                } else {
+                    T.vs[e] = ldg<uint32_t>(vsc, j * vss);
+                    T.vb[e] = ldg<uint32_t>(vbi, j * vss);
+                }
+            } else {
+                T.vs[e] = ldg<uint16_t>(vsc, j * vss + 2 * vg);
+                if constexpr (MODE == MODE_AFFINE) T.vb[e] = ldg<uint16_t>(vbi, j * vss + 2 * vg);
+            }
+        }
+    };
+
+    // ---------------------------------------------------------------- main loop
+    f4 acc_o[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc_o[t] = f4{0.f, 0.f, 0.f, 0.f};
+    float m_run = -INFINITY, l_run = 0.0f;
+    float bsum[2] = {0.0f, 0.0f};     // folded: sum_key p b_g of the softmax head, per group
+    float* sw = s_scores[wave];
+
+    auto process = [&](const Tile& cur, int tt) {
+        const uint32_t base = (uint32_t)(j0 + (int64_t)tt * TK);
+
+        // ---- scores of 2 x 16 keys
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+            float z[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int g = 0; g < NG; ++g) {
+                f4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int u = 0; u < F::SPG; ++u) {
+                    const h8 kbop = unpack_k<MODE, BITS>(&cur.kw[hf][g][u * (BITS == 4 ? 1 : 2)]);
+                    acc = mfma(qa[g * F::SPG + u], kbop, acc);
+                }
+                const uint32_t sw2 = cur.ks[hf][g >> 1];
+                const float s = (g & 1) ? hi_f16(sw2) : lo_f16(sw2);
+                if constexpr (MODE == MODE_AFFINE) {
+                    const uint32_t bw2 = cur.kbias[hf][g >> 1];
+                    const float sc = s * (16777216.0f * sl);
+                    const float bb = (g & 1) ? hi_f16(bw2) : lo_f16(bw2);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) z[j] += sc * acc[j] + bb * qs[j][g];
+                } else {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        z[j] += s * ((16777216.0f * sl) * acc[j] - 128.0f * qs[j][g]);
+                }
+            }
+            const uint32_t j = base + 16 * hf + n;
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                float v = z[jj];
+                if (j > jmax) v = -INFINITY;
+                else if constexpr (MASK) {
+                    const int h = 4 * kb + jj;
+                    if (h < G)
+                        v += kLog2e * load_mask(p.mask, p.mask_dtype,
+                                                b * p.ms0 + (kvh * G + h) * p.ms1 + j * p.ms3);
+                }
+                sw[(4 * kb + jj) * SROW + 16 * hf + n] = v;
+            }
+        }
+        lds_order();
+
+        // ---- online softmax: lane = (head n, keys 8 kb .. 8 kb + 7)
+        float zz[8];
+        {
+            const float4 a = *(const float4*)&sw[n * SROW + 8 * kb];
+            const float4 c = *(const float4*)&sw[n * SROW + 8 * kb + 4];
+            zz[0] = a.x; zz[1] = a.y; zz[2] = a.z; zz[3] = a.w;
+            zz[4] = c.x; zz[5] = c.y; zz[6] = c.z; zz[7] = c.w;
+        }
+        lds_order();
+        float mx = zz[0];
+#pragma unroll
+        for (int e = 1; e < 8; ++e) mx = fmaxf(mx, zz[e]);
+        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        const float m_new = fmaxf(m_run, mx);
+        const bool grow = m_new > m_run;
+        if (__ballot(grow) != 0ull) {
+            const float alpha = grow ? (m_run == -INFINITY ? 0.0f : fast_exp2(m_run - m_new)) : 1.0f;
+            l_run *= alpha;
+            bsum[0] *= alpha;
+            bsum[1] *= alpha;
+            const float ac = FOLD ? __shfl(alpha, ch + 16 * kb, 64) : alpha;
+#pragma unroll
+            for (int t = 0; t < NT; ++t) acc_o[t] *= ac;
+            m_run = m_new;
+        }
+        float pf[8];
+        float ps = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            pf[e] = (m_run == -INFINITY) ? 0.0f : fast_exp2(zz[e] - m_run);
+            ps += pf[e];
+        }
+        l_run += ps;
+
+        if constexpr (FOLD) {
+            // bias sums of the softmax head, per group
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                bsum[0] += pf[e] * lo_f16(cur.vb[e]);
+                if constexpr (NG == 2) bsum[1] += pf[e] * hi_f16(cur.vb[e]);
+            }
+            // P' column (ch, cg): p of head ch (from its softmax lane) times the scale of cg
+            uint32_t pb[4];
+#pragma unroll
+            for (int q2 = 0; q2 < 4; ++q2) {
+                h2 hp = {(_Float16)pf[2 * q2], (_Float16)pf[2 * q2 + 1]};
+                pb[q2] = as_u(hp);
+            }
+            uint32_t pp[4];
+#pragma unroll
+            for (int q2 = 0; q2 < 4; ++q2) {
+                const uint32_t src = (uint32_t)__shfl((int)pb[q2], ch + 16 * kb, 64);
+                const uint32_t sa = cur.vs[2 * q2], sb2 = cur.vs[2 * q2 + 1];
+                const uint32_t spair = (NG == 2 && cg == 1) ? perm_b(sb2, sa, 0x07060302u)
+                                                            : perm_b(sb2, sa, 0x05040100u);
+                pp[q2] = cvalid ? as_u(as_h2(src) * as_h2(spair)) : 0u;
+            }
+            const h8 pop = to_h8(pp[0], pp[1], pp[2], pp[3]);
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                uint32_t a[4];
+#pragma unroll
+                for (int q2 = 0; q2 < 4; ++q2)
+                    a[q2] = pair_sub<BITS>(cur.vw[2 * q2], cur.vw[2 * q2 + 1], t);
+                acc_o[t] = mfma(to_h8(a[0], a[1], a[2], a[3]), pop, acc_o[t]);
+            }
+        } else {
+            uint32_t pb[4];
+#pragma unroll
+            for (int q2 = 0; q2 < 4; ++q2) {
+                h2 hp = {(_Float16)pf[2 * q2], (_Float16)pf[2 * q2 + 1]};
+                pb[q2] = as_u(hp);
+            }
+            const h8 pop = to_h8(pb[0], pb[1], pb[2], pb[3]);
+            uint32_t sp[4], bp[4];
+#pragma unroll
+            for (int q2 = 0; q2 < 4; ++q2) {
+                sp[q2] = perm_b(cur.vs[2 * q2 + 1], cur.vs[2 * q2], 0x05040100u);
+                bp[q2] = MODE == MODE_AFFINE ? perm_b(cur.vb[2 * q2 + 1], cur.vb[2 * q2], 0x05040100u)
+                                             : 0u;
+            }
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                uint32_t a[4];
+#pragma unroll
+                for (int q2 = 0; q2 < 4; ++q2) {
+                    const uint32_t x = pair_int<MODE, BITS>(cur.vw[2 * q2], cur.vw[2 * q2 + 1], t);
+                    if constexpr (MODE == MODE_AFFINE) {
+                        h2 c = as_h2(x) - (h2){(_Float16)1024.0f, (_Float16)1024.0f};
+                        h2 s = as_h2(sp[q2]);
+                        if constexpr (BITS == 4) {
+                            if (t & 1) s = s * (h2){(_Float16)0.0625f, (_Float16)0.0625f};
+                        }
+                        a[q2] = as_u(__builtin_elementwise_fma(c, s, as_h2(bp[q2])));
+                    } else {
+                        h2 c = as_h2(x) - (h2){(_Float16)1152.0f, (_Float16)1152.0f};
+                        a[q2] = as_u(c * as_h2(sp[q2]));
+                    }
+                }
+                acc_o[t] = mfma(to_h8(a[0], a[1], a[2], a[3]), pop, acc_o[t]);
+            }
+        }
+    };
+
+    // ping-pong: the next tile's loads are in flight while the current one
+    // computes.  Prefetches are unconditional (the index is clamped to the last
+    // tile), so the wait counts stay exact on every path.
+    const int my_tiles = wave < ntiles ? (ntiles - wave + NWAVE - 1) / NWAVE : 0;
+    if (my_tiles > 0) {
+        const int last = wave + (my_tiles - 1) * NWAVE;
+        Tile ta, tb;
+        load_tile(wave, ta);
+        for (int i = 0; i < my_tiles; i += 2) {
+            const int tt = wave + i * NWAVE;
+            load_tile(min(tt + NWAVE, last), tb);
+            process(ta, tt);
+            if (i + 1 >= my_tiles) break;
+            load_tile(min(tt + 2 * NWAVE, last), ta);
+            process(tb, tt + NWAVE);
+        }
+    }
+
+    // ---------------------------------------------------------------- merge waves
+    l_run += __shfl_xor(l_run, 16, 64);
+    l_run += __shfl_xor(l_run, 32, 64);
+    if constexpr (FOLD) {
+#pragma unroll
+        for (int g = 0; g < 2; ++g) {
+            bsum[g] += __shfl_xor(bsum[g], 16, 64);
+            bsum[g] += __shfl_xor(bsum[g], 32, 64);
+        }
+    }
+    if (kb == 0) {
+        s_ml[wave][0][n] = m_run;
+        s_ml[wave][1][n] = l_run;
+        s_bias[wave][n][0] = bsum[0];
+        s_bias[wave][n][1] = bsum[1];
+    }
+    __syncthreads();
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < NWAVE; ++w) M = fmaxf(M, s_ml[w][0][n]);
+    float f = (m_run == -INFINITY) ? 0.0f : fast_exp2(m_run - M);
+    if constexpr (FOLD) f = __shfl(f, ch + 16 * kb, 64);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc_o[t] *= f;
+    // deterministic sum of the waves' accumulators, in wave order
+    for (int w = 0; w < NWAVE; ++w) {
+        if (wave == w) {
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    float* slot = &s_o[(t * 4 + j) * 64 + lane];
+                    *slot = (w == 0) ? acc_o[t][j] : *slot + acc_o[t][j];
+                }
+        }
+        __syncthreads();
+    }
+
+    // ---------------------------------------------------------------- output
+    // thread -> (head oh, run of D/16 consecutive d); the first 256 threads
+    constexpr int DPT = D / 16;
+    const int oh = (tid >> 4) & 15;
+    const int oc = tid & 15;
+    const bool ok = tid < 256 && oh < G;
+    float Mh = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < NWAVE; ++w) Mh = fmaxf(Mh, s_ml[w][0][oh]);
+    float Lh = 0.0f, bias_h[2] = {0.0f, 0.0f};
+#pragma unroll
+    for (int w = 0; w < NWAVE; ++w) {
+        const float mw = s_ml[w][0][oh];
+        const float fw = (mw == -INFINITY) ? 0.0f : fast_exp2(mw - Mh);
+        Lh += fw * s_ml[w][1][oh];
+        bias_h[0] += fw * s_bias[w][oh][0];
+        bias_h[1] += fw * s_bias[w][oh][1];
+    }
+    auto o_at = [&](int d) {              // unnormalised o[head oh][d]
+        const int rowi = d / DPT, t = d % DPT;
+        const int kbb = rowi >> 2, j = rowi & 3;
+        if constexpr (FOLD) {
+            const int g = d / GS;
+            const float v = s_o[(t * 4 + j) * 64 + kbb * 16 + oh + G * g];
+            const float sc = (BITS == 4 && (t & 1)) ? 16777216.0f * 0.0625f : 16777216.0f;
+            return v * sc + (g ? bias_h[1] : bias_h[0]);
+        } else {
+            return s_o[(t * 4 + j) * 64 + kbb * 16 + oh];
+        }
+    };
+    const int64_t obase = (b * p.Hq + kvh * G + oh) * D;
+
+    if (p.S == 1) {
+        if (ok) {
+            const float inv = Lh > 0.0f ? 1.0f / Lh : 0.0f;
+#pragma unroll
+            for (int i = 0; i < DPT; ++i) {
+                const int d = oc * DPT + i;
+                ((uint16_t*)p.out)[obase + d] = f32_to_f16(o_at(d) * inv);
+            }
+        }
+        return;
+    }
+
+    const int64_t tile = bk;
+    if (ok) {
+        float* ml = p.part_ml + (tile * p.S + split) * 32;
+        float* po = p.part_o + (tile * p.S + split) * 16 * D;
+#pragma unroll
+        for (int i = 0; i < DPT; ++i) {
+            const int d = oc * DPT + i;
+            po[oh * D + d] = o_at(d);
+        }
+        if (oc == 0) { ml[2 * oh] = Mh; ml[2 * oh + 1] = Lh; }
+    }
+}
+
+template <int MODE, int BITS, int GS, int D, bool FOLD>
+hipError_t launch_m(int64_t B, const AttnLaunch& p, hipStream_t stream) {
+    dim3 grid(p.S, 1, (unsigned)(B * p.Hk));
+    if (p.mask_kind == MASK_ADDITIVE)
+        hipLaunchKernelGGL((attn_matrix_decode<MODE, BITS, GS, D, true, FOLD>), grid, dim3(NTHR), 0,
+                           stream, p);
+    else
+        hipLaunchKernelGGL((attn_matrix_decode<MODE, BITS, GS, D, false, FOLD>), grid, dim3(NTHR),
+                           0, stream, p);
+    return hipGetLastError();
+}
+
+template <int MODE, int BITS, int GS, int D>
+hipError_t by_fold(int64_t B, const AttnLaunch& p, hipStream_t s) {
+    constexpr int NG = D / GS;
+    if constexpr (MODE == MODE_AFFINE && NG <= 2) {
+        if (p.G * NG <= 16) return launch_m<MODE, BITS, GS, D, true>(B, p, s);
+    }
+    return launch_m<MODE, BITS, GS, D, false>(B, p, s);
+}
+
+template <int MODE, int BITS, int GS>
+hipError_t by_d(int D, int64_t B, const AttnLaunch& p, hipStream_t s) {
+    switch (D) {
+        case 64: if constexpr (GS <= 64) return by_fold<MODE, BITS, GS, 64>(B, p, s); else break;
+        case 128: return by_fold<MODE, BITS, GS, 128>(B, p, s);
+        case 256: return by_fold<MODE, BITS, GS, 256>(B, p, s);
+    }
+    return hipErrorNotSupported;
+}
+
+}  // namespace
+
+bool matrix_supported(int q_dtype, int mode, int bits, int group_size, int D, int G, int64_t Lq) {
+    if (q_dtype != DT_F16 || Lq != 1 || G > 16 || G < 1) return false;
+    if (D != 64 && D != 128 && D != 256) return false;
+    if (mode == MODE_Q8_0) return true;
+    if (bits != 4 && bits != 8) return false;
+    if (group_size != 32 && group_size != 64 && group_size != 128) return false;
+    return D % group_size == 0;
+}
+
+hipError_t launch_attn_matrix(int mode, int bits, int D, int64_t B, const AttnLaunch& p,
+                              hipStream_t stream) {
+    const int gs = 1 << p.gs_log2;
+    if (mode == MODE_Q8_0) return by_d<MODE_Q8_0, 8, 32>(D, B, p, stream);
+    if (bits == 4) {
+        if (gs == 32) return by_d<MODE_AFFINE, 4, 32>(D, B, p, stream);
+        if (gs == 64) return by_d<MODE_AFFINE, 4, 64>(D, B, p, stream);
+        if (gs == 128) return by_d<MODE_AFFINE, 4, 128>(D, B, p, stream);
+    } else if (bits == 8) {
+        if (gs == 32) return by_d<MODE_AFFINE, 8, 32>(D, B, p, stream);
+        if (gs == 64) return by_d<MODE_AFFINE, 8, 64>(D, B, p, stream);
+        if (gs == 128) return by_d<MODE_AFFINE, 8, 128>(D, B, p, stream);
+    }
     return hipErrorNotSupported;
 }
 

@@ -54,8 +54,8 @@ struct AttnLaunch {
     int32_t n_rows;                 // G * Lq rows per (b, kv head)
     int32_t n_rt;                   // row tiles per (b, kv head)
     int32_t RT;                     // rows per tile
-    float* partials;                // [B*Hk*n_rt][S][RT][D+2] (m, l, o)
-    uint32_t* tickets;              // [B*Hk*n_rt]
+    float* part_ml;                 // [B*Hk*n_rt][S][16][2] (m, l) of each split
+    float* part_o;                  // [B*Hk*n_rt][S][16][D] unnormalised o of each split
 };
 
 // Launchers (return hipGetLastError() of the launch).

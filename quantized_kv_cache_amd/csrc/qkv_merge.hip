@@ -1,0 +1,104 @@
+// Split merge kernel: one workgroup per (tile, row); 256 threads = D/4 float4
+// columns x (1024/D) split groups.  Every load of a thread is issued before
+// its softmax states are combined (online, in log2 units), the split groups
+// then combine through LDS, and the row is written in the query dtype.
+#include "qkv_merge.hpp"
+
+namespace qkv {
+
+namespace {
+
+struct State {
+    float m, l;
+    float4 o;
+};
+
+__device__ __forceinline__ void combine(State& a, float m, float l, float4 o) {
+    if (m == -INFINITY) return;
+    const float mm = fmaxf(a.m, m);
+    const float fa = (a.m == -INFINITY) ? 0.0f : fast_exp2(a.m - mm);
+    const float fb = fast_exp2(m - mm);
+    a.l = a.l * fa + l * fb;
+    a.o.x = a.o.x * fa + o.x * fb;
+    a.o.y = a.o.y * fa + o.y * fb;
+    a.o.z = a.o.z * fa + o.z * fb;
+    a.o.w = a.o.w * fa + o.w * fb;
+    a.m = mm;
+}
+
+template <int QT, int D>
+__global__ __launch_bounds__(256) void merge_splits_kernel(AttnLaunch p) {
+    constexpr int F4 = D / 4;
+    constexpr int SG = 256 / F4;
+    constexpr int U = 8;                          // loads in flight per batch
+    __shared__ State red[256];
+
+    const int r = blockIdx.x;
+    const int64_t tile = blockIdx.y;
+    const int rt = (int)(tile % p.n_rt);
+    const int64_t bk = tile / p.n_rt;
+    const int pr = rt * 16 + r;
+    if (pr >= p.n_rows) return;                   // whole workgroup leaves together
+    const int64_t b = bk / p.Hk, kvh = bk % p.Hk;
+    const int64_t i = pr / p.G, h = kvh * p.G + pr % p.G;
+    const int f = threadIdx.x % F4, sg = threadIdx.x / F4;
+    const int S = p.S;
+
+    const float2* ml = (const float2*)p.part_ml + (tile * S * 16 + r);
+    const float4* po = (const float4*)p.part_o + ((tile * S * 16 + r) * F4 + f);
+    State st{-INFINITY, 0.0f, {0.f, 0.f, 0.f, 0.f}};
+    for (int s0 = sg; s0 < S; s0 += U * SG) {
+        float2 a[U];
+        float4 o[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int s = s0 + u * SG;
+            if (s < S) {
+                a[u] = ml[(int64_t)s * 16];
+                o[u] = po[(int64_t)s * 16 * F4];
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            if (s0 + u * SG < S) combine(st, a[u].x, a[u].y, o[u]);
+    }
+    red[threadIdx.x] = st;
+    __syncthreads();
+    if (sg != 0) return;
+#pragma unroll
+    for (int g = 1; g < SG; ++g) {
+        const State& o = red[g * F4 + f];
+        combine(st, o.m, o.l, o.o);
+    }
+    const float inv = st.l > 0.0f ? 1.0f / st.l : 0.0f;
+    const int64_t ob = ((b * p.Hq + h) * p.Lq + i) * D + 4 * f;
+    store_from_f32<QT>(p.out, ob, st.o.x * inv);
+    store_from_f32<QT>(p.out, ob + 1, st.o.y * inv);
+    store_from_f32<QT>(p.out, ob + 2, st.o.z * inv);
+    store_from_f32<QT>(p.out, ob + 3, st.o.w * inv);
+}
+
+template <int QT>
+hipError_t launch_q(int D, int64_t B, const AttnLaunch& p, hipStream_t s) {
+    dim3 grid(16, (unsigned)(B * p.Hk * p.n_rt));
+    switch (D) {
+        case 64: hipLaunchKernelGGL((merge_splits_kernel<QT, 64>), grid, dim3(256), 0, s, p); break;
+        case 128: hipLaunchKernelGGL((merge_splits_kernel<QT, 128>), grid, dim3(256), 0, s, p); break;
+        case 256: hipLaunchKernelGGL((merge_splits_kernel<QT, 256>), grid, dim3(256), 0, s, p); break;
+        default: return hipErrorNotSupported;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_merge(int q_dtype, int D, int64_t B, const AttnLaunch& p, hipStream_t stream) {
+    switch (q_dtype) {
+        case DT_F32: return launch_q<DT_F32>(D, B, p, stream);
+        case DT_F16: return launch_q<DT_F16>(D, B, p, stream);
+        case DT_BF16: return launch_q<DT_BF16>(D, B, p, stream);
+    }
+    return hipErrorNotSupported;
+}
+
+}  // namespace qkv
