@@ -159,7 +159,21 @@ __device__ __forceinline__ uint32_t pair_int(const uint32_t* wa, const uint32_t*
 // wave execute in order, so no wait on outstanding global loads is needed.
 __device__ __forceinline__ void lds_order() { __asm__ __volatile__("" ::: "memory"); }
 
-template <int MODE, int BITS, int GS, int D, bool MASK, bool FOLD>
+// Reductions over the four lanes n, n+16, n+32, n+48 (v_permlane*_swap).
+__device__ __forceinline__ float max4(float x) {
+    auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(c[0]), __uint_as_float(c[1]));
+}
+__device__ __forceinline__ float sum4(float x) {
+    auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(c[0]) + __uint_as_float(c[1]);
+}
+
+template <int MODE, int BITS, int GS, int D, bool MASK, bool FOLD, bool CONTIG>
 __global__ __launch_bounds__(NTHR) void attn_matrix_decode(AttnLaunch p) {
     using F = Fmt<MODE, BITS, GS, D>;
     constexpr int NG = F::NG;
@@ -174,7 +188,7 @@ __global__ __launch_bounds__(NTHR) void attn_matrix_decode(AttnLaunch p) {
     __shared__ float s_qsum[16][NG];
     __shared__ float s_ml[NWAVE][2][16];
     __shared__ float s_bias[NWAVE][16][2];
-    __shared__ float s_o[64 * (D / 4)];
+    __shared__ float s_o[NWAVE / 2][64 * (D / 4)];
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
@@ -187,52 +201,6 @@ __global__ __launch_bounds__(NTHR) void attn_matrix_decode(AttnLaunch p) {
     const int64_t kvh = bk % p.Hk;
     const int G = p.G;
     const float sl = p.scale * kLog2e;            // scores kept in log2 units
-
-    // ---------------------------------------------------------------- queries
-    // A operand of q K^T for every K-step, and per-(head, group) sums of q.
-    h8 qa[STEPS];
-    {
-        const uint16_t* qrow = (const uint16_t*)p.q + ((b * p.Hq + kvh * G + n) * D);
-        float part[NG];
-#pragma unroll
-        for (int g = 0; g < NG; ++g) part[g] = 0.0f;
-#pragma unroll
-        for (int st = 0; st < STEPS; ++st) {
-            const int g = st / F::SPG, u = st % F::SPG;
-            const int d0 = g * GS + kb * (GS / 4) + 8 * u;
-            uint32_t w[4];
-#pragma unroll
-            for (int hh = 0; hh < 4; ++hh) {
-                uint16_t lo = 0, hi = 0;
-                if (n < G) {
-                    const int e0 = qpos<BITS>(2 * hh), e1 = qpos<BITS>(2 * hh + 1);
-                    _Float16 v0 = __builtin_bit_cast(_Float16, qrow[d0 + e0]);
-                    _Float16 v1 = __builtin_bit_cast(_Float16, qrow[d0 + e1]);
-                    part[g] += (float)v0 + (float)v1;
-                    if constexpr (BITS == 4) {       // odd nibbles arrive as 16 c
-                        if (hh & 1) { v0 = v0 * (_Float16)0.0625f; v1 = v1 * (_Float16)0.0625f; }
-                    }
-                    lo = __builtin_bit_cast(uint16_t, v0);
-                    hi = __builtin_bit_cast(uint16_t, v1);
-                }
-                w[hh] = (uint32_t)lo | ((uint32_t)hi << 16);
-            }
-            qa[st] = to_h8(w[0], w[1], w[2], w[3]);
-        }
-#pragma unroll
-        for (int g = 0; g < NG; ++g) {
-            float s = part[g];
-            s += __shfl_xor(s, 16, 64);
-            s += __shfl_xor(s, 32, 64);
-            if (wave == 0 && kb == 0) s_qsum[n][g] = s * sl;
-        }
-    }
-    __syncthreads();
-    float qs[4][NG];                    // (scale log2e) sum q of output rows 4kb + j
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int g = 0; g < NG; ++g) qs[j][g] = s_qsum[4 * kb + j][g];
 
     // ---------------------------------------------------------------- key range
     const int64_t j0 = (int64_t)split * p.chunk;
@@ -248,8 +216,10 @@ __global__ __launch_bounds__(NTHR) void attn_matrix_decode(AttnLaunch p) {
     const uint8_t* kbi = (const uint8_t*)p.k.biases + krow0 * F::SROWB;
     const uint8_t* vsc = (const uint8_t*)p.v.scales + vrow0 * F::SROWB;
     const uint8_t* vbi = (const uint8_t*)p.v.biases + vrow0 * F::SROWB;
-    const uint32_t kcs = (uint32_t)(p.k.sl * F::ROWB), vcs = (uint32_t)(p.v.sl * F::ROWB);
-    const uint32_t kss = (uint32_t)(p.k.sl * F::SROWB), vss = (uint32_t)(p.v.sl * F::SROWB);
+    const uint32_t kcs = CONTIG ? F::ROWB : (uint32_t)(p.k.sl * F::ROWB);
+    const uint32_t vcs = CONTIG ? F::ROWB : (uint32_t)(p.v.sl * F::ROWB);
+    const uint32_t kss = CONTIG ? F::SROWB : (uint32_t)(p.k.sl * F::SROWB);
+    const uint32_t vss = CONTIG ? F::SROWB : (uint32_t)(p.v.sl * F::SROWB);
     const uint32_t jmax = (uint32_t)(j1 - 1);
 
     // folded P V: this lane's P' column is (head ch, group cg)
@@ -260,13 +230,18 @@ __global__ __launch_bounds__(NTHR) void attn_matrix_decode(AttnLaunch p) {
 
     // Registers of one tile.  Only loads write them; every use waits in
     // process(), so the loads of the next tile stay in flight meanwhile.
+    // Folded tiles load the scale/bias rows of the tile's 32 keys cooperatively:
+    // lane l holds the scale row (l < 32) or the bias row (l >= 32) of key l % 32,
+    // and lanes fetch the rows they need with cross-lane shuffles.
+    constexpr bool COOP = FOLD;
     struct Tile {
         uint32_t kw[2][NG][KW];       // q K^T codes: key (16 hf + n), per group
         uint32_t ks[2][NSW];          // key scales (fp16)
         uint32_t kbias[2][NSW];
         uint32_t vw[8][VW];           // P V codes: keys 8 kb + e
-        uint32_t vs[8];               // folded: scale row of key 8 kb + e; else the lane's scale
-        uint32_t vb[8];               // folded: bias row of key 8 kb + e (softmax lane); else bias
+        uint32_t vs[8];               // value scale / bias of key 8 kb + e (dequantized form)
+        uint32_t vb[8];
+        uint32_t ksb, vsb;            // cooperative scale/bias rows (folded form)
     };
     auto load_scales = [&](const uint8_t* base, uint32_t off, uint32_t* dst) {
         if constexpr (NG == 1) dst[0] = ldg<uint16_t>(base, off);
@@ -274,63 +249,145 @@ __global__ __launch_bounds__(NTHR) void attn_matrix_decode(AttnLaunch p) {
         else if constexpr (NG == 4) { uint2 x = ldg<uint2>(base, off); dst[0] = x.x; dst[1] = x.y; }
         else { uint4 x = ldg<uint4>(base, off); dst[0] = x.x; dst[1] = x.y; dst[2] = x.z; dst[3] = x.w; }
     };
-
-    auto load_tile = [&](int tt, Tile& T) {
-        const uint32_t base = (uint32_t)(j0 + (int64_t)tt * TK);
+    auto load_codes_k = [&](const uint8_t* base, uint32_t o, uint32_t* dst) {
+        if constexpr (KW == 1) {
+            dst[0] = ldg<uint32_t>(base, o);
+        } else if constexpr (KW == 2) {
+            uint2 x = ldg<uint2>(base, o);
+            dst[0] = x.x; dst[1] = x.y;
+        } else {
 #pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-            const uint32_t j = min(base + 16 * hf + n, jmax);
-            const uint32_t off = j * kcs + kb * F::KCH;
-#pragma unroll
-            for (int g = 0; g < NG; ++g) {
-                const uint32_t o = off + g * (GS * BITS / 8);
-                if constexpr (KW == 1) {
-                    T.kw[hf][g][0] = ldg<uint32_t>(kc, o);
-                } else if constexpr (KW == 2) {
-                    uint2 x = ldg<uint2>(kc, o);
-                    T.kw[hf][g][0] = x.x; T.kw[hf][g][1] = x.y;
-                } else {
-#pragma unroll
-                    for (int q4 = 0; q4 < KW; q4 += 4) {
-                        uint4 x = ldg<uint4>(kc, o + 4 * q4);
-                        T.kw[hf][g][q4] = x.x; T.kw[hf][g][q4 + 1] = x.y;
-                        T.kw[hf][g][q4 + 2] = x.z; T.kw[hf][g][q4 + 3] = x.w;
-                    }
-                }
-            }
-            load_scales(ksc, j * kss, T.ks[hf]);
-            if constexpr (MODE == MODE_AFFINE) load_scales(kbi, j * kss, T.kbias[hf]);
-        }
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const uint32_t j = min(base + 8 * kb + e, jmax);
-            const uint32_t o = j * vcs + n * F::VBYTES;
-            if constexpr (F::VBYTES == 2) {
-                T.vw[e][0] = ldg<uint16_t>(vc, o);
-            } else if constexpr (F::VBYTES == 4) {
-                T.vw[e][0] = ldg<uint32_t>(vc, o);
-            } else if constexpr (F::VBYTES == 8) {
-                uint2 x = ldg<uint2>(vc, o);
-                T.vw[e][0] = x.x; T.vw[e][1] = x.y;
-            } else {
-                uint4 x = ldg<uint4>(vc, o);
-                T.vw[e][0] = x.x; T.vw[e][1] = x.y; T.vw[e][2] = x.z; T.vw[e][3] = x.w;
-            }
-            if constexpr (FOLD) {
-                // scale row (column group cg is picked later) and bias row
-                if constexpr (NG == 1) {
-                    T.vs[e] = ldg<uint16_t>(vsc, j * vss);
-                    T.vb[e] = ldg<uint16_t>(vbi, j * vss);
-                } else {
-                    T.vs[e] = ldg<uint32_t>(vsc, j * vss);
-                    T.vb[e] = ldg<uint32_t>(vbi, j * vss);
-                }
-            } else {
-                T.vs[e] = ldg<uint16_t>(vsc, j * vss + 2 * vg);
-                if constexpr (MODE == MODE_AFFINE) T.vb[e] = ldg<uint16_t>(vbi, j * vss + 2 * vg);
+            for (int q4 = 0; q4 < KW; q4 += 4) {
+                uint4 x = ldg<uint4>(base, o + 4 * q4);
+                dst[q4] = x.x; dst[q4 + 1] = x.y; dst[q4 + 2] = x.z; dst[q4 + 3] = x.w;
             }
         }
     };
+    auto load_codes_v = [&](const uint8_t* base, uint32_t o, uint32_t* dst) {
+        if constexpr (F::VBYTES == 2) {
+            dst[0] = ldg<uint16_t>(base, o);
+        } else if constexpr (F::VBYTES == 4) {
+            dst[0] = ldg<uint32_t>(base, o);
+        } else if constexpr (F::VBYTES == 8) {
+            uint2 x = ldg<uint2>(base, o);
+            dst[0] = x.x; dst[1] = x.y;
+        } else {
+            uint4 x = ldg<uint4>(base, o);
+            dst[0] = x.x; dst[1] = x.y; dst[2] = x.z; dst[3] = x.w;
+        }
+    };
+    // rows of the tile starting at key 'base': K rows 16 hf + n, V rows 8 kb + e;
+    // row offsets are clamped to the last key of the split (ragged tail)
+    auto load_rows = [&](uint32_t jk0, uint32_t jk1, const uint32_t* jv, uint32_t jc, Tile& T,
+                         const uint8_t* kcb, const uint8_t* kscb, const uint8_t* kbib,
+                         const uint8_t* vcb, const uint8_t* vscb, const uint8_t* vbib) {
+        const uint32_t jk[2] = {jk0, jk1};
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+            const uint32_t off = jk[hf] * kcs + kb * F::KCH;
+#pragma unroll
+            for (int g = 0; g < NG; ++g) load_codes_k(kcb, off + g * (GS * BITS / 8), T.kw[hf][g]);
+            if constexpr (!COOP) {
+                load_scales(kscb, jk[hf] * kss, T.ks[hf]);
+                if constexpr (MODE == MODE_AFFINE) load_scales(kbib, jk[hf] * kss, T.kbias[hf]);
+            }
+        }
+        if constexpr (COOP) {
+            const uint8_t* kbase = lane < 32 ? kscb : kbib;
+            const uint8_t* vbase = lane < 32 ? vscb : vbib;
+            if constexpr (NG == 1) {
+                T.ksb = ldg<uint16_t>(kbase, jc * kss);
+                T.vsb = ldg<uint16_t>(vbase, jc * vss);
+            } else {
+                T.ksb = ldg<uint32_t>(kbase, jc * kss);
+                T.vsb = ldg<uint32_t>(vbase, jc * vss);
+            }
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            load_codes_v(vcb, jv[e] * vcs + n * F::VBYTES, T.vw[e]);
+            if constexpr (FOLD) {
+            } else {
+                T.vs[e] = ldg<uint16_t>(vscb, jv[e] * vss + 2 * vg);
+                if constexpr (MODE == MODE_AFFINE) T.vb[e] = ldg<uint16_t>(vbib, jv[e] * vss + 2 * vg);
+            }
+        }
+    };
+    auto load_tile = [&](int tt, Tile& T) {
+        const uint32_t base = (uint32_t)(j0 + (int64_t)tt * TK);
+        if (CONTIG && base + TK - 1 <= jmax) {
+            // whole tile inside the split: per-lane offsets are loop invariant and
+            // the tile advances the (scalar) base pointers
+            const uint32_t jv[8] = {8u * kb, 8u * kb + 1, 8u * kb + 2, 8u * kb + 3,
+                                    8u * kb + 4, 8u * kb + 5, 8u * kb + 6, 8u * kb + 7};
+            load_rows((uint32_t)n, 16u + n, jv, (uint32_t)(lane & 31), T, kc + base * F::ROWB,
+                      ksc + base * F::SROWB,
+                      kbi + base * F::SROWB, vc + base * F::ROWB, vsc + base * F::SROWB,
+                      vbi + base * F::SROWB);
+        } else {
+            uint32_t jv[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) jv[e] = min(base + 8 * kb + e, jmax);
+            load_rows(min(base + n, jmax), min(base + 16 + n, jmax), jv,
+                      min(base + (uint32_t)(lane & 31), jmax), T, kc, ksc, kbi, vc, vsc, vbi);
+        }
+    };
+
+    // the query rows, then the first tile, are requested before anything waits
+    const uint16_t* qrow = (const uint16_t*)p.q + ((b * p.Hq + kvh * G + min(n, G - 1)) * D);
+    uint4 qraw[STEPS];
+#pragma unroll
+    for (int st = 0; st < STEPS; ++st) {
+        const int g = st / F::SPG, u = st % F::SPG;
+        qraw[st] = *(const uint4*)(qrow + g * GS + kb * (GS / 4) + 8 * u);   // 8 consecutive halves
+    }
+    const int my_tiles = wave < ntiles ? (ntiles - wave + NWAVE - 1) / NWAVE : 0;
+    Tile ta, tb, tc;
+    if (my_tiles > 0) load_tile(wave, ta);
+    if (my_tiles > 1) load_tile(wave + NWAVE, tb);
+
+    // ---------------------------------------------------------------- queries
+    // A operand of q K^T for every K-step, and per-(head, group) sums of q.
+    h8 qa[STEPS];
+    {
+        float part[NG];
+#pragma unroll
+        for (int g = 0; g < NG; ++g) part[g] = 0.0f;
+#pragma unroll
+        for (int st = 0; st < STEPS; ++st) {
+            const int g = st / F::SPG;
+            const uint4 raw = qraw[st];
+            const uint32_t hw[4] = {raw.x, raw.y, raw.z, raw.w};
+            _Float16 hv[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                hv[e] = __builtin_bit_cast(_Float16, (uint16_t)(hw[e >> 1] >> (16 * (e & 1))));
+            uint32_t w[4];
+#pragma unroll
+            for (int hh = 0; hh < 4; ++hh) {
+                _Float16 v0 = hv[qpos<BITS>(2 * hh)], v1 = hv[qpos<BITS>(2 * hh + 1)];
+                part[g] += (float)v0 + (float)v1;
+                if constexpr (BITS == 4) {       // odd nibbles arrive as 16 c
+                    if (hh & 1) { v0 = v0 * (_Float16)0.0625f; v1 = v1 * (_Float16)0.0625f; }
+                }
+                w[hh] = n < G ? ((uint32_t)__builtin_bit_cast(uint16_t, v0) |
+                                 ((uint32_t)__builtin_bit_cast(uint16_t, v1) << 16))
+                              : 0u;
+            }
+            qa[st] = to_h8(w[0], w[1], w[2], w[3]);
+        }
+#pragma unroll
+        for (int g = 0; g < NG; ++g) {
+            const float s = sum4(part[g]);
+            if (wave == 0 && kb == 0) s_qsum[n][g] = n < G ? s * sl : 0.0f;
+        }
+    }
+    __syncthreads();
+    float qs[4][NG];                    // (scale log2e) sum q of output rows 4kb + j
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int g = 0; g < NG; ++g) qs[j][g] = s_qsum[4 * kb + j][g];
 
     // ---------------------------------------------------------------- main loop
     f4 acc_o[NT];
@@ -339,14 +396,23 @@ __global__ __launch_bounds__(NTHR) void attn_matrix_decode(AttnLaunch p) {
     float m_run = -INFINITY, l_run = 0.0f;
     float bsum[2] = {0.0f, 0.0f};     // folded: sum_key p b_g of the softmax head, per group
     float* sw = s_scores[wave];
+    const float kscale = 16777216.0f * sl;        // 2^24 undoes the subnormal code scale
 
     auto process = [&](const Tile& cur, int tt) {
         const uint32_t base = (uint32_t)(j0 + (int64_t)tt * TK);
 
         // ---- scores of 2 x 16 keys
+        uint32_t krow_s[2] = {0u, 0u}, krow_b[2] = {0u, 0u};
+        if constexpr (COOP) {
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+                krow_s[hf] = (uint32_t)__shfl((int)cur.ksb, 16 * hf + n, 64);
+                krow_b[hf] = (uint32_t)__shfl((int)cur.ksb, 32 + 16 * hf + n, 64);
+            }
+        }
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf) {
-            float z[4] = {0.f, 0.f, 0.f, 0.f};
+            float z[4];
 #pragma unroll
             for (int g = 0; g < NG; ++g) {
                 f4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -355,18 +421,23 @@ __global__ __launch_bounds__(NTHR) void attn_matrix_decode(AttnLaunch p) {
                     const h8 kbop = unpack_k<MODE, BITS>(&cur.kw[hf][g][u * (BITS == 4 ? 1 : 2)]);
                     acc = mfma(qa[g * F::SPG + u], kbop, acc);
                 }
-                const uint32_t sw2 = cur.ks[hf][g >> 1];
+                const uint32_t sw2 = COOP ? krow_s[hf] : cur.ks[hf][g >> 1];
                 const float s = (g & 1) ? hi_f16(sw2) : lo_f16(sw2);
                 if constexpr (MODE == MODE_AFFINE) {
-                    const uint32_t bw2 = cur.kbias[hf][g >> 1];
-                    const float sc = s * (16777216.0f * sl);
+                    const uint32_t bw2 = COOP ? krow_b[hf] : cur.kbias[hf][g >> 1];
+                    const float sc = s * kscale;
                     const float bb = (g & 1) ? hi_f16(bw2) : lo_f16(bw2);
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) z[j] += sc * acc[j] + bb * qs[j][g];
+                    for (int j = 0; j < 4; ++j) {
+                        const float t = __builtin_fmaf(bb, qs[j][g], sc * acc[j]);
+                        z[j] = g == 0 ? t : z[j] + t;
+                    }
                 } else {
 #pragma unroll
-                    for (int j = 0; j < 4; ++j)
-                        z[j] += s * ((16777216.0f * sl) * acc[j] - 128.0f * qs[j][g]);
+                    for (int j = 0; j < 4; ++j) {
+                        const float t = s * __builtin_fmaf(kscale, acc[j], -128.0f * qs[j][g]);
+                        z[j] = g == 0 ? t : z[j] + t;
+                    }
                 }
             }
             const uint32_t j = base + 16 * hf + n;
@@ -394,11 +465,9 @@ __global__ __launch_bounds__(NTHR) void attn_matrix_decode(AttnLaunch p) {
             zz[4] = c.x; zz[5] = c.y; zz[6] = c.z; zz[7] = c.w;
         }
         lds_order();
-        float mx = zz[0];
-#pragma unroll
-        for (int e = 1; e < 8; ++e) mx = fmaxf(mx, zz[e]);
-        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        float mx = fmaxf(fmaxf(fmaxf(zz[0], zz[1]), fmaxf(zz[2], zz[3])),
+                         fmaxf(fmaxf(zz[4], zz[5]), fmaxf(zz[6], zz[7])));
+        mx = max4(mx);
         const float m_new = fmaxf(m_run, mx);
         const bool grow = m_new > m_run;
         if (__ballot(grow) != 0ull) {
@@ -413,32 +482,39 @@ __global__ __launch_bounds__(NTHR) void attn_matrix_decode(AttnLaunch p) {
         }
         float pf[8];
         float ps = 0.0f;
+        const bool live = m_run != -INFINITY;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            pf[e] = (m_run == -INFINITY) ? 0.0f : fast_exp2(zz[e] - m_run);
+            pf[e] = live ? fast_exp2(zz[e] - m_run) : 0.0f;
             ps += pf[e];
         }
         l_run += ps;
+        uint32_t pb[4];
+#pragma unroll
+        for (int q2 = 0; q2 < 4; ++q2) {
+            h2 hp = {(_Float16)pf[2 * q2], (_Float16)pf[2 * q2 + 1]};
+            pb[q2] = as_u(hp);
+        }
 
         if constexpr (FOLD) {
+            uint32_t vrs[8], vrb[8];      // scale / bias rows of keys 8 kb + e
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                vrs[e] = (uint32_t)__shfl((int)cur.vsb, 8 * kb + e, 64);
+                vrb[e] = (uint32_t)__shfl((int)cur.vsb, 32 + 8 * kb + e, 64);
+            }
             // bias sums of the softmax head, per group
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                bsum[0] += pf[e] * lo_f16(cur.vb[e]);
-                if constexpr (NG == 2) bsum[1] += pf[e] * hi_f16(cur.vb[e]);
+                bsum[0] = __builtin_fmaf(pf[e], lo_f16(vrb[e]), bsum[0]);
+                if constexpr (NG == 2) bsum[1] = __builtin_fmaf(pf[e], hi_f16(vrb[e]), bsum[1]);
             }
             // P' column (ch, cg): p of head ch (from its softmax lane) times the scale of cg
-            uint32_t pb[4];
-#pragma unroll
-            for (int q2 = 0; q2 < 4; ++q2) {
-                h2 hp = {(_Float16)pf[2 * q2], (_Float16)pf[2 * q2 + 1]};
-                pb[q2] = as_u(hp);
-            }
             uint32_t pp[4];
 #pragma unroll
             for (int q2 = 0; q2 < 4; ++q2) {
                 const uint32_t src = (uint32_t)__shfl((int)pb[q2], ch + 16 * kb, 64);
-                const uint32_t sa = cur.vs[2 * q2], sb2 = cur.vs[2 * q2 + 1];
+                const uint32_t sa = vrs[2 * q2], sb2 = vrs[2 * q2 + 1];
                 const uint32_t spair = (NG == 2 && cg == 1) ? perm_b(sb2, sa, 0x07060302u)
                                                             : perm_b(sb2, sa, 0x05040100u);
                 pp[q2] = cvalid ? as_u(as_h2(src) * as_h2(spair)) : 0u;
@@ -453,12 +529,6 @@ __global__ __launch_bounds__(NTHR) void attn_matrix_decode(AttnLaunch p) {
                 acc_o[t] = mfma(to_h8(a[0], a[1], a[2], a[3]), pop, acc_o[t]);
             }
         } else {
-            uint32_t pb[4];
-#pragma unroll
-            for (int q2 = 0; q2 < 4; ++q2) {
-                h2 hp = {(_Float16)pf[2 * q2], (_Float16)pf[2 * q2 + 1]};
-                pb[q2] = as_u(hp);
-            }
             const h8 pop = to_h8(pb[0], pb[1], pb[2], pb[3]);
             uint32_t sp[4], bp[4];
 #pragma unroll
@@ -490,33 +560,29 @@ __global__ __launch_bounds__(NTHR) void attn_matrix_decode(AttnLaunch p) {
         }
     };
 
-    // ping-pong: the next tile's loads are in flight while the current one
-    // computes.  Prefetches are unconditional (the index is clamped to the last
-    // tile), so the wait counts stay exact on every path.
-    const int my_tiles = wave < ntiles ? (ntiles - wave + NWAVE - 1) / NWAVE : 0;
+    // three register buffers in rotation: the loads of the next two tiles are in
+    // flight while the current one computes.  Prefetches are unconditional (the
+    // index is clamped to the last tile), so the wait counts stay exact.
     if (my_tiles > 0) {
         const int last = wave + (my_tiles - 1) * NWAVE;
-        Tile ta, tb;
-        load_tile(wave, ta);
-        for (int i = 0; i < my_tiles; i += 2) {
+        for (int i = 0; i < my_tiles; i += 3) {
             const int tt = wave + i * NWAVE;
-            load_tile(min(tt + NWAVE, last), tb);
+            load_tile(min(tt + 2 * NWAVE, last), tc);
             process(ta, tt);
             if (i + 1 >= my_tiles) break;
-            load_tile(min(tt + 2 * NWAVE, last), ta);
+            load_tile(min(tt + 3 * NWAVE, last), ta);
             process(tb, tt + NWAVE);
+            if (i + 2 >= my_tiles) break;
+            load_tile(min(tt + 4 * NWAVE, last), tb);
+            process(tc, tt + 2 * NWAVE);
         }
     }
 
     // ---------------------------------------------------------------- merge waves
-    l_run += __shfl_xor(l_run, 16, 64);
-    l_run += __shfl_xor(l_run, 32, 64);
+    l_run = sum4(l_run);
     if constexpr (FOLD) {
-#pragma unroll
-        for (int g = 0; g < 2; ++g) {
-            bsum[g] += __shfl_xor(bsum[g], 16, 64);
-            bsum[g] += __shfl_xor(bsum[g], 32, 64);
-        }
+        bsum[0] = sum4(bsum[0]);
+        bsum[1] = sum4(bsum[1]);
     }
     if (kb == 0) {
         s_ml[wave][0][n] = m_run;
@@ -532,26 +598,39 @@ __global__ __launch_bounds__(NTHR) void attn_matrix_decode(AttnLaunch p) {
     if constexpr (FOLD) f = __shfl(f, ch + 16 * kb, 64);
 #pragma unroll
     for (int t = 0; t < NT; ++t) acc_o[t] *= f;
-    // deterministic sum of the waves' accumulators, in wave order
-    for (int w = 0; w < NWAVE; ++w) {
-        if (wave == w) {
+    // tree sum of the waves' accumulators (deterministic order): 8 -> 4 -> 2 -> 1
+#pragma unroll
+    for (int half = NWAVE / 2; half >= 1; half >>= 1) {
+        if (wave >= half && wave < 2 * half) {
 #pragma unroll
             for (int t = 0; t < NT; ++t)
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    float* slot = &s_o[(t * 4 + j) * 64 + lane];
-                    *slot = (w == 0) ? acc_o[t][j] : *slot + acc_o[t][j];
-                }
+                for (int j = 0; j < 4; ++j) s_o[wave - half][(t * 4 + j) * 64 + lane] = acc_o[t][j];
+        }
+        __syncthreads();
+        if (wave < half) {
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc_o[t][j] += s_o[wave][(t * 4 + j) * 64 + lane];
         }
         __syncthreads();
     }
+    if (wave == 0) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) s_o[0][(t * 4 + j) * 64 + lane] = acc_o[t][j];
+    }
+    __syncthreads();
 
     // ---------------------------------------------------------------- output
     // thread -> (head oh, run of D/16 consecutive d); the first 256 threads
     constexpr int DPT = D / 16;
-    const int oh = (tid >> 4) & 15;
+    if (tid >= 256) return;
+    const int oh = tid >> 4;
     const int oc = tid & 15;
-    const bool ok = tid < 256 && oh < G;
+    if (oh >= G) return;
     float Mh = -INFINITY;
 #pragma unroll
     for (int w = 0; w < NWAVE; ++w) Mh = fmaxf(Mh, s_ml[w][0][oh]);
@@ -569,49 +648,55 @@ __global__ __launch_bounds__(NTHR) void attn_matrix_decode(AttnLaunch p) {
         const int kbb = rowi >> 2, j = rowi & 3;
         if constexpr (FOLD) {
             const int g = d / GS;
-            const float v = s_o[(t * 4 + j) * 64 + kbb * 16 + oh + G * g];
+            const float v = s_o[0][(t * 4 + j) * 64 + kbb * 16 + oh + G * g];
             const float sc = (BITS == 4 && (t & 1)) ? 16777216.0f * 0.0625f : 16777216.0f;
             return v * sc + (g ? bias_h[1] : bias_h[0]);
         } else {
-            return s_o[(t * 4 + j) * 64 + kbb * 16 + oh];
+            return s_o[0][(t * 4 + j) * 64 + kbb * 16 + oh];
         }
     };
-    const int64_t obase = (b * p.Hq + kvh * G + oh) * D;
 
     if (p.S == 1) {
-        if (ok) {
-            const float inv = Lh > 0.0f ? 1.0f / Lh : 0.0f;
-#pragma unroll
-            for (int i = 0; i < DPT; ++i) {
-                const int d = oc * DPT + i;
-                ((uint16_t*)p.out)[obase + d] = f32_to_f16(o_at(d) * inv);
-            }
-        }
-        return;
-    }
-
-    const int64_t tile = bk;
-    if (ok) {
-        float* ml = p.part_ml + (tile * p.S + split) * 32;
-        float* po = p.part_o + (tile * p.S + split) * 16 * D;
+        const int64_t obase = (b * p.Hq + kvh * G + oh) * D;
+        const float inv = Lh > 0.0f ? 1.0f / Lh : 0.0f;
 #pragma unroll
         for (int i = 0; i < DPT; ++i) {
             const int d = oc * DPT + i;
-            po[oh * D + d] = o_at(d);
+            ((uint16_t*)p.out)[obase + d] = f32_to_f16(o_at(d) * inv);
         }
-        if (oc == 0) { ml[2 * oh] = Mh; ml[2 * oh + 1] = Lh; }
+        return;
     }
+    const int64_t tile = bk;
+    float* ml = p.part_ml + (tile * p.S + split) * 32;
+    float* po = p.part_o + (tile * p.S + split) * 16 * D;
+#pragma unroll
+    for (int i = 0; i < DPT; ++i) {
+        const int d = oc * DPT + i;
+        po[oh * D + d] = o_at(d);
+    }
+    if (oc == 0) { ml[2 * oh] = Mh; ml[2 * oh + 1] = Lh; }
 }
 
 template <int MODE, int BITS, int GS, int D, bool FOLD>
 hipError_t launch_m(int64_t B, const AttnLaunch& p, hipStream_t stream) {
     dim3 grid(p.S, 1, (unsigned)(B * p.Hk));
-    if (p.mask_kind == MASK_ADDITIVE)
-        hipLaunchKernelGGL((attn_matrix_decode<MODE, BITS, GS, D, true, FOLD>), grid, dim3(NTHR), 0,
-                           stream, p);
-    else
-        hipLaunchKernelGGL((attn_matrix_decode<MODE, BITS, GS, D, false, FOLD>), grid, dim3(NTHR),
-                           0, stream, p);
+    const bool contig = p.k.sl == 1 && p.v.sl == 1;
+    const bool mask = p.mask_kind == MASK_ADDITIVE;
+    if (mask) {
+        if (contig)
+            hipLaunchKernelGGL((attn_matrix_decode<MODE, BITS, GS, D, true, FOLD, true>), grid,
+                               dim3(NTHR), 0, stream, p);
+        else
+            hipLaunchKernelGGL((attn_matrix_decode<MODE, BITS, GS, D, true, FOLD, false>), grid,
+                               dim3(NTHR), 0, stream, p);
+    } else {
+        if (contig)
+            hipLaunchKernelGGL((attn_matrix_decode<MODE, BITS, GS, D, false, FOLD, true>), grid,
+                               dim3(NTHR), 0, stream, p);
+        else
+            hipLaunchKernelGGL((attn_matrix_decode<MODE, BITS, GS, D, false, FOLD, false>), grid,
+                               dim3(NTHR), 0, stream, p);
+    }
     return hipGetLastError();
 }
 
