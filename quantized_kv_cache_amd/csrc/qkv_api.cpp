@@ -140,6 +140,7 @@ qkv_status check_source(const void* x, int32_t dtype, const int64_t xs[3], const
 // ---------------------------------------------------------------- attention plans
 struct Plan {
     bool matrix;
+    bool prefill;                   // tiled matrix kernel (64 rows per workgroup)
     int RT, n_rt, S;
     int64_t chunk;
     size_t ws_bytes;
@@ -167,18 +168,31 @@ Plan make_plan(int64_t B, int64_t Hq, int64_t Lq, int64_t D, int64_t L, const qk
     const int algo = opts ? opts->algo : QKV_ALGO_AUTO;
     const int bits = k->bits;
     pl.matrix = false;
-    // the matrix kernel addresses a kv head's rows with 32-bit offsets
+    pl.prefill = false;
+    // the matrix kernels address a kv head's rows with 32-bit offsets
     const int64_t span = (k->L_cap - 1) * k->stride_l * row_bytes(k) + row_bytes(k);
     if (algo != QKV_ALGO_GENERIC && span < (int64_t(1) << 31) &&
-        qkv::matrix_supported(q_dtype, k->mode, bits, k->group_size, (int)D, G, Lq))
+        qkv::matrix_supported(q_dtype, k->mode, bits, k->group_size, (int)D, G, Lq)) {
         pl.matrix = true;
+        pl.prefill = !qkv::decode_matrix_supported(q_dtype, k->mode, bits, k->group_size, (int)D, G, Lq);
+        // grid rows (64-row tiles) and (batch, kv head) pairs within the y/z grid limits
+        const int64_t tiles64 = ((int64_t)G * Lq + qkv::kPrefillRows - 1) / qkv::kPrefillRows;
+        if (pl.prefill && (tiles64 > 65535 || B * Hk > 65535)) pl.matrix = pl.prefill = false;
+    }
     const int64_t n_rows = (int64_t)G * Lq;
-    pl.RT = pl.matrix ? 16 : 16;
+    pl.RT = 16;
     pl.n_rt = (int)((n_rows + pl.RT - 1) / pl.RT);
-    const int64_t base = B * Hk * pl.n_rt;
-    int S = (opts && opts->num_splits > 0)
-                ? std::min(opts->num_splits, 256)
-                : (pl.matrix ? auto_splits(base, L, 512, 256) : auto_splits(base, L, 256, 512));
+    int S;
+    if (opts && opts->num_splits > 0) {
+        S = std::min(opts->num_splits, 256);
+    } else if (pl.prefill) {
+        // one workgroup per CU fits the largest tiles; split only short row counts
+        const int64_t wgs = B * Hk * ((n_rows + qkv::kPrefillRows - 1) / qkv::kPrefillRows);
+        S = auto_splits(wgs, L, 1024, 256);
+    } else {
+        S = pl.matrix ? auto_splits(B * Hk * pl.n_rt, L, 512, 256)
+                      : auto_splits(B * Hk * pl.n_rt, L, 256, 512);
+    }
     int64_t chunk = (L + S - 1) / S;
     const int64_t gran = pl.matrix ? 64 : 32;
     chunk = (chunk + gran - 1) / gran * gran;
@@ -240,6 +254,8 @@ qkv_status attention(const char* name, const void* q, int32_t q_dtype, int64_t B
         return fail(QKV_EUNSUPPORTED, "%s: no matrix-core kernel for these arguments", name);
 
     Plan pl = make_plan(B, Hq, Lq, D, L, k, q_dtype, opts);
+    if (B * k->H > 65535 || (!pl.prefill && pl.n_rt > 65535) || pl.S > 65535)
+        return fail(QKV_EUNSUPPORTED, "%s: batch x kv heads or row tiles beyond the launch grid", name);
     if (pl.ws_bytes > 0) {
         if (!workspace || workspace_bytes < pl.ws_bytes)
             return fail(QKV_EWORKSPACE, "%s: workspace of %zu bytes needed, %zu given", name,
@@ -277,8 +293,9 @@ qkv_status attention(const char* name, const void* q, int32_t q_dtype, int64_t B
         a.part_o = a.part_ml + (size_t)(B * k->H * pl.n_rt) * (size_t)pl.S * 16 * 2;
     }
     hipStream_t s = static_cast<hipStream_t>(stream);
-    hipError_t e = pl.matrix ? qkv::launch_attn_matrix(k->mode, k->bits, (int)D, B, a, s)
-                             : qkv::launch_attn_generic(q_dtype, k->mode, k->bits, (int)D, B, a, s);
+    hipError_t e = pl.prefill  ? qkv::launch_prefill_matrix(k->mode, k->bits, (int)D, B, a, s)
+                   : pl.matrix ? qkv::launch_attn_matrix(k->mode, k->bits, (int)D, B, a, s)
+                               : qkv::launch_attn_generic(q_dtype, k->mode, k->bits, (int)D, B, a, s);
     if (e == hipSuccess && pl.S > 1) e = qkv::launch_merge(q_dtype, (int)D, B, a, s);
     return hip_status(e, name);
 }
@@ -348,7 +365,7 @@ qkv_status qsdpa_plan(int64_t B, int64_t Hq, int64_t Lq, int64_t D, int64_t L, c
     Plan pl = make_plan(B, Hq, Lq, D, L, k, q_dtype, opts);
     plan->algo = pl.matrix ? QKV_ALGO_MATRIX : QKV_ALGO_GENERIC;
     plan->num_splits = pl.S;
-    plan->row_tile = pl.RT;
+    plan->row_tile = pl.prefill ? qkv::kPrefillRows : pl.RT;
     plan->reserved = 0;
     plan->keys_per_split = pl.chunk;
     plan->workspace_bytes = pl.ws_bytes;

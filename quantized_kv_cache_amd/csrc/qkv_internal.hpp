@@ -65,11 +65,19 @@ hipError_t launch_quantize(int x_dtype, int mode, int bits, int group_size, int 
 hipError_t launch_attn_generic(int q_dtype, int mode, int bits, int D, int64_t B,
                                const AttnLaunch& p, hipStream_t stream);
 
-// Matrix-core decode/prefill for fp16 queries; returns hipErrorNotSupported
+// Matrix-core kernels for fp16 queries and fp16 scales.  matrix_supported
+// tells whether one of them covers the arguments; decode_matrix_supported
+// picks the single-query kernel (launch_attn_matrix) over the tiled prefill
+// kernel (launch_prefill_matrix).  Both launchers return hipErrorNotSupported
 // when no instantiation covers the arguments.
 bool matrix_supported(int q_dtype, int mode, int bits, int group_size, int D, int G,
                       int64_t Lq);
+bool decode_matrix_supported(int q_dtype, int mode, int bits, int group_size, int D, int G,
+                             int64_t Lq);
 hipError_t launch_attn_matrix(int mode, int bits, int D, int64_t B, const AttnLaunch& p,
                               hipStream_t stream);
+hipError_t launch_prefill_matrix(int mode, int bits, int D, int64_t B, const AttnLaunch& p,
+                                 hipStream_t stream);
+constexpr int kPrefillRows = 64;    // rows per workgroup of the prefill kernel
 
 }  // namespace qkv

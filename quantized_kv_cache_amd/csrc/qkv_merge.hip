@@ -1,4 +1,4 @@
-// Split merge kernel: one workgroup per (tile, row); 256 threads = D/4 float4
+// Split merge kernel: one workgroup per (tile, row) (grid x = tile, y = row); 256 threads = D/4 float4
 // columns x (1024/D) split groups.  Every load of a thread is issued before
 // its softmax states are combined (online, in log2 units), the split groups
 // then combine through LDS, and the row is written in the query dtype.
@@ -33,8 +33,8 @@ __global__ __launch_bounds__(256) void merge_splits_kernel(AttnLaunch p) {
     constexpr int U = 8;                          // loads in flight per batch
     __shared__ State red[256];
 
-    const int r = blockIdx.x;
-    const int64_t tile = blockIdx.y;
+    const int r = blockIdx.y;
+    const int64_t tile = blockIdx.x;
     const int rt = (int)(tile % p.n_rt);
     const int64_t bk = tile / p.n_rt;
     const int pr = rt * 16 + r;
@@ -80,7 +80,7 @@ __global__ __launch_bounds__(256) void merge_splits_kernel(AttnLaunch p) {
 
 template <int QT>
 hipError_t launch_q(int D, int64_t B, const AttnLaunch& p, hipStream_t s) {
-    dim3 grid(16, (unsigned)(B * p.Hk * p.n_rt));
+    dim3 grid((unsigned)(B * p.Hk * p.n_rt), 16);
     switch (D) {
         case 64: hipLaunchKernelGGL((merge_splits_kernel<QT, 64>), grid, dim3(256), 0, s, p); break;
         case 128: hipLaunchKernelGGL((merge_splits_kernel<QT, 128>), grid, dim3(256), 0, s, p); break;

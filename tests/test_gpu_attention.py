@@ -115,6 +115,14 @@ PREFILL_CASES = [
     ("f32", "affine", 8, 32, 1, 4, 1, 33, 64, 64, True),
     ("bf16", "q8_0", 8, 32, 1, 4, 2, 9, 70, 256, True),
     ("f16", "affine", 8, 64, 1, 4, 4, 70, 200, 128, True),
+    # fp16 queries: the tiled matrix kernel (64 GQA-packed rows per workgroup),
+    # several row tiles with a ragged last one, ragged key tiles
+    ("f16", "affine", 4, 32, 1, 8, 2, 37, 301, 64, True),
+    ("f16", "affine", 4, 128, 2, 6, 2, 50, 129, 256, False),
+    ("f16", "affine", 8, 128, 1, 4, 1, 100, 100, 128, True),
+    ("f16", "affine", 8, 32, 1, 2, 2, 64, 1000, 256, True),
+    ("f16", "q8_0", 8, 32, 2, 16, 1, 12, 77, 64, True),
+    ("f16", "q8_0", 8, 32, 1, 64, 2, 3, 400, 128, False),
 ]
 
 
@@ -127,6 +135,31 @@ def test_prefill_small(case, algo):
     out = qkv.qsdpa_prefill(to_dev(q, dtype), kp, vp, L, scale, causal=causal, algo=algo)
     ref = oracle_attention(q, dtype, kr, vr, L, mode, bits, gs, scale, causal=causal)
     assert_close(out, ref, f"prefill {case} {algo}")
+
+
+@pytest.mark.parametrize("splits", [1, 3, 16])
+def test_prefill_split_count_invariance(splits):
+    dtype, mode, bits, gs = "f16", "q8_0", 8, 32
+    B, Hq, Hk, Lq, L, D = 1, 16, 2, 20, 1500, 128
+    q, kp, vp, kr, vr = _case(dtype, mode, bits, gs, B, Hq, Hk, Lq, L, D)
+    ref = oracle_attention(q, dtype, kr, vr, L, mode, bits, gs, 0.09, causal=True)
+    qd = to_dev(q, dtype)
+    assert qkv.qsdpa_plan(qd, kp, L, splits)["algo"] == "matrix"
+    out = qkv.qsdpa_prefill(qd, kp, vp, L, 0.09, causal=True, num_splits=splits)
+    assert_close(out, ref, f"prefill splits={splits}")
+
+
+def test_decode_wide_gqa_uses_tiled_kernel():
+    """GQA factor 32 (beyond the single-query kernel) with fp16 queries runs
+    on the tiled matrix kernel."""
+    dtype, mode, bits, gs = "f16", "affine", 4, 64
+    B, Hq, Hk, L, D = 2, 64, 2, 700, 128
+    q, kp, vp, kr, vr = _case(dtype, mode, bits, gs, B, Hq, Hk, 1, L, D)
+    qd = to_dev(q, dtype)
+    plan = qkv.qsdpa_plan(qd, kp, L)
+    assert plan["algo"] == "matrix" and plan["row_tile"] == 64
+    out = qkv.qsdpa_decode(qd, kp, vp, L, 0.1)
+    assert_close(out, oracle_attention(q, dtype, kr, vr, L, mode, bits, gs, 0.1), "G=32 decode")
 
 
 def test_prefill_additive_mask_and_single_query_equals_decode():
