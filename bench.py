@@ -1,20 +1,34 @@
-"""Benchmark: qsdpa_decode on the 64K-context 4-bit GQA-4 decode workload.
+"""Benchmark of the quantized-KV attention hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
-A step is one qsdpa_decode call over the whole cache (B=1, Hq=32, Hk=8,
-D=128, L=65536, affine 4-bit group 64, fp16): the query prologue, the
-packed K/V stream with in-register dequantization, the online softmax and the
-fused split merge.  Inputs are resident in HBM before the timed region.  The
-quantized cache is replicated R times (R * bytes >= 512 MB, twice the MI355X
-Infinity Cache) and step i reads copy i mod R, so every step streams its
-bytes from HBM rather than from the memory-side cache.
+Default workload: qsdpa_decode over the 64K-context 4-bit GQA-4 cache (B=1,
+Hq=32, Hk=8, D=128, L=65536, affine 4-bit group 64, fp16; the shape of the
+MLX benchmark on the page "add fast::quantized_kv_update").  A step is one
+decode call: the attention kernel (packed K/V streamed once, dequantized in
+registers, online softmax per key split) and the split merge kernel.
 
-Prints one JSON line.  ``value`` is the achieved algorithmic HBM bandwidth
-(GB/s) of the whole step; ``roofline`` prices the decode kernel against the
-8 TB/s HBM peak; ``cpu_baseline`` times the CPU oracle on a bounded sample of
-the same workload.  Other workloads (``--workload``) are for exploration and
-print the same record shape.
+Other workloads (``--workload``): tiny_decode, append_decode_b8_8bit (a step
+is one qkv_update_append of a token per sequence plus the decode over the
+grown cache), q8_0_decode_gqa16 and q8_0_prefill_512 (one causal prefill).
+
+Inputs are resident in HBM before the timed region.  The quantized cache is
+replicated R times (R * bytes >= twice the 256 MB Infinity Cache, at most 64
+copies) and step i reads copy i mod R, so each step streams its bytes from
+HBM rather than from the memory-side cache.
+
+Prints one JSON line:
+  value          algorithmic bytes of a step / time per step (GB/s)
+  roofline       the dominant kernel (the attention kernel) alone: its
+                 algorithmic bytes (decode) or flops (prefill) per launch over
+                 its mean duration, timed with HIP events that the library
+                 records on its stream around that kernel, in a second pass
+                 of the same number of steps; traffic = HBM bytes per launch
+                 from rocprofv3 counters (profiles/*.counters.txt) while the
+                 kernel source is unchanged since they were taken, else null
+  cpu_baseline   the CPU oracle timed on a bounded sample of the workload
+``--copy-mib N`` instead runs a plain N MiB device copy ``--steps`` times (the
+known-size kernel the counter readings are scaled by).
 """
 from __future__ import annotations
 
@@ -24,20 +38,18 @@ import os
 import sys
 import time
 
-import numpy as np
-
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, vendor figure
-MFMA_F16_PEAK_TFLOPS = 2500.0    # dense fp16/bf16 matrix peak
+MFMA_F16_PEAK_TFLOPS = 2500.0    # dense fp16/bf16 matrix peak, vendor figure
 MALL_BYTES = 256 * 2 ** 20
+MAX_COPIES = 64
 METRIC = "qsdpa_decode µs/step + achieved HBM GB/s (% peak), L=64K 4-bit GQA-4"
-PROFILE_FILE = os.path.join(ROOT, "profiles", "decode_64k_4bit_gqa4_traffic.json")
 
 
 def pack_bytes(w, L) -> int:
-    """Algorithmic bytes of K and V packs over L tokens of every (b, kv head)."""
+    """Algorithmic bytes of the K and V packs over L tokens of every (b, kv head)."""
     rows = w.B * w.Hk * L
     if w.mode == "q8_0":
         per = w.D + 2 * (w.D // 32)
@@ -47,9 +59,43 @@ def pack_bytes(w, L) -> int:
     return 2 * rows * per
 
 
-def qo_bytes(w, Lq=1) -> int:
-    es = 4 if w.dtype == "f32" else 2
-    return 2 * w.B * w.Hq * Lq * w.D * es
+def q_bytes(w, Lq=1) -> int:
+    return w.B * w.Hq * Lq * w.D * (4 if w.dtype == "f32" else 2)
+
+
+def append_bytes(w) -> int:
+    """One token per (b, kv head): fp16 K and V read, their packed rows written."""
+    return 2 * w.B * w.Hk * w.D * 2 + pack_bytes(w, 1)
+
+
+def prefill_flops(w) -> int:
+    """2 flops per multiply-add of QK^T and PV over the visible (query, key) pairs."""
+    if w.causal:
+        vis = sum(w.L - w.Lq + i + 1 for i in range(w.Lq))
+    else:
+        vis = w.Lq * w.L
+    return 4 * w.B * w.Hq * vis * w.D
+
+
+def counters_path(kernel: str, workload: str) -> str:
+    return os.path.join(ROOT, "profiles", f"{kernel}.{workload}.counters.txt")
+
+
+def stored_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed counter summary, or None when
+    there is none or the kernel's sources changed since it was taken."""
+    path = counters_path(kernel, workload)
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if "=" in line and not line.lstrip().startswith("#"):
+            k, v = line.split("=", 1)
+            kv[k.strip()] = v.strip()
+    from quantized_kv_cache_amd.profiling import kernel_hash
+    if kv.get("kernel_source_hash") != kernel_hash(kernel):
+        return None
+    return int(float(kv["hbm_bytes_per_launch"]))
 
 
 def parse():
@@ -63,24 +109,8 @@ def parse():
     ap.add_argument("--copies", type=int, default=0, help="cache copies (0 = enough for 512 MB)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--copy-mib", type=int, default=0)
     return ap.parse_args()
-
-
-def make_caches(w, qkv, to_dev, copies):
-    from quantized_kv_cache_amd import workloads as W
-    inp = W.make_inputs(w)
-    k = to_dev(inp["k"], w.dtype)
-    v = to_dev(inp["v"], w.dtype)
-    base_k = qkv.qkv_quantize(k, w.mode, w.bits, w.group_size)
-    base_v = qkv.qkv_quantize(v, w.mode, w.bits, w.group_size)
-    del k, v
-    per = pack_bytes(w, w.L)
-    R = copies or max(1, -(-2 * MALL_BYTES // per))
-    ks, vs = [base_k], [base_v]
-    for _ in range(R - 1):
-        ks.append(clone_pack(qkv, base_k))
-        vs.append(clone_pack(qkv, base_v))
-    return inp, ks, vs, R
 
 
 def clone_pack(qkv, p):
@@ -88,78 +118,189 @@ def clone_pack(qkv, p):
                     None if p.biases is None else p.biases.clone())
 
 
-def time_steps(torch, step, steps, warmup, stream):
-    for i in range(warmup):
-        step(i)
+def make_caches(w, qkv, W, copies):
+    inp = W.make_inputs(w)
+    k = W.to_tensor(inp["k"], w.dtype)
+    v = W.to_tensor(inp["v"], w.dtype)
+    base_k = qkv.qkv_quantize(k, w.mode, w.bits, w.group_size, L_cap=w.cap)
+    base_v = qkv.qkv_quantize(v, w.mode, w.bits, w.group_size, L_cap=w.cap)
+    del k, v
+    per = pack_bytes(w, w.cap)
+    R = copies or min(MAX_COPIES, max(1, -(-2 * MALL_BYTES // per)))
+    ks, vs = [base_k], [base_v]
+    for _ in range(R - 1):
+        ks.append(clone_pack(qkv, base_k))
+        vs.append(clone_pack(qkv, base_v))
+    return inp, ks, vs, R
+
+
+def time_region(torch, run, first, steps, stream):
+    """ms per step over `steps` calls of run(i), bracketed by events."""
     torch.cuda.synchronize()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     start.record(stream)
-    for i in range(steps):
-        step(warmup + i)
+    for i in range(first, first + steps):
+        run(i)
     end.record(stream)
     torch.cuda.synchronize()
-    return start.elapsed_time(end) / steps       # ms per step (one launch per decode step)
+    return start.elapsed_time(end) / steps
+
+
+def kernel_pass(torch, run, attn_of, first, steps, stream):
+    """Mean duration (ms) of the attention kernel over `steps` calls, from
+    events the library records on its stream right around that kernel."""
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    for a, b in evs:            # create the HIP events before handing them over
+        a.record(stream)
+        b.record(stream)
+    torch.cuda.synchronize()
+    for n, i in enumerate(range(first, first + steps)):
+        call = attn_of(i)
+        call.set_timing(*evs[n])
+        run(i)
+        call.set_timing(None, None)
+    torch.cuda.synchronize()
+    d = [a.elapsed_time(b) for a, b in evs]
+    return sum(d) / len(d)
 
 
 def cpu_baseline(w, inp, budget_s):
-    """The oracle as it stands on this host: dequantize the packs and run the
-    fp64 attention, repeated until about budget_s seconds have passed."""
+    """The oracle as it stands on this host on a bounded sample of the
+    workload: full steps (quantize-append the step's token, dequantize the
+    packs, fp64 attention) repeated until about budget_s seconds have
+    passed (a prefill step runs a bounded number of query positions)."""
+    import numpy as np
     import oracle as orc
     from tests._cases import oracle_attention, oracle_pack
+    from quantized_kv_cache_amd import workloads as W
     kr = oracle_pack(inp["k"], w.dtype, w.mode, w.bits, w.group_size)
     vr = oracle_pack(inp["v"], w.dtype, w.mode, w.bits, w.group_size)
-    q = inp["q"]
-    n, t0 = 0, time.perf_counter()
+    q, L, mask, causal = inp["q"], w.L, None, w.causal
+    what = "decode step"
+    if w.Lq > 1:
+        # the prefill on its last 16 query positions, with the causal rule as a mask
+        idx = np.arange(w.Lq - 16, w.Lq)
+        q = np.ascontiguousarray(q[:, :, idx])
+        j = np.arange(L)[None, :]
+        mask = np.where(j > (L - w.Lq + idx)[:, None], -np.inf, 0.0).astype(np.float32)[None, None]
+        causal = False
+        what = f"16 of the {w.Lq} query positions of the prefill"
+    rng = np.random.default_rng(w.seed + 1)
+    n, t0, work = 0, time.perf_counter(), 0.0
     while True:
-        oracle_attention(q, w.dtype, kr, vr, w.L, w.mode, w.bits, w.group_size, w.scale,
-                         causal=w.causal)
+        if w.steps:
+            s = W.append_step_inputs(w, rng)
+            kn = oracle_pack(s["k_new"], w.dtype, w.mode, w.bits, w.group_size)
+            vn = oracle_pack(s["v_new"], w.dtype, w.mode, w.bits, w.group_size)
+            kr2 = {k: None if a is None else np.concatenate([a, kn[k]], axis=2) for k, a in kr.items()}
+            vr2 = {k: None if a is None else np.concatenate([a, vn[k]], axis=2) for k, a in vr.items()}
+            oracle_attention(s["q"], w.dtype, kr2, vr2, L + 1, w.mode, w.bits, w.group_size,
+                             w.scale)
+            what = "append+decode step"
+        else:
+            oracle_attention(q, w.dtype, kr, vr, L, w.mode, w.bits, w.group_size, w.scale,
+                             mask=mask, causal=causal)
         n += 1
         el = time.perf_counter() - t0
         if el >= budget_s or n >= 50:
             break
     sec = el / n
-    gbs = (pack_bytes(w, w.L) + qo_bytes(w, w.Lq)) / sec / 1e9
-    return {"value": round(gbs, 3), "unit": "GB/s", "cores": orc.num_threads(), "kind": "oracle",
-            "sample": f"{n} full step(s) of {w.name} (dequantize K/V packs + fp64 attention), "
-                      f"{sec * 1e3:.1f} ms per step"}
+    if w.Lq > 1:
+        frac = 16.0 / w.Lq   # bytes of the sampled part of the step
+        alg = (pack_bytes(w, w.L) + 2 * q_bytes(w, w.Lq)) * frac
+    else:
+        alg = pack_bytes(w, w.L) + 2 * q_bytes(w) + (append_bytes(w) if w.steps else 0)
+    return {"value": round(alg / sec / 1e9, 4), "unit": "GB/s", "cores": orc.num_threads(),
+            "kind": "oracle",
+            "sample": f"{n} x {what} of {w.name}, {sec * 1e3:.1f} ms each; the same "
+                      f"algorithmic bytes per unit of work as the GPU figure"}
+
+
+def copy_mode(args):
+    import torch
+    n = args.copy_mib * 2 ** 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(args.warmup):
+        dst.copy_(src)
+    stream = torch.cuda.current_stream()
+    ms = time_region(torch, lambda i: dst.copy_(src), 0, args.steps, stream)
+    print(json.dumps({"copy_bytes": n, "steps": args.steps, "ms_per_copy": round(ms, 5),
+                      "GB/s": round(2 * n / ms / 1e6, 1)}), flush=True)
 
 
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this benchmark runs on one GPU; multi-GPU runs are not part "
-                                   "of this build", "n_gpus": args.gpus}))
+        print(json.dumps({"error": "this benchmark runs on one GPU; runs on several GPUs are "
+                                   "not supported", "n_gpus": args.gpus}), flush=True)
         sys.exit(2)
+    if args.copy_mib:
+        return copy_mode(args)
     import torch
     import quantized_kv_cache_amd as qkv
     from quantized_kv_cache_amd import workloads as W
-    from tests._cases import to_dev
 
     w = W.WORKLOADS[args.workload]
     torch.cuda.set_device(0)
     stream = torch.cuda.current_stream()
-    inp, ks, vs, R = make_caches(w, qkv, to_dev, args.copies)
-    q = to_dev(inp["q"], w.dtype)
-    out = torch.empty_like(q)
+    inp, ks, vs, R = make_caches(w, qkv, W, args.copies)
     ws = qkv.Workspace()
 
-    if w.Lq == 1:
-        calls = [qkv.PreparedDecode(q, ks[i], vs[i], w.L, w.scale, out, num_splits=args.splits,
-                                    algo=args.algo, workspace=ws) for i in range(R)]
+    if w.steps:
+        # append + decode: step i appends one token per sequence at L + t and attends
+        # L + t + 1 keys (t = i mod steps), on cache copy i mod R
+        rng = inp["rng"]
+        per_step = [W.append_step_inputs(w, rng) for _ in range(w.steps)]
+        kn = [W.to_tensor(s["k_new"], w.dtype) for s in per_step]
+        vn = [W.to_tensor(s["v_new"], w.dtype) for s in per_step]
+        qs = [W.to_tensor(s["q"], w.dtype) for s in per_step]
+        out = torch.empty_like(qs[0])
+        appends = [[qkv.PreparedAppend(ks[c], vs[c], kn[t], vn[t]) for t in range(w.steps)]
+                   for c in range(R)]
+        calls = [[qkv.PreparedAttention(qs[t], ks[c], vs[c], w.L + t + 1, w.scale, out,
+                                        num_splits=args.splits, algo=args.algo, workspace=ws)
+                  for t in range(w.steps)] for c in range(R)]
 
-        def step(i):
-            calls[i % R]()
+        def attn_of(i):
+            return calls[i % R][i % w.steps]
+
+        def run(i):
+            t = i % w.steps
+            appends[i % R][t](w.L + t)
+            calls[i % R][t]()
+        L_mean = w.L + (w.steps + 1) / 2.0
+        step_bytes = pack_bytes(w, L_mean) + 2 * q_bytes(w) + append_bytes(w)
+        plan_L = w.L + w.steps
+        q0 = qs[0]
     else:
-        def step(i):
-            qkv.qsdpa_prefill(q, ks[i % R], vs[i % R], w.L, w.scale, causal=w.causal,
-                              num_splits=args.splits, algo=args.algo, out=out, workspace=ws)
+        q0 = W.to_tensor(inp["q"], w.dtype)
+        out = torch.empty_like(q0)
+        calls = [qkv.PreparedAttention(q0, ks[c], vs[c], w.L, w.scale, out, causal=w.causal,
+                                       num_splits=args.splits, algo=args.algo, workspace=ws)
+                 for c in range(R)]
 
-    ms = time_steps(torch, step, args.steps, args.warmup, stream)
-    alg_bytes = pack_bytes(w, w.L) + qo_bytes(w, w.Lq)
-    gbs = alg_bytes / (ms * 1e-3) / 1e9
-    plan = qkv.qsdpa_plan(q, ks[0], w.L, args.splits, args.algo)
-    matrix = plan["algo"] == "matrix"
+        def attn_of(i):
+            return calls[i % R]
+
+        def run(i):
+            calls[i % R]()
+        step_bytes = pack_bytes(w, w.L) + 2 * q_bytes(w, w.Lq)
+        plan_L = w.L
+
+    for i in range(args.warmup):
+        run(i)
+    ms = time_region(torch, run, args.warmup, args.steps, stream)
+    kms = kernel_pass(torch, run, attn_of, args.warmup + args.steps, args.steps, stream)
+
+    plan = qkv.qsdpa_plan(q0, ks[0], plan_L, args.splits, args.algo)
+    if plan["algo"] == "generic":
+        kernel = "attn_generic_kernel"
+    else:
+        kernel = "attn_matrix_prefill" if plan["row_tile"] == 64 else "attn_matrix_decode"
+    gbs = step_bytes / (ms * 1e-3) / 1e9
     rec = {
         "metric": METRIC if w.name == "decode_64k_4bit_gqa4" else f"{w.name} achieved GB/s",
         "value": round(gbs, 2),
@@ -173,48 +314,33 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f16" if matrix else "f32",
+        "dtype": "f16" if plan["algo"] == "matrix" else "f32",
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hk": w.Hk, "D": w.D, "L": w.L,
                    "Lq": w.Lq, "mode": w.mode, "bits": w.bits, "group_size": w.group_size,
                    "cache_dtype": w.dtype, "cache_copies": R, "algo": args.algo,
-                   "kernel": plan["algo"], "num_splits": plan["num_splits"]},
+                   "kernel": kernel, "num_splits": plan["num_splits"]},
     }
+    traffic = stored_traffic(kernel, w.name)
     if w.Lq == 1:
-        traffic = None
-        if os.path.exists(PROFILE_FILE) and w.name == "decode_64k_4bit_gqa4":
-            prof = json.load(open(PROFILE_FILE))
-            if prof.get("kernel_source_hash") == kernel_hash():
-                traffic = prof.get("hbm_bytes_per_launch")
-        rec["roofline"] = {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS,
-                           "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
-                           "traffic": traffic, "algorithmic_bytes": alg_bytes}
+        # per launch: the K/V pack bytes of the attended keys, q, and out when unsplit
+        kb = pack_bytes(w, w.L if not w.steps else L_mean) + q_bytes(w) * (
+            1 if plan["num_splits"] > 1 else 2)
+        ach = kb / (kms * 1e-3) / 1e9
+        rec["roofline"] = {"bound": "hbm", "achieved": round(ach, 2), "peak": HBM_PEAK_GBS,
+                           "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
+                           "traffic": traffic, "kernel": kernel,
+                           "kernel_us": round(kms * 1e3, 3), "algorithmic_bytes": int(kb)}
     else:
         flops = prefill_flops(w)
-        tf = flops / (ms * 1e-3) / 1e12
+        tf = flops / (kms * 1e-3) / 1e12
         rec["roofline"] = {"bound": "mfma", "achieved": round(tf, 2), "peak": MFMA_F16_PEAK_TFLOPS,
                            "unit": "TFLOP/s", "frac": round(tf / MFMA_F16_PEAK_TFLOPS, 4),
-                           "traffic": None, "algorithmic_flops": flops}
+                           "traffic": traffic, "kernel": kernel,
+                           "kernel_us": round(kms * 1e3, 3), "algorithmic_flops": flops}
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_seconds)
     print(json.dumps(rec), flush=True)
-
-
-def prefill_flops(w) -> int:
-    """2 flops per multiply-add of QK^T and PV over the visible (query, key) pairs."""
-    if w.causal:
-        vis = sum(w.L - w.Lq + i + 1 for i in range(w.Lq))
-    else:
-        vis = w.Lq * w.L
-    return 4 * w.B * w.Hq * vis * w.D
-
-
-def kernel_hash() -> str:
-    import hashlib
-    h = hashlib.sha256()
-    for f in sorted(os.listdir(os.path.join(ROOT, "quantized_kv_cache_amd", "csrc"))):
-        h.update(open(os.path.join(ROOT, "quantized_kv_cache_amd", "csrc", f), "rb").read())
-    return h.hexdigest()[:16]
 
 
 if __name__ == "__main__":

@@ -61,7 +61,7 @@
 extern "C" {
 #endif
 
-#define QKV_ABI_VERSION 1
+#define QKV_ABI_VERSION 2
 
 typedef enum {
     QKV_OK = 0,
@@ -92,10 +92,16 @@ typedef struct {
     int64_t stride_b, stride_h, stride_l;   /* in rows */
 } qkv_pack;
 
-/* Options of the attention calls; a NULL pointer means all defaults. */
+/* Options of the attention calls; a NULL pointer means all defaults.
+ * timing_events: an optional pair of hipEvent_t handles (created by the
+ * caller, with timing enabled).  When both are non-NULL the call records [0]
+ * on its stream right before the attention kernel and [1] right after it,
+ * before the split merge kernel, so that the caller can time the attention
+ * kernel alone with hipEventElapsedTime.  NULL (the default) records nothing. */
 typedef struct {
     int32_t num_splits;    /* key-range partitions per (batch, kv head, row tile); 0 = automatic */
     int32_t algo;          /* qkv_algo */
+    void* timing_events[2];
 } qkv_attn_opts;
 
 /* Quantize x[B,H,L,D] (element strides x_strides = {b, h, l}; D contiguous,

@@ -32,7 +32,8 @@ class QkvPack(ctypes.Structure):
 
 
 class QkvAttnOpts(ctypes.Structure):
-    _fields_ = [("num_splits", ctypes.c_int32), ("algo", ctypes.c_int32)]
+    _fields_ = [("num_splits", ctypes.c_int32), ("algo", ctypes.c_int32),
+                ("timing_events", ctypes.c_void_p * 2)]
 
 
 class QkvAttnPlan(ctypes.Structure):

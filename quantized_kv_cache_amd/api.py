@@ -246,32 +246,85 @@ def qsdpa_prefill(q: torch.Tensor, k: Pack, v: Pack, L: int, scale: float, causa
     return out
 
 
-class PreparedDecode:
-    """A qsdpa_decode call with its arguments marshalled once.
+class PreparedAppend:
+    """A qkv_update_append call with its arguments marshalled once; calling it
+    with an offset quantizes the same k_new/v_new into rows [offset, offset+T)."""
+
+    def __init__(self, k_cache: Pack, v_cache: Pack, k_new: torch.Tensor, v_new: torch.Tensor):
+        if k_new.shape != v_new.shape or k_new.stride() != v_new.stride() or k_new.dtype != v_new.dtype:
+            raise ValueError("k_new and v_new must share shape, strides and dtype")
+        self._keep = (k_cache, v_cache, k_new, v_new)
+        self._kc, self._vc = k_cache.c_struct(), v_cache.c_struct()
+        self._strides = _src_strides(k_new)
+        self._fn = _lib.load().qkv_update_append
+        self._head = (_ptr(k_new), _ptr(v_new), _dt(k_new), self._strides, k_new.shape[2])
+        self._tail = (ctypes.byref(self._kc), ctypes.byref(self._vc), _stream(k_new.device))
+
+    def __call__(self, offset: int) -> None:
+        st = self._fn(*self._head, offset, *self._tail)
+        if st:
+            _lib.check(st)
+
+
+class PreparedAttention:
+    """A qsdpa_decode (q[B,Hq,1,D], no causal mask) or qsdpa_prefill call with
+    its arguments marshalled once.
 
     Calling the object re-issues the same launch (same tensors, same stream)
     with only the ctypes call on the host path -- the form a serving loop or
     a benchmark uses.  The tensors must stay alive and keep their storage."""
 
     def __init__(self, q: torch.Tensor, k: Pack, v: Pack, L: int, scale: float,
-                 out: torch.Tensor, mask: torch.Tensor | None = None, num_splits: int = 0,
-                 algo: str = "auto", workspace: Workspace | None = None):
+                 out: torch.Tensor, mask: torch.Tensor | None = None, causal: bool = False,
+                 num_splits: int = 0, algo: str = "auto", workspace: Workspace | None = None):
         B, Hq, Lq, D = q.shape
-        if Lq != 1 or not q.is_contiguous() or out.shape != q.shape:
-            raise ValueError("decode takes contiguous q, out of shape [B,Hq,1,D]")
+        if not q.is_contiguous() or out.shape != q.shape or not out.is_contiguous():
+            raise ValueError("attention takes contiguous q, out of one shape [B,Hq,Lq,D]")
+        if causal and mask is not None:
+            raise ValueError("pass either causal=True or an additive mask")
         buf, nbytes = _attn_common(q, k, v, num_splits, algo, workspace, L)
-        mp, mdt, ms = _mask_args(mask, (B, Hq, 1, L))
+        mp, mdt, ms = _mask_args(mask, (B, Hq, Lq, L))
         self._keep = (q, k, v, out, buf, mask)
         self._kc, self._vc = k.c_struct(), v.c_struct()
         self._opts = _opts(num_splits, algo)
-        self._fn = _lib.load().qsdpa_decode
-        self._args = (_ptr(q), _dt(q), B, Hq, D, ctypes.byref(self._kc), ctypes.byref(self._vc),
-                      L, float(scale), mp, mdt, ms, _ptr(out), _ptr(buf), nbytes,
-                      ctypes.byref(self._opts), _stream(q.device))
+        L_ = _lib.load()
+        head = (_ptr(q), _dt(q), B, Hq)
+        tail = (ctypes.byref(self._kc), ctypes.byref(self._vc), L, float(scale))
+        rest = (_ptr(out), _ptr(buf), nbytes, ctypes.byref(self._opts), _stream(q.device))
+        if Lq == 1 and not causal:
+            self._fn = L_.qsdpa_decode
+            self._args = head + (D,) + tail + (mp, mdt, ms) + rest
+        else:
+            kind = _lib.QKV_MASK_CAUSAL if causal else (
+                _lib.QKV_MASK_ADDITIVE if mask is not None else _lib.QKV_MASK_NONE)
+            self._fn = L_.qsdpa_prefill
+            self._args = head + (Lq, D) + tail + (kind, mp, mdt, ms) + rest
         self.out = out
+
+    def set_timing(self, begin: torch.cuda.Event | None, end: torch.cuda.Event | None) -> None:
+        """Have later calls record `begin` / `end` (timing-enabled events that
+        have been recorded once, so that their HIP handles exist) around the
+        attention kernel alone; None stops it."""
+        if begin is None or end is None:
+            self._opts.timing_events[0] = self._opts.timing_events[1] = None
+            return
+        self._opts.timing_events[0] = begin.cuda_event
+        self._opts.timing_events[1] = end.cuda_event
 
     def __call__(self) -> torch.Tensor:
         st = self._fn(*self._args)
         if st:
             _lib.check(st)
         return self.out
+
+
+class PreparedDecode(PreparedAttention):
+    """PreparedAttention restricted to decode shapes (q[B,Hq,1,D])."""
+
+    def __init__(self, q: torch.Tensor, k: Pack, v: Pack, L: int, scale: float,
+                 out: torch.Tensor, mask: torch.Tensor | None = None, num_splits: int = 0,
+                 algo: str = "auto", workspace: Workspace | None = None):
+        if q.dim() != 4 or q.shape[2] != 1:
+            raise ValueError("decode takes contiguous q, out of shape [B,Hq,1,D]")
+        super().__init__(q, k, v, L, scale, out, mask=mask, num_splits=num_splits, algo=algo,
+                         workspace=workspace)

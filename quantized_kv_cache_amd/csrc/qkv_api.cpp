@@ -293,9 +293,15 @@ qkv_status attention(const char* name, const void* q, int32_t q_dtype, int64_t B
         a.part_o = a.part_ml + (size_t)(B * k->H * pl.n_rt) * (size_t)pl.S * 16 * 2;
     }
     hipStream_t s = static_cast<hipStream_t>(stream);
+    const bool timed = opts && opts->timing_events[0] && opts->timing_events[1];
+    if (timed) {
+        hipError_t te = hipEventRecord(static_cast<hipEvent_t>(opts->timing_events[0]), s);
+        if (te != hipSuccess) return hip_status(te, name);
+    }
     hipError_t e = pl.prefill  ? qkv::launch_prefill_matrix(k->mode, k->bits, (int)D, B, a, s)
                    : pl.matrix ? qkv::launch_attn_matrix(k->mode, k->bits, (int)D, B, a, s)
                                : qkv::launch_attn_generic(q_dtype, k->mode, k->bits, (int)D, B, a, s);
+    if (e == hipSuccess && timed) e = hipEventRecord(static_cast<hipEvent_t>(opts->timing_events[1]), s);
     if (e == hipSuccess && pl.S > 1) e = qkv::launch_merge(q_dtype, (int)D, B, a, s);
     return hip_status(e, name);
 }

@@ -116,3 +116,14 @@ def append_step_inputs(w: Workload, rng: np.random.Generator, B: int | None = No
 def random_case(seed: int, shape, dist: str = "normal", dtype: str = "f16") -> np.ndarray:
     """A seeded tensor for small fuzz cases."""
     return draw(np.random.default_rng(seed), shape, dist, dtype)
+
+
+def to_tensor(a: np.ndarray, dtype: str, device="cuda"):
+    """A storage array (see the module docstring) as a torch tensor on device."""
+    import torch
+    a = np.ascontiguousarray(a)
+    if dtype == "bf16":
+        t = torch.from_numpy(a.view(np.int16)).view(torch.bfloat16)
+    else:
+        t = torch.from_numpy(a)
+    return t.to(device)

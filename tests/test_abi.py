@@ -29,7 +29,7 @@ def test_exports_every_declared_function(L):
     assert set(names) == set(_lib.EXPORTS), names
     for n in names:
         assert hasattr(L, n), n
-    assert L.qkv_abi_version() == 1
+    assert L.qkv_abi_version() == 2
 
 
 def _pack(**kw):

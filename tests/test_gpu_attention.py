@@ -246,3 +246,24 @@ def test_prefill_workload_sampled_rows():
     dec = qkv.qsdpa_decode(to_dev(np.ascontiguousarray(inp["q"][:, :, -1:]), w.dtype), kp, vp,
                            w.L, w.scale)
     assert_close(out[:, :, -1:], dec.double().cpu().numpy(), "last row vs decode")
+
+
+def test_timing_events_bracket_the_attention_kernel():
+    """Events handed over in the options are recorded around the attention
+    kernel (before the split merge); the result is unchanged."""
+    dtype, mode, bits, gs = "f16", "affine", 4, 64
+    B, Hq, Hk, L, D = 1, 8, 2, 3000, 128
+    q, kp, vp, kr, vr = _case(dtype, mode, bits, gs, B, Hq, Hk, 1, L, D)
+    qd = to_dev(q, dtype)
+    out = torch.empty_like(qd)
+    call = qkv.PreparedAttention(qd, kp, vp, L, 0.1, out, num_splits=4)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    b.record()
+    torch.cuda.synchronize()
+    call.set_timing(a, b)
+    call()
+    call.set_timing(None, None)
+    torch.cuda.synchronize()
+    assert a.elapsed_time(b) > 0.0
+    assert_close(out, oracle_attention(q, dtype, kr, vr, L, mode, bits, gs, 0.1), "timed call")
