@@ -141,6 +141,7 @@ qkv_status check_source(const void* x, int32_t dtype, const int64_t xs[3], const
 struct Plan {
     bool matrix;
     bool prefill;                   // tiled matrix kernel (64 rows per workgroup)
+    bool narrow;                    // single-query kernel for GQA factors <= 4
     int RT, n_rt, S;
     int64_t chunk;
     size_t ws_bytes;
@@ -169,12 +170,15 @@ Plan make_plan(int64_t B, int64_t Hq, int64_t Lq, int64_t D, int64_t L, const qk
     const int bits = k->bits;
     pl.matrix = false;
     pl.prefill = false;
+    pl.narrow = false;
     // the matrix kernels address a kv head's rows with 32-bit offsets
     const int64_t span = (k->L_cap - 1) * k->stride_l * row_bytes(k) + row_bytes(k);
     if (algo != QKV_ALGO_GENERIC && span < (int64_t(1) << 31) &&
         qkv::matrix_supported(q_dtype, k->mode, bits, k->group_size, (int)D, G, Lq)) {
         pl.matrix = true;
-        pl.prefill = !qkv::decode_matrix_supported(q_dtype, k->mode, bits, k->group_size, (int)D, G, Lq);
+        pl.narrow = qkv::narrow_decode_supported(q_dtype, k->mode, bits, k->group_size, (int)D, G, Lq);
+        pl.prefill = !pl.narrow &&
+                     !qkv::decode_matrix_supported(q_dtype, k->mode, bits, k->group_size, (int)D, G, Lq);
         // grid rows (64-row tiles) and (batch, kv head) pairs within the y/z grid limits
         const int64_t tiles64 = ((int64_t)G * Lq + qkv::kPrefillRows - 1) / qkv::kPrefillRows;
         if (pl.prefill && (tiles64 > 65535 || B * Hk > 65535)) pl.matrix = pl.prefill = false;
@@ -194,7 +198,10 @@ Plan make_plan(int64_t B, int64_t Hq, int64_t Lq, int64_t D, int64_t L, const qk
                       : auto_splits(B * Hk * pl.n_rt, L, 256, 512);
     }
     int64_t chunk = (L + S - 1) / S;
-    const int64_t gran = pl.matrix ? 64 : 32;
+    const int64_t gran = !pl.matrix ? 32
+                         : pl.prefill ? 64
+                         : pl.narrow  ? qkv::narrow_decode_key_quantum()
+                                      : qkv::decode_matrix_key_quantum();
     chunk = (chunk + gran - 1) / gran * gran;
     S = (int)((L + chunk - 1) / chunk);
     pl.S = S;
@@ -299,6 +306,7 @@ qkv_status attention(const char* name, const void* q, int32_t q_dtype, int64_t B
         if (te != hipSuccess) return hip_status(te, name);
     }
     hipError_t e = pl.prefill  ? qkv::launch_prefill_matrix(k->mode, k->bits, (int)D, B, a, s)
+                   : pl.narrow ? qkv::launch_attn_narrow(k->mode, k->bits, (int)D, B, a, s)
                    : pl.matrix ? qkv::launch_attn_matrix(k->mode, k->bits, (int)D, B, a, s)
                                : qkv::launch_attn_generic(q_dtype, k->mode, k->bits, (int)D, B, a, s);
     if (e == hipSuccess && timed) e = hipEventRecord(static_cast<hipEvent_t>(opts->timing_events[1]), s);

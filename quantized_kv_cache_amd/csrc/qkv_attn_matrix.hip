@@ -37,8 +37,10 @@
 //  * The waves merge their softmax states through LDS; with several splits
 //    the workgroup writes (m, l, o) to the workspace for the split merge
 //    kernel that runs next on the stream.
-//  * Every cache access is a 32-bit offset from a wave-uniform base (the
-//    host checks that a kv head's rows span less than 2 GiB).
+//  * Every cache access is a raw buffer load: a per-tile buffer resource in
+//    SGPRs, bounded at the split's last key (rows past it read as zeros), and
+//    a loop-invariant 32-bit lane offset, so the load path costs no vector
+//    address arithmetic and the prefetch ring needs no clamping.
 #include "qkv_device.hpp"
 #include "qkv_internal.hpp"
 #include "qkv_merge.hpp"
@@ -71,11 +73,6 @@ __device__ __forceinline__ float hi_f16(uint32_t u) { return f16_to_f32((uint16_
 
 __device__ __forceinline__ f4 mfma(h8 a, h8 b, f4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
-}
-
-template <typename T>
-__device__ __forceinline__ T ldg(const uint8_t* base, uint32_t off) {
-    return *(const T*)(base + off);
 }
 
 // Format traits -------------------------------------------------------------
@@ -173,7 +170,11 @@ __device__ __forceinline__ float sum4(float x) {
     return __uint_as_float(c[0]) + __uint_as_float(c[1]);
 }
 
-template <int MODE, int BITS, int GS, int D, bool MASK, bool FOLD, bool CONTIG>
+// Depth of the per-wave load ring: the K and V code bytes of a 32-key tile
+// decide it, so that about 14-18 KB per wave are always requested.
+constexpr int ring_depth(int row_bytes) { return 2 * TK * row_bytes <= 4096 ? 4 : 3; }
+
+template <int MODE, int BITS, int GS, int D, bool MASK, bool FOLD>
 __global__ __launch_bounds__(NTHR) void attn_matrix_decode(AttnLaunch p) {
     using F = Fmt<MODE, BITS, GS, D>;
     constexpr int NG = F::NG;
@@ -183,6 +184,7 @@ __global__ __launch_bounds__(NTHR) void attn_matrix_decode(AttnLaunch p) {
     constexpr int VW = F::VW;
     constexpr int NSW = F::NSW;
     static_assert(!FOLD || (MODE == MODE_AFFINE && NG <= 2), "folded P V needs <= 2 groups");
+    constexpr int NB = ring_depth(D * BITS / 8);
 
     __shared__ float s_scores[NWAVE][16 * SROW];
     __shared__ float s_qsum[16][NG];
@@ -207,7 +209,10 @@ __global__ __launch_bounds__(NTHR) void attn_matrix_decode(AttnLaunch p) {
     const int64_t j1 = min(p.L, j0 + p.chunk);
     const int ntiles = (int)((j1 - j0 + TK - 1) / TK);
 
-    // wave-uniform bases of this (batch, kv head); rows are 32-bit offsets
+    // Every K/V access is a raw buffer load: a per-tile buffer resource (base at
+    // the tile's first row, in SGPRs) and a loop-invariant per-lane byte offset.
+    // The resource's size stops at the split's last key, so rows past it read
+    // as zeros (they are masked) and tiles need no clamping.
     const int64_t krow0 = b * p.k.sb + kvh * p.k.sh;
     const int64_t vrow0 = b * p.v.sb + kvh * p.v.sh;
     const uint8_t* kc = (const uint8_t*)p.k.codes + krow0 * F::ROWB;
@@ -216,10 +221,10 @@ __global__ __launch_bounds__(NTHR) void attn_matrix_decode(AttnLaunch p) {
     const uint8_t* kbi = (const uint8_t*)p.k.biases + krow0 * F::SROWB;
     const uint8_t* vsc = (const uint8_t*)p.v.scales + vrow0 * F::SROWB;
     const uint8_t* vbi = (const uint8_t*)p.v.biases + vrow0 * F::SROWB;
-    const uint32_t kcs = CONTIG ? F::ROWB : (uint32_t)(p.k.sl * F::ROWB);
-    const uint32_t vcs = CONTIG ? F::ROWB : (uint32_t)(p.v.sl * F::ROWB);
-    const uint32_t kss = CONTIG ? F::SROWB : (uint32_t)(p.k.sl * F::SROWB);
-    const uint32_t vss = CONTIG ? F::SROWB : (uint32_t)(p.v.sl * F::SROWB);
+    const uint32_t kcs = (uint32_t)(p.k.sl * F::ROWB);      // byte strides of one key
+    const uint32_t vcs = (uint32_t)(p.v.sl * F::ROWB);
+    const uint32_t kss = (uint32_t)(p.k.sl * F::SROWB);
+    const uint32_t vss = (uint32_t)(p.v.sl * F::SROWB);
     const uint32_t jmax = (uint32_t)(j1 - 1);
 
     // folded P V: this lane's P' column is (head ch, group cg)
@@ -229,10 +234,10 @@ __global__ __launch_bounds__(NTHR) void attn_matrix_decode(AttnLaunch p) {
     const int vg = (F::VCODES * n) / GS;          // group of the lane's dequantized P V chunk
 
     // Registers of one tile.  Only loads write them; every use waits in
-    // process(), so the loads of the next tile stay in flight meanwhile.
-    // Folded tiles load the scale/bias rows of the tile's 32 keys cooperatively:
-    // lane l holds the scale row (l < 32) or the bias row (l >= 32) of key l % 32,
-    // and lanes fetch the rows they need with cross-lane shuffles.
+    // process(), so the loads of the next tiles stay in flight meanwhile.
+    // Folded tiles load the scale and bias rows of the tile's 32 keys
+    // cooperatively (lane l: key l % 32) and lanes fetch the rows they need
+    // with cross-lane shuffles.
     constexpr bool COOP = FOLD;
     struct Tile {
         uint32_t kw[2][NG][KW];       // q K^T codes: key (16 hf + n), per group
@@ -241,99 +246,92 @@ __global__ __launch_bounds__(NTHR) void attn_matrix_decode(AttnLaunch p) {
         uint32_t vw[8][VW];           // P V codes: keys 8 kb + e
         uint32_t vs[8];               // value scale / bias of key 8 kb + e (dequantized form)
         uint32_t vb[8];
-        uint32_t ksb, vsb;            // cooperative scale/bias rows (folded form)
+        uint32_t ksr, kbr, vsr, vbr;  // cooperative scale / bias rows (folded form)
     };
-    auto load_scales = [&](const uint8_t* base, uint32_t off, uint32_t* dst) {
-        if constexpr (NG == 1) dst[0] = ldg<uint16_t>(base, off);
-        else if constexpr (NG == 2) dst[0] = ldg<uint32_t>(base, off);
-        else if constexpr (NG == 4) { uint2 x = ldg<uint2>(base, off); dst[0] = x.x; dst[1] = x.y; }
-        else { uint4 x = ldg<uint4>(base, off); dst[0] = x.x; dst[1] = x.y; dst[2] = x.z; dst[3] = x.w; }
+    // loop-invariant lane offsets inside a tile
+    const uint32_t o_k0 = (uint32_t)n * kcs + kb * F::KCH;
+    const uint32_t o_k1 = (uint32_t)(16 + n) * kcs + kb * F::KCH;
+    const uint32_t o_ks0 = (uint32_t)n * kss, o_ks1 = (uint32_t)(16 + n) * kss;
+    const uint32_t o_v = (uint32_t)(8 * kb) * vcs + n * F::VBYTES;
+    const uint32_t o_vs = (uint32_t)(8 * kb) * vss + 2 * vg;
+    const uint32_t o_kr = (uint32_t)(lane & 31) * kss, o_vr = (uint32_t)(lane & 31) * vss;
+
+    auto rsrc = [&](const uint8_t* base, int64_t row0, uint32_t stride, uint32_t rowb) {
+        const int64_t rows = min((int64_t)TK, j1 - row0);
+        const uint32_t bytes = rows > 0 ? (uint32_t)(rows - 1) * stride + rowb : 0u;
+        return __builtin_amdgcn_make_buffer_rsrc((void*)(base + row0 * (int64_t)stride), (short)0,
+                                                 (int)bytes, 0x00020000);
     };
-    auto load_codes_k = [&](const uint8_t* base, uint32_t o, uint32_t* dst) {
-        if constexpr (KW == 1) {
-            dst[0] = ldg<uint32_t>(base, o);
-        } else if constexpr (KW == 2) {
-            uint2 x = ldg<uint2>(base, o);
-            dst[0] = x.x; dst[1] = x.y;
+    auto ld32 = [](__amdgpu_buffer_rsrc_t r, uint32_t off) -> uint32_t {
+        return __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0);
+    };
+    auto ld16 = [](__amdgpu_buffer_rsrc_t r, uint32_t off) -> uint32_t {
+        return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, 0);
+    };
+    auto ldn = [&](__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t* dst, int nw) {
+        if (nw == 1) {
+            dst[0] = ld32(r, off);
+        } else if (nw == 2) {
+            auto x = __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0);
+            dst[0] = x[0]; dst[1] = x[1];
         } else {
 #pragma unroll
-            for (int q4 = 0; q4 < KW; q4 += 4) {
-                uint4 x = ldg<uint4>(base, o + 4 * q4);
-                dst[q4] = x.x; dst[q4 + 1] = x.y; dst[q4 + 2] = x.z; dst[q4 + 3] = x.w;
+            for (int q4 = 0; q4 < nw; q4 += 4) {
+                auto x = __builtin_amdgcn_raw_buffer_load_b128(r, (int)(off + 4 * q4), 0, 0);
+                dst[q4] = x[0]; dst[q4 + 1] = x[1]; dst[q4 + 2] = x[2]; dst[q4 + 3] = x[3];
             }
         }
     };
-    auto load_codes_v = [&](const uint8_t* base, uint32_t o, uint32_t* dst) {
-        if constexpr (F::VBYTES == 2) {
-            dst[0] = ldg<uint16_t>(base, o);
-        } else if constexpr (F::VBYTES == 4) {
-            dst[0] = ldg<uint32_t>(base, o);
-        } else if constexpr (F::VBYTES == 8) {
-            uint2 x = ldg<uint2>(base, o);
-            dst[0] = x.x; dst[1] = x.y;
-        } else {
-            uint4 x = ldg<uint4>(base, o);
-            dst[0] = x.x; dst[1] = x.y; dst[2] = x.z; dst[3] = x.w;
-        }
+    auto load_scales = [&](__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t* dst) {
+        if constexpr (NG == 1) dst[0] = ld16(r, off);
+        else ldn(r, off, dst, NSW);
     };
-    // rows of the tile starting at key 'base': K rows 16 hf + n, V rows 8 kb + e;
-    // row offsets are clamped to the last key of the split (ragged tail)
-    auto load_rows = [&](uint32_t jk0, uint32_t jk1, const uint32_t* jv, uint32_t jc, Tile& T,
-                         const uint8_t* kcb, const uint8_t* kscb, const uint8_t* kbib,
-                         const uint8_t* vcb, const uint8_t* vscb, const uint8_t* vbib) {
-        const uint32_t jk[2] = {jk0, jk1};
+    auto load_tile = [&](int tt, Tile& T) {
+        const int64_t row0 = j0 + (int64_t)tt * TK;
+        const auto rk = rsrc(kc, row0, kcs, F::ROWB);
+        const auto rv = rsrc(vc, row0, vcs, F::ROWB);
+        const uint32_t ok[2] = {o_k0, o_k1};
 #pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-            const uint32_t off = jk[hf] * kcs + kb * F::KCH;
+        for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
-            for (int g = 0; g < NG; ++g) load_codes_k(kcb, off + g * (GS * BITS / 8), T.kw[hf][g]);
-            if constexpr (!COOP) {
-                load_scales(kscb, jk[hf] * kss, T.ks[hf]);
-                if constexpr (MODE == MODE_AFFINE) load_scales(kbib, jk[hf] * kss, T.kbias[hf]);
-            }
-        }
+            for (int g = 0; g < NG; ++g) ldn(rk, ok[hf] + g * (GS * BITS / 8), T.kw[hf][g], KW);
         if constexpr (COOP) {
-            const uint8_t* kbase = lane < 32 ? kscb : kbib;
-            const uint8_t* vbase = lane < 32 ? vscb : vbib;
-            if constexpr (NG == 1) {
-                T.ksb = ldg<uint16_t>(kbase, jc * kss);
-                T.vsb = ldg<uint16_t>(vbase, jc * vss);
-            } else {
-                T.ksb = ldg<uint32_t>(kbase, jc * kss);
-                T.vsb = ldg<uint32_t>(vbase, jc * vss);
+            T.ksr = (NG == 1) ? ld16(rsrc(ksc, row0, kss, F::SROWB), o_kr)
+                              : ld32(rsrc(ksc, row0, kss, F::SROWB), o_kr);
+            T.kbr = (NG == 1) ? ld16(rsrc(kbi, row0, kss, F::SROWB), o_kr)
+                              : ld32(rsrc(kbi, row0, kss, F::SROWB), o_kr);
+            T.vsr = (NG == 1) ? ld16(rsrc(vsc, row0, vss, F::SROWB), o_vr)
+                              : ld32(rsrc(vsc, row0, vss, F::SROWB), o_vr);
+            T.vbr = (NG == 1) ? ld16(rsrc(vbi, row0, vss, F::SROWB), o_vr)
+                              : ld32(rsrc(vbi, row0, vss, F::SROWB), o_vr);
+        } else {
+            const auto rks = rsrc(ksc, row0, kss, F::SROWB);
+            load_scales(rks, o_ks0, T.ks[0]);
+            load_scales(rks, o_ks1, T.ks[1]);
+            if constexpr (MODE == MODE_AFFINE) {
+                const auto rkb = rsrc(kbi, row0, kss, F::SROWB);
+                load_scales(rkb, o_ks0, T.kbias[0]);
+                load_scales(rkb, o_ks1, T.kbias[1]);
             }
         }
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            load_codes_v(vcb, jv[e] * vcs + n * F::VBYTES, T.vw[e]);
-            if constexpr (FOLD) {
-            } else {
-                T.vs[e] = ldg<uint16_t>(vscb, jv[e] * vss + 2 * vg);
-                if constexpr (MODE == MODE_AFFINE) T.vb[e] = ldg<uint16_t>(vbib, jv[e] * vss + 2 * vg);
+            if constexpr (F::VBYTES == 2) T.vw[e][0] = ld16(rv, o_v + e * vcs);
+            else ldn(rv, o_v + e * vcs, T.vw[e], VW);
+        }
+        if constexpr (!FOLD) {
+            const auto rvs = rsrc(vsc, row0, vss, F::SROWB);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) T.vs[e] = ld16(rvs, o_vs + e * vss);
+            if constexpr (MODE == MODE_AFFINE) {
+                const auto rvb = rsrc(vbi, row0, vss, F::SROWB);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) T.vb[e] = ld16(rvb, o_vs + e * vss);
             }
         }
     };
-    auto load_tile = [&](int tt, Tile& T) {
-        const uint32_t base = (uint32_t)(j0 + (int64_t)tt * TK);
-        if (CONTIG && base + TK - 1 <= jmax) {
-            // whole tile inside the split: per-lane offsets are loop invariant and
-            // the tile advances the (scalar) base pointers
-            const uint32_t jv[8] = {8u * kb, 8u * kb + 1, 8u * kb + 2, 8u * kb + 3,
-                                    8u * kb + 4, 8u * kb + 5, 8u * kb + 6, 8u * kb + 7};
-            load_rows((uint32_t)n, 16u + n, jv, (uint32_t)(lane & 31), T, kc + base * F::ROWB,
-                      ksc + base * F::SROWB,
-                      kbi + base * F::SROWB, vc + base * F::ROWB, vsc + base * F::SROWB,
-                      vbi + base * F::SROWB);
-        } else {
-            uint32_t jv[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) jv[e] = min(base + 8 * kb + e, jmax);
-            load_rows(min(base + n, jmax), min(base + 16 + n, jmax), jv,
-                      min(base + (uint32_t)(lane & 31), jmax), T, kc, ksc, kbi, vc, vsc, vbi);
-        }
-    };
 
-    // the query rows, then the first tile, are requested before anything waits
+    // the query rows, then the first tiles, are requested before anything waits
     const uint16_t* qrow = (const uint16_t*)p.q + ((b * p.Hq + kvh * G + min(n, G - 1)) * D);
     uint4 qraw[STEPS];
 #pragma unroll
@@ -341,10 +339,17 @@ __global__ __launch_bounds__(NTHR) void attn_matrix_decode(AttnLaunch p) {
         const int g = st / F::SPG, u = st % F::SPG;
         qraw[st] = *(const uint4*)(qrow + g * GS + kb * (GS / 4) + 8 * u);   // 8 consecutive halves
     }
+    // keep the query loads ahead of the tile loads (waiting for q must not
+    // drain the ring)
+    __builtin_amdgcn_sched_barrier(0);
     const int my_tiles = wave < ntiles ? (ntiles - wave + NWAVE - 1) / NWAVE : 0;
-    Tile ta, tb, tc;
-    if (my_tiles > 0) load_tile(wave, ta);
-    if (my_tiles > 1) load_tile(wave + NWAVE, tb);
+    Tile ring[NB];
+#pragma unroll
+    for (int r = 0; r < NB - 1; ++r) {           // tile by tile, in ring order
+        load_tile(wave + r * NWAVE, ring[r]);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
 
     // ---------------------------------------------------------------- queries
     // A operand of q K^T for every K-step, and per-(head, group) sums of q.
@@ -406,8 +411,8 @@ __global__ __launch_bounds__(NTHR) void attn_matrix_decode(AttnLaunch p) {
         if constexpr (COOP) {
 #pragma unroll
             for (int hf = 0; hf < 2; ++hf) {
-                krow_s[hf] = (uint32_t)__shfl((int)cur.ksb, 16 * hf + n, 64);
-                krow_b[hf] = (uint32_t)__shfl((int)cur.ksb, 32 + 16 * hf + n, 64);
+                krow_s[hf] = (uint32_t)__shfl((int)cur.ksr, 16 * hf + n, 64);
+                krow_b[hf] = (uint32_t)__shfl((int)cur.kbr, 16 * hf + n, 64);
             }
         }
 #pragma unroll
@@ -500,8 +505,8 @@ __global__ __launch_bounds__(NTHR) void attn_matrix_decode(AttnLaunch p) {
             uint32_t vrs[8], vrb[8];      // scale / bias rows of keys 8 kb + e
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                vrs[e] = (uint32_t)__shfl((int)cur.vsb, 8 * kb + e, 64);
-                vrb[e] = (uint32_t)__shfl((int)cur.vsb, 32 + 8 * kb + e, 64);
+                vrs[e] = (uint32_t)__shfl((int)cur.vsr, 8 * kb + e, 64);
+                vrb[e] = (uint32_t)__shfl((int)cur.vbr, 8 * kb + e, 64);
             }
             // bias sums of the softmax head, per group
 #pragma unroll
@@ -560,21 +565,23 @@ __global__ __launch_bounds__(NTHR) void attn_matrix_decode(AttnLaunch p) {
         }
     };
 
-    // three register buffers in rotation: the loads of the next two tiles are in
-    // flight while the current one computes.  Prefetches are unconditional (the
-    // index is clamped to the last tile), so the wait counts stay exact.
-    if (my_tiles > 0) {
-        const int last = wave + (my_tiles - 1) * NWAVE;
-        for (int i = 0; i < my_tiles; i += 3) {
-            const int tt = wave + i * NWAVE;
-            load_tile(min(tt + 2 * NWAVE, last), tc);
-            process(ta, tt);
-            if (i + 1 >= my_tiles) break;
-            load_tile(min(tt + 3 * NWAVE, last), ta);
-            process(tb, tt + NWAVE);
-            if (i + 2 >= my_tiles) break;
-            load_tile(min(tt + 4 * NWAVE, last), tb);
-            process(tc, tt + 2 * NWAVE);
+    // NB register buffers in rotation: the loads of the next NB - 1 tiles are in
+    // flight while the current one computes (small tiles get a deeper ring, so
+    // that about 18 KB per wave are always requested).  Prefetches are
+    // unconditional (tiles past the split read as zeros), so the wait counts
+    // stay exact.
+    // Whole rounds of NB steps and no early exit: the loop header only merges
+    // the state before the loop with the state at the end of a round, so the
+    // wait counts stay exact at every step.  Loads past the wave's last tile
+    // read zeros; only the compute of those steps is skipped.
+    const int rounds = (my_tiles + NB - 1) / NB;
+    for (int it = 0; it < rounds; ++it) {
+        const int i = it * NB;
+#pragma unroll
+        for (int r = 0; r < NB; ++r) {
+            load_tile(wave + (i + r + NB - 1) * NWAVE, ring[(r + NB - 1) % NB]);
+            __builtin_amdgcn_sched_barrier(0);      // issue the prefetch before computing
+            if (i + r < my_tiles) process(ring[r], wave + (i + r) * NWAVE);
         }
     }
 
@@ -680,23 +687,12 @@ __global__ __launch_bounds__(NTHR) void attn_matrix_decode(AttnLaunch p) {
 template <int MODE, int BITS, int GS, int D, bool FOLD>
 hipError_t launch_m(int64_t B, const AttnLaunch& p, hipStream_t stream) {
     dim3 grid(p.S, 1, (unsigned)(B * p.Hk));
-    const bool contig = p.k.sl == 1 && p.v.sl == 1;
-    const bool mask = p.mask_kind == MASK_ADDITIVE;
-    if (mask) {
-        if (contig)
-            hipLaunchKernelGGL((attn_matrix_decode<MODE, BITS, GS, D, true, FOLD, true>), grid,
-                               dim3(NTHR), 0, stream, p);
-        else
-            hipLaunchKernelGGL((attn_matrix_decode<MODE, BITS, GS, D, true, FOLD, false>), grid,
-                               dim3(NTHR), 0, stream, p);
-    } else {
-        if (contig)
-            hipLaunchKernelGGL((attn_matrix_decode<MODE, BITS, GS, D, false, FOLD, true>), grid,
-                               dim3(NTHR), 0, stream, p);
-        else
-            hipLaunchKernelGGL((attn_matrix_decode<MODE, BITS, GS, D, false, FOLD, false>), grid,
-                               dim3(NTHR), 0, stream, p);
-    }
+    if (p.mask_kind == MASK_ADDITIVE)
+        hipLaunchKernelGGL((attn_matrix_decode<MODE, BITS, GS, D, true, FOLD>), grid, dim3(NTHR), 0,
+                           stream, p);
+    else
+        hipLaunchKernelGGL((attn_matrix_decode<MODE, BITS, GS, D, false, FOLD>), grid, dim3(NTHR), 0,
+                           stream, p);
     return hipGetLastError();
 }
 
@@ -729,6 +725,8 @@ bool matrix_supported(int q_dtype, int mode, int bits, int group_size, int D, in
     if (group_size != 32 && group_size != 64 && group_size != 128) return false;
     return D % group_size == 0;
 }
+
+int decode_matrix_key_quantum() { return TK * NWAVE; }
 
 bool decode_matrix_supported(int q_dtype, int mode, int bits, int group_size, int D, int G,
                              int64_t Lq) {

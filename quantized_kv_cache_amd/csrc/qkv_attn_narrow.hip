@@ -1,0 +1,568 @@
+// Matrix-core decode for narrow GQA groups (G = Hq/Hk <= 4) with fp16
+// queries: one query per head over a group-quantized KV cache.
+//
+// What is computed follows the MLX page "add fast::quantized_kv_update"
+// (sdpa_vector.h quant_sdpa_vector: scores from packed codes through the
+// per-group factorisation  q . (s c + b) = s (q . c) + b (sum q), online
+// softmax, merge of partial softmax states) and the llama.cpp page "Metal:
+// Optimize q8_0 KV - #25556" (Q8_0 blocks; the heads of a GQA group share
+// every K/V load).  With only G <= 4 query rows per kv head, a 16-row matrix
+// tile would leave 12 rows idle in the scores and the softmax, so this kernel
+// lays the work out differently:
+//
+//  * q K^T on v_mfma_f32_4x4x4_16b_f16: 16 blocks, block b = keys 4b..4b+3 of
+//    a 64-key tile, 4 rows = the G heads, contraction over 4 d per step.  The
+//    result leaves lane l with the G scores of key l, so the key's scale and
+//    bias are lane-local and the softmax runs on real scores only.  The q
+//    operand of all blocks is broadcast from one block (CBSZ / ABID), so
+//    16 steps of q fit in one register pair per lane: lane 4a + i holds head
+//    i's 4 values of step a of the bank.
+//  * Codes enter the matrix core unconverted (masking a packed word leaves
+//    fp16 subnormals c * 2^-24; 4-bit odd nibbles arrive as 16 c against a q
+//    pre-divided by 16; Q8_0 codes have the sign bit flipped, c + 128); each
+//    step lies in one quantization group and the groups have separate
+//    accumulators, so  z = sum_g s_g 2^24 acc_g + b_g sum_{d in g} q_d.
+//  * Online softmax with a lazy maximum: the running maxima change (and the
+//    wave reduces, rescales) only when a tile holds a larger score.
+//  * P V folded into the matrix core as in the 16-head kernel: the value
+//    scale moves into P', whose 16 columns are (head, group) pairs, the bias
+//    term sum_key p b_g is accumulated per lane.  Each lane writes its key's
+//    row of P' to a per-wave LDS tile, and ds_read_b64_tr_b16 reads it back
+//    transposed as the B operand (8 keys of one column per lane).
+//  * K/V stream through raw buffer loads with per-tile resources bounded at
+//    the split's last key, a ring of NB tiles in flight per wave, and whole
+//    rounds of the ring without early exit (loads past the wave's tiles read
+//    zeros, their compute is skipped), which keeps the load wait counts exact.
+#include "qkv_internal.hpp"
+#include "qkv_mfma.hpp"
+
+namespace qkv {
+
+namespace {
+
+using namespace mf;
+
+constexpr int NTK = 64;         // keys per tile (one per lane)
+constexpr int NW = 8;           // waves per workgroup
+constexpr int NTH = NW * 64;
+
+// tiles in the per-wave ring: about 18 KB of K/V in flight per wave
+constexpr int narrow_ring(int row_bytes) { return row_bytes <= 64 ? 3 : 2; }
+
+template <int MODE, int BITS, int GS, int D, bool MASK, int GP>
+__global__ __launch_bounds__(NTH) void attn_decode_narrow(AttnLaunch p) {
+    constexpr int NG = D / GS;
+    constexpr int ROWB = D * BITS / 8;            // code bytes of a row
+    constexpr int KWORDS = ROWB / 4;
+    constexpr int QS = D / 4;                     // q K^T steps (4 d each)
+    constexpr int NBANK = QS / 16;                // q registers pairs (16 steps each)
+    constexpr int NT = D / 16;                    // P V output tiles
+    constexpr int VB = D / 16 * BITS / 8;         // P V code bytes per lane and key
+    constexpr int VW = VB >= 4 ? VB / 4 : 1;
+    constexpr int SROWB = NG * 2;                 // bytes of a row of scales
+    constexpr int NSW = SROWB >= 4 ? SROWB / 4 : 1;
+    constexpr int NB = narrow_ring(ROWB);
+    static_assert(NG <= 4 && NBANK >= 1, "narrow kernel: <= 4 groups, D >= 64");
+    static_assert(GP * NG <= 16, "P' has 16 columns");
+
+    __shared__ __attribute__((aligned(16))) _Float16 s_p[NW][NTK * 16];   // P' rows of each wave
+    __shared__ float s_ml[NW][2][4];
+    __shared__ float s_bias[NW][4][4];
+    __shared__ float s_o[NW / 2][64 * (D / 4)];
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+    const int n = lane & 15;
+    const int kb = lane >> 4;
+    const int split = blockIdx.x;
+    const int64_t bk = blockIdx.z;
+    const int64_t b = bk / p.Hk;
+    const int64_t kvh = bk % p.Hk;
+    const int G = p.G;
+    const float sl = p.scale * kLog2e;            // scores in log2 units
+
+    const int64_t j0 = (int64_t)split * p.chunk;
+    const int64_t j1 = min(p.L, j0 + p.chunk);
+    const int ntiles = (int)((j1 - j0 + NTK - 1) / NTK);
+    const int my_tiles = wave < ntiles ? (ntiles - wave + NW - 1) / NW : 0;
+    const int64_t jmax = j1 - 1;
+
+    const int64_t krow0 = b * p.k.sb + kvh * p.k.sh;
+    const int64_t vrow0 = b * p.v.sb + kvh * p.v.sh;
+    const uint8_t* kc = (const uint8_t*)p.k.codes + krow0 * ROWB;
+    const uint8_t* vc = (const uint8_t*)p.v.codes + vrow0 * ROWB;
+    const uint8_t* ksc = (const uint8_t*)p.k.scales + krow0 * SROWB;
+    const uint8_t* kbi = (const uint8_t*)p.k.biases + krow0 * SROWB;
+    const uint8_t* vsc = (const uint8_t*)p.v.scales + vrow0 * SROWB;
+    const uint8_t* vbi = (const uint8_t*)p.v.biases + vrow0 * SROWB;
+    const uint32_t kcs = (uint32_t)(p.k.sl * ROWB), vcs = (uint32_t)(p.v.sl * ROWB);
+    const uint32_t kss = (uint32_t)(p.k.sl * SROWB), vss = (uint32_t)(p.v.sl * SROWB);
+
+    // ------------------------------------------------------------ queries
+    // lane 4a + i holds, in bank c, head i's q at the 4 d of step 16c + a, in
+    // the order the codes of that step are unpacked (odd 4-bit nibbles / 16)
+    const int qi = lane & 3, qa = lane >> 2;
+    const uint16_t* qrow = (const uint16_t*)p.q + (b * p.Hq + kvh * G + min(qi, G - 1)) * D;
+    auto step_d = [](int u, int e) -> int {       // d of half e of step u
+        if constexpr (BITS == 4) {
+            constexpr int o0[4] = {0, 4, 1, 5}, o1[4] = {2, 6, 3, 7};
+            return 8 * (u >> 1) + ((u & 1) ? o1[e] : o0[e]);
+        } else {
+            constexpr int o[4] = {0, 2, 1, 3};
+            return 4 * u + o[e];
+        }
+    };
+    // raw q chunk of each bank (4-bit: the 8 d of the step's code dword,
+    // 8-bit: its 4 d); the halves are picked after the tile loads are issued
+    constexpr int QCH = BITS == 4 ? 4 : 2;        // dwords per chunk
+    uint32_t qraw[NBANK][QCH];
+#pragma unroll
+    for (int c = 0; c < NBANK; ++c) {
+        const int u = 16 * c + qa;
+        const int d0 = BITS == 4 ? 8 * (u >> 1) : 4 * u;
+        if constexpr (BITS == 4) {
+            const uint4 x = *(const uint4*)(qrow + d0);
+            qraw[c][0] = x.x; qraw[c][1] = x.y; qraw[c][2] = x.z; qraw[c][3] = x.w;
+        } else {
+            const uint2 x = *(const uint2*)(qrow + d0);
+            qraw[c][0] = x.x; qraw[c][1] = x.y;
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    // ------------------------------------------------------------ K/V tiles
+    struct Tile {
+        uint32_t k[KWORDS];           // the lane's key row (q K^T)
+        uint32_t ks[NSW], kbias[NSW]; // its scales / biases
+        uint32_t vs[NSW], vbias[NSW]; // its value scales / biases (P' and the bias sums)
+        uint32_t v[2][8][VW];         // P V codes: key 32 c + 8 kb + e, chunk n
+    };
+    const uint32_t o_k = (uint32_t)lane * kcs;
+    const uint32_t o_ks = (uint32_t)lane * kss, o_vs = (uint32_t)lane * vss;
+    const uint32_t o_v = (uint32_t)(8 * kb) * vcs + (uint32_t)n * VB;
+    auto load_rows16 = [&](__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t* dst) {
+        if constexpr (NG == 1) dst[0] = buf16(r, off);
+        else bufn(r, off, dst, NSW);
+    };
+    auto load_tile = [&](int tt, Tile& T) {
+        const int64_t row0 = j0 + (int64_t)tt * NTK;
+        const auto rk = rows_rsrc(kc, row0, j1, NTK, kcs, ROWB);
+        bufn(rk, o_k, T.k, KWORDS);
+        load_rows16(rows_rsrc(ksc, row0, j1, NTK, kss, SROWB), o_ks, T.ks);
+        if constexpr (MODE == MODE_AFFINE)
+            load_rows16(rows_rsrc(kbi, row0, j1, NTK, kss, SROWB), o_ks, T.kbias);
+        load_rows16(rows_rsrc(vsc, row0, j1, NTK, vss, SROWB), o_vs, T.vs);
+        if constexpr (MODE == MODE_AFFINE)
+            load_rows16(rows_rsrc(vbi, row0, j1, NTK, vss, SROWB), o_vs, T.vbias);
+        const auto rv = rows_rsrc(vc, row0, j1, NTK, vcs, ROWB);
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const uint32_t off = o_v + (uint32_t)(32 * c + e) * vcs;
+                if constexpr (VB == 2) T.v[c][e][0] = buf16(rv, off);
+                else bufn(rv, off, T.v[c][e], VW);
+            }
+    };
+    Tile ring[NB];
+#pragma unroll
+    for (int r = 0; r < NB - 1; ++r) {           // tile by tile, in ring order
+        load_tile(wave + r * NW, ring[r]);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    // An opaque zero, defined after the tile loads (the memory clobber keeps
+    // them ahead of it): the q arithmetic below depends on it, so the wait for
+    // the q loads cannot be placed before the tile loads are issued.
+    uint32_t after_loads;
+    __asm__ __volatile__("s_mov_b32 %0, 0" : "=s"(after_loads) : : "memory");
+
+    // q banks and the per-(head, group) sums of q (scale log2e applied)
+    h4 qb[NBANK];
+    float qs[4][NG];
+    {
+        float part[NG];
+#pragma unroll
+        for (int g = 0; g < NG; ++g) part[g] = 0.0f;
+#pragma unroll
+        for (int c = 0; c < NBANK; ++c) {
+            _Float16 hv[4];
+            const int u = 16 * c + qa;
+            const int d0 = BITS == 4 ? 8 * (u >> 1) : 4 * u;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int dd = step_d(u, e) - d0;       // 0 .. 2 QCH - 1
+                uint32_t w = qraw[c][0];
+#pragma unroll
+                for (int k2 = 1; k2 < QCH; ++k2)
+                    if ((dd >> 1) == k2) w = qraw[c][k2];
+                w ^= after_loads;
+                const _Float16 x = __builtin_bit_cast(_Float16, (uint16_t)((dd & 1) ? (w >> 16) : (w & 0xffffu)));
+                part[d0 / GS] += (float)x;
+                const bool sixteenth = BITS == 4 && e >= 2;
+                hv[e] = qi < G ? (sixteenth ? x * (_Float16)0.0625f : x) : (_Float16)0.0f;
+            }
+            qb[c] = (h4){hv[0], hv[1], hv[2], hv[3]};
+        }
+#pragma unroll
+        for (int g = 0; g < NG; ++g) {
+            float s = part[g];
+#pragma unroll
+            for (int o = 4; o < 64; o <<= 1) s += __shfl_xor(s, o, 64);
+#pragma unroll
+            for (int h = 0; h < 4; ++h)
+                qs[h][g] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, s), h)) * sl;
+        }
+    }
+
+    // ------------------------------------------------------------ main loop
+    f4 acc_o[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc_o[t] = f4{0.f, 0.f, 0.f, 0.f};
+    float m_h[4], l_h[4], bs[4][NG];              // m uniform; l, bs per-lane partial sums
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+        m_h[h] = -INFINITY;
+        l_h[h] = 0.0f;
+#pragma unroll
+        for (int g = 0; g < NG; ++g) bs[h][g] = 0.0f;
+    }
+    _Float16* pw = s_p[wave];
+    const float kscale = 16777216.0f * sl;       // 2^24 undoes the subnormal code scale
+    // P' column of this lane: (head ch, group cg); the column layout uses GP
+    // (2 or 4) head slots per group, G <= GP of them real
+    const int ch = n % GP;
+
+    auto process = [&](const Tile& T, int tt) {
+        const int64_t row0 = j0 + (int64_t)tt * NTK;
+        // ---- q K^T: scores of key row0 + lane for the 4 heads
+        f4 acc[NG];
+#pragma unroll
+        for (int g = 0; g < NG; ++g) acc[g] = f4{0.f, 0.f, 0.f, 0.f};
+        static_for<0, QS>([&](auto uc) {
+            constexpr int u = decltype(uc)::value;
+            uint32_t b0, b1;
+            if constexpr (BITS == 4) {
+                const uint32_t x = T.k[u >> 1];
+                if constexpr (u & 1) {
+                    const uint32_t t = perm_b(0u, x, 0x0C030C01u);
+                    b0 = t & 0x000F000Fu;
+                    b1 = t & 0x00F000F0u;
+                } else {
+                    b0 = x & 0x000F000Fu;
+                    b1 = x & 0x00F000F0u;
+                }
+            } else {
+                const uint32_t f = MODE == MODE_Q8_0 ? 0x00800080u : 0u;
+                const uint32_t x = T.k[u];
+                b0 = (x & 0x00FF00FFu) ^ f;
+                b1 = perm_b(0u, x, 0x0C030C01u) ^ f;
+            }
+            constexpr int g = (BITS == 4 ? 8 * (u >> 1) : 4 * u) / GS;
+            acc[g] = mfma4_bcast<u & 15>(qb[u >> 4], to_h4(b0, b1), acc[g]);
+        });
+        float z[4];
+#pragma unroll
+        for (int h = 0; h < 4; ++h) z[h] = 0.0f;
+#pragma unroll
+        for (int g = 0; g < NG; ++g) {
+            const uint32_t sw = T.ks[g >> 1];
+            const float s = (g & 1) ? hi_f16(sw) : lo_f16(sw);
+            const float S = s * kscale;
+            if constexpr (MODE == MODE_AFFINE) {
+                const uint32_t bw = T.kbias[g >> 1];
+                const float bb = (g & 1) ? hi_f16(bw) : lo_f16(bw);
+#pragma unroll
+                for (int h = 0; h < 4; ++h) z[h] = __builtin_fmaf(bb, qs[h][g], __builtin_fmaf(acc[g][h], S, z[h]));
+            } else {
+                const float Tq = -128.0f * s;
+#pragma unroll
+                for (int h = 0; h < 4; ++h) z[h] = __builtin_fmaf(Tq, qs[h][g], __builtin_fmaf(acc[g][h], S, z[h]));
+            }
+        }
+        const int64_t j = row0 + lane;
+        if (row0 + NTK - 1 > jmax) {              // tile crosses the end of the split
+            if (j > jmax) {
+#pragma unroll
+                for (int h = 0; h < 4; ++h) z[h] = -INFINITY;
+            }
+        }
+        if constexpr (MASK) {
+            if (j <= jmax) {
+#pragma unroll
+                for (int h = 0; h < 4; ++h)
+                    if (h < G)
+                        z[h] += kLog2e * load_mask(p.mask, p.mask_dtype,
+                                                   b * p.ms0 + (kvh * G + h) * p.ms1 + j * p.ms3);
+            }
+        }
+#pragma unroll
+        for (int h = 0; h < 4; ++h)
+            if (h >= G) z[h] = -INFINITY;
+
+        // ---- online softmax, lazy maximum
+        bool grow = false;
+#pragma unroll
+        for (int h = 0; h < 4; ++h) grow |= z[h] > m_h[h];
+        if (__ballot(grow) != 0ull) {
+            float alpha[4];
+#pragma unroll
+            for (int h = 0; h < 4; ++h) {
+                const float mn = fmaxf(m_h[h], wave_max(z[h]));
+                alpha[h] = (m_h[h] == -INFINITY) ? 0.0f : fast_exp2(m_h[h] - mn);
+                m_h[h] = mn;
+                l_h[h] *= alpha[h];
+#pragma unroll
+                for (int g = 0; g < NG; ++g) bs[h][g] *= alpha[h];
+            }
+            const float ac = ch == 0 ? alpha[0] : ch == 1 ? alpha[1] : ch == 2 ? alpha[2] : alpha[3];
+#pragma unroll
+            for (int t = 0; t < NT; ++t) acc_o[t] *= ac;
+        }
+        float pr[4];
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+            pr[h] = m_h[h] == -INFINITY ? 0.0f : fast_exp2(z[h] - m_h[h]);
+            l_h[h] += pr[h];
+        }
+        // ---- P' row of this key (column h + G g = p_h s_g) and the bias sums
+        _Float16 prow[16];
+#pragma unroll
+        for (int q = 0; q < 16; ++q) prow[q] = (_Float16)0.0f;
+#pragma unroll
+        for (int g = 0; g < NG; ++g) {
+            const uint32_t sw = T.vs[g >> 1];
+            const _Float16 sv = __builtin_bit_cast(_Float16, (uint16_t)((g & 1) ? (sw >> 16) : (sw & 0xffffu)));
+            float bv;
+            if constexpr (MODE == MODE_AFFINE) {
+                const uint32_t bw = T.vbias[g >> 1];
+                bv = (g & 1) ? hi_f16(bw) : lo_f16(bw);
+            } else {
+                bv = -128.0f * (float)sv;
+            }
+#pragma unroll
+            for (int h = 0; h < GP; ++h) prow[h + GP * g] = (_Float16)pr[h] * sv;
+#pragma unroll
+            for (int h = 0; h < 4; ++h) bs[h][g] = __builtin_fmaf(pr[h], bv, bs[h][g]);
+        }
+        {
+            uint32_t w[8];
+#pragma unroll
+            for (int q = 0; q < 8; ++q)
+                w[q] = (uint32_t)__builtin_bit_cast(uint16_t, prow[2 * q]) |
+                       ((uint32_t)__builtin_bit_cast(uint16_t, prow[2 * q + 1]) << 16);
+            uint4* dst = (uint4*)(pw + lane * 16);
+            dst[0] = uint4{w[0], w[1], w[2], w[3]};
+            dst[1] = uint4{w[4], w[5], w[6], w[7]};
+        }
+        lds_order();
+        // ---- P V: two 32-key steps; B = P'^T by the LDS transpose read
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            const int k0 = 32 * c + 8 * kb;
+            const _Float16* pa = pw + (k0 + (n >> 2)) * 16 + 4 * (n & 3);
+            const s4 ra = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s4*)(pa));
+            const s4 rb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s4*)(pa + 4 * 16));
+            const h8 pop = __builtin_bit_cast(h8, (short __attribute__((ext_vector_type(8)))){
+                ra[0], ra[1], ra[2], ra[3], rb[0], rb[1], rb[2], rb[3]});
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                uint32_t a[4];
+#pragma unroll
+                for (int q2 = 0; q2 < 4; ++q2) {
+                    uint32_t x = pair_sub<BITS>(T.v[c][2 * q2], T.v[c][2 * q2 + 1], t);
+                    if constexpr (MODE == MODE_Q8_0) x ^= 0x00800080u;
+                    a[q2] = x;
+                }
+                acc_o[t] = mfma16(to_h8(a[0], a[1], a[2], a[3]), pop, acc_o[t]);
+            }
+        }
+        lds_order();
+    };
+
+    // whole rounds of the ring; loads are unconditional (tiles past the
+    // wave's last read zeros) and only the compute of such steps is skipped
+    const int rounds = (my_tiles + NB - 1) / NB;
+    for (int it = 0; it < rounds; ++it) {
+        const int i = it * NB;
+#pragma unroll
+        for (int r = 0; r < NB; ++r) {
+            load_tile(wave + (i + r + NB - 1) * NW, ring[(r + NB - 1) % NB]);
+            __builtin_amdgcn_sched_barrier(0);
+            if (i + r < my_tiles) process(ring[r], wave + (i + r) * NW);
+        }
+    }
+
+    // ------------------------------------------------------------ merge waves
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+        l_h[h] = wave_sum(l_h[h]);
+#pragma unroll
+        for (int g = 0; g < NG; ++g) bs[h][g] = wave_sum(bs[h][g]);
+    }
+    if (lane == 0) {
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+            s_ml[wave][0][h] = m_h[h];
+            s_ml[wave][1][h] = l_h[h];
+#pragma unroll
+            for (int g = 0; g < NG; ++g) s_bias[wave][h][g] = bs[h][g];
+        }
+    }
+    __syncthreads();
+    {
+        float f[4];
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+            float M = -INFINITY;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) M = fmaxf(M, s_ml[w][0][h]);
+            f[h] = m_h[h] == -INFINITY ? 0.0f : fast_exp2(m_h[h] - M);
+        }
+        const float fc = ch == 0 ? f[0] : ch == 1 ? f[1] : ch == 2 ? f[2] : f[3];
+#pragma unroll
+        for (int t = 0; t < NT; ++t) acc_o[t] *= fc;
+    }
+#pragma unroll
+    for (int half = NW / 2; half >= 1; half >>= 1) {
+        if (wave >= half && wave < 2 * half) {
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) s_o[wave - half][(t * 4 + jj) * 64 + lane] = acc_o[t][jj];
+        }
+        __syncthreads();
+        if (wave < half) {
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) acc_o[t][jj] += s_o[wave][(t * 4 + jj) * 64 + lane];
+        }
+        __syncthreads();
+    }
+    if (wave == 0) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) s_o[0][(t * 4 + jj) * 64 + lane] = acc_o[t][jj];
+    }
+    __syncthreads();
+
+    // ------------------------------------------------------------ output
+    // thread -> (head oh, run of D/16 consecutive d); the first 16 G threads
+    constexpr int DPT = D / 16;
+    const int oh = tid >> 4;
+    const int oc = tid & 15;
+    if (oh >= G) return;
+    float Mh = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) Mh = fmaxf(Mh, s_ml[w][0][oh]);
+    float Lh = 0.0f, bias_h[NG];
+#pragma unroll
+    for (int g = 0; g < NG; ++g) bias_h[g] = 0.0f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+        const float mw = s_ml[w][0][oh];
+        const float fw = (mw == -INFINITY) ? 0.0f : fast_exp2(mw - Mh);
+        Lh += fw * s_ml[w][1][oh];
+#pragma unroll
+        for (int g = 0; g < NG; ++g) bias_h[g] += fw * s_bias[w][oh][g];
+    }
+    // o[oh][d]: P V row d of tile t sits at A-row n = d / DPT (d = DPT n + t);
+    // the output lane (column, kb) holds rows 4 kb + jj
+    auto o_at = [&](int d) {
+        const int rowi = d / DPT, t = d % DPT;
+        const int kbb = rowi >> 2, jj = rowi & 3;
+        const int g = d / GS;
+        const float v = s_o[0][(t * 4 + jj) * 64 + kbb * 16 + oh + GP * g];
+        const float sc = (BITS == 4 && (t & 1)) ? 16777216.0f * 0.0625f : 16777216.0f;
+        return v * sc + bias_h[g];
+    };
+    if (p.S == 1) {
+        const int64_t obase = (b * p.Hq + kvh * G + oh) * D;
+        const float inv = Lh > 0.0f ? 1.0f / Lh : 0.0f;
+#pragma unroll
+        for (int i = 0; i < DPT; ++i) {
+            const int d = oc * DPT + i;
+            ((uint16_t*)p.out)[obase + d] = f32_to_f16(o_at(d) * inv);
+        }
+        return;
+    }
+    float* ml = p.part_ml + (bk * p.S + split) * 32;
+    float* po = p.part_o + (bk * p.S + split) * 16 * D;
+#pragma unroll
+    for (int i = 0; i < DPT; ++i) {
+        const int d = oc * DPT + i;
+        po[oh * D + d] = o_at(d);
+    }
+    if (oc == 0) {
+        ml[2 * oh] = Mh;
+        ml[2 * oh + 1] = Lh;
+    }
+}
+
+template <int MODE, int BITS, int GS, int D, int GP>
+hipError_t launch_g(int64_t B, const AttnLaunch& p, hipStream_t stream) {
+    dim3 grid(p.S, 1, (unsigned)(B * p.Hk));
+    if (p.mask_kind == MASK_ADDITIVE)
+        hipLaunchKernelGGL((attn_decode_narrow<MODE, BITS, GS, D, true, GP>), grid, dim3(NTH), 0, stream, p);
+    else
+        hipLaunchKernelGGL((attn_decode_narrow<MODE, BITS, GS, D, false, GP>), grid, dim3(NTH), 0, stream, p);
+    return hipGetLastError();
+}
+
+template <int MODE, int BITS, int GS, int D>
+hipError_t launch_n(int64_t B, const AttnLaunch& p, hipStream_t stream) {
+    if (p.G <= 2) return launch_g<MODE, BITS, GS, D, 2>(B, p, stream);
+    return launch_g<MODE, BITS, GS, D, 4>(B, p, stream);
+}
+
+// The instantiated shapes: D <= 128, and 8-bit codes with at most 2 groups
+// per row (larger rows would not keep a ring of tiles in registers).
+template <int BITS, int GS, int D>
+constexpr bool narrow_shape() {
+    return D <= 128 && D % GS == 0 && D / GS <= 4 && (BITS == 4 || D / GS <= 2);
+}
+
+template <int MODE, int BITS, int GS>
+hipError_t by_d(int D, int64_t B, const AttnLaunch& p, hipStream_t s) {
+    switch (D) {
+        case 64: if constexpr (narrow_shape<BITS, GS, 64>()) return launch_n<MODE, BITS, GS, 64>(B, p, s); else break;
+        case 128: if constexpr (narrow_shape<BITS, GS, 128>()) return launch_n<MODE, BITS, GS, 128>(B, p, s); else break;
+    }
+    return hipErrorNotSupported;
+}
+
+}  // namespace
+
+bool narrow_decode_supported(int q_dtype, int mode, int bits, int group_size, int D, int G,
+                             int64_t Lq) {
+    if (q_dtype != DT_F16 || Lq != 1 || G < 1 || G > 4) return false;
+    if (D != 64 && D != 128) return false;
+    const int gs = mode == MODE_Q8_0 ? 32 : group_size;
+    if (mode == MODE_AFFINE && (bits != 4 && bits != 8)) return false;
+    if (gs != 32 && gs != 64 && gs != 128) return false;
+    if (D % gs) return false;
+    const int ng = D / gs;
+    return ng <= 4 && (bits == 4 || ng <= 2);
+}
+
+int narrow_decode_key_quantum() { return NTK * NW; }
+
+hipError_t launch_attn_narrow(int mode, int bits, int D, int64_t B, const AttnLaunch& p,
+                              hipStream_t stream) {
+    const int gs = 1 << p.gs_log2;
+    if (mode == MODE_Q8_0) return by_d<MODE_Q8_0, 8, 32>(D, B, p, stream);
+    if (bits == 4) {
+        if (gs == 32) return by_d<MODE_AFFINE, 4, 32>(D, B, p, stream);
+        if (gs == 64) return by_d<MODE_AFFINE, 4, 64>(D, B, p, stream);
+        if (gs == 128) return by_d<MODE_AFFINE, 4, 128>(D, B, p, stream);
+    } else if (bits == 8) {
+        if (gs == 32) return by_d<MODE_AFFINE, 8, 32>(D, B, p, stream);
+        if (gs == 64) return by_d<MODE_AFFINE, 8, 64>(D, B, p, stream);
+        if (gs == 128) return by_d<MODE_AFFINE, 8, 128>(D, B, p, stream);
+    }
+    return hipErrorNotSupported;
+}
+
+}  // namespace qkv

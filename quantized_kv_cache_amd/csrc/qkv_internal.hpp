@@ -79,5 +79,15 @@ hipError_t launch_attn_matrix(int mode, int bits, int D, int64_t B, const AttnLa
 hipError_t launch_prefill_matrix(int mode, int bits, int D, int64_t B, const AttnLaunch& p,
                                  hipStream_t stream);
 constexpr int kPrefillRows = 64;    // rows per workgroup of the prefill kernel
+// Keys of one tile per wave of the single-query kernels: splits are rounded
+// to a multiple of it.
+int decode_matrix_key_quantum();
+// Single-query kernel for GQA factors up to 4 (4x4x4 matrix tiles, one key
+// per lane); used ahead of launch_attn_matrix where it applies.
+bool narrow_decode_supported(int q_dtype, int mode, int bits, int group_size, int D, int G,
+                             int64_t Lq);
+int narrow_decode_key_quantum();
+hipError_t launch_attn_narrow(int mode, int bits, int D, int64_t B, const AttnLaunch& p,
+                              hipStream_t stream);
 
 }  // namespace qkv

@@ -73,6 +73,60 @@ def test_decode_split_count_invariance(splits):
             assert_close(out, ref, f"splits={splits} {algo}")
 
 
+NARROW_CASES = [
+    # mode, bits, gs, B, Hq, Hk, L, D: GQA factor <= 4 with fp16 queries (one key
+    # per lane, 4x4x4 matrix tiles), several tiles per wave and ragged ends
+    ("affine", 4, 32, 2, 6, 2, 1000, 128),      # G = 3, 4 groups
+    ("affine", 8, 128, 1, 4, 4, 700, 128),      # G = 1, 1 group
+    ("affine", 4, 64, 1, 8, 4, 2049, 64),       # G = 2
+    ("q8_0", 8, 32, 1, 8, 2, 513, 64),          # G = 4, Q8_0
+    ("affine", 8, 32, 1, 4, 1, 333, 64),        # G = 4, 8-bit, 2 groups
+    ("affine", 4, 128, 3, 12, 3, 4500, 128),    # G = 4, batch 3
+]
+
+
+@pytest.mark.parametrize("case", NARROW_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_decode_narrow_gqa(case):
+    mode, bits, gs, B, Hq, Hk, L, D = case
+    q, kp, vp, kr, vr = _case("f16", mode, bits, gs, B, Hq, Hk, 1, L, D)
+    qd = to_dev(q, "f16")
+    ref = oracle_attention(q, "f16", kr, vr, L, mode, bits, gs, 0.1)
+    for splits in (0, 1, 3):
+        out = qkv.qsdpa_decode(qd, kp, vp, L, 0.1, num_splits=splits)
+        assert_close(out, ref, f"narrow {case} splits={splits}")
+
+
+def test_decode_strided_packs():
+    """Packs that are views with a row stride (every second cache row)."""
+    dtype, mode, bits, gs = "f16", "affine", 4, 64
+    q, kp, vp, kr, vr = _case(dtype, mode, bits, gs, 1, 8, 2, 1, 1200, 128)
+
+    def every_other(p):
+        return qkv.Pack(p.mode, p.bits, p.group_size, p.D, p.codes[:, :, ::2],
+                        p.scales[:, :, ::2], None if p.biases is None else p.biases[:, :, ::2])
+    ks, vs = every_other(kp), every_other(vp)
+    krs = {k: None if a is None else np.ascontiguousarray(a[:, :, ::2]) for k, a in kr.items()}
+    vrs = {k: None if a is None else np.ascontiguousarray(a[:, :, ::2]) for k, a in vr.items()}
+    qd = to_dev(q, dtype)
+    for L in (600, 377):
+        out = qkv.qsdpa_decode(qd, ks, vs, L, 0.1)
+        assert_close(out, oracle_attention(q, dtype, krs, vrs, L, mode, bits, gs, 0.1), f"L={L}")
+
+
+def test_decode_narrow_additive_mask():
+    dtype, mode, bits, gs = "f16", "affine", 4, 64
+    B, Hq, Hk, L, D = 2, 8, 2, 700, 128
+    q, kp, vp, kr, vr = _case(dtype, mode, bits, gs, B, Hq, Hk, 1, L, D)
+    rng = np.random.default_rng(11)
+    mask = (rng.standard_normal((B, Hq, 1, L)) * 2).astype(np.float32)
+    mask[rng.random(mask.shape) < 0.3] = -np.inf
+    mask[0, 5, 0, :] = -np.inf                        # a fully masked row -> zeros
+    out = qkv.qsdpa_decode(to_dev(q, dtype), kp, vp, L, 0.125, mask=to_dev(mask, "f32"))
+    ref = oracle_attention(q, dtype, kr, vr, L, mode, bits, gs, 0.125, mask=mask)
+    assert_close(out, ref, "masked narrow decode")
+    assert torch.all(out[0, 5] == 0)
+
+
 def test_decode_attends_only_first_L_rows():
     """Rows beyond L (garbage in the cache) never influence the result."""
     dtype, mode, bits, gs = "f16", "affine", 8, 64
