@@ -296,10 +296,7 @@ def main():
     kms = kernel_pass(torch, run, attn_of, args.warmup + args.steps, args.steps, stream)
 
     plan = qkv.qsdpa_plan(q0, ks[0], plan_L, args.splits, args.algo)
-    if plan["algo"] == "generic":
-        kernel = "attn_generic_kernel"
-    else:
-        kernel = "attn_matrix_prefill" if plan["row_tile"] == 64 else "attn_matrix_decode"
+    kernel = plan["kernel"]
     gbs = step_bytes / (ms * 1e-3) / 1e9
     rec = {
         "metric": METRIC if w.name == "decode_64k_4bit_gqa4" else f"{w.name} achieved GB/s",

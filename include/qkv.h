@@ -134,15 +134,24 @@ qkv_status qkv_update_append(const void* k_new, const void* v_new, int32_t dtype
 size_t qsdpa_workspace_bytes(int64_t B, int64_t Hq, int64_t Lq, int64_t D, int64_t L,
                              const qkv_pack* k, int32_t q_dtype, const qkv_attn_opts* opts);
 
+/* Kernels a plan can name (qkv_attn_plan.kernel). */
+typedef enum {
+    QKV_KERNEL_GENERIC = 0,        /* any dtype / format, CUDA-core arithmetic */
+    QKV_KERNEL_DECODE = 1,         /* single query, fp16, GQA factor <= 16, 16x16x32 MFMA */
+    QKV_KERNEL_DECODE_NARROW = 2,  /* single query, fp16, GQA factor <= 4, 4x4x4 MFMA */
+    QKV_KERNEL_PREFILL = 3         /* 64-row tiles, fp16, K/V dequantized into LDS */
+} qkv_kernel;
+
 /* The launch plan an attention call with these arguments would use:
- * the kernel (QKV_ALGO_GENERIC or QKV_ALGO_MATRIX), the key splits, the rows
- * per tile and the workspace size.  Errors: EINVAL for null pointers or
- * shapes that the attention calls would reject as such. */
+ * the algorithm class (QKV_ALGO_GENERIC or QKV_ALGO_MATRIX) and the kernel
+ * (qkv_kernel), the key splits, the (GQA-packed) query rows per workgroup
+ * and the workspace size.  Errors: EINVAL for null pointers or shapes that
+ * the attention calls would reject as such. */
 typedef struct {
     int32_t algo;
     int32_t num_splits;
     int32_t row_tile;
-    int32_t reserved;
+    int32_t kernel;
     int64_t keys_per_split;
     size_t workspace_bytes;
 } qkv_attn_plan;

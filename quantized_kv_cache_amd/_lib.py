@@ -14,6 +14,7 @@ QKV_F32, QKV_F16, QKV_BF16 = 0, 1, 2
 QKV_AFFINE, QKV_Q8_0 = 0, 1
 QKV_MASK_NONE, QKV_MASK_CAUSAL, QKV_MASK_ADDITIVE = 0, 1, 2
 QKV_ALGO_AUTO, QKV_ALGO_GENERIC, QKV_ALGO_MATRIX = 0, 1, 2
+QKV_KERNEL_GENERIC, QKV_KERNEL_DECODE, QKV_KERNEL_DECODE_NARROW, QKV_KERNEL_PREFILL = 0, 1, 2, 3
 
 # every symbol include/qkv.h declares
 EXPORTS = ["qkv_quantize", "qkv_update_append", "qsdpa_workspace_bytes", "qsdpa_plan",
@@ -38,7 +39,7 @@ class QkvAttnOpts(ctypes.Structure):
 
 class QkvAttnPlan(ctypes.Structure):
     _fields_ = [("algo", ctypes.c_int32), ("num_splits", ctypes.c_int32),
-                ("row_tile", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("row_tile", ctypes.c_int32), ("kernel", ctypes.c_int32),
                 ("keys_per_split", ctypes.c_int64), ("workspace_bytes", ctypes.c_size_t)]
 
 

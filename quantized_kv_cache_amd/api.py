@@ -152,6 +152,11 @@ def qsdpa_workspace_bytes(q: torch.Tensor, k: Pack, L: int, num_splits: int = 0,
                                                  _dt(q), ctypes.byref(_opts(num_splits, algo))))
 
 
+# kernel names of qsdpa_plan()["kernel"] (the device function names)
+KERNEL_NAMES = {0: "attn_generic_kernel", 1: "attn_matrix_decode", 2: "attn_decode_narrow",
+                3: "attn_matrix_prefill"}
+
+
 def qsdpa_plan(q: torch.Tensor, k: Pack, L: int, num_splits: int = 0,
                algo: str = "auto") -> dict:
     """The launch plan of an attention call: kernel, splits, row tile, workspace."""
@@ -162,7 +167,7 @@ def qsdpa_plan(q: torch.Tensor, k: Pack, L: int, num_splits: int = 0,
     _lib.check(st)
     return {"algo": {1: "generic", 2: "matrix"}[pl.algo], "num_splits": pl.num_splits,
             "row_tile": pl.row_tile, "keys_per_split": pl.keys_per_split,
-            "workspace_bytes": pl.workspace_bytes}
+            "workspace_bytes": pl.workspace_bytes, "kernel": KERNEL_NAMES[pl.kernel]}
 
 
 class Workspace:

@@ -194,8 +194,10 @@ Plan make_plan(int64_t B, int64_t Hq, int64_t Lq, int64_t D, int64_t L, const qk
         const int64_t wgs = B * Hk * ((n_rows + qkv::kPrefillRows - 1) / qkv::kPrefillRows);
         S = auto_splits(wgs, L, 1024, 256);
     } else {
-        S = pl.matrix ? auto_splits(B * Hk * pl.n_rt, L, 512, 256)
-                      : auto_splits(B * Hk * pl.n_rt, L, 256, 512);
+        // the generic kernel walks a split serially in 32-key blocks, so short
+        // splits (down to 64 keys) pay off even for small caches
+        S = pl.matrix ? auto_splits(B * Hk * pl.n_rt, L, 256, 256)
+                      : auto_splits(B * Hk * pl.n_rt, L, 64, 512);
     }
     int64_t chunk = (L + S - 1) / S;
     const int64_t gran = !pl.matrix ? 32
@@ -380,7 +382,10 @@ qkv_status qsdpa_plan(int64_t B, int64_t Hq, int64_t Lq, int64_t D, int64_t L, c
     plan->algo = pl.matrix ? QKV_ALGO_MATRIX : QKV_ALGO_GENERIC;
     plan->num_splits = pl.S;
     plan->row_tile = pl.prefill ? qkv::kPrefillRows : pl.RT;
-    plan->reserved = 0;
+    plan->kernel = !pl.matrix  ? QKV_KERNEL_GENERIC
+                   : pl.prefill ? QKV_KERNEL_PREFILL
+                   : pl.narrow  ? QKV_KERNEL_DECODE_NARROW
+                                : QKV_KERNEL_DECODE;
     plan->keys_per_split = pl.chunk;
     plan->workspace_bytes = pl.ws_bytes;
     return ok();

@@ -170,9 +170,19 @@ __device__ __forceinline__ float sum4(float x) {
     return __uint_as_float(c[0]) + __uint_as_float(c[1]);
 }
 
-// Depth of the per-wave load ring: the K and V code bytes of a 32-key tile
-// decide it, so that about 14-18 KB per wave are always requested.
-constexpr int ring_depth(int row_bytes) { return 2 * TK * row_bytes <= 4096 ? 4 : 3; }
+// Depth of the per-wave load ring (1..4 tiles): as many tiles as fit in the
+// registers left after the query operand, the output accumulators and about
+// 80 working registers.
+template <int MODE, int BITS, int GS, int D, bool FOLD>
+constexpr int ring_depth() {
+    using F = Fmt<MODE, BITS, GS, D>;
+    const int scale_sets = MODE == MODE_AFFINE ? 2 : 1;
+    const int words = 2 * F::NG * F::KW + (FOLD ? 4 : 2 * F::NSW * scale_sets) + 8 * F::VW +
+                      (FOLD ? 0 : 8 * scale_sets);
+    const int budget = 256 - 4 * F::STEPS - 4 * (D / 16) - 80;
+    const int nb = budget / words;
+    return nb < 1 ? 1 : nb > 4 ? 4 : nb;
+}
 
 template <int MODE, int BITS, int GS, int D, bool MASK, bool FOLD>
 __global__ __launch_bounds__(NTHR) void attn_matrix_decode(AttnLaunch p) {
@@ -184,13 +194,13 @@ __global__ __launch_bounds__(NTHR) void attn_matrix_decode(AttnLaunch p) {
     constexpr int VW = F::VW;
     constexpr int NSW = F::NSW;
     static_assert(!FOLD || (MODE == MODE_AFFINE && NG <= 2), "folded P V needs <= 2 groups");
-    constexpr int NB = ring_depth(D * BITS / 8);
+    constexpr int NB = ring_depth<MODE, BITS, GS, D, FOLD>();
 
     __shared__ float s_scores[NWAVE][16 * SROW];
     __shared__ float s_qsum[16][NG];
     __shared__ float s_ml[NWAVE][2][16];
     __shared__ float s_bias[NWAVE][16][2];
-    __shared__ float s_o[NWAVE / 2][64 * (D / 4)];
+    __shared__ __attribute__((aligned(16))) float s_o[NWAVE / 2][64 * (D / 4)];   // [t][lane][4]
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
@@ -345,7 +355,7 @@ __global__ __launch_bounds__(NTHR) void attn_matrix_decode(AttnLaunch p) {
     const int my_tiles = wave < ntiles ? (ntiles - wave + NWAVE - 1) / NWAVE : 0;
     Tile ring[NB];
 #pragma unroll
-    for (int r = 0; r < NB - 1; ++r) {           // tile by tile, in ring order
+    for (int r = 0; r < (NB > 1 ? NB - 1 : 1); ++r) {   // tile by tile, in ring order
         load_tile(wave + r * NWAVE, ring[r]);
         __builtin_amdgcn_sched_barrier(0);
     }
@@ -574,14 +584,25 @@ __global__ __launch_bounds__(NTHR) void attn_matrix_decode(AttnLaunch p) {
     // the state before the loop with the state at the end of a round, so the
     // wait counts stay exact at every step.  Loads past the wave's last tile
     // read zeros; only the compute of those steps is skipped.
-    const int rounds = (my_tiles + NB - 1) / NB;
-    for (int it = 0; it < rounds; ++it) {
-        const int i = it * NB;
+    if constexpr (NB == 1) {
+        // one register tile: the first load is issued with the queries, the
+        // next one right after a tile is consumed
+        for (int i = 0; i < my_tiles; ++i) {
+            process(ring[0], wave + i * NWAVE);
+            __builtin_amdgcn_sched_barrier(0);
+            load_tile(wave + (i + 1) * NWAVE, ring[0]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    } else {
+        const int rounds = (my_tiles + NB - 1) / NB;
+        for (int it = 0; it < rounds; ++it) {
+            const int i = it * NB;
 #pragma unroll
-        for (int r = 0; r < NB; ++r) {
-            load_tile(wave + (i + r + NB - 1) * NWAVE, ring[(r + NB - 1) % NB]);
-            __builtin_amdgcn_sched_barrier(0);      // issue the prefetch before computing
-            if (i + r < my_tiles) process(ring[r], wave + (i + r) * NWAVE);
+            for (int r = 0; r < NB; ++r) {
+                load_tile(wave + (i + r + NB - 1) * NWAVE, ring[(r + NB - 1) % NB]);
+                __builtin_amdgcn_sched_barrier(0);      // issue the prefetch before computing
+                if (i + r < my_tiles) process(ring[r], wave + (i + r) * NWAVE);
+            }
         }
     }
 
@@ -611,23 +632,20 @@ __global__ __launch_bounds__(NTHR) void attn_matrix_decode(AttnLaunch p) {
         if (wave >= half && wave < 2 * half) {
 #pragma unroll
             for (int t = 0; t < NT; ++t)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) s_o[wave - half][(t * 4 + j) * 64 + lane] = acc_o[t][j];
+                *(f4*)&s_o[wave - half][(t * 64 + lane) * 4] = acc_o[t];
         }
         __syncthreads();
         if (wave < half) {
 #pragma unroll
             for (int t = 0; t < NT; ++t)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) acc_o[t][j] += s_o[wave][(t * 4 + j) * 64 + lane];
+                acc_o[t] += *(const f4*)&s_o[wave][(t * 64 + lane) * 4];
         }
         __syncthreads();
     }
     if (wave == 0) {
 #pragma unroll
         for (int t = 0; t < NT; ++t)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) s_o[0][(t * 4 + j) * 64 + lane] = acc_o[t][j];
+            *(f4*)&s_o[0][(t * 64 + lane) * 4] = acc_o[t];
     }
     __syncthreads();
 
@@ -655,11 +673,11 @@ __global__ __launch_bounds__(NTHR) void attn_matrix_decode(AttnLaunch p) {
         const int kbb = rowi >> 2, j = rowi & 3;
         if constexpr (FOLD) {
             const int g = d / GS;
-            const float v = s_o[0][(t * 4 + j) * 64 + kbb * 16 + oh + G * g];
+            const float v = s_o[0][(t * 64 + kbb * 16 + oh + G * g) * 4 + j];
             const float sc = (BITS == 4 && (t & 1)) ? 16777216.0f * 0.0625f : 16777216.0f;
             return v * sc + (g ? bias_h[1] : bias_h[0]);
         } else {
-            return s_o[0][(t * 4 + j) * 64 + kbb * 16 + oh];
+            return s_o[0][(t * 64 + kbb * 16 + oh) * 4 + j];
         }
     };
 

@@ -68,7 +68,7 @@ __global__ __launch_bounds__(NTH) void attn_decode_narrow(AttnLaunch p) {
     __shared__ __attribute__((aligned(16))) _Float16 s_p[NW][NTK * 16];   // P' rows of each wave
     __shared__ float s_ml[NW][2][4];
     __shared__ float s_bias[NW][4][4];
-    __shared__ float s_o[NW / 2][64 * (D / 4)];
+    __shared__ __attribute__((aligned(16))) float s_o[NW / 2][64 * (D / 4)];   // [t][lane][4]
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -428,23 +428,20 @@ __global__ __launch_bounds__(NTH) void attn_decode_narrow(AttnLaunch p) {
         if (wave >= half && wave < 2 * half) {
 #pragma unroll
             for (int t = 0; t < NT; ++t)
-#pragma unroll
-                for (int jj = 0; jj < 4; ++jj) s_o[wave - half][(t * 4 + jj) * 64 + lane] = acc_o[t][jj];
+                *(f4*)&s_o[wave - half][(t * 64 + lane) * 4] = acc_o[t];
         }
         __syncthreads();
         if (wave < half) {
 #pragma unroll
             for (int t = 0; t < NT; ++t)
-#pragma unroll
-                for (int jj = 0; jj < 4; ++jj) acc_o[t][jj] += s_o[wave][(t * 4 + jj) * 64 + lane];
+                acc_o[t] += *(const f4*)&s_o[wave][(t * 64 + lane) * 4];
         }
         __syncthreads();
     }
     if (wave == 0) {
 #pragma unroll
         for (int t = 0; t < NT; ++t)
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj) s_o[0][(t * 4 + jj) * 64 + lane] = acc_o[t][jj];
+            *(f4*)&s_o[0][(t * 64 + lane) * 4] = acc_o[t];
     }
     __syncthreads();
 
@@ -474,7 +471,7 @@ __global__ __launch_bounds__(NTH) void attn_decode_narrow(AttnLaunch p) {
         const int rowi = d / DPT, t = d % DPT;
         const int kbb = rowi >> 2, jj = rowi & 3;
         const int g = d / GS;
-        const float v = s_o[0][(t * 4 + jj) * 64 + kbb * 16 + oh + GP * g];
+        const float v = s_o[0][(t * 64 + kbb * 16 + oh + GP * g) * 4 + jj];
         const float sc = (BITS == 4 && (t & 1)) ? 16777216.0f * 0.0625f : 16777216.0f;
         return v * sc + bias_h[g];
     };

@@ -135,3 +135,30 @@ def test_workspace_bytes(L):
     # splits x 16 rows x (m, l, o[D]) floats per (b, kv head, row tile)
     assert n == 2 * 2 * 16 * 130 * 4
     assert L.qsdpa_workspace_bytes(1, 3, 1, 128, 64, ctypes.byref(kp), _lib.QKV_F16, None) == 0
+
+
+@pytest.mark.parametrize("shape, kernel", [
+    # (B, Hq, Hk, Lq, D, L, q dtype, mode, bits, gs) -> kernel chosen by the plan
+    ((1, 4, 1, 1, 64, 256, "f32", "affine", 8, 64), _lib.QKV_KERNEL_GENERIC),
+    ((1, 32, 8, 1, 128, 65536, "f16", "affine", 4, 64), _lib.QKV_KERNEL_DECODE_NARROW),
+    ((8, 32, 8, 1, 128, 16448, "f16", "affine", 8, 64), _lib.QKV_KERNEL_DECODE_NARROW),
+    ((1, 32, 2, 1, 256, 20480, "f16", "q8_0", 8, 32), _lib.QKV_KERNEL_DECODE),
+    ((1, 32, 2, 512, 256, 20480, "f16", "q8_0", 8, 32), _lib.QKV_KERNEL_PREFILL),
+    ((1, 64, 2, 1, 128, 700, "f16", "affine", 4, 64), _lib.QKV_KERNEL_PREFILL),   # G = 32
+    ((1, 8, 2, 1, 128, 700, "bf16", "affine", 4, 64), _lib.QKV_KERNEL_GENERIC),
+])
+def test_plan_kernel_choice(L, shape, kernel):
+    """The plan names the kernel each workload shape runs on (host logic only)."""
+    B, Hq, Hk, Lq, D, Lk, qdt, mode, bits, gs = shape
+    dt = {"f32": _lib.QKV_F32, "f16": _lib.QKV_F16, "bf16": _lib.QKV_BF16}[qdt]
+    kp = _lib.QkvPack(mode=_lib.QKV_AFFINE if mode == "affine" else _lib.QKV_Q8_0, bits=bits,
+                      group_size=gs, scale_dtype=dt if mode == "affine" else _lib.QKV_F16,
+                      B=B, H=Hk, L_cap=Lk, D=D, codes=FAKE, scales=FAKE + 0x10000000,
+                      biases=FAKE + 0x20000000 if mode == "affine" else None,
+                      stride_b=Hk * Lk, stride_h=Lk, stride_l=1)
+    pl = _lib.QkvAttnPlan()
+    assert L.qsdpa_plan(B, Hq, Lq, D, Lk, ctypes.byref(kp), dt, None, ctypes.byref(pl)) == 0
+    assert pl.kernel == kernel
+    assert pl.algo == (_lib.QKV_ALGO_GENERIC if kernel == _lib.QKV_KERNEL_GENERIC
+                       else _lib.QKV_ALGO_MATRIX)
+    assert 1 <= pl.num_splits <= 256 and pl.num_splits * pl.keys_per_split >= Lk
