@@ -40,7 +40,8 @@
 //  * Every cache access is a raw buffer load: a per-tile buffer resource in
 //    SGPRs, bounded at the split's last key (rows past it read as zeros), and
 //    a loop-invariant 32-bit lane offset, so the load path costs no vector
-//    address arithmetic and the prefetch ring needs no clamping.
+//    address arithmetic and needs no clamping.  Each wave keeps one tile in
+//    registers and issues the next tile's loads as soon as it is consumed.
 #include "qkv_device.hpp"
 #include "qkv_internal.hpp"
 #include "qkv_merge.hpp"
@@ -170,20 +171,6 @@ __device__ __forceinline__ float sum4(float x) {
     return __uint_as_float(c[0]) + __uint_as_float(c[1]);
 }
 
-// Depth of the per-wave load ring (1..4 tiles): as many tiles as fit in the
-// registers left after the query operand, the output accumulators and about
-// 80 working registers.
-template <int MODE, int BITS, int GS, int D, bool FOLD>
-constexpr int ring_depth() {
-    using F = Fmt<MODE, BITS, GS, D>;
-    const int scale_sets = MODE == MODE_AFFINE ? 2 : 1;
-    const int words = 2 * F::NG * F::KW + (FOLD ? 4 : 2 * F::NSW * scale_sets) + 8 * F::VW +
-                      (FOLD ? 0 : 8 * scale_sets);
-    const int budget = 256 - 4 * F::STEPS - 4 * (D / 16) - 80;
-    const int nb = budget / words;
-    return nb < 1 ? 1 : nb > 4 ? 4 : nb;
-}
-
 template <int MODE, int BITS, int GS, int D, bool MASK, bool FOLD>
 __global__ __launch_bounds__(NTHR) void attn_matrix_decode(AttnLaunch p) {
     using F = Fmt<MODE, BITS, GS, D>;
@@ -194,7 +181,6 @@ __global__ __launch_bounds__(NTHR) void attn_matrix_decode(AttnLaunch p) {
     constexpr int VW = F::VW;
     constexpr int NSW = F::NSW;
     static_assert(!FOLD || (MODE == MODE_AFFINE && NG <= 2), "folded P V needs <= 2 groups");
-    constexpr int NB = ring_depth<MODE, BITS, GS, D, FOLD>();
 
     __shared__ float s_scores[NWAVE][16 * SROW];
     __shared__ float s_qsum[16][NG];
@@ -244,7 +230,7 @@ __global__ __launch_bounds__(NTHR) void attn_matrix_decode(AttnLaunch p) {
     const int vg = (F::VCODES * n) / GS;          // group of the lane's dequantized P V chunk
 
     // Registers of one tile.  Only loads write them; every use waits in
-    // process(), so the loads of the next tiles stay in flight meanwhile.
+    // process().
     // Folded tiles load the scale and bias rows of the tile's 32 keys
     // cooperatively (lane l: key l % 32) and lanes fetch the rows they need
     // with cross-lane shuffles.
@@ -350,15 +336,11 @@ __global__ __launch_bounds__(NTHR) void attn_matrix_decode(AttnLaunch p) {
         qraw[st] = *(const uint4*)(qrow + g * GS + kb * (GS / 4) + 8 * u);   // 8 consecutive halves
     }
     // keep the query loads ahead of the tile loads (waiting for q must not
-    // drain the ring)
+    // wait for the tile)
     __builtin_amdgcn_sched_barrier(0);
     const int my_tiles = wave < ntiles ? (ntiles - wave + NWAVE - 1) / NWAVE : 0;
-    Tile ring[NB];
-#pragma unroll
-    for (int r = 0; r < (NB > 1 ? NB - 1 : 1); ++r) {   // tile by tile, in ring order
-        load_tile(wave + r * NWAVE, ring[r]);
-        __builtin_amdgcn_sched_barrier(0);
-    }
+    Tile cur;
+    load_tile(wave, cur);
     __builtin_amdgcn_sched_barrier(0);
 
     // ---------------------------------------------------------------- queries
@@ -575,35 +557,15 @@ __global__ __launch_bounds__(NTHR) void attn_matrix_decode(AttnLaunch p) {
         }
     };
 
-    // NB register buffers in rotation: the loads of the next NB - 1 tiles are in
-    // flight while the current one computes (small tiles get a deeper ring, so
-    // that about 18 KB per wave are always requested).  Prefetches are
-    // unconditional (tiles past the split read as zeros), so the wait counts
-    // stay exact.
-    // Whole rounds of NB steps and no early exit: the loop header only merges
-    // the state before the loop with the state at the end of a round, so the
-    // wait counts stay exact at every step.  Loads past the wave's last tile
-    // read zeros; only the compute of those steps is skipped.
-    if constexpr (NB == 1) {
-        // one register tile: the first load is issued with the queries, the
-        // next one right after a tile is consumed
-        for (int i = 0; i < my_tiles; ++i) {
-            process(ring[0], wave + i * NWAVE);
-            __builtin_amdgcn_sched_barrier(0);
-            load_tile(wave + (i + 1) * NWAVE, ring[0]);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-    } else {
-        const int rounds = (my_tiles + NB - 1) / NB;
-        for (int it = 0; it < rounds; ++it) {
-            const int i = it * NB;
-#pragma unroll
-            for (int r = 0; r < NB; ++r) {
-                load_tile(wave + (i + r + NB - 1) * NWAVE, ring[(r + NB - 1) % NB]);
-                __builtin_amdgcn_sched_barrier(0);      // issue the prefetch before computing
-                if (i + r < my_tiles) process(ring[r], wave + (i + r) * NWAVE);
-            }
-        }
+    // One register tile per wave: the next tile's loads are issued as soon as
+    // a tile is consumed (deeper register rings measured no faster: with every
+    // CU streaming they only lengthen the memory queues).  Loads past the
+    // split read zeros, so the loop needs no clamping and its waits are exact.
+    for (int i = 0; i < my_tiles; ++i) {
+        process(cur, wave + i * NWAVE);
+        __builtin_amdgcn_sched_barrier(0);
+        load_tile(wave + (i + 1) * NWAVE, cur);
+        __builtin_amdgcn_sched_barrier(0);
     }
 
     // ---------------------------------------------------------------- merge waves

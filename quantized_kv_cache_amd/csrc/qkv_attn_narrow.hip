@@ -30,9 +30,9 @@
 //    row of P' to a per-wave LDS tile, and ds_read_b64_tr_b16 reads it back
 //    transposed as the B operand (8 keys of one column per lane).
 //  * K/V stream through raw buffer loads with per-tile resources bounded at
-//    the split's last key, a ring of NB tiles in flight per wave, and whole
-//    rounds of the ring without early exit (loads past the wave's tiles read
-//    zeros, their compute is skipped), which keeps the load wait counts exact.
+//    the split's last key (rows past it read as zeros, so no clamping).  Each
+//    wave keeps one tile in registers and issues the next tile's loads as
+//    soon as it has consumed one.
 #include "qkv_internal.hpp"
 #include "qkv_mfma.hpp"
 
@@ -46,9 +46,6 @@ constexpr int NTK = 64;         // keys per tile (one per lane)
 constexpr int NW = 8;           // waves per workgroup
 constexpr int NTH = NW * 64;
 
-// tiles in the per-wave ring: about 18 KB of K/V in flight per wave
-constexpr int narrow_ring(int row_bytes) { return row_bytes <= 64 ? 3 : 2; }
-
 template <int MODE, int BITS, int GS, int D, bool MASK, int GP>
 __global__ __launch_bounds__(NTH) void attn_decode_narrow(AttnLaunch p) {
     constexpr int NG = D / GS;
@@ -61,7 +58,6 @@ __global__ __launch_bounds__(NTH) void attn_decode_narrow(AttnLaunch p) {
     constexpr int VW = VB >= 4 ? VB / 4 : 1;
     constexpr int SROWB = NG * 2;                 // bytes of a row of scales
     constexpr int NSW = SROWB >= 4 ? SROWB / 4 : 1;
-    constexpr int NB = narrow_ring(ROWB);
     static_assert(NG <= 4 && NBANK >= 1, "narrow kernel: <= 4 groups, D >= 64");
     static_assert(GP * NG <= 16, "P' has 16 columns");
 
@@ -165,12 +161,9 @@ __global__ __launch_bounds__(NTH) void attn_decode_narrow(AttnLaunch p) {
                 else bufn(rv, off, T.v[c][e], VW);
             }
     };
-    Tile ring[NB];
-#pragma unroll
-    for (int r = 0; r < NB - 1; ++r) {           // tile by tile, in ring order
-        load_tile(wave + r * NW, ring[r]);
-        __builtin_amdgcn_sched_barrier(0);
-    }
+    Tile cur;
+    load_tile(wave, cur);
+    __builtin_amdgcn_sched_barrier(0);
     // An opaque zero, defined after the tile loads (the memory clobber keeps
     // them ahead of it): the q arithmetic below depends on it, so the wait for
     // the q loads cannot be placed before the tile loads are issued.
@@ -380,17 +373,15 @@ __global__ __launch_bounds__(NTH) void attn_decode_narrow(AttnLaunch p) {
         lds_order();
     };
 
-    // whole rounds of the ring; loads are unconditional (tiles past the
-    // wave's last read zeros) and only the compute of such steps is skipped
-    const int rounds = (my_tiles + NB - 1) / NB;
-    for (int it = 0; it < rounds; ++it) {
-        const int i = it * NB;
-#pragma unroll
-        for (int r = 0; r < NB; ++r) {
-            load_tile(wave + (i + r + NB - 1) * NW, ring[(r + NB - 1) % NB]);
-            __builtin_amdgcn_sched_barrier(0);
-            if (i + r < my_tiles) process(ring[r], wave + (i + r) * NW);
-        }
+    // One register tile per wave: the next tile's loads are issued as soon as
+    // a tile is consumed.  Deeper register rings measured slower (with every
+    // CU streaming they only lengthen the memory queues; 64K-context 4-bit
+    // decode: 3 tiles 28.1 us, 2 tiles 26.0 us, 1 tile 24.9 us per call).
+    for (int i = 0; i < my_tiles; ++i) {
+        process(cur, wave + i * NW);
+        __builtin_amdgcn_sched_barrier(0);
+        load_tile(wave + (i + 1) * NW, cur);
+        __builtin_amdgcn_sched_barrier(0);
     }
 
     // ------------------------------------------------------------ merge waves
@@ -515,7 +506,7 @@ hipError_t launch_n(int64_t B, const AttnLaunch& p, hipStream_t stream) {
 }
 
 // The instantiated shapes: D <= 128, and 8-bit codes with at most 2 groups
-// per row (larger rows would not keep a ring of tiles in registers).
+// per row (larger rows exceed the register budget of one tile).
 template <int BITS, int GS, int D>
 constexpr bool narrow_shape() {
     return D <= 128 && D % GS == 0 && D / GS <= 4 && (BITS == 4 || D / GS <= 2);
