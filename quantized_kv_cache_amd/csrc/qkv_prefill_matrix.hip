@@ -11,10 +11,14 @@
 // (qmm.cu: dequantize a tile into shared memory, then matrix multiply), laid
 // out for gfx950:
 //
-//  * A workgroup (4 waves) owns 64 GQA-packed rows (row p = query i * G +
-//    head g of one kv head): 16 rows per wave.  It streams key tiles of 64:
-//    the 256 threads dequantize the next K and V tile (fp16, row-major, in
-//    LDS, double buffered) while the current one is consumed.
+//  * A workgroup owns 64 GQA-packed rows (row p = query i * G + head g of one
+//    kv head) and streams key tiles of 64.  Its 512 threads dequantize the
+//    next K and V tile (fp16, row-major, in LDS, double buffered) while the
+//    current one is consumed.
+//  * 8 waves: waves w and w + 4 share the 16-row block w % 4 and take the two
+//    32-key halves of every tile, so each SIMD runs two waves (one hides the
+//    other's LDS and matrix latencies).  The two halves keep separate
+//    softmax states and are merged through LDS at the end.
 //  * S^T = K Q^T on v_mfma_f32_16x16x32_f16 (A = K rows from LDS, B = the
 //    wave's queries in registers), so each lane holds 4 keys x its row per
 //    16-key subtile: the online softmax of a row is lane-local plus a 4-lane
@@ -28,84 +32,49 @@
 //    cross a row's last visible key; fully hidden tiles are skipped.
 //  * With several key splits the rows' (m, l, o) go to the workspace for the
 //    split merge kernel.
-#include "qkv_device.hpp"
 #include "qkv_internal.hpp"
+#include "qkv_mfma.hpp"
 
 namespace qkv {
 
 namespace {
 
-typedef _Float16 h2 __attribute__((ext_vector_type(2)));
-typedef _Float16 h4 __attribute__((ext_vector_type(4)));
-typedef _Float16 h8 __attribute__((ext_vector_type(8)));
-typedef short s4 __attribute__((ext_vector_type(4)));
-typedef float f4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+using namespace mf;
 
 constexpr int BM = 64;          // rows per workgroup
 constexpr int BN = 64;          // keys per tile
-constexpr int PNTHR = 256;
-
-__device__ __forceinline__ uint32_t perm_b(uint32_t hi, uint32_t lo, uint32_t sel) {
-    return __builtin_amdgcn_perm(hi, lo, sel);
-}
-__device__ __forceinline__ h2 as_h2(uint32_t u) { return __builtin_bit_cast(h2, u); }
-__device__ __forceinline__ uint32_t as_u(h2 h) { return __builtin_bit_cast(uint32_t, h); }
-__device__ __forceinline__ f4 mfma(h8 a, h8 b, f4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
-}
-__device__ __forceinline__ float max4(float x) {
-    auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-    auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return fmaxf(__uint_as_float(c[0]), __uint_as_float(c[1]));
-}
-__device__ __forceinline__ float sum4(float x) {
-    auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-    auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return __uint_as_float(c[0]) + __uint_as_float(c[1]);
-}
+constexpr int PW = 8;           // waves
+constexpr int PNTHR = PW * 64;
 
 // Dequantize 16 consecutive codes of a row (one uint4) into 8 fp16 pairs.
 // Affine: s * c + b rounded once (v_pk_fma_f16); Q8_0: d * c (c exact in fp16).
 template <int MODE, int BITS>
 __device__ __forceinline__ void dequant16(uint4 w, uint32_t s2, uint32_t b2, uint32_t out[8]) {
     const uint32_t x[4] = {w.x, w.y, w.z, w.w};
-    if constexpr (MODE == MODE_Q8_0) {
-        // bytes c -> halves 1024 + (c + 128), minus 1152, times d
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 4; ++i) {
+        if constexpr (MODE == MODE_Q8_0) {
+            // bytes c -> halves 1024 + (c + 128), minus 1152, times d
             const uint32_t u = x[i] ^ 0x80808080u;
-            const uint32_t lo = perm_b(0x64646464u, u, 0x04010400u);   // [u0, 0x64, u1, 0x64]
-            const uint32_t hi = perm_b(0x64646464u, u, 0x04030402u);   // [u2, 0x64, u3, 0x64]
-            const h2 c0 = as_h2(lo) - (h2){(_Float16)1152.0f, (_Float16)1152.0f};
-            const h2 c1 = as_h2(hi) - (h2){(_Float16)1152.0f, (_Float16)1152.0f};
+            const h2 c0 = as_h2(perm_b(0x64646464u, u, 0x04010400u)) - (h2){(_Float16)1152.0f, (_Float16)1152.0f};
+            const h2 c1 = as_h2(perm_b(0x64646464u, u, 0x04030402u)) - (h2){(_Float16)1152.0f, (_Float16)1152.0f};
             out[2 * i] = as_u(c0 * as_h2(s2));
             out[2 * i + 1] = as_u(c1 * as_h2(s2));
-        }
-    } else if constexpr (BITS == 8) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const uint32_t lo = perm_b(0x64646464u, x[i], 0x04010400u);
-            const uint32_t hi = perm_b(0x64646464u, x[i], 0x04030402u);
-            const h2 c0 = as_h2(lo) - (h2){(_Float16)1024.0f, (_Float16)1024.0f};
-            const h2 c1 = as_h2(hi) - (h2){(_Float16)1024.0f, (_Float16)1024.0f};
+        } else {
+            const h2 c0 = as_h2(perm_b(0x64646464u, x[i], 0x04010400u)) - (h2){(_Float16)1024.0f, (_Float16)1024.0f};
+            const h2 c1 = as_h2(perm_b(0x64646464u, x[i], 0x04030402u)) - (h2){(_Float16)1024.0f, (_Float16)1024.0f};
             out[2 * i] = as_u(__builtin_elementwise_fma(c0, as_h2(s2), as_h2(b2)));
             out[2 * i + 1] = as_u(__builtin_elementwise_fma(c1, as_h2(s2), as_h2(b2)));
         }
-    } else {
-        (void)out;   // 4-bit uses dequant8x4
     }
 }
 
 // 4-bit: 8 consecutive codes (one dword) into 4 fp16 pairs.
 __device__ __forceinline__ void dequant8_4bit(uint32_t w, uint32_t s2, uint32_t b2, uint32_t out[4]) {
-    // element e sits in bits [4e, 4e + 4): pairs (0,1), (2,3), (4,5), (6,7)
+    // element e sits in bits [4e, 4e + 4)
     const uint32_t a = perm_b(0u, w, 0x0C010C00u);             // [b0, 0, b1, 0]: (c0|c1<<4, c2|c3<<4)
     const uint32_t c = perm_b(0u, w, 0x0C030C02u);             // bytes 2, 3
     const h2 k1024 = {(_Float16)1024.0f, (_Float16)1024.0f};
-    // pair (e0, e2) from low nibbles, (e1, e3) from high nibbles of bytes 0, 1
     const h2 lo0 = as_h2((a & 0x000F000Fu) | 0x64006400u) - k1024;          // c0, c2
     const h2 hi0 = as_h2(((a >> 4) & 0x000F000Fu) | 0x64006400u) - k1024;   // c1, c3
     const h2 lo1 = as_h2((c & 0x000F000Fu) | 0x64006400u) - k1024;          // c4, c6
@@ -121,23 +90,27 @@ __device__ __forceinline__ void dequant8_4bit(uint32_t w, uint32_t s2, uint32_t 
     out[3] = perm_b(as_u(v57), as_u(v46), 0x07060302u);
 }
 
-template <int MODE, int BITS, int GS, int D, int MK>
+template <int MODE, int BITS, int GS, int D>
 __global__ __launch_bounds__(PNTHR) void attn_matrix_prefill(AttnLaunch p) {
     constexpr int NG = D / GS;
     constexpr int ROWB = D * BITS / 8;             // code bytes per row
     constexpr int LDROW = D + 16;                  // LDS row stride in halves (pad 32 B)
     constexpr int STEPS = D / 32;                  // K-steps of S^T
     constexpr int NT = D / 16;                     // output d-tiles
-    constexpr int TPR = PNTHR / BN;                // dequant threads per key row (4)
-    constexpr int DPT = D / TPR;                   // d per dequant thread
+    constexpr int TPR = D / 16 < 8 ? D / 16 : 8;   // dequant threads per key row
+    constexpr int DPT = D / TPR;                   // d per dequant thread (16 or 32: one group)
     constexpr int CB = DPT * BITS / 8;             // code bytes per dequant thread
-    constexpr int NCH = CB / 16 > 0 ? CB / 16 : 1; // uint4 loads per dequant thread (4-bit D=64: 1/2)
+    constexpr int NCH = CB / 16 > 0 ? CB / 16 : 1; // uint4 loads per dequant thread
+    constexpr int DQ_THREADS = TPR * BN;
+    static_assert(DPT % 16 == 0 && DPT <= GS, "a dequant thread covers whole 16-d steps of one group");
 
     __shared__ __attribute__((aligned(16))) _Float16 s_k[2][BN * LDROW];
     __shared__ __attribute__((aligned(16))) _Float16 s_v[2][BN * LDROW];
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int rb = wave & 3;                       // 16-row block
+    const int kh = wave >> 2;                      // 32-key half of each tile
     const int lane = tid & 63;
     const int n = lane & 15;
     const int kb = lane >> 4;
@@ -150,7 +123,7 @@ __global__ __launch_bounds__(PNTHR) void attn_matrix_prefill(AttnLaunch p) {
     const float sl = p.scale * kLog2e;
 
     // this lane's row (the B column of S^T and of O^T)
-    const int row = rt * BM + wave * 16 + n;
+    const int row = rt * BM + rb * 16 + n;
     const bool row_ok = row < p.n_rows;
     const int rowc = row_ok ? row : p.n_rows - 1;
     const int64_t qi = rowc / G;
@@ -181,14 +154,16 @@ __global__ __launch_bounds__(PNTHR) void attn_matrix_prefill(AttnLaunch p) {
         }
     }
 
-    // ---- dequantization of a K/V tile into LDS
+    // ---- dequantization of a K/V tile into LDS (threads below DQ_THREADS)
     const int64_t krow0 = b * p.k.sb + kvh * p.k.sh;
     const int64_t vrow0 = b * p.v.sb + kvh * p.v.sh;
-    const int drow = tid / TPR;                    // key row of the tile
-    const int dq = tid % TPR;                      // quarter of the row
+    const bool dq_on = tid < DQ_THREADS;
+    const int drow = (tid / TPR) % BN;             // key row of the tile
+    const int dq = tid % TPR;                      // slice of the row
+    const int dgrp = (dq * DPT) / GS;              // its quantization group
     struct Raw {
         uint4 kc[NCH], vc[NCH];
-        uint32_t ks, kbias, vs, vbias;             // fp16 pairs (scale, bias) of the quarter's group(s)
+        uint32_t ks, kbias, vs, vbias;             // fp16 scale / bias of the slice's group
     };
     auto load_raw = [&](int t, Raw& R) {
         int64_t j = j_begin + (int64_t)t * BN + drow;
@@ -207,18 +182,11 @@ __global__ __launch_bounds__(PNTHR) void attn_matrix_prefill(AttnLaunch p) {
                 R.vc[c] = uint4{bb.x, bb.y, 0u, 0u};
             }
         }
-        // scales of the groups the quarter touches (a quarter spans 1 or 2 groups)
-        const int g0 = (dq * DPT) / GS;
-        const uint16_t* ksc = (const uint16_t*)p.k.scales + kr * NG;
-        const uint16_t* vsc = (const uint16_t*)p.v.scales + vr * NG;
-        const int g1 = min(g0 + 1, NG - 1);
-        R.ks = (uint32_t)ksc[g0] | ((uint32_t)ksc[g1] << 16);
-        R.vs = (uint32_t)vsc[g0] | ((uint32_t)vsc[g1] << 16);
+        R.ks = ((const uint16_t*)p.k.scales)[kr * NG + dgrp];
+        R.vs = ((const uint16_t*)p.v.scales)[vr * NG + dgrp];
         if constexpr (MODE == MODE_AFFINE) {
-            const uint16_t* kbi = (const uint16_t*)p.k.biases + kr * NG;
-            const uint16_t* vbi = (const uint16_t*)p.v.biases + vr * NG;
-            R.kbias = (uint32_t)kbi[g0] | ((uint32_t)kbi[g1] << 16);
-            R.vbias = (uint32_t)vbi[g0] | ((uint32_t)vbi[g1] << 16);
+            R.kbias = ((const uint16_t*)p.k.biases)[kr * NG + dgrp];
+            R.vbias = ((const uint16_t*)p.v.biases)[vr * NG + dgrp];
         } else {
             R.kbias = R.vbias = 0u;
         }
@@ -226,17 +194,11 @@ __global__ __launch_bounds__(PNTHR) void attn_matrix_prefill(AttnLaunch p) {
     auto store_tile = [&](const Raw& R, int buf) {
         _Float16* kd = &s_k[buf][drow * LDROW + dq * DPT];
         _Float16* vd = &s_v[buf][drow * LDROW + dq * DPT];
-        const int g0 = (dq * DPT) / GS;
-        auto pair_of = [&](uint32_t two, int d) -> uint32_t {     // fp16 of group of d, twice
-            const int g = (dq * DPT + d) / GS - g0;
-            const uint32_t h = g ? (two >> 16) : (two & 0xffffu);
-            return h | (h << 16);
-        };
+        const uint32_t ks2 = R.ks | (R.ks << 16), kb2 = R.kbias | (R.kbias << 16);
+        const uint32_t vs2 = R.vs | (R.vs << 16), vb2 = R.vbias | (R.vbias << 16);
 #pragma unroll
         for (int c = 0; c < DPT / 16; ++c) {              // 16 d per step
             uint32_t ko[8], vo[8];
-            const uint32_t ks2 = pair_of(R.ks, 16 * c), kb2 = pair_of(R.kbias, 16 * c);
-            const uint32_t vs2 = pair_of(R.vs, 16 * c), vb2 = pair_of(R.vbias, 16 * c);
             if constexpr (BITS == 4) {
                 const uint4 kw = R.kc[c / 2], vw = R.vc[c / 2];
                 const uint32_t kx[4] = {kw.x, kw.y, kw.z, kw.w}, vx[4] = {vw.x, vw.y, vw.z, vw.w};
@@ -262,7 +224,7 @@ __global__ __launch_bounds__(PNTHR) void attn_matrix_prefill(AttnLaunch p) {
     float m_run = -INFINITY, l_run = 0.0f;
 
     Raw ra;
-    if (ntile > 0) {
+    if (ntile > 0 && dq_on) {
         load_raw(0, ra);
         store_tile(ra, 0);
         if (ntile > 1) load_raw(1, ra);
@@ -271,29 +233,29 @@ __global__ __launch_bounds__(PNTHR) void attn_matrix_prefill(AttnLaunch p) {
 
     for (int t = 0; t < ntile; ++t) {
         const int buf = t & 1;
-        const int64_t j0 = j_begin + (int64_t)t * BN;
+        const int64_t j0 = j_begin + (int64_t)t * BN + 32 * kh;   // first key of this wave's half
         const _Float16* kt = s_k[buf];
         const _Float16* vt = s_v[buf];
 
-        // S^T for 4 subtiles of 16 keys: lane holds keys 16 u + 4 kb + jj of row n
-        float sc[4][4];
+        // S^T for the half's 2 subtiles of 16 keys: lane holds keys 16 u + 4 kb + jj of row n
+        float sc[2][4];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
+        for (int u = 0; u < 2; ++u) {
             f4 s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int st = 0; st < STEPS; ++st) {
-                const h8 ka = *(const h8*)(kt + (16 * u + n) * LDROW + 32 * st + 8 * kb);
-                s = mfma(ka, qb[st], s);
+                const h8 ka = *(const h8*)(kt + (32 * kh + 16 * u + n) * LDROW + 32 * st + 8 * kb);
+                s = mfma16(ka, qb[st], s);
             }
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) sc[u][jj] = s[jj] * sl;
         }
-        // masking: only tiles reaching past the first row's last visible key,
+        // masking: only halves reaching past the first row's last visible key,
         // the ragged end of the split, or with an additive mask
-        const bool edge = (j0 + BN - 1 > lo_vis) || (j0 + BN > j_end) || p.mask_kind == MASK_ADDITIVE;
+        const bool edge = (j0 + 31 > lo_vis) || (j0 + 32 > j_end) || p.mask_kind == MASK_ADDITIVE;
         if (edge) {
 #pragma unroll
-            for (int u = 0; u < 4; ++u)
+            for (int u = 0; u < 2; ++u)
 #pragma unroll
                 for (int jj = 0; jj < 4; ++jj) {
                     const int64_t j = j0 + 16 * u + 4 * kb + jj;
@@ -305,10 +267,10 @@ __global__ __launch_bounds__(PNTHR) void attn_matrix_prefill(AttnLaunch p) {
                     sc[u][jj] = v;
                 }
         }
-        // online softmax of row n over the tile (16 keys in this lane, x4 lanes)
+        // online softmax of row n over the half (8 keys in this lane, x4 lanes)
         float mx = sc[0][0];
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
+        for (int u = 0; u < 2; ++u)
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) mx = fmaxf(mx, sc[u][jj]);
         mx = max4(mx);
@@ -322,10 +284,10 @@ __global__ __launch_bounds__(PNTHR) void attn_matrix_prefill(AttnLaunch p) {
             m_run = m_new;
         }
         const bool live = m_run != -INFINITY;
-        uint32_t pp[4][2];        // P^T operand halves: keys (16u + 4kb + jj) in pairs
+        uint32_t pp[2][2];        // P^T operand halves: keys (16u + 4kb + jj) in pairs
         float ps = 0.0f;
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
+        for (int u = 0; u < 2; ++u) {
             float e[4];
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) {
@@ -337,18 +299,16 @@ __global__ __launch_bounds__(PNTHR) void attn_matrix_prefill(AttnLaunch p) {
             pp[u][1] = as_u(c);
         }
         l_run += ps;
-        // O^T += V^T P^T: K-step ks covers subtiles 2 ks, 2 ks + 1; the lane's 8 keys are
-        // 4 kb .. 4 kb + 3 of each subtile, in the order of pp
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            const h8 pb = __builtin_bit_cast(h8, u4{pp[2 * ks][0], pp[2 * ks][1], pp[2 * ks + 1][0],
-                                                   pp[2 * ks + 1][1]});
+        // O^T += V^T P^T over the half: the lane's 8 keys are 4 kb .. 4 kb + 3 of
+        // each subtile, in the order of pp
+        {
+            const h8 pb = to_h8(pp[0][0], pp[0][1], pp[1][0], pp[1][1]);
+            const int k0a = 32 * kh + 4 * kb;            // subtile 0, keys 4kb..
+            const int k0b = 32 * kh + 16 + 4 * kb;       // subtile 1
 #pragma unroll
             for (int t2 = 0; t2 < NT; ++t2) {
                 // lane (s = n within its 16-lane group) points at V[k0 + s/4][16 t2 + 4 (s%4)];
                 // the transpose read returns V[k0 .. k0+3][16 t2 + n]
-                const int k0a = 32 * ks + 4 * kb;            // subtile 2ks, keys 4kb..
-                const int k0b = 32 * ks + 16 + 4 * kb;       // subtile 2ks+1
                 const _Float16* pa = vt + (k0a + (n >> 2)) * LDROW + 16 * t2 + 4 * (n & 3);
                 const _Float16* pb2 = vt + (k0b + (n >> 2)) * LDROW + 16 * t2 + 4 * (n & 3);
                 const s4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -357,22 +317,46 @@ __global__ __launch_bounds__(PNTHR) void attn_matrix_prefill(AttnLaunch p) {
                     (__attribute__((address_space(3))) s4*)(pb2));
                 const h8 aop = __builtin_bit_cast(h8, (short __attribute__((ext_vector_type(8)))){
                     va[0], va[1], va[2], va[3], vb[0], vb[1], vb[2], vb[3]});
-                acc[t2] = mfma(aop, pb, acc[t2]);
+                acc[t2] = mfma16(aop, pb, acc[t2]);
             }
         }
         // next tile -> the other buffer, then one barrier per tile
-        if (t + 1 < ntile) {
+        if (t + 1 < ntile && dq_on) {
             store_tile(ra, buf ^ 1);
             if (t + 2 < ntile) load_raw(t + 2, ra);
         }
         __syncthreads();
     }
 
+    // ---- merge the two key halves of each row block through LDS (the tile
+    // buffers are free after the loop's last barrier)
+    l_run = sum4(l_run);
+    float* xo = (float*)&s_k[0][0];                // [rb][t][lane][4] floats
+    float* xml = (float*)&s_v[0][0];               // [rb][lane][2]
+    if (kh == 1) {
+#pragma unroll
+        for (int t2 = 0; t2 < NT; ++t2) *(f4*)&xo[((rb * NT + t2) * 64 + lane) * 4] = acc[t2];
+        xml[(rb * 64 + lane) * 2] = m_run;
+        xml[(rb * 64 + lane) * 2 + 1] = l_run;
+    }
+    __syncthreads();
+    if (kh == 1) return;
+    {
+        const float m1 = xml[(rb * 64 + lane) * 2], l1 = xml[(rb * 64 + lane) * 2 + 1];
+        const float M = fmaxf(m_run, m1);
+        const float f0 = m_run == -INFINITY ? 0.0f : fast_exp2(m_run - M);
+        const float f1 = m1 == -INFINITY ? 0.0f : fast_exp2(m1 - M);
+#pragma unroll
+        for (int t2 = 0; t2 < NT; ++t2)
+            acc[t2] = acc[t2] * f0 + *(const f4*)&xo[((rb * NT + t2) * 64 + lane) * 4] * f1;
+        l_run = l_run * f0 + l1 * f1;
+        m_run = M;
+    }
+
     // ---- output: lane holds O^T[d = 16 t + 4 kb + jj][row n]
-    const float L = sum4(l_run);
     if (!row_ok) return;
     if (p.S == 1) {
-        const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+        const float inv = l_run > 0.0f ? 1.0f / l_run : 0.0f;
         _Float16* op = (_Float16*)p.out + ((b * p.Hq + qh) * p.Lq + qi) * D;
 #pragma unroll
         for (int t2 = 0; t2 < NT; ++t2) {
@@ -390,14 +374,14 @@ __global__ __launch_bounds__(PNTHR) void attn_matrix_prefill(AttnLaunch p) {
 #pragma unroll
     for (int t2 = 0; t2 < NT; ++t2)
         *(float4*)(po + 16 * t2 + 4 * kb) = float4{acc[t2][0], acc[t2][1], acc[t2][2], acc[t2][3]};
-    if (kb == 0) { ml[0] = m_run; ml[1] = L; }
+    if (kb == 0) { ml[0] = m_run; ml[1] = l_run; }
 }
 
 template <int MODE, int BITS, int GS, int D>
 hipError_t launch_p(int64_t B, const AttnLaunch& p, hipStream_t s) {
     const int nwg = (p.n_rows + BM - 1) / BM;
     dim3 grid(p.S, nwg, (unsigned)(B * p.Hk));
-    hipLaunchKernelGGL((attn_matrix_prefill<MODE, BITS, GS, D, 0>), grid, dim3(PNTHR), 0, s, p);
+    hipLaunchKernelGGL((attn_matrix_prefill<MODE, BITS, GS, D>), grid, dim3(PNTHR), 0, s, p);
     return hipGetLastError();
 }
 
