@@ -1,7 +1,9 @@
-// Split merge kernel: one workgroup per (tile, row) (grid x = tile, y = row); 256 threads = D/4 float4
-// columns x (1024/D) split groups.  Every load of a thread is issued before
-// its softmax states are combined (online, in log2 units), the split groups
-// then combine through LDS, and the row is written in the query dtype.
+// Split merge kernel.  One workgroup per (row tile, row, 64-d chunk of the
+// output row): grid x = tile, y = row, z = chunk.  Its 256 threads are 16
+// float4 columns x 16 split groups, so a thread combines at most S/16 split
+// states (all its loads issued before it waits: one memory round trip for
+// S <= 128).  States combine online in log2 units, the split groups combine
+// through LDS, and the chunk is written in the query dtype.
 #include "qkv_merge.hpp"
 
 namespace qkv {
@@ -26,22 +28,25 @@ __device__ __forceinline__ void combine(State& a, float m, float l, float4 o) {
     a.m = mm;
 }
 
+constexpr int MC = 16;          // float4 columns per workgroup (64 d)
+constexpr int SG = 256 / MC;    // split groups
+constexpr int U = 8;            // loads in flight per batch
+
 template <int QT, int D>
 __global__ __launch_bounds__(256) void merge_splits_kernel(AttnLaunch p) {
     constexpr int F4 = D / 4;
-    constexpr int SG = 256 / F4;
-    constexpr int U = 8;                          // loads in flight per batch
     __shared__ State red[256];
 
-    const int r = blockIdx.y;
     const int64_t tile = blockIdx.x;
+    const int r = blockIdx.y;
     const int rt = (int)(tile % p.n_rt);
     const int64_t bk = tile / p.n_rt;
     const int pr = rt * 16 + r;
     if (pr >= p.n_rows) return;                   // whole workgroup leaves together
     const int64_t b = bk / p.Hk, kvh = bk % p.Hk;
     const int64_t i = pr / p.G, h = kvh * p.G + pr % p.G;
-    const int f = threadIdx.x % F4, sg = threadIdx.x / F4;
+    const int f = blockIdx.z * MC + threadIdx.x % MC;   // float4 column of the row
+    const int sg = threadIdx.x / MC;
     const int S = p.S;
 
     const float2* ml = (const float2*)p.part_ml + (tile * S * 16 + r);
@@ -67,7 +72,7 @@ __global__ __launch_bounds__(256) void merge_splits_kernel(AttnLaunch p) {
     if (sg != 0) return;
 #pragma unroll
     for (int g = 1; g < SG; ++g) {
-        const State& o = red[g * F4 + f];
+        const State& o = red[g * MC + threadIdx.x];
         combine(st, o.m, o.l, o.o);
     }
     const float inv = st.l > 0.0f ? 1.0f / st.l : 0.0f;
@@ -80,7 +85,9 @@ __global__ __launch_bounds__(256) void merge_splits_kernel(AttnLaunch p) {
 
 template <int QT>
 hipError_t launch_q(int D, int64_t B, const AttnLaunch& p, hipStream_t s) {
-    dim3 grid((unsigned)(B * p.Hk * p.n_rt), 16);
+    // rows of a tile that exist: all 16 unless the (single) tile is short
+    const unsigned rows = (unsigned)(p.n_rows < 16 ? p.n_rows : 16);
+    dim3 grid((unsigned)(B * p.Hk * p.n_rt), rows, (unsigned)(D / (4 * MC)));
     switch (D) {
         case 64: hipLaunchKernelGGL((merge_splits_kernel<QT, 64>), grid, dim3(256), 0, s, p); break;
         case 128: hipLaunchKernelGGL((merge_splits_kernel<QT, 128>), grid, dim3(256), 0, s, p); break;
