@@ -564,7 +564,9 @@ __global__ __launch_bounds__(NTHR) void attn_matrix_decode(AttnLaunch p) {
     for (int i = 0; i < my_tiles; ++i) {
         process(cur, wave + i * NWAVE);
         __builtin_amdgcn_sched_barrier(0);
-        load_tile(wave + (i + 1) * NWAVE, cur);
+        // no loads after the last tile: they would hold the wave (and the
+        // workgroup merge behind it) until the CU's memory queue drains
+        if (i + 1 < my_tiles) load_tile(wave + (i + 1) * NWAVE, cur);
         __builtin_amdgcn_sched_barrier(0);
     }
 

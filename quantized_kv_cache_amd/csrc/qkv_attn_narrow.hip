@@ -45,6 +45,8 @@ using namespace mf;
 constexpr int NTK = 64;         // keys per tile (one per lane)
 constexpr int NW = 8;           // waves per workgroup
 constexpr int NTH = NW * 64;
+constexpr float kLazy = 8.0f;                  // running-maximum slack (log2 units)
+constexpr uint32_t kLazyBigScale = 0x5800u;    // fp16 128 = 2^(15 - kLazy)
 
 template <int MODE, int BITS, int GS, int D, bool MASK, int GP>
 __global__ __launch_bounds__(NTH) void attn_decode_narrow(AttnLaunch p) {
@@ -63,8 +65,9 @@ __global__ __launch_bounds__(NTH) void attn_decode_narrow(AttnLaunch p) {
 
     __shared__ __attribute__((aligned(16))) _Float16 s_p[NW][NTK * 16];   // P' rows of each wave
     __shared__ float s_ml[NW][2][4];
+    __shared__ int s_next;                        // next tile of the split to hand out
     __shared__ float s_bias[NW][4][4];
-    __shared__ __attribute__((aligned(16))) float s_o[NW / 2][64 * (D / 4)];   // [t][lane][4]
+    __shared__ __attribute__((aligned(16))) float s_o[NW][64 * (D / 4)];   // [t][lane][4] per wave
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -77,11 +80,12 @@ __global__ __launch_bounds__(NTH) void attn_decode_narrow(AttnLaunch p) {
     const int64_t kvh = bk % p.Hk;
     const int G = p.G;
     const float sl = p.scale * kLog2e;            // scores in log2 units
+    if (tid == 0) s_next = NW;                    // tiles 0 .. NW-1 go to the waves in order
+    __syncthreads();
 
     const int64_t j0 = (int64_t)split * p.chunk;
     const int64_t j1 = min(p.L, j0 + p.chunk);
     const int ntiles = (int)((j1 - j0 + NTK - 1) / NTK);
-    const int my_tiles = wave < ntiles ? (ntiles - wave + NW - 1) / NW : 0;
     const int64_t jmax = j1 - 1;
 
     const int64_t krow0 = b * p.k.sb + kvh * p.k.sh;
@@ -293,10 +297,20 @@ __global__ __launch_bounds__(NTH) void attn_decode_narrow(AttnLaunch p) {
         for (int h = 0; h < 4; ++h)
             if (h >= G) z[h] = -INFINITY;
 
-        // ---- online softmax, lazy maximum
+        // ---- online softmax, lazy maximum: the running maximum is raised only
+        // when a score exceeds it by kLazy (log2 units), so p = 2^(z - m) <= 2^kLazy
+        // and P' = p s_v stays in fp16 range for |s_v| < 2^(15 - kLazy); a key with
+        // a larger value scale raises it as soon as its score exceeds it
+        bool big_sv = false;
+#pragma unroll
+        for (int q = 0; q < NSW; ++q) {
+            const uint32_t a = T.vs[q] & 0x7FFF7FFFu;
+            big_sv |= (a & 0xFFFFu) >= kLazyBigScale || (a >> 16) >= kLazyBigScale;
+        }
+        const float slack = big_sv ? 0.0f : kLazy;
         bool grow = false;
 #pragma unroll
-        for (int h = 0; h < 4; ++h) grow |= z[h] > m_h[h];
+        for (int h = 0; h < 4; ++h) grow |= z[h] > m_h[h] + slack;
         if (__ballot(grow) != 0ull) {
             float alpha[4];
 #pragma unroll
@@ -363,7 +377,7 @@ __global__ __launch_bounds__(NTH) void attn_decode_narrow(AttnLaunch p) {
                 uint32_t a[4];
 #pragma unroll
                 for (int q2 = 0; q2 < 4; ++q2) {
-                    uint32_t x = pair_sub<BITS>(T.v[c][2 * q2], T.v[c][2 * q2 + 1], t);
+                    uint32_t x = pair_sub_byte<BITS>(T.v[c][2 * q2], T.v[c][2 * q2 + 1], t);
                     if constexpr (MODE == MODE_Q8_0) x ^= 0x00800080u;
                     a[q2] = x;
                 }
@@ -377,14 +391,27 @@ __global__ __launch_bounds__(NTH) void attn_decode_narrow(AttnLaunch p) {
     // a tile is consumed.  Deeper register rings measured slower (with every
     // CU streaming they only lengthen the memory queues; 64K-context 4-bit
     // decode: 3 tiles 28.1 us, 2 tiles 26.0 us, 1 tile 24.9 us per call).
-    for (int i = 0; i < my_tiles; ++i) {
-        process(cur, wave + i * NW);
+    // After its first tile a wave takes the split's next unclaimed tile (an
+    // LDS counter), so waves whose data arrives early take more tiles and the
+    // workgroup's waves finish together.
+    int tt = wave;
+    while (tt < ntiles) {
+        int nxt = 0;
+        if (lane == 0) nxt = atomicAdd(&s_next, 1);
+        process(cur, tt);                         // hides the atomic's latency
+        nxt = __builtin_amdgcn_readfirstlane(nxt);
         __builtin_amdgcn_sched_barrier(0);
-        load_tile(wave + (i + 1) * NW, cur);
+        // no loads after the last tile: they would hold the wave (and the
+        // workgroup merge behind it) until the CU's memory queue drains
+        if (nxt < ntiles) load_tile(nxt, cur);
         __builtin_amdgcn_sched_barrier(0);
+        tt = nxt;
     }
 
     // ------------------------------------------------------------ merge waves
+    // Every wave leaves its unscaled state in LDS; after one barrier each
+    // thread combines the 8 waves' states for its output elements (a single
+    // synchronisation: the tail after the slowest wave stays short).
 #pragma unroll
     for (int h = 0; h < 4; ++h) {
         l_h[h] = wave_sum(l_h[h]);
@@ -400,92 +427,56 @@ __global__ __launch_bounds__(NTH) void attn_decode_narrow(AttnLaunch p) {
             for (int g = 0; g < NG; ++g) s_bias[wave][h][g] = bs[h][g];
         }
     }
-    __syncthreads();
-    {
-        float f[4];
 #pragma unroll
-        for (int h = 0; h < 4; ++h) {
-            float M = -INFINITY;
-#pragma unroll
-            for (int w = 0; w < NW; ++w) M = fmaxf(M, s_ml[w][0][h]);
-            f[h] = m_h[h] == -INFINITY ? 0.0f : fast_exp2(m_h[h] - M);
-        }
-        const float fc = ch == 0 ? f[0] : ch == 1 ? f[1] : ch == 2 ? f[2] : f[3];
-#pragma unroll
-        for (int t = 0; t < NT; ++t) acc_o[t] *= fc;
-    }
-#pragma unroll
-    for (int half = NW / 2; half >= 1; half >>= 1) {
-        if (wave >= half && wave < 2 * half) {
-#pragma unroll
-            for (int t = 0; t < NT; ++t)
-                *(f4*)&s_o[wave - half][(t * 64 + lane) * 4] = acc_o[t];
-        }
-        __syncthreads();
-        if (wave < half) {
-#pragma unroll
-            for (int t = 0; t < NT; ++t)
-                acc_o[t] += *(const f4*)&s_o[wave][(t * 64 + lane) * 4];
-        }
-        __syncthreads();
-    }
-    if (wave == 0) {
-#pragma unroll
-        for (int t = 0; t < NT; ++t)
-            *(f4*)&s_o[0][(t * 64 + lane) * 4] = acc_o[t];
-    }
+    for (int t = 0; t < NT; ++t) *(f4*)&s_o[wave][(t * 64 + lane) * 4] = acc_o[t];
     __syncthreads();
 
     // ------------------------------------------------------------ output
-    // thread -> (head oh, run of D/16 consecutive d); the first 16 G threads
+    // Element e -> (jj, head oh, kbb, t): the P V value of d = DPT (4 kbb + jj) + t
+    // sits in lane 16 kbb + (oh + GP g), register jj, of tile t (DPT = D / 16).
     constexpr int DPT = D / 16;
-    const int oh = tid >> 4;
-    const int oc = tid & 15;
-    if (oh >= G) return;
-    float Mh = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) Mh = fmaxf(Mh, s_ml[w][0][oh]);
-    float Lh = 0.0f, bias_h[NG];
-#pragma unroll
-    for (int g = 0; g < NG; ++g) bias_h[g] = 0.0f;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-        const float mw = s_ml[w][0][oh];
-        const float fw = (mw == -INFINITY) ? 0.0f : fast_exp2(mw - Mh);
-        Lh += fw * s_ml[w][1][oh];
-#pragma unroll
-        for (int g = 0; g < NG; ++g) bias_h[g] += fw * s_bias[w][oh][g];
-    }
-    // o[oh][d]: P V row d of tile t sits at A-row n = d / DPT (d = DPT n + t);
-    // the output lane (column, kb) holds rows 4 kb + jj
-    auto o_at = [&](int d) {
-        const int rowi = d / DPT, t = d % DPT;
-        const int kbb = rowi >> 2, jj = rowi & 3;
-        const int g = d / GS;
-        const float v = s_o[0][(t * 64 + kbb * 16 + oh + GP * g) * 4 + jj];
-        const float sc = (BITS == 4 && (t & 1)) ? 16777216.0f * 0.0625f : 16777216.0f;
-        return v * sc + bias_h[g];
-    };
-    if (p.S == 1) {
-        const int64_t obase = (b * p.Hq + kvh * G + oh) * D;
-        const float inv = Lh > 0.0f ? 1.0f / Lh : 0.0f;
-#pragma unroll
-        for (int i = 0; i < DPT; ++i) {
-            const int d = oc * DPT + i;
-            ((uint16_t*)p.out)[obase + d] = f32_to_f16(o_at(d) * inv);
-        }
-        return;
-    }
     float* ml = p.part_ml + (bk * p.S + split) * 32;
     float* po = p.part_o + (bk * p.S + split) * 16 * D;
+    const int64_t obase = (b * p.Hq + kvh * G) * D;
+    for (int e = tid; e < G * D; e += NTH) {
+        const int jj = e & 3;
+        const int oh = (e >> 2) % G;
+        const int rest = (e >> 2) / G;
+        const int kbb = rest & 3, t = rest >> 2;
+        const int d = DPT * (4 * kbb + jj) + t;
+        const int g = d / GS;
+        float fw[NW];
+        float Mh = -INFINITY;
 #pragma unroll
-    for (int i = 0; i < DPT; ++i) {
-        const int d = oc * DPT + i;
-        po[oh * D + d] = o_at(d);
-    }
-    if (oc == 0) {
-        ml[2 * oh] = Mh;
-        ml[2 * oh + 1] = Lh;
+        for (int w = 0; w < NW; ++w) Mh = fmaxf(Mh, s_ml[w][0][oh]);
+        float Lh = 0.0f, bias = 0.0f, v = 0.0f;
+        const int slot = (kbb * 16 + oh + GP * g) * 4 + jj;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+            const float mw = s_ml[w][0][oh];
+            fw[w] = (mw == -INFINITY) ? 0.0f : fast_exp2(mw - Mh);
+            Lh += fw[w] * s_ml[w][1][oh];
+            bias += fw[w] * s_bias[w][oh][g];
+            v += fw[w] * s_o[w][t * 256 + slot];
+        }
+        // 4-bit odd d: the tile of its code's whole byte minus the even d's tile
+        if (BITS == 4 && (t & 1)) {
+            float ve = 0.0f;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) ve += fw[w] * s_o[w][(t - 1) * 256 + slot];
+            v = (v - ve) * 0.0625f;
+        }
+        const float o = v * 16777216.0f + bias;
+        if (p.S == 1) {
+            const float inv = Lh > 0.0f ? 1.0f / Lh : 0.0f;
+            ((uint16_t*)p.out)[obase + oh * D + d] = f32_to_f16(o * inv);
+        } else {
+            po[oh * D + d] = o;
+            if (d == 0) {
+                ml[2 * oh] = Mh;
+                ml[2 * oh + 1] = Lh;
+            }
+        }
     }
 }
 

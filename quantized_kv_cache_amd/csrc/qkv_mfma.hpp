@@ -73,6 +73,19 @@ __device__ __forceinline__ uint32_t pair_sub(const uint32_t* wa, const uint32_t*
     }
 }
 
+// As pair_sub, but a 4-bit odd code arrives as its whole byte, lo + 16 hi:
+// a product accumulated from it minus the one from the even code (lo) of the
+// same byte is 16 times the product of the odd code (saves the mask).
+template <int BITS>
+__device__ __forceinline__ uint32_t pair_sub_byte(const uint32_t* wa, const uint32_t* wb, int t) {
+    if constexpr (BITS == 4) {
+        const uint32_t x = pair_bytes(wa, wb, t >> 1);
+        return (t & 1) ? x : (x & 0x000F000Fu);
+    } else {
+        return pair_bytes(wa, wb, t);
+    }
+}
+
 // Compiler-only ordering of a wave's LDS scratch: LDS instructions of one
 // wave execute in order, so no wait on outstanding global loads is needed.
 __device__ __forceinline__ void lds_order() { __asm__ __volatile__("" ::: "memory"); }
@@ -91,16 +104,27 @@ __device__ __forceinline__ float sum4(float x) {
     return __uint_as_float(c[0]) + __uint_as_float(c[1]);
 }
 
-// Reductions over all 64 lanes (butterfly; every lane gets the result).
+// Reductions over all 64 lanes; every lane gets the result.  Within each row
+// of 16 lanes by DPP (quad permutes, then the half-row and row mirrors pair
+// lanes of different quads and halves), then across rows by max4 / sum4:
+// VALU-only, no LDS round trips.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
 __device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
-    return x;
+    x = fmaxf(x, dpp_f<0xB1>(x));     // quad_perm [1, 0, 3, 2]
+    x = fmaxf(x, dpp_f<0x4E>(x));     // quad_perm [2, 3, 0, 1]
+    x = fmaxf(x, dpp_f<0x141>(x));    // row_half_mirror
+    x = fmaxf(x, dpp_f<0x140>(x));    // row_mirror
+    return max4(x);
 }
 __device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o, 64);
-    return x;
+    x += dpp_f<0xB1>(x);
+    x += dpp_f<0x4E>(x);
+    x += dpp_f<0x141>(x);
+    x += dpp_f<0x140>(x);
+    return sum4(x);
 }
 
 // A raw buffer resource over rows [row0, row0 + min(tile, end - row0)) of a

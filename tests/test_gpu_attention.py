@@ -96,6 +96,38 @@ def test_decode_narrow_gqa(case):
         assert_close(out, ref, f"narrow {case} splits={splits}")
 
 
+@pytest.mark.parametrize("mode,bits,vmean,vstd", [
+    ("affine", 4, 0.0, 1.0), ("q8_0", 8, 0.0, 1.0),
+    ("affine", 4, 3000.0, 600.0),       # 4-bit value scales ~190
+    ("q8_0", 8, 20000.0, 600.0),        # Q8_0 value scales ~160
+])
+def test_decode_narrow_rising_scores(mode, bits, vmean, vstd):
+    """Scores that rise along the keys (the running maximum is raised many
+    times, by small and large steps) with value scales small and large
+    (|s_v| >= 128 takes the exact maximum): the lazily raised maximum must not
+    change the result.  The large values sit around a large mean so that the
+    outputs are not cancellations far below the value range."""
+    B, Hq, Hk, L = 1, 8, 2, 3000
+    D, gs = (128, 64) if mode == "affine" else (64, 32)
+    rng = np.random.default_rng(2024 + bits + int(vstd))
+    ramp = np.linspace(0.2, 3.0, L, dtype=np.float32)[None, None, :, None]
+    q = rng.standard_normal((B, Hq, 1, D)).astype(np.float16)
+    k = (rng.standard_normal((B, Hk, L, D)).astype(np.float32) * ramp).astype(np.float16)
+    k[:, :, 1500:1510] *= 2.5                          # a jump well past the slack
+    v = (vmean + rng.standard_normal((B, Hk, L, D)) * vstd).astype(np.float16)
+    kp = qkv.qkv_quantize(to_dev(k, "f16"), mode, bits, gs)
+    vp = qkv.qkv_quantize(to_dev(v, "f16"), mode, bits, gs)
+    kr, vr = oracle_pack(k, "f16", mode, bits, gs), oracle_pack(v, "f16", mode, bits, gs)
+    assert_pack_equal(pack_numpy(kp), kr)
+    assert_pack_equal(pack_numpy(vp), vr)
+    ref = oracle_attention(q, "f16", kr, vr, L, mode, bits, gs, 0.25)
+    qd = to_dev(q, "f16")
+    for splits in (0, 1):
+        out = qkv.qsdpa_decode(qd, kp, vp, L, 0.25, num_splits=splits)
+        assert qkv.qsdpa_plan(qd, kp, L, num_splits=splits)["kernel"] == "attn_decode_narrow"
+        assert_close(out, ref, f"rising scores {mode} v={vmean}+-{vstd} splits={splits}")
+
+
 def test_decode_strided_packs():
     """Packs that are views with a row stride (every second cache row)."""
     dtype, mode, bits, gs = "f16", "affine", 4, 64
