@@ -122,6 +122,39 @@ __device__ __forceinline__ h8 unpack_k(const uint32_t* w) {
     }
 }
 
+// 8 codes of one key (one K-step chunk) -> B operand halves dequantized to
+// fp16, in unpack_k's half order: Q8_0 d c, affine s c + b (s2, b2: the
+// group's scale and bias in both halves).
+template <int MODE, int BITS>
+__device__ __forceinline__ h8 dequant_k(const uint32_t* w, uint32_t s2, uint32_t b2) {
+    uint32_t a[4];
+    if constexpr (BITS == 4) {
+        const uint32_t x = w[0];
+        const uint32_t t = perm_b(0u, x, 0x0C030C01u);           // bytes 1, 3 -> halves
+        a[0] = x & 0x000F000Fu;
+        a[1] = (x >> 4) & 0x000F000Fu;
+        a[2] = t & 0x000F000Fu;
+        a[3] = (t >> 4) & 0x000F000Fu;
+    } else {
+        a[0] = w[0] & 0x00FF00FFu;
+        a[1] = perm_b(0u, w[0], 0x0C030C01u);
+        a[2] = w[1] & 0x00FF00FFu;
+        a[3] = perm_b(0u, w[1], 0x0C030C01u);
+    }
+    const h2 k1024 = {(_Float16)1024.0f, (_Float16)1024.0f};
+    const h2 k1152 = {(_Float16)1152.0f, (_Float16)1152.0f};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        if constexpr (MODE == MODE_Q8_0) {
+            // byte c (two's complement) -> half 1024 + (c + 128) -> c, times d
+            a[i] = as_u((as_h2(a[i] ^ 0x64806480u) - k1152) * as_h2(s2));
+        } else {
+            a[i] = as_u(__builtin_elementwise_fma(as_h2(a[i] | 0x64006400u) - k1024, as_h2(s2), as_h2(b2)));
+        }
+    }
+    return to_h8(a[0], a[1], a[2], a[3]);
+}
+
 // Byte 'byte' of the chunks of two keys -> [key a byte, 0, key b byte, 0].
 __device__ __forceinline__ uint32_t pair_bytes(const uint32_t* wa, const uint32_t* wb, int byte) {
     const uint32_t sel = (uint32_t)(byte & 3) | 0x0C00u | ((uint32_t)(4 + (byte & 3)) << 16) |
@@ -147,9 +180,8 @@ __device__ __forceinline__ uint32_t pair_int(const uint32_t* wa, const uint32_t*
     if constexpr (BITS == 4) {
         return pair_sub<4>(wa, wb, t) | 0x64006400u;
     } else {
-        uint32_t x = pair_bytes(wa, wb, t);
-        if constexpr (MODE == MODE_Q8_0) x ^= 0x00800080u;
-        return x | 0x64006400u;
+        const uint32_t x = pair_bytes(wa, wb, t);              // upper bytes are zero
+        return MODE == MODE_Q8_0 ? x ^ 0x64806480u : x | 0x64006400u;
     }
 }
 
@@ -182,11 +214,14 @@ __global__ __launch_bounds__(NTHR) void attn_matrix_decode(AttnLaunch p) {
     constexpr int NSW = F::NSW;
     static_assert(!FOLD || (MODE == MODE_AFFINE && NG <= 2), "folded P V needs <= 2 groups");
 
-    __shared__ float s_scores[NWAVE][16 * SROW];
+    // Per-wave LDS: the score scratch of its tiles while it streams, then its
+    // output state for the workgroup merge (written only after its last tile;
+    // no other wave touches its scratch).
+    constexpr int WAVE_FLOATS = 64 * (D / 4) > 16 * SROW ? 64 * (D / 4) : 16 * SROW;
+    __shared__ __attribute__((aligned(16))) float s_wave[NWAVE][WAVE_FLOATS];
     __shared__ float s_qsum[16][NG];
     __shared__ float s_ml[NWAVE][2][16];
     __shared__ float s_bias[NWAVE][16][2];
-    __shared__ __attribute__((aligned(16))) float s_o[NWAVE / 2][64 * (D / 4)];   // [t][lane][4]
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
@@ -364,7 +399,7 @@ __global__ __launch_bounds__(NTHR) void attn_matrix_decode(AttnLaunch p) {
             for (int hh = 0; hh < 4; ++hh) {
                 _Float16 v0 = hv[qpos<BITS>(2 * hh)], v1 = hv[qpos<BITS>(2 * hh + 1)];
                 part[g] += (float)v0 + (float)v1;
-                if constexpr (BITS == 4) {       // odd nibbles arrive as 16 c
+                if constexpr (BITS == 4 && FOLD) {   // raw odd nibbles arrive as 16 c
                     if (hh & 1) { v0 = v0 * (_Float16)0.0625f; v1 = v1 * (_Float16)0.0625f; }
                 }
                 w[hh] = n < G ? ((uint32_t)__builtin_bit_cast(uint16_t, v0) |
@@ -392,7 +427,7 @@ __global__ __launch_bounds__(NTHR) void attn_matrix_decode(AttnLaunch p) {
     for (int t = 0; t < NT; ++t) acc_o[t] = f4{0.f, 0.f, 0.f, 0.f};
     float m_run = -INFINITY, l_run = 0.0f;
     float bsum[2] = {0.0f, 0.0f};     // folded: sum_key p b_g of the softmax head, per group
-    float* sw = s_scores[wave];
+    float* sw = s_wave[wave];
     const float kscale = 16777216.0f * sl;        // 2^24 undoes the subnormal code scale
 
     auto process = [&](const Tile& cur, int tt) {
@@ -410,6 +445,28 @@ __global__ __launch_bounds__(NTHR) void attn_matrix_decode(AttnLaunch p) {
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf) {
             float z[4];
+            if constexpr (!FOLD) {
+                // keys dequantized to fp16 per element (one accumulator for all
+                // groups; the group scale and bias are in the operand)
+                f4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int g = 0; g < NG; ++g) {
+                    const uint32_t sw2 = cur.ks[hf][g >> 1];
+                    const uint32_t s2 = perm_b(sw2, sw2, (g & 1) ? 0x03020302u : 0x01000100u);
+                    uint32_t b2 = 0u;
+                    if constexpr (MODE == MODE_AFFINE) {
+                        const uint32_t bw2 = cur.kbias[hf][g >> 1];
+                        b2 = perm_b(bw2, bw2, (g & 1) ? 0x03020302u : 0x01000100u);
+                    }
+#pragma unroll
+                    for (int u = 0; u < F::SPG; ++u) {
+                        const h8 kop = dequant_k<MODE, BITS>(&cur.kw[hf][g][u * (BITS == 4 ? 1 : 2)], s2, b2);
+                        acc = mfma(qa[g * F::SPG + u], kop, acc);
+                    }
+                }
+#pragma unroll
+                for (int j = 0; j < 4; ++j) z[j] = acc[j] * sl;
+            } else
 #pragma unroll
             for (int g = 0; g < NG; ++g) {
                 f4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -571,6 +628,8 @@ __global__ __launch_bounds__(NTHR) void attn_matrix_decode(AttnLaunch p) {
     }
 
     // ---------------------------------------------------------------- merge waves
+    // Every wave leaves its unscaled state in LDS; after one barrier each
+    // thread combines the waves' states for its output elements.
     l_run = sum4(l_run);
     if constexpr (FOLD) {
         bsum[0] = sum4(bsum[0]);
@@ -582,88 +641,80 @@ __global__ __launch_bounds__(NTHR) void attn_matrix_decode(AttnLaunch p) {
         s_bias[wave][n][0] = bsum[0];
         s_bias[wave][n][1] = bsum[1];
     }
-    __syncthreads();
-    float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < NWAVE; ++w) M = fmaxf(M, s_ml[w][0][n]);
-    float f = (m_run == -INFINITY) ? 0.0f : fast_exp2(m_run - M);
-    if constexpr (FOLD) f = __shfl(f, ch + 16 * kb, 64);
-#pragma unroll
-    for (int t = 0; t < NT; ++t) acc_o[t] *= f;
-    // tree sum of the waves' accumulators (deterministic order): 8 -> 4 -> 2 -> 1
-#pragma unroll
-    for (int half = NWAVE / 2; half >= 1; half >>= 1) {
-        if (wave >= half && wave < 2 * half) {
-#pragma unroll
-            for (int t = 0; t < NT; ++t)
-                *(f4*)&s_o[wave - half][(t * 64 + lane) * 4] = acc_o[t];
-        }
-        __syncthreads();
-        if (wave < half) {
-#pragma unroll
-            for (int t = 0; t < NT; ++t)
-                acc_o[t] += *(const f4*)&s_o[wave][(t * 64 + lane) * 4];
-        }
-        __syncthreads();
-    }
-    if (wave == 0) {
-#pragma unroll
-        for (int t = 0; t < NT; ++t)
-            *(f4*)&s_o[0][(t * 64 + lane) * 4] = acc_o[t];
-    }
+    for (int t = 0; t < NT; ++t) *(f4*)&s_wave[wave][(t * 64 + lane) * 4] = acc_o[t];   // [t][lane][4]
     __syncthreads();
 
     // ---------------------------------------------------------------- output
-    // thread -> (head oh, run of D/16 consecutive d); the first 256 threads
+    // Item i -> (j, head oh, kbb, tc), j fastest: the P V values of the 4
+    // consecutive d = DPT (4 kbb + j) + 4 tc + 0..3 sit in lane 16 kbb +
+    // column, register j, of tiles 4 tc .. 4 tc + 3 (column = oh, or oh + G g
+    // in the folded form; DPT = D / 16).  Consecutive threads read
+    // consecutive LDS words; each item is one 16-byte (or 8-byte) store.
     constexpr int DPT = D / 16;
-    if (tid >= 256) return;
-    const int oh = tid >> 4;
-    const int oc = tid & 15;
-    if (oh >= G) return;
-    float Mh = -INFINITY;
+    static_assert(DPT % 4 == 0, "4 consecutive d per output item");
+    float* ml = p.part_ml + (bk * p.S + split) * 32;
+    float* po = p.part_o + (bk * p.S + split) * 16 * D;
+    const int64_t obase = (b * p.Hq + kvh * G) * D;
+    int cur_h = -1;
+    float fw[NWAVE], Mh = 0.0f, Lh = 0.0f, bias_h[2] = {0.0f, 0.0f};
+    for (int i = tid; i < G * D / 4; i += NTHR) {
+        const int j = i & 3;
+        const int oh = (i >> 2) % G;
+        const int rest = (i >> 2) / G;
+        const int kbb = rest & 3, tc = rest >> 2;
+        const int d0 = DPT * (4 * kbb + j) + 4 * tc;
+        if (oh != cur_h) {                // per-head wave factors (once per head)
+            cur_h = oh;
+            Mh = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < NWAVE; ++w) Mh = fmaxf(Mh, s_ml[w][0][oh]);
-    float Lh = 0.0f, bias_h[2] = {0.0f, 0.0f};
+            for (int w = 0; w < NWAVE; ++w) Mh = fmaxf(Mh, s_ml[w][0][oh]);
+            Lh = 0.0f;
+            bias_h[0] = bias_h[1] = 0.0f;
 #pragma unroll
-    for (int w = 0; w < NWAVE; ++w) {
-        const float mw = s_ml[w][0][oh];
-        const float fw = (mw == -INFINITY) ? 0.0f : fast_exp2(mw - Mh);
-        Lh += fw * s_ml[w][1][oh];
-        bias_h[0] += fw * s_bias[w][oh][0];
-        bias_h[1] += fw * s_bias[w][oh][1];
-    }
-    auto o_at = [&](int d) {              // unnormalised o[head oh][d]
-        const int rowi = d / DPT, t = d % DPT;
-        const int kbb = rowi >> 2, j = rowi & 3;
-        if constexpr (FOLD) {
-            const int g = d / GS;
-            const float v = s_o[0][(t * 64 + kbb * 16 + oh + G * g) * 4 + j];
-            const float sc = (BITS == 4 && (t & 1)) ? 16777216.0f * 0.0625f : 16777216.0f;
-            return v * sc + (g ? bias_h[1] : bias_h[0]);
+            for (int w = 0; w < NWAVE; ++w) {
+                const float mw = s_ml[w][0][oh];
+                fw[w] = (mw == -INFINITY) ? 0.0f : fast_exp2(mw - Mh);
+                Lh += fw[w] * s_ml[w][1][oh];
+                bias_h[0] += fw[w] * s_bias[w][oh][0];
+                bias_h[1] += fw[w] * s_bias[w][oh][1];
+            }
+        }
+        const int g = FOLD ? d0 / GS : 0;             // 4 consecutive d share a group
+        const int slot = (kbb * 16 + oh + (FOLD ? G * g : 0)) * 4 + j;
+        float o[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int t = 4 * tc + q;
+            float v = 0.0f;
+#pragma unroll
+            for (int w = 0; w < NWAVE; ++w) v += fw[w] * s_wave[w][t * 256 + slot];
+            if constexpr (FOLD) {
+                const float sc = (BITS == 4 && (q & 1)) ? 16777216.0f * 0.0625f : 16777216.0f;
+                v = v * sc + (g ? bias_h[1] : bias_h[0]);
+            }
+            o[q] = v;
+        }
+        if (p.S == 1) {
+            const float inv = Lh > 0.0f ? 1.0f / Lh : 0.0f;
+            uint16_t* dst = (uint16_t*)p.out + obase + oh * D + d0;
+            const uint16_t h[4] = {f32_to_f16(o[0] * inv), f32_to_f16(o[1] * inv),
+                                   f32_to_f16(o[2] * inv), f32_to_f16(o[3] * inv)};
+            if ((reinterpret_cast<uintptr_t>(p.out) & 7) == 0) {   // out only needs 2-byte alignment
+                *(uint2*)dst = uint2{(uint32_t)h[0] | ((uint32_t)h[1] << 16),
+                                     (uint32_t)h[2] | ((uint32_t)h[3] << 16)};
+            } else {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) dst[q] = h[q];
+            }
         } else {
-            return s_o[0][(t * 64 + kbb * 16 + oh) * 4 + j];
+            *(float4*)(po + oh * D + d0) = float4{o[0], o[1], o[2], o[3]};
+            if (d0 == 0) {
+                ml[2 * oh] = Mh;
+                ml[2 * oh + 1] = Lh;
+            }
         }
-    };
-
-    if (p.S == 1) {
-        const int64_t obase = (b * p.Hq + kvh * G + oh) * D;
-        const float inv = Lh > 0.0f ? 1.0f / Lh : 0.0f;
-#pragma unroll
-        for (int i = 0; i < DPT; ++i) {
-            const int d = oc * DPT + i;
-            ((uint16_t*)p.out)[obase + d] = f32_to_f16(o_at(d) * inv);
-        }
-        return;
     }
-    const int64_t tile = bk;
-    float* ml = p.part_ml + (tile * p.S + split) * 32;
-    float* po = p.part_o + (tile * p.S + split) * 16 * D;
-#pragma unroll
-    for (int i = 0; i < DPT; ++i) {
-        const int d = oc * DPT + i;
-        po[oh * D + d] = o_at(d);
-    }
-    if (oc == 0) { ml[2 * oh] = Mh; ml[2 * oh + 1] = Lh; }
 }
 
 template <int MODE, int BITS, int GS, int D, bool FOLD>

@@ -63,11 +63,14 @@ __global__ __launch_bounds__(NTH) void attn_decode_narrow(AttnLaunch p) {
     static_assert(NG <= 4 && NBANK >= 1, "narrow kernel: <= 4 groups, D >= 64");
     static_assert(GP * NG <= 16, "P' has 16 columns");
 
-    __shared__ __attribute__((aligned(16))) _Float16 s_p[NW][NTK * 16];   // P' rows of each wave
+    // Per-wave LDS: the P' rows of its tiles while it streams, then its
+    // output state for the workgroup merge (a wave writes the latter only
+    // after its last tile, and no other wave touches its P' rows).
+    constexpr int WAVE_FLOATS = 64 * (D / 4) > NTK * 8 ? 64 * (D / 4) : NTK * 8;
+    __shared__ __attribute__((aligned(16))) float s_wave[NW][WAVE_FLOATS];
     __shared__ float s_ml[NW][2][4];
     __shared__ int s_next;                        // next tile of the split to hand out
     __shared__ float s_bias[NW][4][4];
-    __shared__ __attribute__((aligned(16))) float s_o[NW][64 * (D / 4)];   // [t][lane][4] per wave
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -224,7 +227,7 @@ __global__ __launch_bounds__(NTH) void attn_decode_narrow(AttnLaunch p) {
 #pragma unroll
         for (int g = 0; g < NG; ++g) bs[h][g] = 0.0f;
     }
-    _Float16* pw = s_p[wave];
+    _Float16* pw = (_Float16*)s_wave[wave];        // [key][16] P' rows
     const float kscale = 16777216.0f * sl;       // 2^24 undoes the subnormal code scale
     // P' column of this lane: (head ch, group cg); the column layout uses GP
     // (2 or 4) head slots per group, G <= GP of them real
@@ -428,7 +431,7 @@ __global__ __launch_bounds__(NTH) void attn_decode_narrow(AttnLaunch p) {
         }
     }
 #pragma unroll
-    for (int t = 0; t < NT; ++t) *(f4*)&s_o[wave][(t * 64 + lane) * 4] = acc_o[t];
+    for (int t = 0; t < NT; ++t) *(f4*)&s_wave[wave][(t * 64 + lane) * 4] = acc_o[t];   // [t][lane][4]
     __syncthreads();
 
     // ------------------------------------------------------------ output
@@ -457,13 +460,13 @@ __global__ __launch_bounds__(NTH) void attn_decode_narrow(AttnLaunch p) {
             fw[w] = (mw == -INFINITY) ? 0.0f : fast_exp2(mw - Mh);
             Lh += fw[w] * s_ml[w][1][oh];
             bias += fw[w] * s_bias[w][oh][g];
-            v += fw[w] * s_o[w][t * 256 + slot];
+            v += fw[w] * s_wave[w][t * 256 + slot];
         }
         // 4-bit odd d: the tile of its code's whole byte minus the even d's tile
         if (BITS == 4 && (t & 1)) {
             float ve = 0.0f;
 #pragma unroll
-            for (int w = 0; w < NW; ++w) ve += fw[w] * s_o[w][(t - 1) * 256 + slot];
+            for (int w = 0; w < NW; ++w) ve += fw[w] * s_wave[w][(t - 1) * 256 + slot];
             v = (v - ve) * 0.0625f;
         }
         const float o = v * 16777216.0f + bias;
@@ -526,7 +529,7 @@ bool narrow_decode_supported(int q_dtype, int mode, int bits, int group_size, in
     return ng <= 4 && (bits == 4 || ng <= 2);
 }
 
-int narrow_decode_key_quantum() { return NTK * NW; }
+int narrow_decode_key_quantum() { return NTK * 8; }
 
 hipError_t launch_attn_narrow(int mode, int bits, int D, int64_t B, const AttnLaunch& p,
                               hipStream_t stream) {
