@@ -435,47 +435,65 @@ __global__ __launch_bounds__(NTH) void attn_decode_narrow(AttnLaunch p) {
     __syncthreads();
 
     // ------------------------------------------------------------ output
-    // Element e -> (jj, head oh, kbb, t): the P V value of d = DPT (4 kbb + jj) + t
-    // sits in lane 16 kbb + (oh + GP g), register jj, of tile t (DPT = D / 16).
+    // Item i -> (jj, head oh, kbb, tc), jj fastest: the P V values of the 4
+    // consecutive d = DPT (4 kbb + jj) + 4 tc + 0..3 sit in lane
+    // 16 kbb + (oh + GP g), register jj, of tiles 4 tc .. 4 tc + 3
+    // (DPT = D / 16).  Consecutive threads read consecutive LDS words; each
+    // item is one 16-byte (or 8-byte) store.
     constexpr int DPT = D / 16;
+    static_assert(DPT % 4 == 0, "4 consecutive d per output item");
     float* ml = p.part_ml + (bk * p.S + split) * 32;
     float* po = p.part_o + (bk * p.S + split) * 16 * D;
     const int64_t obase = (b * p.Hq + kvh * G) * D;
-    for (int e = tid; e < G * D; e += NTH) {
-        const int jj = e & 3;
-        const int oh = (e >> 2) % G;
-        const int rest = (e >> 2) / G;
-        const int kbb = rest & 3, t = rest >> 2;
-        const int d = DPT * (4 * kbb + jj) + t;
-        const int g = d / GS;
+    for (int i = tid; i < G * D / 4; i += NTH) {
+        const int jj = i & 3;
+        const int oh = (i >> 2) % G;
+        const int rest = (i >> 2) / G;
+        const int kbb = rest & 3, tc = rest >> 2;
+        const int d0 = DPT * (4 * kbb + jj) + 4 * tc;
+        const int g = d0 / GS;                        // 4 consecutive d share a group
         float fw[NW];
         float Mh = -INFINITY;
 #pragma unroll
         for (int w = 0; w < NW; ++w) Mh = fmaxf(Mh, s_ml[w][0][oh]);
-        float Lh = 0.0f, bias = 0.0f, v = 0.0f;
-        const int slot = (kbb * 16 + oh + GP * g) * 4 + jj;
+        float Lh = 0.0f, bias = 0.0f;
 #pragma unroll
         for (int w = 0; w < NW; ++w) {
             const float mw = s_ml[w][0][oh];
             fw[w] = (mw == -INFINITY) ? 0.0f : fast_exp2(mw - Mh);
             Lh += fw[w] * s_ml[w][1][oh];
             bias += fw[w] * s_bias[w][oh][g];
-            v += fw[w] * s_wave[w][t * 256 + slot];
         }
-        // 4-bit odd d: the tile of its code's whole byte minus the even d's tile
-        if (BITS == 4 && (t & 1)) {
-            float ve = 0.0f;
+        const int slot = (kbb * 16 + oh + GP * g) * 4 + jj;
+        float v[4];
 #pragma unroll
-            for (int w = 0; w < NW; ++w) ve += fw[w] * s_wave[w][(t - 1) * 256 + slot];
-            v = (v - ve) * 0.0625f;
+        for (int q = 0; q < 4; ++q) {
+            v[q] = 0.0f;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) v[q] += fw[w] * s_wave[w][(4 * tc + q) * 256 + slot];
         }
-        const float o = v * 16777216.0f + bias;
+        float o[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            // 4-bit odd d: the tile of its code's whole byte minus the even d's tile
+            const float x = (BITS == 4 && (q & 1)) ? (v[q] - v[q - 1]) * 0.0625f : v[q];
+            o[q] = x * 16777216.0f + bias;
+        }
         if (p.S == 1) {
             const float inv = Lh > 0.0f ? 1.0f / Lh : 0.0f;
-            ((uint16_t*)p.out)[obase + oh * D + d] = f32_to_f16(o * inv);
+            uint16_t* dst = (uint16_t*)p.out + obase + oh * D + d0;
+            const uint16_t h[4] = {f32_to_f16(o[0] * inv), f32_to_f16(o[1] * inv),
+                                   f32_to_f16(o[2] * inv), f32_to_f16(o[3] * inv)};
+            if ((reinterpret_cast<uintptr_t>(p.out) & 7) == 0) {   // out only needs 2-byte alignment
+                *(uint2*)dst = uint2{(uint32_t)h[0] | ((uint32_t)h[1] << 16),
+                                     (uint32_t)h[2] | ((uint32_t)h[3] << 16)};
+            } else {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) dst[q] = h[q];
+            }
         } else {
-            po[oh * D + d] = o;
-            if (d == 0) {
+            *(float4*)(po + oh * D + d0) = float4{o[0], o[1], o[2], o[3]};
+            if (d0 == 0) {
                 ml[2 * oh] = Mh;
                 ml[2 * oh + 1] = Lh;
             }
