@@ -45,6 +45,7 @@ constexpr int BM = 64;          // rows per workgroup
 constexpr int BN = 64;          // keys per tile
 constexpr int PW = 8;           // waves
 constexpr int PNTHR = PW * 64;
+constexpr float kLazy = 8.0f;   // running-maximum slack (log2 units)
 
 // Dequantize 16 consecutive codes of a row (one uint4) into 8 fp16 pairs.
 // Affine: s * c + b rounded once (v_pk_fma_f16); Q8_0: d * c (c exact in fp16).
@@ -101,7 +102,6 @@ __global__ __launch_bounds__(PNTHR) void attn_matrix_prefill(AttnLaunch p) {
     constexpr int DPT = D / TPR;                   // d per dequant thread (16 or 32: one group)
     constexpr int CB = DPT * BITS / 8;             // code bytes per dequant thread
     constexpr int NCH = CB / 16 > 0 ? CB / 16 : 1; // uint4 loads per dequant thread
-    constexpr int DQ_THREADS = TPR * BN;
     static_assert(DPT % 16 == 0 && DPT <= GS, "a dequant thread covers whole 16-d steps of one group");
 
     __shared__ __attribute__((aligned(16))) _Float16 s_k[2][BN * LDROW];
@@ -154,67 +154,101 @@ __global__ __launch_bounds__(PNTHR) void attn_matrix_prefill(AttnLaunch p) {
         }
     }
 
-    // ---- dequantization of a K/V tile into LDS (threads below DQ_THREADS)
+    // ---- dequantization of a K/V tile into LDS.  Thread -> (key row drow,
+    // slice dq of DPT d): lane l of wave w takes row 8 w + l % 8 and slice
+    // l / 8, so the 8 lanes of each store group write 8 consecutive rows.  The
+    // row stride is 8 dwords modulo the 32 LDS banks, so rows r and r + 4 of a
+    // group would collide; rows 4..7 of each group store their 16-byte chunks
+    // in swapped pairs (the pair's codes are swapped before dequantization),
+    // which puts the group's 8 stores on distinct banks.
     const int64_t krow0 = b * p.k.sb + kvh * p.k.sh;
     const int64_t vrow0 = b * p.v.sb + kvh * p.v.sh;
-    const bool dq_on = tid < DQ_THREADS;
-    const int drow = (tid / TPR) % BN;             // key row of the tile
-    const int dq = tid % TPR;                      // slice of the row
+    const int drow = 8 * wave + (lane & 7);        // key row of the tile
+    const int dq = lane >> 3;                      // slice of the row
+    const bool dq_on = dq < TPR;
     const int dgrp = (dq * DPT) / GS;              // its quantization group
+    const bool swap = (drow >> 2) & 1;
+    constexpr int SROWB = NG * 2;                  // scale bytes per row
+    const uint8_t* kcb = (const uint8_t*)p.k.codes + krow0 * ROWB;
+    const uint8_t* vcb = (const uint8_t*)p.v.codes + vrow0 * ROWB;
+    const uint8_t* ksb = (const uint8_t*)p.k.scales + krow0 * SROWB;
+    const uint8_t* vsb = (const uint8_t*)p.v.scales + vrow0 * SROWB;
+    const uint8_t* kbb = (const uint8_t*)p.k.biases + krow0 * SROWB;
+    const uint8_t* vbb = (const uint8_t*)p.v.biases + vrow0 * SROWB;
+    const uint32_t kcs = (uint32_t)(p.k.sl * ROWB), vcs = (uint32_t)(p.v.sl * ROWB);
+    const uint32_t kss = (uint32_t)(p.k.sl * SROWB), vss = (uint32_t)(p.v.sl * SROWB);
+    const uint32_t o_kc = (uint32_t)drow * kcs + dq * CB, o_vc = (uint32_t)drow * vcs + dq * CB;
+    const uint32_t o_ks = (uint32_t)drow * kss + 2 * dgrp, o_vs = (uint32_t)drow * vss + 2 * dgrp;
     struct Raw {
         uint4 kc[NCH], vc[NCH];
         uint32_t ks, kbias, vs, vbias;             // fp16 scale / bias of the slice's group
     };
+    // rows past the split's end read as zeros (buffer bounds): their scores are
+    // masked and their zero values add nothing
     auto load_raw = [&](int t, Raw& R) {
-        int64_t j = j_begin + (int64_t)t * BN + drow;
-        j = min(j, p.L - 1);
-        const int64_t kr = krow0 + j * p.k.sl, vr = vrow0 + j * p.v.sl;
-        const uint8_t* kcp = (const uint8_t*)p.k.codes + kr * ROWB + dq * CB;
-        const uint8_t* vcp = (const uint8_t*)p.v.codes + vr * ROWB + dq * CB;
+        const int64_t r0 = j_begin + (int64_t)t * BN;
+        const auto rk = rows_rsrc(kcb, r0, j_end, BN, kcs, ROWB);
+        const auto rv = rows_rsrc(vcb, r0, j_end, BN, vcs, ROWB);
 #pragma unroll
         for (int c = 0; c < NCH; ++c) {
             if constexpr (CB >= 16) {
-                R.kc[c] = *(const uint4*)(kcp + 16 * c);
-                R.vc[c] = *(const uint4*)(vcp + 16 * c);
+                const auto x = __builtin_amdgcn_raw_buffer_load_b128(rk, (int)(o_kc + 16 * c), 0, 0);
+                const auto y = __builtin_amdgcn_raw_buffer_load_b128(rv, (int)(o_vc + 16 * c), 0, 0);
+                R.kc[c] = uint4{x[0], x[1], x[2], x[3]};
+                R.vc[c] = uint4{y[0], y[1], y[2], y[3]};
             } else {
-                const uint2 a = *(const uint2*)kcp, bb = *(const uint2*)vcp;
-                R.kc[c] = uint4{a.x, a.y, 0u, 0u};
-                R.vc[c] = uint4{bb.x, bb.y, 0u, 0u};
+                const auto x = __builtin_amdgcn_raw_buffer_load_b64(rk, (int)o_kc, 0, 0);
+                const auto y = __builtin_amdgcn_raw_buffer_load_b64(rv, (int)o_vc, 0, 0);
+                R.kc[c] = uint4{x[0], x[1], 0u, 0u};
+                R.vc[c] = uint4{y[0], y[1], 0u, 0u};
             }
         }
-        R.ks = ((const uint16_t*)p.k.scales)[kr * NG + dgrp];
-        R.vs = ((const uint16_t*)p.v.scales)[vr * NG + dgrp];
+        R.ks = buf16(rows_rsrc(ksb, r0, j_end, BN, kss, SROWB), o_ks);
+        R.vs = buf16(rows_rsrc(vsb, r0, j_end, BN, vss, SROWB), o_vs);
         if constexpr (MODE == MODE_AFFINE) {
-            R.kbias = ((const uint16_t*)p.k.biases)[kr * NG + dgrp];
-            R.vbias = ((const uint16_t*)p.v.biases)[vr * NG + dgrp];
+            R.kbias = buf16(rows_rsrc(kbb, r0, j_end, BN, kss, SROWB), o_ks);
+            R.vbias = buf16(rows_rsrc(vbb, r0, j_end, BN, vss, SROWB), o_vs);
         } else {
             R.kbias = R.vbias = 0u;
         }
     };
-    auto store_tile = [&](const Raw& R, int buf) {
-        _Float16* kd = &s_k[buf][drow * LDROW + dq * DPT];
-        _Float16* vd = &s_v[buf][drow * LDROW + dq * DPT];
-        const uint32_t ks2 = R.ks | (R.ks << 16), kb2 = R.kbias | (R.kbias << 16);
-        const uint32_t vs2 = R.vs | (R.vs << 16), vb2 = R.vbias | (R.vbias << 16);
-#pragma unroll
-        for (int c = 0; c < DPT / 16; ++c) {              // 16 d per step
-            uint32_t ko[8], vo[8];
-            if constexpr (BITS == 4) {
-                const uint4 kw = R.kc[c / 2], vw = R.vc[c / 2];
-                const uint32_t kx[4] = {kw.x, kw.y, kw.z, kw.w}, vx[4] = {vw.x, vw.y, vw.z, vw.w};
-                dequant8_4bit(kx[2 * (c & 1)], ks2, kb2, ko);
-                dequant8_4bit(kx[2 * (c & 1) + 1], ks2, kb2, ko + 4);
-                dequant8_4bit(vx[2 * (c & 1)], vs2, vb2, vo);
-                dequant8_4bit(vx[2 * (c & 1) + 1], vs2, vb2, vo + 4);
-            } else {
-                dequant16<MODE, BITS>(R.kc[c], ks2, kb2, ko);
-                dequant16<MODE, BITS>(R.vc[c], vs2, vb2, vo);
-            }
-            *(uint4*)(kd + 16 * c) = uint4{ko[0], ko[1], ko[2], ko[3]};
-            *(uint4*)(kd + 16 * c + 8) = uint4{ko[4], ko[5], ko[6], ko[7]};
-            *(uint4*)(vd + 16 * c) = uint4{vo[0], vo[1], vo[2], vo[3]};
-            *(uint4*)(vd + 16 * c + 8) = uint4{vo[4], vo[5], vo[6], vo[7]};
+    // one 16-d step: 16 codes (one uint4 of 8-bit codes, or two dwords of 4-bit
+    // codes) -> the slice's chunks 2 c16 and 2 c16 + 1 in LDS, in swapped order
+    // on swapping rows (codes swapped first, so the stores need no selects)
+    auto store_step = [&](uint4 w, uint32_t s2, uint32_t b2, _Float16* dst, int c16) {
+        uint32_t o[8];
+        if constexpr (BITS == 4) {
+            const uint32_t lo = swap ? w.y : w.x, hi = swap ? w.x : w.y;
+            dequant8_4bit(lo, s2, b2, o);
+            dequant8_4bit(hi, s2, b2, o + 4);
+        } else {
+            const uint4 x = swap ? uint4{w.z, w.w, w.x, w.y} : w;
+            dequant16<MODE, BITS>(x, s2, b2, o);
         }
+        const int c0 = 2 * c16 + (swap ? 1 : 0), c1 = 2 * c16 + (swap ? 0 : 1);
+        *(uint4*)(dst + 8 * c0) = uint4{o[0], o[1], o[2], o[3]};
+        *(uint4*)(dst + 8 * c1) = uint4{o[4], o[5], o[6], o[7]};
+    };
+    // the K (or V) half of a tile: the slice's codes -> fp16 rows in LDS
+    auto store_half = [&](const uint4* codes, uint32_t sc, uint32_t bi, _Float16* dst) {
+        const uint32_t s2 = sc | (sc << 16), b2 = bi | (bi << 16);
+#pragma unroll
+        for (int c16 = 0; c16 < DPT / 16; ++c16) {
+            uint4 w;
+            if constexpr (BITS == 4) {
+                const uint4 x = codes[c16 / 2];
+                w = (c16 & 1) ? uint4{x.z, x.w, 0u, 0u} : uint4{x.x, x.y, 0u, 0u};
+            } else {
+                w = codes[c16];
+            }
+            store_step(w, s2, b2, dst, c16);
+        }
+    };
+    auto store_k = [&](const Raw& R, int buf) {
+        store_half(R.kc, R.ks, R.kbias, &s_k[buf][drow * LDROW + dq * DPT]);
+    };
+    auto store_v = [&](const Raw& R, int buf) {
+        store_half(R.vc, R.vs, R.vbias, &s_v[buf][drow * LDROW + dq * DPT]);
     };
 
     // ---- main loop
@@ -226,7 +260,8 @@ __global__ __launch_bounds__(PNTHR) void attn_matrix_prefill(AttnLaunch p) {
     Raw ra;
     if (ntile > 0 && dq_on) {
         load_raw(0, ra);
-        store_tile(ra, 0);
+        store_k(ra, 0);
+        store_v(ra, 0);
         if (ntile > 1) load_raw(1, ra);
     }
     __syncthreads();
@@ -274,10 +309,12 @@ __global__ __launch_bounds__(PNTHR) void attn_matrix_prefill(AttnLaunch p) {
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) mx = fmaxf(mx, sc[u][jj]);
         mx = max4(mx);
-        const float m_new = fmaxf(m_run, mx);
-        if (__ballot(m_new > m_run) != 0ull) {
-            const float alpha = (m_new > m_run) ? (m_run == -INFINITY ? 0.0f : fast_exp2(m_run - m_new))
-                                                : 1.0f;
+        // lazy maximum: raised only when a score exceeds it by kLazy (log2
+        // units), so p = 2^(s - m) <= 2^kLazy stays well inside fp16
+        const bool grow = mx > m_run + kLazy;
+        const float m_new = grow ? fmaxf(m_run, mx) : m_run;
+        if (__ballot(grow) != 0ull) {
+            const float alpha = grow ? (m_run == -INFINITY ? 0.0f : fast_exp2(m_run - m_new)) : 1.0f;
             l_run *= alpha;
 #pragma unroll
             for (int t2 = 0; t2 < NT; ++t2) acc[t2] *= alpha;
@@ -322,7 +359,8 @@ __global__ __launch_bounds__(PNTHR) void attn_matrix_prefill(AttnLaunch p) {
         }
         // next tile -> the other buffer, then one barrier per tile
         if (t + 1 < ntile && dq_on) {
-            store_tile(ra, buf ^ 1);
+            store_k(ra, buf ^ 1);
+            store_v(ra, buf ^ 1);
             if (t + 2 < ntile) load_raw(t + 2, ra);
         }
         __syncthreads();
