@@ -140,7 +140,8 @@ qkv_status check_source(const void* x, int32_t dtype, const int64_t xs[3], const
 // ---------------------------------------------------------------- attention plans
 struct Plan {
     bool matrix;
-    bool prefill;                   // tiled matrix kernel (64 rows per workgroup)
+    bool prefill;                   // tiled matrix kernel
+    int wg_rows;                    // its rows per workgroup
     bool narrow;                    // single-query kernel for GQA factors <= 4
     int RT, n_rt, S;
     int64_t chunk;
@@ -179,11 +180,14 @@ Plan make_plan(int64_t B, int64_t Hq, int64_t Lq, int64_t D, int64_t L, const qk
         pl.narrow = qkv::narrow_decode_supported(q_dtype, k->mode, bits, k->group_size, (int)D, G, Lq);
         pl.prefill = !pl.narrow &&
                      !qkv::decode_matrix_supported(q_dtype, k->mode, bits, k->group_size, (int)D, G, Lq);
-        // grid rows (64-row tiles) and (batch, kv head) pairs within the y/z grid limits
-        const int64_t tiles64 = ((int64_t)G * Lq + qkv::kPrefillRows - 1) / qkv::kPrefillRows;
-        if (pl.prefill && (tiles64 > 65535 || B * Hk > 65535)) pl.matrix = pl.prefill = false;
     }
     const int64_t n_rows = (int64_t)G * Lq;
+    pl.wg_rows = n_rows >= qkv::kPrefillWideMinRows ? qkv::kPrefillRowsWide : qkv::kPrefillRows;
+    if (pl.prefill) {
+        // grid rows (row tiles) and (batch, kv head) pairs within the y/z grid limits
+        const int64_t tiles = (n_rows + pl.wg_rows - 1) / pl.wg_rows;
+        if (tiles > 65535 || B * Hk > 65535) pl.matrix = pl.prefill = false;
+    }
     pl.RT = 16;
     pl.n_rt = (int)((n_rows + pl.RT - 1) / pl.RT);
     int S;
@@ -191,7 +195,7 @@ Plan make_plan(int64_t B, int64_t Hq, int64_t Lq, int64_t D, int64_t L, const qk
         S = std::min(opts->num_splits, 256);
     } else if (pl.prefill) {
         // one workgroup per CU fits the largest tiles; split only short row counts
-        const int64_t wgs = B * Hk * ((n_rows + qkv::kPrefillRows - 1) / qkv::kPrefillRows);
+        const int64_t wgs = B * Hk * ((n_rows + pl.wg_rows - 1) / pl.wg_rows);
         S = auto_splits(wgs, L, 1024, 256);
     } else {
         // the generic kernel walks a split serially in 32-key blocks, so short
@@ -296,6 +300,7 @@ qkv_status attention(const char* name, const void* q, int32_t q_dtype, int64_t B
     a.chunk = pl.chunk;
     a.n_rows = (int32_t)(G * Lq);
     a.n_rt = pl.n_rt;
+    a.wg_rows = pl.wg_rows;
     a.RT = pl.RT;
     if (pl.ws_bytes > 0) {
         a.part_ml = static_cast<float*>(workspace);
@@ -381,7 +386,7 @@ qkv_status qsdpa_plan(int64_t B, int64_t Hq, int64_t Lq, int64_t D, int64_t L, c
     Plan pl = make_plan(B, Hq, Lq, D, L, k, q_dtype, opts);
     plan->algo = pl.matrix ? QKV_ALGO_MATRIX : QKV_ALGO_GENERIC;
     plan->num_splits = pl.S;
-    plan->row_tile = pl.prefill ? qkv::kPrefillRows : pl.RT;
+    plan->row_tile = pl.prefill ? pl.wg_rows : pl.RT;
     plan->kernel = !pl.matrix  ? QKV_KERNEL_GENERIC
                    : pl.prefill ? QKV_KERNEL_PREFILL
                    : pl.narrow  ? QKV_KERNEL_DECODE_NARROW

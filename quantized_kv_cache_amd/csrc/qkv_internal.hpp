@@ -54,6 +54,7 @@ struct AttnLaunch {
     int32_t n_rows;                 // G * Lq rows per (b, kv head)
     int32_t n_rt;                   // row tiles per (b, kv head)
     int32_t RT;                     // rows per tile
+    int32_t wg_rows;                // rows per workgroup of the prefill kernel (64 or 128)
     float* part_ml;                 // [B*Hk*n_rt][S][16][2] (m, l) of each split
     float* part_o;                  // [B*Hk*n_rt][S][16][D] unnormalised o of each split
 };
@@ -78,7 +79,12 @@ hipError_t launch_attn_matrix(int mode, int bits, int D, int64_t B, const AttnLa
                               hipStream_t stream);
 hipError_t launch_prefill_matrix(int mode, int bits, int D, int64_t B, const AttnLaunch& p,
                                  hipStream_t stream);
-constexpr int kPrefillRows = 64;    // rows per workgroup of the prefill kernel
+// Rows per workgroup of the prefill kernel: 128 (each dequantized K/V tile
+// serves twice the rows) once a (batch, kv head) has at least
+// kPrefillWideMinRows GQA-packed rows, else 64.
+constexpr int kPrefillRows = 64;
+constexpr int kPrefillRowsWide = 128;
+constexpr int kPrefillWideMinRows = 256;
 // Keys of one tile per wave of the single-query kernels: splits are rounded
 // to a multiple of it.
 int decode_matrix_key_quantum();

@@ -1,5 +1,5 @@
-// Split merge kernel.  One workgroup per (row tile, row, 64-d chunk of the
-// output row): grid x = tile, y = row, z = chunk.  Its 256 threads are 16
+// Split merge kernels.  Many splits: one workgroup per (row tile, row, 64-d
+// chunk of the output row): grid x = tile, y = row, z = chunk.  Its 256 threads are 16
 // float4 columns x 16 split groups, so a thread combines at most S/16 split
 // states (all its loads issued before it waits: one memory round trip for
 // S <= 128).  States combine online in log2 units, the split groups combine
@@ -83,8 +83,80 @@ __global__ __launch_bounds__(256) void merge_splits_kernel(AttnLaunch p) {
     store_from_f32<QT>(p.out, ob + 3, st.o.w * inv);
 }
 
+// Few splits (S <= kSmallS, the prefill case): one thread per float4 column
+// of a row combines all S states itself; a workgroup covers 256 / (D / 4)
+// rows, so every load is a full-row, coalesced access.
+constexpr int kSmallS = 8;
+
+template <int QT, int D>
+__global__ __launch_bounds__(256) void merge_splits_small(AttnLaunch p) {
+    constexpr int F4 = D / 4;
+    constexpr int RPW = 256 / F4;                 // rows per workgroup
+    const int64_t tile = blockIdx.x;
+    const int r = blockIdx.y * RPW + threadIdx.x / F4;
+    const int rt = (int)(tile % p.n_rt);
+    const int64_t bk = tile / p.n_rt;
+    const int pr = rt * 16 + r;
+    if (pr >= p.n_rows) return;
+    const int64_t b = bk / p.Hk, kvh = bk % p.Hk;
+    const int64_t i = pr / p.G, h = kvh * p.G + pr % p.G;
+    const int f = threadIdx.x % F4;
+    const int S = p.S;
+    const float2* ml = (const float2*)p.part_ml + (tile * S * 16 + r);
+    const float4* po = (const float4*)p.part_o + ((tile * S * 16 + r) * F4 + f);
+    float2 a[kSmallS];
+    float4 o[kSmallS];
+#pragma unroll
+    for (int s = 0; s < kSmallS; ++s) {
+        if (s < S) {
+            a[s] = ml[(int64_t)s * 16];
+            o[s] = po[(int64_t)s * 16 * F4];
+        }
+    }
+    float M = -INFINITY;
+#pragma unroll
+    for (int s = 0; s < kSmallS; ++s)
+        if (s < S) M = fmaxf(M, a[s].x);
+    float l = 0.0f;
+    float4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < kSmallS; ++s) {
+        if (s < S && a[s].x != -INFINITY) {
+            const float w = fast_exp2(a[s].x - M);
+            l += w * a[s].y;
+            acc.x += w * o[s].x;
+            acc.y += w * o[s].y;
+            acc.z += w * o[s].z;
+            acc.w += w * o[s].w;
+        }
+    }
+    const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+    const int64_t ob = ((b * p.Hq + h) * p.Lq + i) * D + 4 * f;
+    store_from_f32<QT>(p.out, ob, acc.x * inv);
+    store_from_f32<QT>(p.out, ob + 1, acc.y * inv);
+    store_from_f32<QT>(p.out, ob + 2, acc.z * inv);
+    store_from_f32<QT>(p.out, ob + 3, acc.w * inv);
+}
+
+template <int QT, int D>
+hipError_t launch_small(int64_t B, const AttnLaunch& p, hipStream_t s) {
+    constexpr int RPW = 256 / (D / 4);
+    const unsigned rows = (unsigned)(p.n_rows < 16 ? p.n_rows : 16);
+    dim3 grid((unsigned)(B * p.Hk * p.n_rt), (rows + RPW - 1) / RPW, 1);
+    hipLaunchKernelGGL((merge_splits_small<QT, D>), grid, dim3(256), 0, s, p);
+    return hipGetLastError();
+}
+
 template <int QT>
 hipError_t launch_q(int D, int64_t B, const AttnLaunch& p, hipStream_t s) {
+    if (p.S <= kSmallS) {
+        switch (D) {
+            case 64: return launch_small<QT, 64>(B, p, s);
+            case 128: return launch_small<QT, 128>(B, p, s);
+            case 256: return launch_small<QT, 256>(B, p, s);
+            default: return hipErrorNotSupported;
+        }
+    }
     // rows of a tile that exist: all 16 unless the (single) tile is short
     const unsigned rows = (unsigned)(p.n_rows < 16 ? p.n_rows : 16);
     dim3 grid((unsigned)(B * p.Hk * p.n_rt), rows, (unsigned)(D / (4 * MC)));

@@ -41,7 +41,6 @@ namespace {
 
 using namespace mf;
 
-constexpr int BM = 64;          // rows per workgroup
 constexpr int BN = 64;          // keys per tile
 constexpr int PW = 8;           // waves
 constexpr int PNTHR = PW * 64;
@@ -91,8 +90,16 @@ __device__ __forceinline__ void dequant8_4bit(uint32_t w, uint32_t s2, uint32_t 
     out[3] = perm_b(as_u(v57), as_u(v46), 0x07060302u);
 }
 
-template <int MODE, int BITS, int GS, int D>
+// RB 16-row blocks per workgroup: RB = 4 (64 rows; waves w and w + 4 take
+// the two 32-key halves of each tile) or RB = 8 (128 rows; every wave takes
+// all 64 keys, so each dequantized tile serves twice the rows).
+template <int MODE, int BITS, int GS, int D, int RB>
 __global__ __launch_bounds__(PNTHR) void attn_matrix_prefill(AttnLaunch p) {
+    static_assert(RB == 4 || RB == 8, "64 or 128 rows per workgroup");
+    constexpr int KH = PW / RB;                    // key parts per tile (2 or 1)
+    constexpr int BMR = 16 * RB;                   // rows per workgroup
+    constexpr int KPW = BN / KH;                   // keys per wave and tile
+    constexpr int NSUB = KPW / 16;                 // 16-key subtiles per wave
     constexpr int NG = D / GS;
     constexpr int ROWB = D * BITS / 8;             // code bytes per row
     constexpr int LDROW = D + 16;                  // LDS row stride in halves (pad 32 B)
@@ -109,13 +116,13 @@ __global__ __launch_bounds__(PNTHR) void attn_matrix_prefill(AttnLaunch p) {
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int rb = wave & 3;                       // 16-row block
-    const int kh = wave >> 2;                      // 32-key half of each tile
+    const int rb = wave % RB;                      // 16-row block
+    const int kh = wave / RB;                      // key part of each tile
     const int lane = tid & 63;
     const int n = lane & 15;
     const int kb = lane >> 4;
     const int split = blockIdx.x;
-    const int rt = blockIdx.y;                     // 64-row tile
+    const int rt = blockIdx.y;                     // row tile
     const int64_t bk = blockIdx.z;
     const int64_t b = bk / p.Hk;
     const int64_t kvh = bk % p.Hk;
@@ -123,7 +130,7 @@ __global__ __launch_bounds__(PNTHR) void attn_matrix_prefill(AttnLaunch p) {
     const float sl = p.scale * kLog2e;
 
     // this lane's row (the B column of S^T and of O^T)
-    const int row = rt * BM + rb * 16 + n;
+    const int row = rt * BMR + rb * 16 + n;
     const bool row_ok = row < p.n_rows;
     const int rowc = row_ok ? row : p.n_rows - 1;
     const int64_t qi = rowc / G;
@@ -134,12 +141,12 @@ __global__ __launch_bounds__(PNTHR) void attn_matrix_prefill(AttnLaunch p) {
     const int64_t j_begin = (int64_t)split * p.chunk;
     int64_t j_end = min(p.L, j_begin + p.chunk);
     if (p.mask_kind == MASK_CAUSAL) {
-        const int last_row = min(rt * BM + BM, p.n_rows) - 1;
+        const int last_row = min(rt * BMR + BMR, p.n_rows) - 1;
         j_end = min(j_end, p.L - p.Lq + last_row / G + 1);
     }
     const int ntile = j_end > j_begin ? (int)((j_end - j_begin + BN - 1) / BN) : 0;
     // first key hidden from some row of the tile (tiles before it need no mask)
-    const int first_row = rt * BM;
+    const int first_row = rt * BMR;
     const int64_t lo_vis = (p.mask_kind == MASK_CAUSAL) ? p.L - p.Lq + first_row / G : p.L - 1;
 
     // ---- queries: B operand of S^T = K Q^T (row n, d = 32 st + 8 kb .. + 7)
@@ -257,40 +264,44 @@ __global__ __launch_bounds__(PNTHR) void attn_matrix_prefill(AttnLaunch p) {
     for (int t = 0; t < NT; ++t) acc[t] = f4{0.f, 0.f, 0.f, 0.f};
     float m_run = -INFINITY, l_run = 0.0f;
 
-    Raw ra;
+    // Raw codes are loaded two tiles ahead into two register sets that
+    // alternate between iterations (iter(t, cur): cur holds tile t + 1 and is
+    // refilled with tile t + 3 once dequantized).
+    Raw raw0, raw1;
     if (ntile > 0 && dq_on) {
-        load_raw(0, ra);
-        store_k(ra, 0);
-        store_v(ra, 0);
-        if (ntile > 1) load_raw(1, ra);
+        load_raw(0, raw0);
+        store_k(raw0, 0);
+        store_v(raw0, 0);
+        if (ntile > 1) load_raw(1, raw0);
+        if (ntile > 2) load_raw(2, raw1);
     }
     __syncthreads();
 
-    for (int t = 0; t < ntile; ++t) {
+    auto iter = [&](int t, Raw& cur) {
         const int buf = t & 1;
-        const int64_t j0 = j_begin + (int64_t)t * BN + 32 * kh;   // first key of this wave's half
+        const int64_t j0 = j_begin + (int64_t)t * BN + KPW * kh;  // first key of this wave's part
         const _Float16* kt = s_k[buf];
         const _Float16* vt = s_v[buf];
 
-        // S^T for the half's 2 subtiles of 16 keys: lane holds keys 16 u + 4 kb + jj of row n
-        float sc[2][4];
+        // S^T for the part's subtiles of 16 keys: lane holds keys 16 u + 4 kb + jj of row n
+        float sc[NSUB][4];
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
+        for (int u = 0; u < NSUB; ++u) {
             f4 s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int st = 0; st < STEPS; ++st) {
-                const h8 ka = *(const h8*)(kt + (32 * kh + 16 * u + n) * LDROW + 32 * st + 8 * kb);
+                const h8 ka = *(const h8*)(kt + (KPW * kh + 16 * u + n) * LDROW + 32 * st + 8 * kb);
                 s = mfma16(ka, qb[st], s);
             }
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) sc[u][jj] = s[jj] * sl;
         }
-        // masking: only halves reaching past the first row's last visible key,
+        // masking: only parts reaching past the first row's last visible key,
         // the ragged end of the split, or with an additive mask
-        const bool edge = (j0 + 31 > lo_vis) || (j0 + 32 > j_end) || p.mask_kind == MASK_ADDITIVE;
+        const bool edge = (j0 + KPW - 1 > lo_vis) || (j0 + KPW > j_end) || p.mask_kind == MASK_ADDITIVE;
         if (edge) {
 #pragma unroll
-            for (int u = 0; u < 2; ++u)
+            for (int u = 0; u < NSUB; ++u)
 #pragma unroll
                 for (int jj = 0; jj < 4; ++jj) {
                     const int64_t j = j0 + 16 * u + 4 * kb + jj;
@@ -302,10 +313,10 @@ __global__ __launch_bounds__(PNTHR) void attn_matrix_prefill(AttnLaunch p) {
                     sc[u][jj] = v;
                 }
         }
-        // online softmax of row n over the half (8 keys in this lane, x4 lanes)
+        // online softmax of row n over the part (4 NSUB keys in this lane, x4 lanes)
         float mx = sc[0][0];
 #pragma unroll
-        for (int u = 0; u < 2; ++u)
+        for (int u = 0; u < NSUB; ++u)
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) mx = fmaxf(mx, sc[u][jj]);
         mx = max4(mx);
@@ -321,10 +332,10 @@ __global__ __launch_bounds__(PNTHR) void attn_matrix_prefill(AttnLaunch p) {
             m_run = m_new;
         }
         const bool live = m_run != -INFINITY;
-        uint32_t pp[2][2];        // P^T operand halves: keys (16u + 4kb + jj) in pairs
+        uint32_t pp[NSUB][2];     // P^T operand halves: keys (16u + 4kb + jj) in pairs
         float ps = 0.0f;
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
+        for (int u = 0; u < NSUB; ++u) {
             float e[4];
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) {
@@ -336,12 +347,13 @@ __global__ __launch_bounds__(PNTHR) void attn_matrix_prefill(AttnLaunch p) {
             pp[u][1] = as_u(c);
         }
         l_run += ps;
-        // O^T += V^T P^T over the half: the lane's 8 keys are 4 kb .. 4 kb + 3 of
-        // each subtile, in the order of pp
-        {
-            const h8 pb = to_h8(pp[0][0], pp[0][1], pp[1][0], pp[1][1]);
-            const int k0a = 32 * kh + 4 * kb;            // subtile 0, keys 4kb..
-            const int k0b = 32 * kh + 16 + 4 * kb;       // subtile 1
+        // O^T += V^T P^T over the part, 32 keys (two subtiles) per step: the
+        // lane's 8 keys are 4 kb .. 4 kb + 3 of each subtile, in the order of pp
+#pragma unroll
+        for (int sp = 0; sp < NSUB / 2; ++sp) {
+            const h8 pb = to_h8(pp[2 * sp][0], pp[2 * sp][1], pp[2 * sp + 1][0], pp[2 * sp + 1][1]);
+            const int k0a = KPW * kh + 32 * sp + 4 * kb;   // subtile 2 sp, keys 4kb..
+            const int k0b = k0a + 16;                     // subtile 2 sp + 1
 #pragma unroll
             for (int t2 = 0; t2 < NT; ++t2) {
                 // lane (s = n within its 16-lane group) points at V[k0 + s/4][16 t2 + 4 (s%4)];
@@ -359,16 +371,21 @@ __global__ __launch_bounds__(PNTHR) void attn_matrix_prefill(AttnLaunch p) {
         }
         // next tile -> the other buffer, then one barrier per tile
         if (t + 1 < ntile && dq_on) {
-            store_k(ra, buf ^ 1);
-            store_v(ra, buf ^ 1);
-            if (t + 2 < ntile) load_raw(t + 2, ra);
+            store_k(cur, buf ^ 1);
+            store_v(cur, buf ^ 1);
+            if (t + 3 < ntile) load_raw(t + 3, cur);
         }
         __syncthreads();
+    };
+    for (int t = 0; t < ntile; t += 2) {
+        iter(t, raw0);
+        if (t + 1 < ntile) iter(t + 1, raw1);
     }
 
     // ---- merge the two key halves of each row block through LDS (the tile
     // buffers are free after the loop's last barrier)
     l_run = sum4(l_run);
+    if constexpr (KH == 2) {
     float* xo = (float*)&s_k[0][0];                // [rb][t][lane][4] floats
     float* xml = (float*)&s_v[0][0];               // [rb][lane][2]
     if (kh == 1) {
@@ -389,6 +406,7 @@ __global__ __launch_bounds__(PNTHR) void attn_matrix_prefill(AttnLaunch p) {
             acc[t2] = acc[t2] * f0 + *(const f4*)&xo[((rb * NT + t2) * 64 + lane) * 4] * f1;
         l_run = l_run * f0 + l1 * f1;
         m_run = M;
+    }
     }
 
     // ---- output: lane holds O^T[d = 16 t + 4 kb + jj][row n]
@@ -417,9 +435,15 @@ __global__ __launch_bounds__(PNTHR) void attn_matrix_prefill(AttnLaunch p) {
 
 template <int MODE, int BITS, int GS, int D>
 hipError_t launch_p(int64_t B, const AttnLaunch& p, hipStream_t s) {
-    const int nwg = (p.n_rows + BM - 1) / BM;
+    const int bm = p.wg_rows;
+    const int nwg = (p.n_rows + bm - 1) / bm;
     dim3 grid(p.S, nwg, (unsigned)(B * p.Hk));
-    hipLaunchKernelGGL((attn_matrix_prefill<MODE, BITS, GS, D>), grid, dim3(PNTHR), 0, s, p);
+    if (bm == 128)
+        hipLaunchKernelGGL((attn_matrix_prefill<MODE, BITS, GS, D, 8>), grid, dim3(PNTHR), 0, s, p);
+    else if (bm == 64)
+        hipLaunchKernelGGL((attn_matrix_prefill<MODE, BITS, GS, D, 4>), grid, dim3(PNTHR), 0, s, p);
+    else
+        return hipErrorNotSupported;
     return hipGetLastError();
 }
 

@@ -162,3 +162,19 @@ def test_plan_kernel_choice(L, shape, kernel):
     assert pl.algo == (_lib.QKV_ALGO_GENERIC if kernel == _lib.QKV_KERNEL_GENERIC
                        else _lib.QKV_ALGO_MATRIX)
     assert 1 <= pl.num_splits <= 256 and pl.num_splits * pl.keys_per_split >= Lk
+    if kernel == _lib.QKV_KERNEL_PREFILL:
+        # 128 GQA-packed rows per workgroup from 256 rows per (batch, kv head)
+        assert pl.row_tile == (128 if (Hq // Hk) * Lq >= 256 else 64)
+
+
+@pytest.mark.parametrize("Lq,rows", [(15, 64), (16, 128), (100, 128)])
+def test_prefill_row_tile(L, Lq, rows):
+    """Prefill row tiles: 64 rows below 256 GQA-packed rows per (batch, kv
+    head), 128 from there (host logic only)."""
+    kp = _lib.QkvPack(mode=_lib.QKV_Q8_0, bits=8, group_size=32, scale_dtype=_lib.QKV_F16,
+                      B=1, H=2, L_cap=4096, D=128, codes=FAKE, scales=FAKE + 0x10000000,
+                      biases=None, stride_b=2 * 4096, stride_h=4096, stride_l=1)
+    pl = _lib.QkvAttnPlan()
+    assert L.qsdpa_plan(1, 32, Lq, 128, 4096, ctypes.byref(kp), _lib.QKV_F16, None,
+                        ctypes.byref(pl)) == 0
+    assert pl.kernel == _lib.QKV_KERNEL_PREFILL and pl.row_tile == rows

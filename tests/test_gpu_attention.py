@@ -209,6 +209,10 @@ PREFILL_CASES = [
     ("f16", "affine", 8, 32, 1, 2, 2, 64, 1000, 256, True),
     ("f16", "q8_0", 8, 32, 2, 16, 1, 12, 77, 64, True),
     ("f16", "q8_0", 8, 32, 1, 64, 2, 3, 400, 128, False),
+    # 128-row workgroups (from 256 GQA-packed rows): ragged last row tile
+    ("f16", "q8_0", 8, 32, 1, 16, 2, 33, 700, 256, True),
+    ("f16", "affine", 4, 64, 1, 8, 1, 70, 300, 128, False),
+    ("f16", "affine", 8, 32, 2, 4, 2, 130, 260, 64, True),
 ]
 
 
@@ -223,16 +227,20 @@ def test_prefill_small(case, algo):
     assert_close(out, ref, f"prefill {case} {algo}")
 
 
+@pytest.mark.parametrize("Lq,rows", [(20, 64), (40, 128)])
 @pytest.mark.parametrize("splits", [1, 3, 16])
-def test_prefill_split_count_invariance(splits):
+def test_prefill_split_count_invariance(splits, Lq, rows):
+    """Any split count gives the oracle's result, with 64- and 128-row
+    workgroups (160 and 320 GQA-packed rows)."""
     dtype, mode, bits, gs = "f16", "q8_0", 8, 32
-    B, Hq, Hk, Lq, L, D = 1, 16, 2, 20, 1500, 128
+    B, Hq, Hk, L, D = 1, 16, 2, 1500, 128
     q, kp, vp, kr, vr = _case(dtype, mode, bits, gs, B, Hq, Hk, Lq, L, D)
     ref = oracle_attention(q, dtype, kr, vr, L, mode, bits, gs, 0.09, causal=True)
     qd = to_dev(q, dtype)
-    assert qkv.qsdpa_plan(qd, kp, L, splits)["algo"] == "matrix"
+    plan = qkv.qsdpa_plan(qd, kp, L, splits)
+    assert plan["algo"] == "matrix" and plan["row_tile"] == rows
     out = qkv.qsdpa_prefill(qd, kp, vp, L, 0.09, causal=True, num_splits=splits)
-    assert_close(out, ref, f"prefill splits={splits}")
+    assert_close(out, ref, f"prefill splits={splits} rows={rows}")
 
 
 def test_decode_wide_gqa_uses_tiled_kernel():
