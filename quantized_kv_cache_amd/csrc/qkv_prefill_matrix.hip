@@ -11,14 +11,16 @@
 // (qmm.cu: dequantize a tile into shared memory, then matrix multiply), laid
 // out for gfx950:
 //
-//  * A workgroup owns 64 GQA-packed rows (row p = query i * G + head g of one
-//    kv head) and streams key tiles of 64.  Its 512 threads dequantize the
-//    next K and V tile (fp16, row-major, in LDS, double buffered) while the
-//    current one is consumed.
-//  * 8 waves: waves w and w + 4 share the 16-row block w % 4 and take the two
-//    32-key halves of every tile, so each SIMD runs two waves (one hides the
-//    other's LDS and matrix latencies).  The two halves keep separate
-//    softmax states and are merged through LDS at the end.
+//  * A workgroup owns 128 (or, for few rows, 64) GQA-packed rows (row
+//    p = query i * G + head g of one kv head) and streams key tiles of 64.
+//    Its 512 threads dequantize the next K and V tile (fp16, row-major, in
+//    LDS, double buffered) while the current one is consumed; the stores of
+//    each 8-lane group hit distinct LDS banks.
+//  * 8 waves, two per SIMD (one hides the other's LDS and matrix latencies).
+//    With 128 rows each wave takes a 16-row block over all 64 keys of a
+//    tile; with 64 rows waves w and w + 4 share the 16-row block w % 4 and
+//    take the two 32-key halves, keeping separate softmax states that are
+//    merged through LDS at the end.
 //  * S^T = K Q^T on v_mfma_f32_16x16x32_f16 (A = K rows from LDS, B = the
 //    wave's queries in registers), so each lane holds 4 keys x its row per
 //    16-key subtile: the online softmax of a row is lane-local plus a 4-lane

@@ -26,17 +26,32 @@ CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc")
 KERNEL_SOURCES = {
     "attn_matrix_decode": ["qkv_attn_matrix.hip", "qkv_mfma.hpp", "qkv_device.hpp", "qkv_internal.hpp"],
     "attn_decode_narrow": ["qkv_attn_narrow.hip", "qkv_mfma.hpp", "qkv_device.hpp", "qkv_internal.hpp"],
-    "attn_matrix_prefill": ["qkv_prefill_matrix.hip", "qkv_device.hpp", "qkv_internal.hpp"],
+    "attn_matrix_prefill": ["qkv_prefill_matrix.hip", "qkv_mfma.hpp", "qkv_device.hpp", "qkv_internal.hpp"],
     "attn_generic_kernel": ["qkv_attn_generic.hip", "qkv_device.hpp", "qkv_internal.hpp"],
     "merge_splits_kernel": ["qkv_merge.hip", "qkv_merge.hpp", "qkv_device.hpp"],
+    "merge_splits_small": ["qkv_merge.hip", "qkv_merge.hpp", "qkv_device.hpp"],
     "quantize_rows_kernel": ["qkv_quantize.hip", "qkv_device.hpp", "qkv_internal.hpp"],
 }
+
+
+def _code_only(text: str) -> str:
+    """Source text without // comments, trailing blanks and empty lines (the
+    counters describe the code, so comment edits do not invalidate them)."""
+    out = []
+    for line in text.split("\n"):
+        i = line.find("//")
+        if i >= 0:
+            line = line[:i]
+        line = line.rstrip()
+        if line:
+            out.append(line)
+    return "\n".join(out)
 
 
 def kernel_hash(kernel: str) -> str:
     h = hashlib.sha256()
     for f in KERNEL_SOURCES[kernel]:
-        h.update(open(os.path.join(CSRC, f), "rb").read())
+        h.update(_code_only(open(os.path.join(CSRC, f)).read()).encode())
     return h.hexdigest()[:16]
 
 

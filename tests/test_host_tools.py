@@ -1,0 +1,27 @@
+"""Host-side helpers of the measurement path (no GPU): kernel-name parsing of
+rocprofv3 output and the source hash that ties stored HBM counters to the
+kernel code they were taken on."""
+from quantized_kv_cache_amd import profiling as P
+
+
+def test_short_name_strips_namespaces_templates_and_parameters():
+    name = ("void qkv::(anonymous namespace)::attn_decode_narrow<0, 4, 64, 128, false, 4>"
+            "(qkv::AttnLaunch)")
+    assert P.short_name(name) == "attn_decode_narrow"
+    assert P.short_name("__amd_rocclr_copyBuffer") == "__amd_rocclr_copyBuffer"
+    assert P.short_name("void qkv::(anonymous namespace)::merge_splits_small<1, 256>"
+                        "(qkv::AttnLaunch)") == "merge_splits_small"
+
+
+def test_code_only_ignores_comments_and_blank_lines():
+    a = "int x = 1;  // one\n\n// a comment line\nint y = 2;\n"
+    b = "int x = 1;\nint y = 2;   \n"
+    c = "int x = 1;\nint y = 3;\n"
+    assert P._code_only(a) == P._code_only(b)
+    assert P._code_only(a) != P._code_only(c)
+
+
+def test_every_profiled_kernel_has_sources_and_a_stable_hash():
+    for k in P.KERNEL_SOURCES:
+        h = P.kernel_hash(k)
+        assert len(h) == 16 and h == P.kernel_hash(k)
