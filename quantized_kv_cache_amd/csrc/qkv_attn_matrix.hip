@@ -228,10 +228,17 @@ __global__ __launch_bounds__(NTHR) void attn_matrix_decode(AttnLaunch p) {
     const int lane = tid & 63;
     const int n = lane & 15;          // A/B row or column index
     const int kb = lane >> 4;         // K-block of the lane (0..3)
+    // grid: x = key split, y = kv head, z = batch
     const int split = blockIdx.x;
-    const int64_t bk = blockIdx.z;
-    const int64_t b = bk / p.Hk;
-    const int64_t kvh = bk % p.Hk;
+    const int64_t kvh = blockIdx.y;
+    const int64_t b = blockIdx.z;
+    pin_sgpr(p.q); pin_sgpr(p.Hq); pin_sgpr(p.Hk); pin_sgpr(p.G); pin_sgpr(p.L);
+    pin_sgpr(p.chunk); pin_sgpr(p.scale);
+    pin_sgpr(p.k.codes); pin_sgpr(p.k.scales); pin_sgpr(p.k.biases);
+    pin_sgpr(p.k.sb); pin_sgpr(p.k.sh); pin_sgpr(p.k.sl);
+    pin_sgpr(p.v.codes); pin_sgpr(p.v.scales); pin_sgpr(p.v.biases);
+    pin_sgpr(p.v.sb); pin_sgpr(p.v.sh); pin_sgpr(p.v.sl);
+    const int64_t bk = b * p.Hk + kvh;
     const int G = p.G;
     const float sl = p.scale * kLog2e;            // scores kept in log2 units
 
@@ -719,7 +726,7 @@ __global__ __launch_bounds__(NTHR) void attn_matrix_decode(AttnLaunch p) {
 
 template <int MODE, int BITS, int GS, int D, bool FOLD>
 hipError_t launch_m(int64_t B, const AttnLaunch& p, hipStream_t stream) {
-    dim3 grid(p.S, 1, (unsigned)(B * p.Hk));
+    dim3 grid(p.S, (unsigned)p.Hk, (unsigned)B);
     if (p.mask_kind == MASK_ADDITIVE)
         hipLaunchKernelGGL((attn_matrix_decode<MODE, BITS, GS, D, true, FOLD>), grid, dim3(NTHR), 0,
                            stream, p);

@@ -81,14 +81,19 @@ __global__ __launch_bounds__(NTH) void attn_decode_narrow(AttnLaunch p) {
     const int lane = tid & 63;
     const int n = lane & 15;
     const int kb = lane >> 4;
+    // grid: x = key split, y = kv head, z = batch
     const int split = blockIdx.x;
-    const int64_t bk = blockIdx.z;
-    const int64_t b = bk / p.Hk;
-    const int64_t kvh = bk % p.Hk;
+    const int64_t kvh = blockIdx.y;
+    const int64_t b = blockIdx.z;
+    pin_sgpr(p.q); pin_sgpr(p.Hq); pin_sgpr(p.Hk); pin_sgpr(p.G); pin_sgpr(p.L);
+    pin_sgpr(p.chunk); pin_sgpr(p.scale);
+    pin_sgpr(p.k.codes); pin_sgpr(p.k.scales); pin_sgpr(p.k.biases);
+    pin_sgpr(p.k.sb); pin_sgpr(p.k.sh); pin_sgpr(p.k.sl);
+    pin_sgpr(p.v.codes); pin_sgpr(p.v.scales); pin_sgpr(p.v.biases);
+    pin_sgpr(p.v.sb); pin_sgpr(p.v.sh); pin_sgpr(p.v.sl);
+    const int64_t bk = b * p.Hk + kvh;
     const int G = p.G;
     const float sl = p.scale * kLog2e;            // scores in log2 units
-    if (tid == 0) s_next = NW;                    // tiles 0 .. NW-1 go to the waves in order
-    __syncthreads();
 
     const int64_t j0 = (int64_t)split * p.chunk;
     const int64_t j1 = min(p.L, j0 + p.chunk);
@@ -180,6 +185,8 @@ __global__ __launch_bounds__(NTH) void attn_decode_narrow(AttnLaunch p) {
     // the q loads cannot be placed before the tile loads are issued.
     uint32_t after_loads;
     __asm__ __volatile__("s_mov_b32 %0, 0" : "=s"(after_loads) : : "memory");
+    if (tid == 0) s_next = NW;                    // tiles 0 .. NW-1 go to the waves in order
+    __syncthreads();                              // (waits for no global load)
 
     // q banks and the per-(head, group) sums of q (scale log2e applied)
     h4 qb[NBANK];
@@ -507,7 +514,7 @@ __global__ __launch_bounds__(NTH) void attn_decode_narrow(AttnLaunch p) {
 
 template <int MODE, int BITS, int GS, int D, int GP>
 hipError_t launch_g(int64_t B, const AttnLaunch& p, hipStream_t stream) {
-    dim3 grid(p.S, 1, (unsigned)(B * p.Hk));
+    dim3 grid(p.S, (unsigned)p.Hk, (unsigned)B);
     if (p.mask_kind == MASK_ADDITIVE)
         hipLaunchKernelGGL((attn_decode_narrow<MODE, BITS, GS, D, true, GP>), grid, dim3(NTH), 0, stream, p);
     else

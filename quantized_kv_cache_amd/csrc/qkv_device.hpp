@@ -54,6 +54,14 @@ __device__ __forceinline__ float load_mask(const void* p, int dt, int64_t i) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Makes x live in SGPRs at this point.  Kernels pin every argument they read
+// at their start, so that all argument loads are issued together and waited
+// for once (a later first read would cost another trip to memory).
+template <typename T>
+__device__ __forceinline__ void pin_sgpr(const T& x) {
+    __asm__ __volatile__("" ::"s"(x));
+}
+
 constexpr float kLog2e = 1.4426950408889634f;
 
 }  // namespace qkv

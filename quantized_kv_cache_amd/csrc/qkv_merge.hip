@@ -28,6 +28,28 @@ __device__ __forceinline__ void combine(State& a, float m, float l, float4 o) {
     a.m = mm;
 }
 
+// Every argument the merge reads, fetched in one round trip at the start.
+__device__ __forceinline__ void pin_args(const AttnLaunch& p) {
+    pin_sgpr(p.n_rt); pin_sgpr(p.n_rows); pin_sgpr(p.Hk); pin_sgpr(p.G); pin_sgpr(p.S);
+    pin_sgpr(p.part_ml); pin_sgpr(p.part_o); pin_sgpr(p.out); pin_sgpr(p.Hq); pin_sgpr(p.Lq);
+}
+
+// Output row r of 16-row tile 'tile' (tile = (b Hk + kvh) n_rt + rt): its
+// GQA-packed row pr = 16 rt + r, query i = pr / G and head h = kvh G + pr % G.
+// Tiles number below 2^24 (the grid's x size), so 32-bit division suffices.
+struct Row {
+    int pr;
+    int64_t b, kvh, i, h;
+};
+__device__ __forceinline__ Row locate(const AttnLaunch& p, uint32_t tile, int r) {
+    const uint32_t nrt = (uint32_t)p.n_rt, hk = (uint32_t)p.Hk, g = (uint32_t)p.G;
+    const uint32_t bk = tile / nrt, rt = tile - bk * nrt;
+    const uint32_t pr = rt * 16u + (uint32_t)r;
+    const uint32_t b = bk / hk, kvh = bk - b * hk;
+    const uint32_t i = pr / g;
+    return Row{(int)pr, (int64_t)b, (int64_t)kvh, (int64_t)i, (int64_t)(kvh * g + (pr - i * g))};
+}
+
 constexpr int MC = 16;          // float4 columns per workgroup (64 d)
 constexpr int SG = 256 / MC;    // split groups
 constexpr int U = 8;            // loads in flight per batch
@@ -37,14 +59,12 @@ __global__ __launch_bounds__(256) void merge_splits_kernel(AttnLaunch p) {
     constexpr int F4 = D / 4;
     __shared__ State red[256];
 
+    pin_args(p);
     const int64_t tile = blockIdx.x;
     const int r = blockIdx.y;
-    const int rt = (int)(tile % p.n_rt);
-    const int64_t bk = tile / p.n_rt;
-    const int pr = rt * 16 + r;
-    if (pr >= p.n_rows) return;                   // whole workgroup leaves together
-    const int64_t b = bk / p.Hk, kvh = bk % p.Hk;
-    const int64_t i = pr / p.G, h = kvh * p.G + pr % p.G;
+    const Row rw = locate(p, (uint32_t)tile, r);
+    if (rw.pr >= p.n_rows) return;                // whole workgroup leaves together
+    const int64_t b = rw.b, kvh = rw.kvh, i = rw.i, h = rw.h;
     const int f = blockIdx.z * MC + threadIdx.x % MC;   // float4 column of the row
     const int sg = threadIdx.x / MC;
     const int S = p.S;
@@ -92,14 +112,12 @@ template <int QT, int D>
 __global__ __launch_bounds__(256) void merge_splits_small(AttnLaunch p) {
     constexpr int F4 = D / 4;
     constexpr int RPW = 256 / F4;                 // rows per workgroup
+    pin_args(p);
     const int64_t tile = blockIdx.x;
     const int r = blockIdx.y * RPW + threadIdx.x / F4;
-    const int rt = (int)(tile % p.n_rt);
-    const int64_t bk = tile / p.n_rt;
-    const int pr = rt * 16 + r;
-    if (pr >= p.n_rows) return;
-    const int64_t b = bk / p.Hk, kvh = bk % p.Hk;
-    const int64_t i = pr / p.G, h = kvh * p.G + pr % p.G;
+    const Row rw = locate(p, (uint32_t)tile, r);
+    if (rw.pr >= p.n_rows) return;
+    const int64_t b = rw.b, kvh = rw.kvh, i = rw.i, h = rw.h;
     const int f = threadIdx.x % F4;
     const int S = p.S;
     const float2* ml = (const float2*)p.part_ml + (tile * S * 16 + r);

@@ -125,9 +125,17 @@ __global__ __launch_bounds__(PNTHR) void attn_matrix_prefill(AttnLaunch p) {
     const int kb = lane >> 4;
     const int split = blockIdx.x;
     const int rt = blockIdx.y;                     // row tile
-    const int64_t bk = blockIdx.z;
-    const int64_t b = bk / p.Hk;
-    const int64_t kvh = bk % p.Hk;
+    pin_sgpr(p.q); pin_sgpr(p.Hq); pin_sgpr(p.Hk); pin_sgpr(p.G); pin_sgpr(p.L); pin_sgpr(p.Lq);
+    pin_sgpr(p.chunk); pin_sgpr(p.scale); pin_sgpr(p.mask_kind); pin_sgpr(p.n_rows);
+    pin_sgpr(p.k.codes); pin_sgpr(p.k.scales); pin_sgpr(p.k.biases);
+    pin_sgpr(p.k.sb); pin_sgpr(p.k.sh); pin_sgpr(p.k.sl);
+    pin_sgpr(p.v.codes); pin_sgpr(p.v.scales); pin_sgpr(p.v.biases);
+    pin_sgpr(p.v.sb); pin_sgpr(p.v.sh); pin_sgpr(p.v.sl);
+    // z = batch x kv head (below 2^16: 32-bit division)
+    const uint32_t bk32 = blockIdx.z, hk32 = (uint32_t)p.Hk;
+    const int64_t bk = bk32;
+    const int64_t b = bk32 / hk32;
+    const int64_t kvh = bk32 - (uint32_t)b * hk32;
     const int G = p.G;
     const float sl = p.scale * kLog2e;
 
