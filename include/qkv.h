@@ -125,12 +125,16 @@ qkv_status qkv_update_append(const void* k_new, const void* v_new, int32_t dtype
                              const qkv_pack* k_cache, const qkv_pack* v_cache, void* stream);
 
 /* Bytes of workspace the attention calls need for these sizes (0 when no
- * key partitioning is used): per row tile and split, the partial softmax
- * state (m, l) and an unnormalised output row.  The workspace needs no
- * initialisation; a call writes it with its first kernel and reads it with
- * the split merge kernel it launches next on the same stream.  Calls that may
- * overlap (different streams) need separate workspaces.  It must be 256-byte
- * aligned. */
+ * key partitioning is used): a ticket area (4 bytes per batch x kv head x
+ * row tile, rounded up to 256 bytes), then per row tile and split the partial
+ * softmax state (m, l) and an unnormalised output row.  The ticket area must
+ * hold zeros when the workspace is first used (zero-fill the workspace once
+ * after allocating it); every call leaves it zero.  The partial states need no
+ * initialisation: a call writes them and either merges them in the same
+ * kernel (the last workgroup of each batch x kv head, counted by its ticket)
+ * or with the split merge kernel it launches next on the same stream.  Calls
+ * that may overlap (different streams) need separate workspaces.  It must be
+ * 256-byte aligned. */
 size_t qsdpa_workspace_bytes(int64_t B, int64_t Hq, int64_t Lq, int64_t D, int64_t L,
                              const qkv_pack* k, int32_t q_dtype, const qkv_attn_opts* opts);
 

@@ -172,7 +172,8 @@ def qsdpa_plan(q: torch.Tensor, k: Pack, L: int, num_splits: int = 0,
 
 class Workspace:
     """Reusable attention workspace (grows on demand), one buffer per device,
-    for calls on one stream."""
+    for calls on one stream.  Buffers start zero-filled (the ticket area at
+    their start must be; the calls leave it zero)."""
 
     def __init__(self):
         self._buf: dict[torch.device, torch.Tensor] = {}
@@ -183,7 +184,7 @@ class Workspace:
         device = torch.device(device)
         buf = self._buf.get(device)
         if buf is None or buf.numel() < nbytes:
-            buf = torch.empty(((nbytes + 255) // 256) * 256, dtype=torch.uint8, device=device)
+            buf = torch.zeros(((nbytes + 255) // 256) * 256, dtype=torch.uint8, device=device)
             self._buf[device] = buf
         return buf
 

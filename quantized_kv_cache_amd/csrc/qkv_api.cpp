@@ -150,7 +150,8 @@ struct Plan {
 
 size_t ws_for(int64_t B, int64_t Hk, int n_rt, int S, int RT, int64_t D) {
     if (S <= 1) return 0;
-    return (size_t)(B * Hk * n_rt) * (size_t)S * (size_t)RT * (size_t)(D + 2) * 4;  // ml + o
+    return qkv::ticket_bytes(B * Hk * n_rt) +
+           (size_t)(B * Hk * n_rt) * (size_t)S * (size_t)RT * (size_t)(D + 2) * 4;  // ml + o
 }
 
 // Split count: enough workgroups to cover the CUs about twice, each split at
@@ -303,8 +304,10 @@ qkv_status attention(const char* name, const void* q, int32_t q_dtype, int64_t B
     a.wg_rows = pl.wg_rows;
     a.RT = pl.RT;
     if (pl.ws_bytes > 0) {
-        a.part_ml = static_cast<float*>(workspace);
-        a.part_o = a.part_ml + (size_t)(B * k->H * pl.n_rt) * (size_t)pl.S * 16 * 2;
+        const int64_t tiles = B * k->H * pl.n_rt;
+        a.tickets = static_cast<uint32_t*>(workspace);
+        a.part_ml = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + qkv::ticket_bytes(tiles));
+        a.part_o = a.part_ml + (size_t)tiles * (size_t)pl.S * 16 * 2;
     }
     hipStream_t s = static_cast<hipStream_t>(stream);
     const bool timed = opts && opts->timing_events[0] && opts->timing_events[1];
@@ -317,7 +320,8 @@ qkv_status attention(const char* name, const void* q, int32_t q_dtype, int64_t B
                    : pl.matrix ? qkv::launch_attn_matrix(k->mode, k->bits, (int)D, B, a, s)
                                : qkv::launch_attn_generic(q_dtype, k->mode, k->bits, (int)D, B, a, s);
     if (e == hipSuccess && timed) e = hipEventRecord(static_cast<hipEvent_t>(opts->timing_events[1]), s);
-    if (e == hipSuccess && pl.S > 1) e = qkv::launch_merge(q_dtype, (int)D, B, a, s);
+    // the narrow decode kernel merges its splits itself
+    if (e == hipSuccess && pl.S > 1 && !pl.narrow) e = qkv::launch_merge(q_dtype, (int)D, B, a, s);
     return hip_status(e, name);
 }
 

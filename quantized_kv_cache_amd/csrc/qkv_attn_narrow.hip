@@ -38,6 +38,7 @@
 //  * The 8 waves' states merge after one barrier; each thread then writes 4
 //    consecutive output d.
 #include "qkv_internal.hpp"
+#include "qkv_merge.hpp"
 #include "qkv_mfma.hpp"
 
 namespace qkv {
@@ -74,6 +75,7 @@ __global__ __launch_bounds__(NTH) void attn_decode_narrow(AttnLaunch p) {
     __shared__ __attribute__((aligned(16))) float s_wave[NW][WAVE_FLOATS];
     __shared__ float s_ml[NW][2][4];
     __shared__ int s_next;                        // next tile of the split to hand out
+    __shared__ bool s_last;                       // this workgroup merges the splits
     __shared__ float s_bias[NW][4][4];
 
     const int tid = threadIdx.x;
@@ -453,8 +455,10 @@ __global__ __launch_bounds__(NTH) void attn_decode_narrow(AttnLaunch p) {
     // item is one 16-byte (or 8-byte) store.
     constexpr int DPT = D / 16;
     static_assert(DPT % 4 == 0, "4 consecutive d per output item");
-    float* ml = p.part_ml + (bk * p.S + split) * 32;
-    float* po = p.part_o + (bk * p.S + split) * 16 * D;
+    // with several splits: this split's state, stored at device scope for the
+    // fused merge ([16 rows][D] o and [16 rows][2] (m, l); rows = heads)
+    const auto rml = flat_rsrc(p.part_ml + (bk * p.S + split) * 32, 32 * 4);
+    const auto rpo = flat_rsrc(p.part_o + (bk * p.S + split) * 16 * D, 16 * D * 4);
     const int64_t obase = (b * p.Hq + kvh * G) * D;
     for (int i = tid; i < G * D / 4; i += NTH) {
         const int jj = i & 3;
@@ -503,13 +507,27 @@ __global__ __launch_bounds__(NTH) void attn_decode_narrow(AttnLaunch p) {
                 for (int q = 0; q < 4; ++q) dst[q] = h[q];
             }
         } else {
-            *(float4*)(po + oh * D + d0) = float4{o[0], o[1], o[2], o[3]};
+            const u4 ov = {__float_as_uint(o[0]), __float_as_uint(o[1]), __float_as_uint(o[2]),
+                           __float_as_uint(o[3])};
+            __builtin_amdgcn_raw_buffer_store_b128(ov, rpo, (oh * D + d0) * 4, 0, kScopeDevice);
             if (d0 == 0) {
-                ml[2 * oh] = Mh;
-                ml[2 * oh + 1] = Lh;
+                const u2 mv = {__float_as_uint(Mh), __float_as_uint(Lh)};
+                __builtin_amdgcn_raw_buffer_store_b64(mv, rml, 2 * oh * 4, 0, kScopeDevice);
             }
         }
     }
+    if (p.S == 1) return;
+
+    // ------------------------------------------------------------ fused split merge
+    // The workgroup's state stores are complete (device scope) before its
+    // ticket; the workgroup that takes the last ticket of this (batch, kv head)
+    // combines the S states (all stored before their tickets) and writes out.
+    wait_stores();
+    __syncthreads();
+    if (tid == 0) s_last = take_last_ticket(p.tickets + bk, p.S);
+    __syncthreads();
+    if (!s_last) return;
+    merge_last<NTH, D, GP>(p, b, kvh, bk, &s_wave[0][0]);
 }
 
 template <int MODE, int BITS, int GS, int D, int GP>

@@ -57,6 +57,7 @@ struct AttnLaunch {
     int32_t wg_rows;                // rows per workgroup of the prefill kernel (64 or 128)
     float* part_ml;                 // [B*Hk*n_rt][S][16][2] (m, l) of each split
     float* part_o;                  // [B*Hk*n_rt][S][16][D] unnormalised o of each split
+    uint32_t* tickets;              // [B*Hk*n_rt] fused-merge tickets (zero between calls)
 };
 
 // Launchers (return hipGetLastError() of the launch).

@@ -10,23 +10,9 @@ namespace qkv {
 
 namespace {
 
-struct State {
-    float m, l;
-    float4 o;
-};
+using State = SplitState;
 
-__device__ __forceinline__ void combine(State& a, float m, float l, float4 o) {
-    if (m == -INFINITY) return;
-    const float mm = fmaxf(a.m, m);
-    const float fa = (a.m == -INFINITY) ? 0.0f : fast_exp2(a.m - mm);
-    const float fb = fast_exp2(m - mm);
-    a.l = a.l * fa + l * fb;
-    a.o.x = a.o.x * fa + o.x * fb;
-    a.o.y = a.o.y * fa + o.y * fb;
-    a.o.z = a.o.z * fa + o.z * fb;
-    a.o.w = a.o.w * fa + o.w * fb;
-    a.m = mm;
-}
+__device__ __forceinline__ void combine(State& a, float m, float l, float4 o) { combine_state(a, m, l, o); }
 
 // Every argument the merge reads, fetched in one round trip at the start.
 __device__ __forceinline__ void pin_args(const AttnLaunch& p) {

@@ -24,12 +24,14 @@ import statistics
 CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc")
 # sources whose change invalidates a kernel's counter readings
 KERNEL_SOURCES = {
-    "attn_matrix_decode": ["qkv_attn_matrix.hip", "qkv_mfma.hpp", "qkv_device.hpp", "qkv_internal.hpp"],
-    "attn_decode_narrow": ["qkv_attn_narrow.hip", "qkv_mfma.hpp", "qkv_device.hpp", "qkv_internal.hpp"],
+    "attn_matrix_decode": ["qkv_attn_matrix.hip", "qkv_merge.hpp", "qkv_mfma.hpp", "qkv_device.hpp",
+                           "qkv_internal.hpp"],
+    "attn_decode_narrow": ["qkv_attn_narrow.hip", "qkv_merge.hpp", "qkv_mfma.hpp", "qkv_device.hpp",
+                           "qkv_internal.hpp"],
     "attn_matrix_prefill": ["qkv_prefill_matrix.hip", "qkv_mfma.hpp", "qkv_device.hpp", "qkv_internal.hpp"],
     "attn_generic_kernel": ["qkv_attn_generic.hip", "qkv_device.hpp", "qkv_internal.hpp"],
-    "merge_splits_kernel": ["qkv_merge.hip", "qkv_merge.hpp", "qkv_device.hpp"],
-    "merge_splits_small": ["qkv_merge.hip", "qkv_merge.hpp", "qkv_device.hpp"],
+    "merge_splits_kernel": ["qkv_merge.hip", "qkv_merge.hpp", "qkv_device.hpp", "qkv_internal.hpp"],
+    "merge_splits_small": ["qkv_merge.hip", "qkv_merge.hpp", "qkv_device.hpp", "qkv_internal.hpp"],
     "quantize_rows_kernel": ["qkv_quantize.hip", "qkv_device.hpp", "qkv_internal.hpp"],
 }
 

@@ -132,8 +132,9 @@ def test_workspace_bytes(L):
                                    ctypes.byref(one)) == 0
     n = L.qsdpa_workspace_bytes(1, 4, 1, 128, 64, ctypes.byref(kp), _lib.QKV_F16,
                                 ctypes.byref(four))
-    # splits x 16 rows x (m, l, o[D]) floats per (b, kv head, row tile)
-    assert n == 2 * 2 * 16 * 130 * 4
+    # a 256-byte ticket area, then splits x 16 rows x (m, l, o[D]) floats per
+    # (b, kv head, row tile)
+    assert n == 256 + 2 * 2 * 16 * 130 * 4
     assert L.qsdpa_workspace_bytes(1, 3, 1, 128, 64, ctypes.byref(kp), _lib.QKV_F16, None) == 0
 
 

@@ -96,6 +96,31 @@ def test_decode_narrow_gqa(case):
         assert_close(out, ref, f"narrow {case} splits={splits}")
 
 
+def test_decode_fused_merge_repeats():
+    """The narrow decode merges its splits inside the kernel: the workgroup
+    that takes the last ticket of a kv head combines the states.  Calls
+    alternating between two caches on one workspace must each give the first
+    output of their cache bit for bit (a stale split state of the other cache
+    would change it), and the ticket area must be zero afterwards."""
+    mode, bits, gs, B, Hq, Hk, L, D = "affine", 4, 64, 2, 16, 4, 16384, 128
+    ws = qkv.Workspace()
+    firsts = []
+    for dist in ("normal", "uniform"):
+        q, kp, vp, kr, vr = _case("f16", mode, bits, gs, B, Hq, Hk, 1, L, D, dist=dist)
+        qd = to_dev(q, "f16")
+        plan = qkv.qsdpa_plan(qd, kp, L, num_splits=32)
+        assert plan["kernel"] == "attn_decode_narrow" and plan["num_splits"] == 32
+        out = qkv.qsdpa_decode(qd, kp, vp, L, 0.1, num_splits=32, workspace=ws)
+        assert_close(out, oracle_attention(q, "f16", kr, vr, L, mode, bits, gs, 0.1), f"fused {dist}")
+        firsts.append((qd, kp, vp, out.clone()))
+    for i in range(200):
+        qd, kp, vp, ref = firsts[i % 2]
+        out = qkv.qsdpa_decode(qd, kp, vp, L, 0.1, num_splits=32, workspace=ws)
+        assert torch.equal(out, ref), f"call {i} differs from the first call on its cache"
+    torch.cuda.synchronize()
+    assert not ws.get(1, qd.device)[:256].any(), "tickets not back to zero"
+
+
 @pytest.mark.parametrize("mode,bits,vmean,vstd", [
     ("affine", 4, 0.0, 1.0), ("q8_0", 8, 0.0, 1.0),
     ("affine", 4, 3000.0, 600.0),       # 4-bit value scales ~190
