@@ -45,6 +45,7 @@
 #include "qkv_device.hpp"
 #include "qkv_internal.hpp"
 #include "qkv_merge.hpp"
+#include "qkv_mfma.hpp"
 
 namespace qkv {
 
@@ -217,8 +218,18 @@ __global__ __launch_bounds__(NTHR) void attn_matrix_decode(AttnLaunch p) {
     // Per-wave LDS: the score scratch of its tiles while it streams, then its
     // output state for the workgroup merge (written only after its last tile;
     // no other wave touches its scratch).
-    constexpr int WAVE_FLOATS = 64 * (D / 4) > 16 * SROW ? 64 * (D / 4) : 16 * SROW;
+    // K tiles are staged in LDS (after the score scratch): TK key rows of
+    // ROWB bytes, 16-byte chunks XOR-swizzled per row (kswz), filled by
+    // direct-to-LDS loads that read whole rows (KPI rows per instruction).
+    constexpr int ROWB = F::ROWB;
+    constexpr int NCH = ROWB / 16;                // 16-byte chunks per key row
+    constexpr int KPI = 1024 / ROWB;              // key rows per load instruction
+    constexpr int NKI = TK / KPI;                 // K load instructions per tile
+    constexpr int KSTAGE = 16 * SROW;             // float offset of the K stage in a wave's region
+    constexpr int WAVE_FLOATS = 64 * (D / 4) > KSTAGE + TK * ROWB / 4 ? 64 * (D / 4) : KSTAGE + TK * ROWB / 4;
+    static_assert(NCH >= 2 && NCH <= 16 && TK % KPI == 0, "K stage layout");
     __shared__ __attribute__((aligned(16))) float s_wave[NWAVE][WAVE_FLOATS];
+    __shared__ __attribute__((aligned(16))) uint16_t s_q[16 * D];   // the 16 query rows (rows >= G zero)
     __shared__ float s_qsum[16][NG];
     __shared__ float s_ml[NWAVE][2][16];
     __shared__ float s_bias[NWAVE][16][2];
@@ -278,7 +289,6 @@ __global__ __launch_bounds__(NTHR) void attn_matrix_decode(AttnLaunch p) {
     // with cross-lane shuffles.
     constexpr bool COOP = FOLD;
     struct Tile {
-        uint32_t kw[2][NG][KW];       // q K^T codes: key (16 hf + n), per group
         uint32_t ks[2][NSW];          // key scales (fp16)
         uint32_t kbias[2][NSW];
         uint32_t vw[8][VW];           // P V codes: keys 8 kb + e
@@ -286,9 +296,38 @@ __global__ __launch_bounds__(NTHR) void attn_matrix_decode(AttnLaunch p) {
         uint32_t vb[8];
         uint32_t ksr, kbr, vsr, vbr;  // cooperative scale / bias rows (folded form)
     };
-    // loop-invariant lane offsets inside a tile
-    const uint32_t o_k0 = (uint32_t)n * kcs + kb * F::KCH;
-    const uint32_t o_k1 = (uint32_t)(16 + n) * kcs + kb * F::KCH;
+    // K stage: chunk position of chunk c in row r is c ^ kswz(r); the shift
+    // makes the 16 rows that one LDS read spans start on distinct banks
+    constexpr int SWS = NCH == 16 ? 0 : NCH == 8 ? 1 : NCH == 4 ? 2 : 3;
+    auto kswz = [](int r) { return (r >> SWS) & (NCH - 1); };
+    uint8_t* kstage = reinterpret_cast<uint8_t*>(&s_wave[wave][KSTAGE]);
+    // lane offset of K load instruction i: row KPI i + lane / NCH, position
+    // lane % NCH holds the row's chunk (lane % NCH) ^ kswz(row)
+    uint32_t o_kl[NKI];
+#pragma unroll
+    for (int i = 0; i < NKI; ++i) {
+        const int r = KPI * i + lane / NCH;
+        o_kl[i] = (uint32_t)r * kcs + 16u * (uint32_t)((lane % NCH) ^ kswz(r));
+    }
+    // nw dwords at byte b (within one 16-byte chunk, or two whole chunks) of
+    // staged row r
+    auto lds_k = [&](int r, int b, uint32_t* dst, int nw) {
+        const int sw = kswz(r);
+#pragma unroll
+        for (int c0 = 0; c0 < (nw > 4 ? nw / 4 : 1); ++c0) {
+            const int bb = b + 16 * c0;
+            const uint8_t* src = kstage + r * ROWB + 16 * ((bb >> 4) ^ sw) + (bb & 15);
+            if (nw == 1) {
+                dst[0] = *(const uint32_t*)src;
+            } else if (nw == 2) {
+                const uint2 x = *(const uint2*)src;
+                dst[0] = x.x; dst[1] = x.y;
+            } else {
+                const uint4 x = *(const uint4*)src;
+                dst[4 * c0] = x.x; dst[4 * c0 + 1] = x.y; dst[4 * c0 + 2] = x.z; dst[4 * c0 + 3] = x.w;
+            }
+        }
+    };
     const uint32_t o_ks0 = (uint32_t)n * kss, o_ks1 = (uint32_t)(16 + n) * kss;
     const uint32_t o_v = (uint32_t)(8 * kb) * vcs + n * F::VBYTES;
     const uint32_t o_vs = (uint32_t)(8 * kb) * vss + 2 * vg;
@@ -328,11 +367,9 @@ __global__ __launch_bounds__(NTHR) void attn_matrix_decode(AttnLaunch p) {
         const int64_t row0 = j0 + (int64_t)tt * TK;
         const auto rk = rsrc(kc, row0, kcs, F::ROWB);
         const auto rv = rsrc(vc, row0, vcs, F::ROWB);
-        const uint32_t ok[2] = {o_k0, o_k1};
 #pragma unroll
-        for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-            for (int g = 0; g < NG; ++g) ldn(rk, ok[hf] + g * (GS * BITS / 8), T.kw[hf][g], KW);
+        for (int i = 0; i < NKI; ++i)
+            mf::buf_to_lds16(rk, kstage + 1024 * i, o_kl[i]);
         if constexpr (COOP) {
             T.ksr = (NG == 1) ? ld16(rsrc(ksc, row0, kss, F::SROWB), o_kr)
                               : ld32(rsrc(ksc, row0, kss, F::SROWB), o_kr);
@@ -369,21 +406,28 @@ __global__ __launch_bounds__(NTHR) void attn_matrix_decode(AttnLaunch p) {
         }
     };
 
-    // the query rows, then the first tiles, are requested before anything waits
-    const uint16_t* qrow = (const uint16_t*)p.q + ((b * p.Hq + kvh * G + min(n, G - 1)) * D);
-    uint4 qraw[STEPS];
-#pragma unroll
-    for (int st = 0; st < STEPS; ++st) {
-        const int g = st / F::SPG, u = st % F::SPG;
-        qraw[st] = *(const uint4*)(qrow + g * GS + kb * (GS / 4) + 8 * u);   // 8 consecutive halves
-    }
-    // keep the query loads ahead of the tile loads (waiting for q must not
+    // the workgroup's G query rows are read once (wave w: bytes 1024 w ..
+    // 1024 w + 1023 of the 16 x D block, zeros past row G), then the first
+    // tiles are requested before anything waits
+    constexpr int QB = 16 * D * 2;
+    const auto rq = flat_rsrc((const uint16_t*)p.q + (b * p.Hq + kvh * G) * D, (uint32_t)(G * D * 2));
+    u4 qv = {0u, 0u, 0u, 0u};
+    if (1024 * wave < QB) qv = __builtin_amdgcn_raw_buffer_load_b128(rq, 1024 * wave + 16 * lane, 0, 0);
+    // keep the query load ahead of the tile loads (waiting for q must not
     // wait for the tile)
     __builtin_amdgcn_sched_barrier(0);
     const int my_tiles = wave < ntiles ? (ntiles - wave + NWAVE - 1) / NWAVE : 0;
     Tile cur;
     load_tile(wave, cur);
     __builtin_amdgcn_sched_barrier(0);
+    if (1024 * wave < QB) *(u4*)((uint8_t*)s_q + 1024 * wave + 16 * lane) = qv;
+    __syncthreads();
+    uint4 qraw[STEPS];
+#pragma unroll
+    for (int st = 0; st < STEPS; ++st) {
+        const int g = st / F::SPG, u = st % F::SPG;
+        qraw[st] = *(const uint4*)(s_q + n * D + g * GS + kb * (GS / 4) + 8 * u);   // 8 consecutive halves
+    }
 
     // ---------------------------------------------------------------- queries
     // A operand of q K^T for every K-step, and per-(head, group) sums of q.
@@ -439,6 +483,13 @@ __global__ __launch_bounds__(NTHR) void attn_matrix_decode(AttnLaunch p) {
 
     auto process = [&](const Tile& cur, int tt) {
         const uint32_t base = (uint32_t)(j0 + (int64_t)tt * TK);
+        // this lane's K codes from the stage: key 16 hf + n, per group the
+        // KCH bytes at kb KCH (the B operand of every K-step)
+        uint32_t kw[2][NG][KW];
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+            for (int g = 0; g < NG; ++g) lds_k(16 * hf + n, g * (GS * BITS / 8) + kb * F::KCH, kw[hf][g], KW);
 
         // ---- scores of 2 x 16 keys
         uint32_t krow_s[2] = {0u, 0u}, krow_b[2] = {0u, 0u};
@@ -467,7 +518,7 @@ __global__ __launch_bounds__(NTHR) void attn_matrix_decode(AttnLaunch p) {
                     }
 #pragma unroll
                     for (int u = 0; u < F::SPG; ++u) {
-                        const h8 kop = dequant_k<MODE, BITS>(&cur.kw[hf][g][u * (BITS == 4 ? 1 : 2)], s2, b2);
+                        const h8 kop = dequant_k<MODE, BITS>(&kw[hf][g][u * (BITS == 4 ? 1 : 2)], s2, b2);
                         acc = mfma(qa[g * F::SPG + u], kop, acc);
                     }
                 }
@@ -479,7 +530,7 @@ __global__ __launch_bounds__(NTHR) void attn_matrix_decode(AttnLaunch p) {
                 f4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int u = 0; u < F::SPG; ++u) {
-                    const h8 kbop = unpack_k<MODE, BITS>(&cur.kw[hf][g][u * (BITS == 4 ? 1 : 2)]);
+                    const h8 kbop = unpack_k<MODE, BITS>(&kw[hf][g][u * (BITS == 4 ? 1 : 2)]);
                     acc = mfma(qa[g * F::SPG + u], kbop, acc);
                 }
                 const uint32_t sw2 = COOP ? krow_s[hf] : cur.ks[hf][g >> 1];

@@ -143,6 +143,12 @@ __device__ __forceinline__ uint32_t buf32(__amdgpu_buffer_rsrc_t r, uint32_t off
 __device__ __forceinline__ uint32_t buf16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
     return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, 0);
 }
+// 16 bytes per lane from the buffer straight into LDS: lane l's bytes land
+// at lds + 16 l (the wave writes 1 KB there; completion counts in vmcnt).
+__device__ __forceinline__ void buf_to_lds16(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t off) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, off, 0, 0,
+                                             0);
+}
 // nw (1, 2 or a multiple of 4) consecutive dwords
 __device__ __forceinline__ void bufn(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t* dst, int nw) {
     if (nw == 1) {
