@@ -268,6 +268,34 @@ def test_prefill_split_count_invariance(splits, Lq, rows):
     assert_close(out, ref, f"prefill splits={splits} rows={rows}")
 
 
+SIXTEEN_ROW_CASES = [
+    # mode, bits, gs, B, Hq, Hk, L, D: GQA factor 5..16 with fp16 queries (the
+    # 16-row kernel).  Key rows of 32, 64, 128 and 256 bytes (the LDS stage's
+    # four swizzles), folded (G x groups <= 16) and dequantized key paths
+    ("affine", 4, 32, 2, 16, 2, 700, 64),       # 32-byte rows, G = 8, folded
+    ("affine", 4, 64, 1, 32, 2, 1000, 128),     # 64-byte rows, G = 16
+    ("affine", 4, 64, 2, 16, 2, 513, 128),      # 64-byte rows, G = 8, folded
+    ("affine", 8, 64, 1, 16, 2, 777, 64),       # 64-byte rows, 8-bit, one group
+    ("affine", 8, 64, 2, 24, 2, 600, 128),      # 128-byte rows, G = 12
+    ("affine", 4, 32, 1, 10, 2, 900, 256),      # 128-byte rows, 8 groups, G = 5
+    ("affine", 8, 128, 1, 16, 2, 1100, 256),    # 256-byte rows, G = 8, folded
+    ("q8_0", 8, 32, 2, 32, 4, 650, 64),         # 64-byte rows, Q8_0
+    ("q8_0", 8, 32, 1, 16, 1, 1300, 128),       # 128-byte rows, Q8_0, G = 16
+]
+
+
+@pytest.mark.parametrize("case", SIXTEEN_ROW_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_decode_sixteen_row_formats(case):
+    mode, bits, gs, B, Hq, Hk, L, D = case
+    q, kp, vp, kr, vr = _case("f16", mode, bits, gs, B, Hq, Hk, 1, L, D)
+    qd = to_dev(q, "f16")
+    assert qkv.qsdpa_plan(qd, kp, L)["kernel"] == "attn_matrix_decode"
+    ref = oracle_attention(q, "f16", kr, vr, L, mode, bits, gs, 0.125)
+    for splits in (0, 1, 3):
+        out = qkv.qsdpa_decode(qd, kp, vp, L, 0.125, num_splits=splits)
+        assert_close(out, ref, f"16-row {case} splits={splits}")
+
+
 def test_decode_wide_gqa_uses_tiled_kernel():
     """GQA factor 32 (beyond the single-query kernel) with fp16 queries runs
     on the tiled matrix kernel."""
