@@ -11,16 +11,25 @@
 //
 //  * One workgroup (8 waves) per (key split, batch x kv head) streams its
 //    chunk of packed K/V exactly once; the G query heads of the kv head are
-//    the 16 rows of the matrix tiles (rows >= G are zero).  Each wave takes
-//    every 8th tile of 32 keys and keeps the next tile's loads in flight.
+//    the 16 rows of the matrix tiles (rows >= G are zero), read once per
+//    workgroup (one 16-byte load per thread) and shared through LDS.  Each
+//    wave takes every 8th tile of 32 keys.
+//  * A wave's K tile goes straight into LDS (buffer_load ... lds) with loads
+//    that read whole key rows, into rows whose 16-byte chunks are
+//    XOR-swizzled so that the 16 rows of one fragment read start on distinct
+//    banks; the MFMA fragments are read back from there.  Loads that spread
+//    one instruction over 16 key rows were measured far slower.  V codes and
+//    the scales go to registers.
 //  * q K^T: A = queries [16 heads x 32 d], B = key codes [32 d x 16 keys].
-//    Codes enter the matrix core unconverted: masking a packed word leaves
-//    fp16 subnormals c * 2^-24 (4-bit: the odd nibble of a byte becomes
-//    16 c * 2^-24, compensated by a query pre-divided by 16; Q8_0: the sign
-//    bit is flipped so c + 128 is unsigned).  Each K-step of 32 d lies in one
-//    quantization group, so every group has its own accumulator and the
-//    per-key scale/bias (and the Q8_0 -128 offset) are applied afterwards in
-//    fp32:  z = sum_g s_g * 2^24 * acc_g + b_g * sum_{d in g} q_d.
+//    Folded form (affine caches with G * groups <= 16): codes enter the
+//    matrix core unconverted: masking a packed word leaves fp16 subnormals
+//    c * 2^-24 (4-bit: the odd nibble of a byte becomes 16 c * 2^-24,
+//    compensated by a query pre-divided by 16).  Each K-step of 32 d lies in
+//    one quantization group, so every group has its own accumulator and the
+//    per-key scale/bias are applied afterwards in fp32:
+//    z = sum_g s_g * 2^24 * acc_g + b_g * sum_{d in g} q_d.  Otherwise (Q8_0,
+//    wide groups) the key codes are dequantized to fp16 before the matrix
+//    core and one accumulator covers all groups.
 //  * The 16x16 score tiles go through a per-wave LDS scratch to the layout
 //    of the P operand: each lane owns one head and 8 keys, so the running
 //    max, the rescale of its accumulators and exp2 are lane-local (the 4
@@ -41,7 +50,7 @@
 //    SGPRs, bounded at the split's last key (rows past it read as zeros), and
 //    a loop-invariant 32-bit lane offset, so the load path costs no vector
 //    address arithmetic and needs no clamping.  Each wave keeps one tile in
-//    registers and issues the next tile's loads as soon as it is consumed.
+//    flight and issues the next tile's loads as soon as it is consumed.
 #include "qkv_device.hpp"
 #include "qkv_internal.hpp"
 #include "qkv_merge.hpp"

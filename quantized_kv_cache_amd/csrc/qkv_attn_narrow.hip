@@ -36,7 +36,9 @@
 //    soon as it has consumed one; tiles after a wave's first come from an
 //    LDS counter, so the waves of a workgroup finish together.
 //  * The 8 waves' states merge after one barrier; each thread then writes 4
-//    consecutive output d.
+//    consecutive output d.  With several key splits the workgroup stores
+//    its state at device scope and takes a ticket; the one that takes the
+//    last ticket of its (batch, kv head) merges the splits (merge_last).
 #include "qkv_internal.hpp"
 #include "qkv_merge.hpp"
 #include "qkv_mfma.hpp"
