@@ -121,6 +121,27 @@ def test_decode_fused_merge_repeats():
     assert not ws.get(1, qd.device)[:256].any(), "tickets not back to zero"
 
 
+def test_decode_fused_merge_mixed_plans_share_a_workspace():
+    """Calls with different split counts, batch sizes and kernels on one
+    workspace: each leaves the ticket area at zero, so every later call is
+    right too."""
+    ws = qkv.Workspace()
+    cases = [("affine", 4, 64, 1, 8, 2, 3000, 128), ("q8_0", 8, 32, 3, 12, 3, 2500, 64),
+             ("affine", 8, 64, 2, 16, 2, 1800, 128)]      # the last one: 16-head kernel
+    prepared = []
+    for mode, bits, gs, B, Hq, Hk, L, D in cases:
+        q, kp, vp, kr, vr = _case("f16", mode, bits, gs, B, Hq, Hk, 1, L, D)
+        ref = oracle_attention(q, "f16", kr, vr, L, mode, bits, gs, 0.2)
+        prepared.append((to_dev(q, "f16"), kp, vp, L, ref))
+    for rep in range(3):
+        for ci, (qd, kp, vp, L, ref) in enumerate(prepared):
+            for splits in (5, 0, 1, 2):
+                out = qkv.qsdpa_decode(qd, kp, vp, L, 0.2, num_splits=splits, workspace=ws)
+                assert_close(out, ref, f"case {ci} splits={splits} rep {rep}")
+    torch.cuda.synchronize()
+    assert not ws.get(1, prepared[0][0].device)[:256].any(), "tickets not back to zero"
+
+
 @pytest.mark.parametrize("mode,bits,vmean,vstd", [
     ("affine", 4, 0.0, 1.0), ("q8_0", 8, 0.0, 1.0),
     ("affine", 4, 3000.0, 600.0),       # 4-bit value scales ~190
