@@ -421,7 +421,17 @@ __global__ __launch_bounds__(NTHR) void attn_matrix_decode(AttnLaunch p) {
     constexpr int QB = 16 * D * 2;
     const auto rq = flat_rsrc((const uint16_t*)p.q + (b * p.Hq + kvh * G) * D, (uint32_t)(G * D * 2));
     u4 qv = {0u, 0u, 0u, 0u};
-    if (1024 * wave < QB) qv = __builtin_amdgcn_raw_buffer_load_b128(rq, 1024 * wave + 16 * lane, 0, 0);
+    if (1024 * wave < QB) {
+        const uint32_t off = 1024 * wave + 16 * lane;
+        if ((reinterpret_cast<uintptr_t>(p.q) & 15) == 0) {   // q only needs 2-byte alignment
+            qv = __builtin_amdgcn_raw_buffer_load_b128(rq, (int)off, 0, 0);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                qv[i] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rq, (int)(off + 4 * i), 0, 0) |
+                        ((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rq, (int)(off + 4 * i + 2), 0, 0) << 16);
+        }
+    }
     // keep the query load ahead of the tile loads (waiting for q must not
     // wait for the tile)
     __builtin_amdgcn_sched_barrier(0);

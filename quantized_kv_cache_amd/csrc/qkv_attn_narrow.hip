@@ -120,6 +120,9 @@ __global__ __launch_bounds__(NTH) void attn_decode_narrow(AttnLaunch p) {
     // the order the codes of that step are unpacked (odd 4-bit nibbles / 16)
     const int qi = lane & 3, qa = lane >> 2;
     const uint16_t* qrow = (const uint16_t*)p.q + (b * p.Hq + kvh * G + min(qi, G - 1)) * D;
+    // every q load below is at a multiple of 16 (8-bit codes: 8) bytes from q
+    const bool q_al16 = (reinterpret_cast<uintptr_t>(p.q) & 15) == 0;
+    const bool q_al8 = (reinterpret_cast<uintptr_t>(p.q) & 7) == 0;
     auto step_d = [](int u, int e) -> int {       // d of half e of step u
         if constexpr (BITS == 4) {
             constexpr int o0[4] = {0, 4, 1, 5}, o1[4] = {2, 6, 3, 7};
@@ -138,10 +141,10 @@ __global__ __launch_bounds__(NTH) void attn_decode_narrow(AttnLaunch p) {
         const int u = 16 * c + qa;
         const int d0 = BITS == 4 ? 8 * (u >> 1) : 4 * u;
         if constexpr (BITS == 4) {
-            const uint4 x = *(const uint4*)(qrow + d0);
+            const uint4 x = load_h8(qrow + d0, q_al16);
             qraw[c][0] = x.x; qraw[c][1] = x.y; qraw[c][2] = x.z; qraw[c][3] = x.w;
         } else {
-            const uint2 x = *(const uint2*)(qrow + d0);
+            const uint2 x = load_h4(qrow + d0, q_al8);
             qraw[c][0] = x.x; qraw[c][1] = x.y;
         }
     }

@@ -54,6 +54,21 @@ __device__ __forceinline__ float load_mask(const void* p, int dt, int64_t i) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// 8 (or 4) consecutive 16-bit values at p, which the API only requires to be
+// 2-byte aligned: one 16-byte (8-byte) load when the caller knows p is that
+// aligned, 16-bit loads otherwise.
+__device__ __forceinline__ uint4 load_h8(const uint16_t* p, bool aligned16) {
+    if (aligned16) return *(const uint4*)p;
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w[i] = (uint32_t)p[2 * i] | ((uint32_t)p[2 * i + 1] << 16);
+    return uint4{w[0], w[1], w[2], w[3]};
+}
+__device__ __forceinline__ uint2 load_h4(const uint16_t* p, bool aligned8) {
+    if (aligned8) return *(const uint2*)p;
+    return uint2{(uint32_t)p[0] | ((uint32_t)p[1] << 16), (uint32_t)p[2] | ((uint32_t)p[3] << 16)};
+}
+
 // Makes x live in SGPRs at this point.  Kernels pin every argument they read
 // at their start, so that all argument loads are issued together and waited
 // for once (a later first read would cost another trip to memory).

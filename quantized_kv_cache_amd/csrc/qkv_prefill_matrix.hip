@@ -163,9 +163,11 @@ __global__ __launch_bounds__(PNTHR) void attn_matrix_prefill(AttnLaunch p) {
     h8 qb[STEPS];
     {
         const _Float16* qrow = (const _Float16*)p.q + ((b * p.Hq + qh) * p.Lq + qi) * D;
+        // the loads are at multiples of 16 bytes from q
+        const bool q_al16 = (reinterpret_cast<uintptr_t>(p.q) & 15) == 0;
 #pragma unroll
         for (int st = 0; st < STEPS; ++st) {
-            const uint4 raw = *(const uint4*)(qrow + 32 * st + 8 * kb);
+            const uint4 raw = load_h8((const uint16_t*)(qrow + 32 * st + 8 * kb), q_al16);
             u4 v = {row_ok ? raw.x : 0u, row_ok ? raw.y : 0u, row_ok ? raw.z : 0u, row_ok ? raw.w : 0u};
             qb[st] = __builtin_bit_cast(h8, v);
         }
@@ -424,11 +426,17 @@ __global__ __launch_bounds__(PNTHR) void attn_matrix_prefill(AttnLaunch p) {
     if (p.S == 1) {
         const float inv = l_run > 0.0f ? 1.0f / l_run : 0.0f;
         _Float16* op = (_Float16*)p.out + ((b * p.Hq + qh) * p.Lq + qi) * D;
+        const bool out_al8 = (reinterpret_cast<uintptr_t>(p.out) & 7) == 0;
 #pragma unroll
         for (int t2 = 0; t2 < NT; ++t2) {
             h4 o4 = {(_Float16)(acc[t2][0] * inv), (_Float16)(acc[t2][1] * inv),
                      (_Float16)(acc[t2][2] * inv), (_Float16)(acc[t2][3] * inv)};
-            *(h4*)(op + 16 * t2 + 4 * kb) = o4;
+            if (out_al8) {                             // out only needs 2-byte alignment
+                *(h4*)(op + 16 * t2 + 4 * kb) = o4;
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) op[16 * t2 + 4 * kb + e] = o4[e];
+            }
         }
         return;
     }

@@ -317,6 +317,38 @@ def test_decode_sixteen_row_formats(case):
         assert_close(out, ref, f"16-row {case} splits={splits}")
 
 
+def _offset_view(t: torch.Tensor) -> torch.Tensor:
+    """A contiguous copy of t whose data starts 2 bytes past a 16-byte
+    boundary (the API only requires element alignment)."""
+    buf = torch.empty(t.numel() + 8, dtype=t.dtype, device=t.device)
+    v = buf[1:1 + t.numel()].view(t.shape)
+    v.copy_(t)
+    assert v.data_ptr() % 16 == 2
+    return v
+
+
+@pytest.mark.parametrize("kind,mode,bits,gs,Hq,Lq,kernel", [
+    ("narrow", "affine", 4, 64, 8, 1, "attn_decode_narrow"),
+    ("narrow8", "affine", 8, 64, 4, 1, "attn_decode_narrow"),
+    ("sixteen_row", "q8_0", 8, 32, 16, 1, "attn_matrix_decode"),
+    ("prefill", "q8_0", 8, 32, 8, 24, "attn_matrix_prefill"),
+])
+def test_matrix_kernels_take_two_byte_aligned_q_and_out(kind, mode, bits, gs, Hq, Lq, kernel):
+    B, Hk, L, D = 1, 2, 900, 128
+    q, kp, vp, kr, vr = _case("f16", mode, bits, gs, B, Hq, Hk, Lq, L, D)
+    causal = kind == "prefill"
+    ref = oracle_attention(q, "f16", kr, vr, L, mode, bits, gs, 0.1, causal=causal)
+    qd = _offset_view(to_dev(q, "f16"))
+    assert qkv.qsdpa_plan(qd, kp, L)["kernel"] == kernel
+    out = _offset_view(torch.zeros_like(qd))
+    for splits in (1, 3):
+        if Lq == 1:
+            qkv.qsdpa_decode(qd, kp, vp, L, 0.1, num_splits=splits, out=out)
+        else:
+            qkv.qsdpa_prefill(qd, kp, vp, L, 0.1, causal=True, num_splits=splits, out=out)
+        assert_close(out, ref, f"{kind} offset q/out splits={splits}")
+
+
 def test_decode_wide_gqa_uses_tiled_kernel():
     """GQA factor 32 (beyond the single-query kernel) with fp16 queries runs
     on the tiled matrix kernel."""
