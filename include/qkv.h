@@ -46,8 +46,9 @@
  *    biases : same as scales (affine only)
  *  where r = b*stride_b + h*stride_h + l*stride_l (strides in ROWS; the
  *  dense layout [B,H,L_cap] is {H*L_cap, L_cap, 1}).
- *  Requirements: codes 16-byte aligned; scales/biases aligned to their
- *  element size; D in {64, 128, 256}; bits in {4, 8} with group_size in
+ *  Requirements: codes 16-byte aligned; scales/biases aligned to one row
+ *  of scales (min(16, (D / group_size) * element size) bytes); D in
+ *  {64, 128, 256}; bits in {4, 8} with group_size in
  *  {32, 64, 128} dividing D (affine), bits 8 and group_size 32 (Q8_0);
  *  affine scale_dtype equal to the dtype of the values it was made from.
  */

@@ -98,9 +98,12 @@ qkv_status check_pack(const qkv_pack* p, const char* name) {
     if (p->D != 64 && p->D != 128 && p->D != 256)
         return fail(QKV_EUNSUPPORTED, "%s: head size D=%lld not in {64, 128, 256}", name, (long long)p->D);
     if (!aligned(p->codes, 16)) return fail(QKV_EINVAL, "%s: codes not 16-byte aligned", name);
+    // scale and bias planes: aligned to one row of them (up to 16 bytes), the
+    // width of the kernels' row loads
     const size_t ss = dtype_size(p->scale_dtype);
-    if (!aligned(p->scales, ss) || (p->biases && !aligned(p->biases, ss)))
-        return fail(QKV_EINVAL, "%s: scales/biases misaligned", name);
+    const size_t ra = std::min<size_t>(16, (size_t)(p->D / p->group_size) * ss);
+    if (!aligned(p->scales, ra) || (p->biases && !aligned(p->biases, ra)))
+        return fail(QKV_EINVAL, "%s: scales/biases misaligned (need %zu-byte alignment)", name, ra);
     return QKV_OK;
 }
 

@@ -53,6 +53,8 @@ def _quant(L, pk, x=FAKE + 0x400000, dt=_lib.QKV_F16, strides=(16384, 8192, 128)
     (dict(D=160, group_size=64), _lib.QKV_EINVAL, "multiple"),
     (dict(codes=FAKE + 4), _lib.QKV_EINVAL, "aligned"),
     (dict(scales=FAKE + 0x100001), _lib.QKV_EINVAL, "misaligned"),
+    (dict(scales=FAKE + 0x100002), _lib.QKV_EINVAL, "misaligned"),     # a scale row is 4 bytes
+    (dict(biases=FAKE + 0x200002), _lib.QKV_EINVAL, "misaligned"),
     (dict(biases=None), _lib.QKV_EINVAL, "biases"),
     (dict(codes=None), _lib.QKV_EINVAL, "null"),
     (dict(mode=_lib.QKV_Q8_0, bits=8, group_size=32), _lib.QKV_EINVAL, "biases"),
