@@ -33,8 +33,8 @@
 //  * K/V stream through raw buffer loads with per-tile resources bounded at
 //    the split's last key (rows past it read as zeros, so no clamping).  Each
 //    wave keeps one tile in registers and issues the next tile's loads as
-//    soon as it has consumed one; tiles after a wave's first come from an
-//    LDS counter, so the waves of a workgroup finish together.
+//    soon as it has consumed one; wave w takes tiles w, w + 8, ... (a fixed
+//    order, so the result is the same on every call).
 //  * The 8 waves' states merge after one barrier; each thread then writes 4
 //    consecutive output d.  With several key splits the workgroup stores
 //    its state at device scope and takes a ticket; the one that takes the
@@ -76,7 +76,6 @@ __global__ __launch_bounds__(NTH) void attn_decode_narrow(AttnLaunch p) {
     constexpr int WAVE_FLOATS = 64 * (D / 4) > NTK * 8 ? 64 * (D / 4) : NTK * 8;
     __shared__ __attribute__((aligned(16))) float s_wave[NW][WAVE_FLOATS];
     __shared__ float s_ml[NW][2][4];
-    __shared__ int s_next;                        // next tile of the split to hand out
     __shared__ bool s_last;                       // this workgroup merges the splits
     __shared__ float s_bias[NW][4][4];
 
@@ -192,8 +191,6 @@ __global__ __launch_bounds__(NTH) void attn_decode_narrow(AttnLaunch p) {
     // the q loads cannot be placed before the tile loads are issued.
     uint32_t after_loads;
     __asm__ __volatile__("s_mov_b32 %0, 0" : "=s"(after_loads) : : "memory");
-    if (tid == 0) s_next = NW;                    // tiles 0 .. NW-1 go to the waves in order
-    __syncthreads();                              // (waits for no global load)
 
     // q banks and the per-(head, group) sums of q (scale log2e applied)
     h4 qb[NBANK];
@@ -411,16 +408,14 @@ __global__ __launch_bounds__(NTH) void attn_decode_narrow(AttnLaunch p) {
     // One register tile per wave: the next tile's loads are issued as soon as
     // a tile is consumed.  Deeper register rings measured slower (with every
     // CU streaming they only lengthen the memory queues; 64K-context 4-bit
-    // decode with this loop: 2 tiles 24.5 us, 1 tile 22.5 us per call).
-    // After its first tile a wave takes the split's next unclaimed tile (an
-    // LDS counter), so waves whose data arrives early take more tiles and the
-    // workgroup's waves finish together.
+    // decode with this loop: 2 tiles 24.5 us, 1 tile 22.5 us per call).  Wave
+    // w takes tiles w, w + NW, ...: with tiles handed out by an LDS counter
+    // the partition (and so the rounding) changed from call to call, for no
+    // measurable gain.
     int tt = wave;
     while (tt < ntiles) {
-        int nxt = 0;
-        if (lane == 0) nxt = atomicAdd(&s_next, 1);
-        process(cur, tt);                         // hides the atomic's latency
-        nxt = __builtin_amdgcn_readfirstlane(nxt);
+        const int nxt = tt + NW;
+        process(cur, tt);
         __builtin_amdgcn_sched_barrier(0);
         // no loads after the last tile: they would hold the wave (and the
         // workgroup merge behind it) until the CU's memory queue drains

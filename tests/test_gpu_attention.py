@@ -121,6 +121,47 @@ def test_decode_fused_merge_repeats():
     assert not ws.get(1, qd.device)[:256].any(), "tickets not back to zero"
 
 
+def test_decode_fused_merge_ignores_stale_states():
+    """Every workgroup of the narrow decode stores its split state and waits
+    for the stores before it takes its ticket, so the merging workgroup reads
+    only states of this call: whatever an earlier call (of any kernel) left in
+    the state area must not reach the result.  The state area is filled with
+    random bytes, then with a dominating state (every float 100, or its
+    complement: an output near 1 if any of it were merged), before calls with
+    32 and 7 splits; then 20 more calls must repeat the first bit for bit (the
+    tiles of a split go to its waves in a fixed order)."""
+    mode, bits, gs, B, Hq, Hk, L, D = "affine", 4, 64, 2, 16, 4, 16384, 128
+    q, kp, vp, kr, vr = _case("f16", mode, bits, gs, B, Hq, Hk, 1, L, D)
+    qd = to_dev(q, "f16")
+    ref = oracle_attention(q, "f16", kr, vr, L, mode, bits, gs, 0.1)
+    ws = qkv.Workspace()
+    need = qkv.qsdpa_plan(qd, kp, L, num_splits=32)["workspace_bytes"]
+    buf = ws.get(need, qd.device)
+    gen = torch.Generator(device=qd.device).manual_seed(7)
+    hundred = np.array([100.0], dtype=np.float32).view(np.uint32)
+    for splits in (32, 7):
+        assert qkv.qsdpa_plan(qd, kp, L, num_splits=splits)["kernel"] == "attn_decode_narrow"
+        first = None
+        for fill in ("random", "dominating", "complement"):
+            area = buf[256:]
+            if fill == "random":
+                area.copy_(torch.randint(0, 256, (area.numel(),), dtype=torch.uint8,
+                                         device=qd.device, generator=gen))
+            else:
+                word = hundred if fill == "dominating" else ~hundred
+                word_bytes = torch.from_numpy(word.view(np.uint8).copy()).to(qd.device)
+                area.view(-1, 4).copy_(word_bytes.expand(area.numel() // 4, 4))
+            out = qkv.qsdpa_decode(qd, kp, vp, L, 0.1, num_splits=splits, workspace=ws)
+            assert_close(out, ref, f"splits={splits} stale {fill}")
+            first = out.clone() if first is None else first
+            assert torch.equal(out, first), f"splits={splits} stale {fill}: result changed"
+        for i in range(20):
+            out = qkv.qsdpa_decode(qd, kp, vp, L, 0.1, num_splits=splits, workspace=ws)
+            assert torch.equal(out, first), f"splits={splits}: call {i} differs from the first"
+    torch.cuda.synchronize()
+    assert not buf[:256].any(), "tickets not back to zero"
+
+
 def test_decode_fused_merge_mixed_plans_share_a_workspace():
     """Calls with different split counts, batch sizes and kernels on one
     workspace: each leaves the ticket area at zero, so every later call is
