@@ -27,6 +27,13 @@ Prints one JSON line:
                  from rocprofv3 counters (profiles/*.counters.txt) while the
                  kernel source is unchanged since they were taken, else null
   cpu_baseline   the CPU oracle timed on a bounded sample of the workload
+  read_ceiling   a plain streaming read (include/qkv_measure.h) in the same job:
+                 of the step's K/V pack bytes, rotating over as many buffers as
+                 there are cache copies, and of one 1 GiB buffer (each the best
+                 of 256 ... 8192 workgroups); step_frac is the attention
+                 kernel's rate over the same-size read's
+  latency_us     single calls, each after a 512 MB write that evicts the
+                 Infinity Cache: p10 / median / p90 over 50 calls
 ``--copy-mib N`` instead runs a plain N MiB device copy ``--steps`` times (the
 known-size kernel the counter readings are scaled by).
 """
@@ -164,6 +171,57 @@ def kernel_pass(torch, run, attn_of, first, steps, stream):
     torch.cuda.synchronize()
     d = [a.elapsed_time(b) for a, b in evs]
     return sum(d) / len(d)
+
+
+def read_ceiling(torch, nbytes, copies, steps, stream):
+    """Time a plain streaming read (include/qkv_measure.h) of nbytes per step,
+    rotating over 'copies' buffers as the benchmark rotates over cache copies,
+    and of one 1 GiB buffer, each with the best of a few workgroup counts.
+    Returns (ms per same-size read, ms per 1 GiB read, their workgroups)."""
+    import ctypes
+    from quantized_kv_cache_amd import _lib
+    lib = _lib.load()
+    n16 = (nbytes + 15) // 16 * 16
+    bufs = [torch.ones(n16, dtype=torch.uint8, device="cuda") for _ in range(copies)]
+    big = torch.ones(2 ** 30, dtype=torch.uint8, device="cuda")
+    sink = torch.empty(4 * 8192, dtype=torch.int32, device="cuda")
+    sp = ctypes.c_void_p(stream.cuda_stream)
+
+    def rd(t, wgs):
+        st = lib.qkv_measure_read(ctypes.c_void_p(t.data_ptr()), t.numel(), wgs,
+                                  ctypes.c_void_p(sink.data_ptr()), sp)
+        if st != _lib.QKV_OK:
+            raise RuntimeError(lib.qkv_last_error().decode())
+
+    def best(run_one, n, reps):
+        res = []
+        for wgs in (256, 512, 1024, 2048, 4096, 8192):
+            for i in range(n):
+                run_one(i, wgs)
+            res.append((time_region(torch, lambda i: run_one(i, wgs), 0, reps, stream), wgs))
+        return min(res)
+    ms, wg = best(lambda i, g: rd(bufs[i % copies], g), 2 * copies, steps)
+    ms_big, wg_big = best(lambda i, g: rd(big, g), 3, 20)
+    del bufs, big
+    return ms, ms_big, wg, wg_big
+
+
+def call_latency(torch, run, first, n, stream):
+    """n single steps, each after a 512 MB write (evicts the Infinity Cache),
+    bracketed by their own events: p10, median and p90 in microseconds."""
+    scrub = torch.empty(512 * 2 ** 20, dtype=torch.uint8, device="cuda")
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(n)]
+    for k in range(n):
+        scrub.fill_(k & 255)
+        a, b = evs[k]
+        a.record(stream)
+        run(first + k)
+        b.record(stream)
+    torch.cuda.synchronize()
+    us = sorted(a.elapsed_time(b) * 1e3 for a, b in evs)
+    return {"p10": round(us[n // 10], 2), "median": round(us[n // 2], 2),
+            "p90": round(us[(9 * n) // 10], 2), "calls": n, "scrub_mib": 512}
 
 
 def cpu_baseline(w, inp, budget_s):
@@ -341,6 +399,15 @@ def main():
                            "unit": "TFLOP/s", "frac": round(tf / MFMA_F16_PEAK_TFLOPS, 4),
                            "traffic": traffic, "kernel": kernel,
                            "kernel_us": round(kms * 1e3, 3), "algorithmic_flops": flops}
+    rd_ms, big_ms, rd_wg, big_wg = read_ceiling(torch, pack_bytes(w, w.L), R, args.steps, stream)
+    rd_gbs = pack_bytes(w, w.L) / (rd_ms * 1e-3) / 1e9
+    rec["read_ceiling"] = {"step_bytes_GBps": round(rd_gbs, 1),
+                           "GiB_GBps": round(2 ** 30 / (big_ms * 1e-3) / 1e9, 1),
+                           "step_bytes": pack_bytes(w, w.L), "step_us": round(rd_ms * 1e3, 3),
+                           "workgroups": [rd_wg, big_wg]}
+    if w.Lq == 1:
+        rec["read_ceiling"]["step_frac"] = round(rec["roofline"]["achieved"] / rd_gbs, 4)
+    rec["latency_us"] = call_latency(torch, run, 2 * (args.warmup + args.steps), 50, stream)
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_seconds)
     print(json.dumps(rec), flush=True)

@@ -1,4 +1,4 @@
-"""ctypes declarations of libqkv.so's C ABI (include/qkv.h)."""
+"""ctypes declarations of libqkv.so's C ABI (include/qkv.h, include/qkv_measure.h)."""
 from __future__ import annotations
 
 import ctypes
@@ -18,7 +18,8 @@ QKV_KERNEL_GENERIC, QKV_KERNEL_DECODE, QKV_KERNEL_DECODE_NARROW, QKV_KERNEL_PREF
 
 # every symbol include/qkv.h declares
 EXPORTS = ["qkv_quantize", "qkv_update_append", "qsdpa_workspace_bytes", "qsdpa_plan",
-           "qsdpa_decode", "qsdpa_prefill", "qkv_last_error", "qkv_abi_version"]
+           "qsdpa_decode", "qsdpa_prefill", "qkv_last_error", "qkv_abi_version",
+           "qkv_measure_read"]
 
 
 class QkvPack(ctypes.Structure):
@@ -83,6 +84,8 @@ def load():
     L.qkv_last_error.restype = ctypes.c_char_p
     L.qkv_abi_version.argtypes = []
     L.qkv_abi_version.restype = I32
+    L.qkv_measure_read.argtypes = [P, SZ, I32, P, P]      # include/qkv_measure.h
+    L.qkv_measure_read.restype = I32
     _lib = L
     return L
 

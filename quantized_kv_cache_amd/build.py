@@ -17,7 +17,7 @@ LIB = os.path.join(HERE, "libqkv.so")
 ROOT = os.path.dirname(HERE)
 
 SOURCES = ["qkv_api.cpp", "qkv_quantize.hip", "qkv_attn_generic.hip", "qkv_attn_matrix.hip",
-           "qkv_attn_narrow.hip", "qkv_prefill_matrix.hip", "qkv_merge.hip"]
+           "qkv_attn_narrow.hip", "qkv_prefill_matrix.hip", "qkv_merge.hip", "qkv_measure.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

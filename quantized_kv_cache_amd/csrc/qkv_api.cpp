@@ -11,6 +11,7 @@
 #include <string>
 
 #include "../../include/qkv.h"
+#include "../../include/qkv_measure.h"
 #include "qkv_internal.hpp"
 #include "qkv_merge.hpp"
 
@@ -421,6 +422,18 @@ qkv_status qsdpa_prefill(const void* q, int32_t q_dtype, int64_t B, int64_t Hq, 
                          size_t workspace_bytes, const qkv_attn_opts* opts, void* stream) {
     return attention("qsdpa_prefill", q, q_dtype, B, Hq, Lq, D, k, v, L, scale, mask_kind, mask,
                      mask_dtype, mask_strides, out, workspace, workspace_bytes, opts, stream);
+}
+
+qkv_status qkv_measure_read(const void* buf, size_t bytes, int32_t workgroups, uint32_t* sink,
+                            void* stream) {
+    if (!buf || !sink) return fail(QKV_EINVAL, "qkv_measure_read: null pointer");
+    if (bytes == 0 || bytes % 16 || !aligned(buf, 16))
+        return fail(QKV_EINVAL, "qkv_measure_read: bytes must be a nonzero multiple of 16 at a 16-byte aligned address");
+    if (workgroups < 1 || workgroups > QKV_MEASURE_MAX_WORKGROUPS)
+        return fail(QKV_EINVAL, "qkv_measure_read: workgroups=%d outside [1, %d]", workgroups,
+                    QKV_MEASURE_MAX_WORKGROUPS);
+    return hip_status(qkv::launch_measure_read(buf, bytes, workgroups, sink, static_cast<hipStream_t>(stream)),
+                      "qkv_measure_read");
 }
 
 const char* qkv_last_error(void) { return g_last_error.c_str(); }

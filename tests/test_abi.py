@@ -1,7 +1,8 @@
 """The C ABI on the host: the library loads, exports every function that
-include/qkv.h declares, and rejects bad arguments before any HIP call (these
+include/*.h declares, and rejects bad arguments before any HIP call (these
 checks run without a GPU; no call here reaches a kernel launch)."""
 import ctypes
+import glob
 import os
 import re
 
@@ -14,9 +15,11 @@ FAKE = 0x10000000        # aligned, never dereferenced: validation fails first
 
 
 def header_functions():
-    src = open(os.path.join(ROOT, "include", "qkv.h")).read()
-    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\**(\w+)\s*\(", src, flags=re.M)))
+    names = set()
+    for h in sorted(glob.glob(os.path.join(ROOT, "include", "*.h"))):
+        src = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\**(\w+)\s*\(", src, flags=re.M))
+    return sorted(names)
 
 
 @pytest.fixture(scope="module")
@@ -181,3 +184,12 @@ def test_prefill_row_tile(L, Lq, rows):
     assert L.qsdpa_plan(1, 32, Lq, 128, 4096, ctypes.byref(kp), _lib.QKV_F16, None,
                         ctypes.byref(pl)) == 0
     assert pl.kernel == _lib.QKV_KERNEL_PREFILL and pl.row_tile == rows
+
+
+def test_measure_read_rejects_bad_arguments(L):
+    sink = FAKE + 0x400000
+    for buf, nbytes, wgs, snk in ((0, 4096, 64, sink), (FAKE, 4096, 64, 0), (FAKE, 0, 64, sink),
+                                  (FAKE, 4100, 64, sink), (FAKE + 8, 4096, 64, sink),
+                                  (FAKE, 4096, 0, sink), (FAKE, 4096, 8193, sink)):
+        assert L.qkv_measure_read(buf, nbytes, wgs, snk, None) == _lib.QKV_EINVAL, (buf, nbytes, wgs)
+        assert L.qkv_last_error()
