@@ -13,6 +13,12 @@
 #include "../../include/qkv.h"
 #include "../../include/qkv_measure.h"
 #include "qkv_internal.hpp"
+
+namespace qkv {
+// Plain streaming read of a device buffer (qkv_measure.hip).
+hipError_t launch_measure_read(const void* buf, size_t bytes, int workgroups, uint32_t* sink,
+                               hipStream_t stream);
+}  // namespace qkv
 #include "qkv_merge.hpp"
 
 namespace {

@@ -97,8 +97,4 @@ int narrow_decode_key_quantum();
 hipError_t launch_attn_narrow(int mode, int bits, int D, int64_t B, const AttnLaunch& p,
                               hipStream_t stream);
 
-// Plain streaming read (measurement helper).
-hipError_t launch_measure_read(const void* buf, size_t bytes, int workgroups, uint32_t* sink,
-                               hipStream_t stream);
-
 }  // namespace qkv
