@@ -209,9 +209,9 @@ Plan make_plan(int64_t B, int64_t Hq, int64_t Lq, int64_t D, int64_t L, const qk
         const int64_t wgs = B * Hk * ((n_rows + pl.wg_rows - 1) / pl.wg_rows);
         S = auto_splits(wgs, L, 1024, 256);
     } else {
-        // the generic kernel walks a split serially in 32-key blocks (two
-        // memory round trips each), so even single-block splits pay off for
-        // small caches (256 keys: 11.2 us with 8 splits, 16.0 us with 4)
+        // the generic kernel walks a split serially in 32-key blocks (one
+        // memory round trip each), so even single-block splits pay off for
+        // small caches (256 keys: 10.5 us with 8 splits, 12.9 us with 4)
         S = pl.matrix ? auto_splits(B * Hk * pl.n_rt, L, 256, 256)
                       : auto_splits(B * Hk * pl.n_rt, L, 32, 512);
     }

@@ -16,7 +16,11 @@
 // the llama.cpp page "Metal: Optimize q8_0 KV - #25556" does for two heads)
 // and, for prefill, among neighbouring queries.  Keys are consumed in blocks
 // of 32: scores (8 lanes per key, butterfly sum), an online-softmax update per
-// row, the V block dequantized once into LDS, then o = o*alpha + P V.
+// row, the V block dequantized once into LDS, then o = o*alpha + P V.  Thread
+// t holds the packed K and V words of key t / 8, d slice t % 8 of a block
+// (one quantization group) in registers; the next block's words are requested
+// before the current block is processed, so a block costs one memory round
+// trip at most (the first block's loads overlap the query loads).
 // With several splits each workgroup writes its (m, l, o) state to the
 // workspace and the split merge kernel combines them with the log-sum-exp
 // rule and writes the output.  This kernel favours generality over
@@ -32,22 +36,24 @@ namespace {
 constexpr int KB = 32;      // keys per block
 constexpr int RTG = 16;     // rows per tile
 
-// Dequantize element d of a cache row (row index r in the pack).
-template <int MODE, int BITS, int ST>
-__device__ __forceinline__ float dequant_elem(const uint8_t* codes, const void* scales,
-                                              const void* biases, int64_t r, int d, int D,
-                                              int gs_log2) {
-    const int NG = D >> gs_log2;
-    const int g = d >> gs_log2;
+// The packed words of one d slice (DPK = D / 8 consecutive d, inside one
+// quantization group) of one K row and one V row, with their scale / bias.
+template <int MODE, int BITS, int D>
+struct RawSlice {
+    static constexpr int DPK = D / 8;
+    static constexpr int W = DPK * BITS / 32 > 0 ? DPK * BITS / 32 : 1;
+    uint32_t k[W], v[W];
+    float ks, kb, vs, vb;
+};
+
+// Element e of a slice, dequantized in fp32: affine s c + b, Q8_0 d c.
+template <int MODE, int BITS>
+__device__ __forceinline__ float slice_elem(const uint32_t* w, float s, float b, int e) {
     if constexpr (MODE == MODE_Q8_0) {
-        const int8_t c = ((const int8_t*)codes)[r * D + d];
-        return f16_to_f32(((const uint16_t*)scales)[r * NG + g]) * (float)c;
+        const int8_t c = (int8_t)((w[e >> 2] >> (8 * (e & 3))) & 0xFFu);
+        return s * (float)c;
     } else {
-        const uint32_t* w = (const uint32_t*)(codes + r * (int64_t)(D * BITS / 8));
-        constexpr int PER = 32 / BITS;
-        const uint32_t c = (w[d / PER] >> ((d % PER) * BITS)) & ((1u << BITS) - 1u);
-        const float s = load_as_f32<ST>(scales, r * NG + g);
-        const float b = load_as_f32<ST>(biases, r * NG + g);
+        const uint32_t c = (w[(e * BITS) >> 5] >> ((e * BITS) & 31)) & ((1u << BITS) - 1u);
         return s * (float)c + b;
     }
 }
@@ -71,19 +77,6 @@ __global__ __launch_bounds__(256) void attn_generic_kernel(AttnLaunch p) {
     const int r0 = rt * RTG;
     const int nr = min(RTG, p.n_rows - r0);
 
-    // queries of the tile, pre-multiplied by the softmax scale (fp32)
-    for (int idx = tid; idx < RTG * D; idx += 256) {
-        const int r = idx / D, d = idx % D;
-        float val = 0.0f;
-        if (r < nr) {
-            const int pr = r0 + r;
-            const int64_t i = pr / p.G, h = kvh * p.G + pr % p.G;
-            val = load_as_f32<QT>(p.q, ((b * p.Hq + h) * p.Lq + i) * D + d) * p.scale;
-        }
-        qs[r][d] = val;
-    }
-    if (tid < RTG) { m_s[tid] = -INFINITY; l_s[tid] = 0.0f; }
-
     // key range of this split, cut at the last key any row of the tile sees
     int64_t j_begin = (int64_t)split * p.chunk;
     int64_t j_end = min(p.L, j_begin + p.chunk);
@@ -97,6 +90,48 @@ __global__ __launch_bounds__(256) void attn_generic_kernel(AttnLaunch p) {
     const uint8_t* kc = (const uint8_t*)p.k.codes;
     const uint8_t* vc = (const uint8_t*)p.v.codes;
 
+    // this thread's key of a block and d slice (one quantization group)
+    using Raw = RawSlice<MODE, BITS, D>;
+    constexpr int ROWB = D * BITS / 8;
+    const int kk = tid / 8, part = tid % 8;
+    const int NGr = D >> p.gs_log2;
+    const int gsl = (part * Raw::DPK) >> p.gs_log2;
+    // rows past the range load the range's last row (never used: their scores
+    // are -inf and their V entries 0), so the loads need no branch
+    const int64_t j_last = max(j_end - 1, (int64_t)0);
+    auto load_raw = [&](int64_t jb, Raw& R) {
+        const int64_t j = min(jb + kk, j_last);
+        const int64_t kr = krow0 + j * p.k.sl, vr = vrow0 + j * p.v.sl;
+        const uint32_t* kw = (const uint32_t*)(kc + kr * ROWB) + part * Raw::W;
+        const uint32_t* vw = (const uint32_t*)(vc + vr * ROWB) + part * Raw::W;
+#pragma unroll
+        for (int w = 0; w < Raw::W; ++w) { R.k[w] = kw[w]; R.v[w] = vw[w]; }
+        R.ks = load_as_f32<ST>(p.k.scales, kr * NGr + gsl);
+        R.vs = load_as_f32<ST>(p.v.scales, vr * NGr + gsl);
+        if constexpr (MODE == MODE_Q8_0) {
+            R.kb = R.vb = 0.0f;
+        } else {
+            R.kb = load_as_f32<ST>(p.k.biases, kr * NGr + gsl);
+            R.vb = load_as_f32<ST>(p.v.biases, vr * NGr + gsl);
+        }
+    };
+    Raw cur, nxt;
+    load_raw(j_begin, cur);
+
+    // queries of the tile, pre-multiplied by the softmax scale (fp32); rows
+    // past the tile's last read row 0 and store zeros, so every load is
+    // issued before the first wait
+#pragma unroll
+    for (int it = 0; it < RTG * D / 256; ++it) {
+        const int idx = tid + 256 * it;
+        const int r = idx / D, d = idx % D;
+        const int pr = r0 + (r < nr ? r : 0);
+        const int64_t i = pr / p.G, h = kvh * p.G + pr % p.G;
+        const float x = load_as_f32<QT>(p.q, ((b * p.Hq + h) * p.Lq + i) * D + d);
+        qs[r][d] = r < nr ? x * p.scale : 0.0f;
+    }
+    if (tid < RTG) { m_s[tid] = -INFINITY; l_s[tid] = 0.0f; }
+
     const int orow = tid / 16, ochunk = tid % 16;
     float o[DPO];
 #pragma unroll
@@ -104,21 +139,19 @@ __global__ __launch_bounds__(256) void attn_generic_kernel(AttnLaunch p) {
     __syncthreads();
 
     for (int64_t jb = j_begin; jb < j_end; jb += KB) {
+        if (jb + KB < j_end) load_raw(jb + KB, nxt);
         // ---- scores: 8 lanes per key
         {
-            const int kk = tid / 8, part = tid % 8;
             const int64_t j = jb + kk;
             const bool valid = j < j_end;
             float acc[RTG];
 #pragma unroll
             for (int r = 0; r < RTG; ++r) acc[r] = 0.0f;
             if (valid) {
-                const int64_t kr = krow0 + j * p.k.sl;
-#pragma unroll 4
+#pragma unroll
                 for (int e = 0; e < DPK; ++e) {
                     const int d = part * DPK + e;
-                    const float kv = dequant_elem<MODE, BITS, ST>(kc, p.k.scales, p.k.biases, kr,
-                                                                  d, D, p.gs_log2);
+                    const float kv = slice_elem<MODE, BITS>(cur.k, cur.ks, cur.kb, e);
 #pragma unroll
                     for (int r = 0; r < RTG; ++r) acc[r] += qs[r][d] * kv;
                 }
@@ -175,28 +208,24 @@ __global__ __launch_bounds__(256) void attn_generic_kernel(AttnLaunch p) {
                 a_s[r] = alpha;
             }
         }
-        // ---- V block -> LDS (fp32)
-        for (int idx = tid; idx < KB * D; idx += 256) {
-            const int kk = idx / D, d = idx % D;
-            const int64_t j = jb + kk;
-            vt[kk][d] = (j < j_end) ? dequant_elem<MODE, BITS, ST>(vc, p.v.scales, p.v.biases,
-                                                                   vrow0 + j * p.v.sl, d, D,
-                                                                   p.gs_log2)
-                                    : 0.0f;
-        }
+        // ---- V block -> LDS (fp32; keys past the range hold zeros)
+#pragma unroll
+        for (int e = 0; e < DPK; ++e)
+            vt[kk][part * DPK + e] = (jb + kk < j_end) ? slice_elem<MODE, BITS>(cur.v, cur.vs, cur.vb, e) : 0.0f;
         __syncthreads();
         // ---- o = o * alpha + P V
         {
             const float alpha = a_s[orow];
 #pragma unroll
             for (int i = 0; i < DPO; ++i) o[i] *= alpha;
-            for (int kk = 0; kk < KB; ++kk) {
-                const float pk = sc[orow][kk];
+            for (int key = 0; key < KB; ++key) {
+                const float pk = sc[orow][key];
 #pragma unroll
-                for (int i = 0; i < DPO; ++i) o[i] += pk * vt[kk][ochunk * DPO + i];
+                for (int i = 0; i < DPO; ++i) o[i] += pk * vt[key][ochunk * DPO + i];
             }
         }
         __syncthreads();
+        cur = nxt;
     }
 
     const bool row_ok = orow < nr;
