@@ -34,6 +34,7 @@ Prints one JSON line:
                  kernel's rate over the same-size read's
   latency_us     single calls, each after a 512 MB write that evicts the
                  Infinity Cache: p10 / median / p90 over 50 calls
+                 (``--no-extras`` skips these two, for profiled runs)
 ``--copy-mib N`` instead runs a plain N MiB device copy ``--steps`` times (the
 known-size kernel the counter readings are scaled by).
 """
@@ -115,6 +116,9 @@ def parse():
     ap.add_argument("--splits", type=int, default=0)
     ap.add_argument("--copies", type=int, default=0, help="cache copies (0 = enough for 512 MB)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip read_ceiling and latency_us (profiled runs: only the timed steps "
+                         "and the kernel pass launch the attention kernel)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-mib", type=int, default=0)
     return ap.parse_args()
@@ -399,15 +403,16 @@ def main():
                            "unit": "TFLOP/s", "frac": round(tf / MFMA_F16_PEAK_TFLOPS, 4),
                            "traffic": traffic, "kernel": kernel,
                            "kernel_us": round(kms * 1e3, 3), "algorithmic_flops": flops}
-    rd_ms, big_ms, rd_wg, big_wg = read_ceiling(torch, pack_bytes(w, w.L), R, args.steps, stream)
-    rd_gbs = pack_bytes(w, w.L) / (rd_ms * 1e-3) / 1e9
-    rec["read_ceiling"] = {"step_bytes_GBps": round(rd_gbs, 1),
-                           "GiB_GBps": round(2 ** 30 / (big_ms * 1e-3) / 1e9, 1),
-                           "step_bytes": pack_bytes(w, w.L), "step_us": round(rd_ms * 1e3, 3),
-                           "workgroups": [rd_wg, big_wg]}
-    if w.Lq == 1:
-        rec["read_ceiling"]["step_frac"] = round(rec["roofline"]["achieved"] / rd_gbs, 4)
-    rec["latency_us"] = call_latency(torch, run, 2 * (args.warmup + args.steps), 50, stream)
+    if not args.no_extras:
+        rd_ms, big_ms, rd_wg, big_wg = read_ceiling(torch, pack_bytes(w, w.L), R, args.steps, stream)
+        rd_gbs = pack_bytes(w, w.L) / (rd_ms * 1e-3) / 1e9
+        rec["read_ceiling"] = {"step_bytes_GBps": round(rd_gbs, 1),
+                               "GiB_GBps": round(2 ** 30 / (big_ms * 1e-3) / 1e9, 1),
+                               "step_bytes": pack_bytes(w, w.L), "step_us": round(rd_ms * 1e3, 3),
+                               "workgroups": [rd_wg, big_wg]}
+        if w.Lq == 1:
+            rec["read_ceiling"]["step_frac"] = round(rec["roofline"]["achieved"] / rd_gbs, 4)
+        rec["latency_us"] = call_latency(torch, run, 2 * (args.warmup + args.steps), 50, stream)
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_seconds)
     print(json.dumps(rec), flush=True)
