@@ -2,7 +2,7 @@
  * path).
  *
  * The decode streams its packed K/V cache from HBM once per call, so its
- * speed is judged against what a plain streaming read achieves on the same
+ * speed is compared with what a plain streaming read achieves on the same
  * machine with the same byte count.  This entry point provides that read.
  */
 #ifndef QKV_MEASURE_H

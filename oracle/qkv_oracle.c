@@ -19,7 +19,7 @@
  *   [LLAMA]    llama.cpp PR page "Metal: Optimize q8_0 KV - #25556"
  *              (Q8_0 KV blocks: 32 signed int8 codes, one fp16 scale)
  *
- * Readings taken where the pages are silent (each is listed in the design doc):
+ * Readings taken where the pages are silent:
  *   - codes are rounded half-to-even from the STORED (dtype-rounded) scale
  *     and bias, with IEEE fp32 subtract and divide, no fused multiply-add;
  *   - the scale is floored at eps = T(1e-7) before it is stored;
