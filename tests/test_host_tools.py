@@ -25,3 +25,19 @@ def test_every_profiled_kernel_has_sources_and_a_stable_hash():
     for k in P.KERNEL_SOURCES:
         h = P.kernel_hash(k)
         assert len(h) == 16 and h == P.kernel_hash(k)
+
+
+def test_stored_counters_match_the_current_kernels():
+    """Every HBM-counter summary in profiles/ was taken on the kernel sources
+    as they are now (the benchmark reports its traffic only then)."""
+    import glob
+    import os
+    import re
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    files = sorted(glob.glob(os.path.join(root, "profiles", "*.counters.txt")))
+    assert files
+    for f in files:
+        txt = open(f).read()
+        kernel = re.search(r"^kernel = (\w+)$", txt, flags=re.M).group(1)
+        stored = re.search(r"^kernel_source_hash = (\w+)$", txt, flags=re.M).group(1)
+        assert stored == P.kernel_hash(kernel), os.path.basename(f)
