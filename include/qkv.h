@@ -108,6 +108,15 @@ typedef struct {
 /* Quantize x[B,H,L,D] (element strides x_strides = {b, h, l}; D contiguous,
  * strides multiples of 8, x 16-byte aligned) into rows [0, L) of dst, whose
  * B, H, D must match.  x_dtype must equal dst->scale_dtype for AFFINE.
+ * The operation is the group-wise affine quantize of the MLX page "add
+ * fast::quantized_kv_update" (kernels/quantized.h affine_quantize: per group,
+ * scale (max - min) / (2^bits - 1) floored at T(1e-7), bias = min, codes
+ * packed as sdpa_vector.h load_keys reads them) and of the MLX CUDA page
+ * "Fixed mma and working dequant" (quantized.cu affine_quantize), or the Q8_0
+ * block of the llama.cpp page "Metal: Optimize q8_0 KV - #25556" (32 signed
+ * int8 codes with one fp16 scale); the exact arithmetic is stated under
+ * "Cache format" above.  L = 0 enqueues nothing.  dst rows >= L are not
+ * touched.
  * Errors: EINVAL (null pointers, L > L_cap, misalignment, shape mismatch),
  * EUNSUPPORTED (format outside the instantiated set). */
 qkv_status qkv_quantize(const void* x, int32_t x_dtype, const int64_t x_strides[3], int64_t L,
@@ -182,11 +191,23 @@ qkv_status qsdpa_decode(const void* q, int32_t q_dtype, int64_t B, int64_t Hq, i
                         void* out, void* workspace, size_t workspace_bytes,
                         const qkv_attn_opts* opts, void* stream);
 
-/* Prefill: q, out [B,Hq,Lq,D] contiguous; keys [0, L).  QKV_MASK_CAUSAL hides
- * key j from query i when j > L - Lq + i (the queries are the last Lq
- * positions); QKV_MASK_ADDITIVE adds mask element (b,h,i,j) at
- * b*ms[0]+h*ms[1]+i*ms[2]+j*ms[3].  Lq = 1 gives the same result as
- * qsdpa_decode.  Errors as qsdpa_decode, plus EINVAL when causal and L < Lq. */
+/* Prefill: q, out [B,Hq,Lq,D] contiguous; keys [0, L).
+ *   out[b,h,i] = softmax_j(scale * q[b,h,i] . K[b,h/(Hq/Hk),j] + m_ij) V
+ * for every query row i < Lq: the composition that the MLX page "add
+ * fast::quantized_kv_update" gives for more than one query per head
+ * (mlx/fast.cpp quantized_scaled_dot_product_attention, fallback:
+ * quantized_matmul(q, K^T), plus the additive mask, softmax over the keys,
+ * quantized_matmul with V, query heads grouped onto kv heads by a reshape),
+ * with the scale applied in fp32 as in its fused kernel; and the prompt
+ * processing over a Q8_0 cache of the llama.cpp page "Metal: Optimize q8_0
+ * KV - #25556" (512-query prompt batches at 10K and 20K cache depth, the new
+ * tokens being the last positions of the cache).  m_ij: QKV_MASK_NONE 0;
+ * QKV_MASK_CAUSAL -inf when j > L - Lq + i (the queries are the last Lq
+ * positions, bottom-right aligned); QKV_MASK_ADDITIVE mask element (b,h,i,j)
+ * at b*ms[0]+h*ms[1]+i*ms[2]+j*ms[3] of mask_dtype.  A row with no visible
+ * key produces zeros.  Lq = 1 gives the same result as qsdpa_decode.  out
+ * must not overlap q, the packs or the workspace.  Errors as qsdpa_decode,
+ * plus EINVAL when causal and L < Lq. */
 qkv_status qsdpa_prefill(const void* q, int32_t q_dtype, int64_t B, int64_t Hq, int64_t Lq,
                          int64_t D, const qkv_pack* k, const qkv_pack* v, int64_t L, float scale,
                          int32_t mask_kind, const void* mask, int32_t mask_dtype,

@@ -83,12 +83,23 @@ def oracle_attention(q: np.ndarray, qdt: str, kp: dict, vp: dict, L: int, mode: 
     return orc.attention(orc.to_f32(q, qdt), kh, vh, scale, mask=mask, causal=causal)
 
 
-def assert_close(gpu: torch.Tensor, ref: np.ndarray, what: str = ""):
+def err_over_tol(gpu, ref: np.ndarray) -> float:
+    """max |gpu - ref| / (ATOL + RTOL |ref|): below 1 passes, and how far
+    below is the precision headroom."""
+    g = gpu.detach().float().cpu().numpy().astype(np.float64) if isinstance(gpu, torch.Tensor) \
+        else np.asarray(gpu, np.float64)
+    return float(np.max(np.abs(g - ref) / (ATOL + RTOL * np.abs(ref))))
+
+
+def assert_close(gpu: torch.Tensor, ref: np.ndarray, what: str = "", report: bool = False):
     g = gpu.detach().float().cpu().numpy().astype(np.float64)
     assert g.shape == ref.shape, (g.shape, ref.shape)
     assert np.all(np.isfinite(g)), f"{what}: non-finite output"
     err = np.abs(g - ref)
     tol = ATOL + RTOL * np.abs(ref)
+    if report:
+        print(f"[headroom] {what}: max err/tol = {float(np.max(err / tol)):.4f}, "
+              f"max err = {float(err.max()):.3e}, output std = {float(ref.std()):.3e}", flush=True)
     if not np.all(err <= tol):
         i = np.unravel_index(np.argmax(err - tol), err.shape)
         raise AssertionError(f"{what}: {int((err > tol).sum())} of {err.size} outside tolerance; "
@@ -100,5 +111,6 @@ def scale_dtype_of(mode: str, dtype: str) -> str:
 
 
 __all__ = ["ATOL", "RTOL", "TORCH_DT", "to_dev", "from_dev", "pack_numpy", "oracle_pack",
-           "assert_pack_equal", "dequant", "oracle_attention", "assert_close", "scale_dtype_of",
+           "assert_pack_equal", "dequant", "oracle_attention", "assert_close", "err_over_tol",
+           "scale_dtype_of",
            "W", "orc"]

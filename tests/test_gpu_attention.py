@@ -1,6 +1,8 @@
 """GPU parity of qsdpa_decode / qsdpa_prefill against the oracle on the same
 seeded inputs: |gpu - ref| <= 2e-3 + 1e-2 |ref| element-wise, where ref is
 the oracle's fp64 attention over its own dequantized packs."""
+import dataclasses
+import math
 import zlib
 
 import numpy as np
@@ -8,8 +10,8 @@ import pytest
 import torch
 
 import quantized_kv_cache_amd as qkv
-from tests._cases import (W, assert_close, assert_pack_equal, oracle_attention, oracle_pack,
-                          orc, pack_numpy, to_dev)
+from tests._cases import (W, assert_close, assert_pack_equal, err_over_tol, oracle_attention,
+                          oracle_pack, orc, pack_numpy, to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -430,19 +432,51 @@ def _workload_packs(w, L=None):
     return inp, kp, vp, kr, vr
 
 
-@pytest.mark.parametrize("name", ["tiny_decode", "decode_64k_4bit_gqa4", "q8_0_decode_gqa16"])
+# The timed 64K 4-bit workload draws U[0,1) inputs with scale 1, so its
+# outputs all sit near 0.5 with a spread below the tolerance: its own check
+# cannot see a lost key split.  The same shape, format, kernel and plan with
+# N(0,1) inputs and scale 1/sqrt(128) can: the test below also shows, with the
+# oracle alone, that hiding the 2048 keys of one split moves the output
+# outside the tolerance.
+C2_NORMAL = dataclasses.replace(W.WORKLOADS["decode_64k_4bit_gqa4"],
+                                name="decode_64k_4bit_gqa4_normal", dist="normal",
+                                scale=1.0 / math.sqrt(128.0), seed=33)
+
+
+@pytest.mark.parametrize("name", ["tiny_decode", "decode_64k_4bit_gqa4", "q8_0_decode_gqa16",
+                                  "decode_64k_4bit_gqa4_normal"])
 def test_decode_workload_full(name):
-    w = W.WORKLOADS[name]
+    w = C2_NORMAL if name == C2_NORMAL.name else W.WORKLOADS[name]
     print(f"[decode] {name}", flush=True)
     inp, kp, vp, kr, vr = _workload_packs(w)
-    out = qkv.qsdpa_decode(to_dev(inp["q"], w.dtype), kp, vp, w.L, w.scale)
+    qd = to_dev(inp["q"], w.dtype)
+    if w is C2_NORMAL:
+        timed = W.WORKLOADS["decode_64k_4bit_gqa4"]
+        assert qkv.qsdpa_plan(qd, kp, w.L) == qkv.qsdpa_plan(
+            to_dev(W.make_inputs(timed, L=1)["q"], timed.dtype), kp, timed.L)
+    out = qkv.qsdpa_decode(qd, kp, vp, w.L, w.scale)
     ref = oracle_attention(inp["q"], w.dtype, kr, vr, w.L, w.mode, w.bits, w.group_size, w.scale)
-    assert_close(out, ref, name)
+    assert_close(out, ref, name, report=True)
+    if w is C2_NORMAL or name == "decode_64k_4bit_gqa4":
+        # the check's power: the oracle with one split's keys hidden
+        chunk = qkv.qsdpa_plan(qd, kp, w.L)["keys_per_split"]
+        assert chunk == 2048
+        for split in (0, 13, 31):
+            mask = np.zeros((1, 1, 1, w.L), np.float32)
+            mask[..., split * chunk:(split + 1) * chunk] = -np.inf
+            dropped = oracle_attention(inp["q"], w.dtype, kr, vr, w.L, w.mode, w.bits,
+                                       w.group_size, w.scale, mask=mask)
+            r = err_over_tol(dropped, ref)
+            print(f"[sensitivity] {name}: split {split} hidden -> max err/tol {r:.2f}", flush=True)
+            if w is C2_NORMAL:
+                assert r > 2.0, "this check would not see a dropped split"
 
 
 def test_append_decode_workload_steps():
-    """The batched append+decode workload at full size for its first and a
-    later step (B=8, Hq=32, Hk=8, D=128, cache 16384 + t, 8-bit)."""
+    """The batched append+decode workload at full size, all 64 steps (B=8,
+    Hq=32, Hk=8, D=128, cache 16384 + t, 8-bit): every appended row is
+    bit-exact, and the attention is checked at the first steps and at the
+    last one, which fills the cache to its capacity (row 16447)."""
     w = W.WORKLOADS["append_decode_b8_8bit"]
     print("[append+decode] full size", flush=True)
     inp = W.make_inputs(w)
@@ -451,39 +485,49 @@ def test_append_decode_workload_steps():
     vp = qkv.empty_pack(w.B, w.Hk, w.cap, w.D, w.mode, w.bits, w.group_size, torch.float16)
     qkv.qkv_quantize(to_dev(inp["k"], "f16"), out=kp)
     qkv.qkv_quantize(to_dev(inp["v"], "f16"), out=vp)
-    kr = oracle_pack(inp["k"], "f16", w.mode, w.bits, w.group_size)
-    vr = oracle_pack(inp["v"], "f16", w.mode, w.bits, w.group_size)
-    for t in range(3):
+    refs = []
+    for src in ("k", "v"):
+        pk = oracle_pack(inp[src], "f16", w.mode, w.bits, w.group_size)
+        full = {n: np.zeros(a.shape[:2] + (w.cap,) + a.shape[3:], a.dtype) for n, a in pk.items()}
+        for n, a in pk.items():
+            full[n][:, :, :w.L] = a
+        refs.append(full)
+    kr, vr = refs
+    assert w.L + w.steps == w.cap
+    for t in range(w.steps):
         s = W.append_step_inputs(w, rng)
         qkv.qkv_update_append(kp, vp, to_dev(s["k_new"], "f16"), to_dev(s["v_new"], "f16"),
                               w.L + t)
-        kr = {k: np.concatenate([a, b], axis=2) for (k, a), b in
-              zip(kr.items(), oracle_pack(s["k_new"], "f16", w.mode, w.bits, w.group_size).values())}
-        vr = {k: np.concatenate([a, b], axis=2) for (k, a), b in
-              zip(vr.items(), oracle_pack(s["v_new"], "f16", w.mode, w.bits, w.group_size).values())}
+        for ref, new in ((kr, s["k_new"]), (vr, s["v_new"])):
+            for n, a in oracle_pack(new, "f16", w.mode, w.bits, w.group_size).items():
+                ref[n][:, :, w.L + t] = a[:, :, 0]
         L = w.L + t + 1
         out = qkv.qsdpa_decode(to_dev(s["q"], "f16"), kp, vp, L, w.scale)
-        if t in (0, 2):
+        if t in (0, 2, w.steps - 1):
+            rows = slice(w.L - 2, L)
+            assert_pack_equal(pack_numpy(kp), kr, rows=rows)
+            assert_pack_equal(pack_numpy(vp), vr, rows=rows)
             ref = oracle_attention(s["q"], "f16", kr, vr, L, w.mode, w.bits, w.group_size, w.scale)
-            assert_close(out, ref, f"step {t}")
+            assert_close(out, ref, f"append+decode step {t} (L={L})", report=True)
+    assert_pack_equal(pack_numpy(kp), kr)
+    assert_pack_equal(pack_numpy(vp), vr)
 
 
-def test_prefill_workload_sampled_rows():
+def test_prefill_workload_all_rows():
     """The 512-query causal prefill at full size (L=20480, GQA-16, D=256,
-    Q8_0), checked on sampled query positions that the oracle computes one by
-    one with the bottom-right causal rule written as an explicit mask."""
+    Q8_0): every query row against the oracle with the bottom-right causal
+    rule, which covers every 128-row workgroup and both key splits."""
     w = W.WORKLOADS["q8_0_prefill_512"]
     print("[prefill] full size", flush=True)
     inp, kp, vp, kr, vr = _workload_packs(w)
-    out = qkv.qsdpa_prefill(to_dev(inp["q"], w.dtype), kp, vp, w.L, w.scale, causal=True)
-    idx = np.array([0, 1, 7, 100, 255, 256, 300, 459, 510, 511])
-    qs = np.ascontiguousarray(inp["q"][:, :, idx])
-    j = np.arange(w.L)[None, :]
-    mask = np.where(j > (w.L - w.Lq + idx)[:, None], -np.inf, 0.0).astype(np.float32)
-    ref = oracle_attention(qs, w.dtype, kr, vr, w.L, w.mode, w.bits, w.group_size, w.scale,
-                           mask=mask[None, None])
-    assert_close(out[:, :, idx], ref, "prefill sampled rows")
-    # rows of the last query equal a decode of that query over every key
+    qd = to_dev(inp["q"], w.dtype)
+    plan = qkv.qsdpa_plan(qd, kp, w.L)
+    print(f"[prefill] plan {plan}", flush=True)
+    out = qkv.qsdpa_prefill(qd, kp, vp, w.L, w.scale, causal=True)
+    ref = oracle_attention(inp["q"], w.dtype, kr, vr, w.L, w.mode, w.bits, w.group_size, w.scale,
+                           causal=True)
+    assert_close(out, ref, "prefill all 512 rows", report=True)
+    # the last query row equals a decode of that query over every key
     dec = qkv.qsdpa_decode(to_dev(np.ascontiguousarray(inp["q"][:, :, -1:]), w.dtype), kp, vp,
                            w.L, w.scale)
     assert_close(out[:, :, -1:], dec.double().cpu().numpy(), "last row vs decode")

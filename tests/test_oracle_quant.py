@@ -172,3 +172,153 @@ def test_append_rowwise_equals_whole_quantize(orc, mode, bits, gs):
     for k, v in whole.items():
         if v is not None:
             assert np.array_equal(cache[k].view(np.uint8), v.view(np.uint8))
+
+
+# --------------------------------------------------------------------------- exact ties
+@pytest.mark.parametrize("name", ["affine_ties_4bit_g32.txt", "affine_ties_8bit_g32.txt"])
+def test_golden_affine_ties(orc, name):
+    """Quotients that are exactly k + 1/2 go to the even neighbour (the
+    fixtures' headers derive every code); half-up rounding or a reciprocal
+    multiply of the scale fails here."""
+    g = _golden.load(name)
+    x = _as_storage(g["x"], g["dtype"])[None, :]
+    assert np.array_equal(x.astype(np.float64)[0], np.asarray(g["x"], np.float64))
+    codes, s, b = orc.quantize_affine(x, g["dtype"], g["bits"], g["group_size"])
+    D = x.shape[-1]
+    assert _unpack(codes, g["bits"], D)[0].tolist() == g["codes_unpacked"]
+    assert _f32(orc, s, g["dtype"])[0].tolist() == g["scales"]
+    assert _f32(orc, b, g["dtype"])[0].tolist() == g["biases"]
+
+
+def test_golden_q8_0_ties(orc):
+    g = _golden.load("q8_0_ties.txt")
+    x = _as_storage(g["x"], g["dtype"])[None, :]
+    assert np.array_equal(x.astype(np.float64)[0], np.asarray(g["x"], np.float64))
+    codes, d = orc.quantize_q8_0(x, g["dtype"])
+    assert codes[0].tolist() == g["codes"]
+    assert orc.to_f32(d, "f16")[0].astype(np.float64).tolist() == g["d"]
+
+
+# --------------------------------------------------------------------------- independent re-derivation
+# A second implementation of both quantizers in numpy float32 (IEEE subtract
+# and divide, np.rint = round half to even, dtype casts by numpy / torch), from
+# the same definitions: MLX page "add fast::quantized_kv_update",
+# kernels/quantized.h affine_quantize (scale (max - min) / (2^bits - 1) floored
+# at T(1e-7), bias = min, both stored in T); llama.cpp page "Metal: Optimize
+# q8_0 KV - #25556" (Q8_0: fp16 d = amax / 127, codes in [-127, 127]).  It
+# must agree with the C oracle bit for bit.
+def _np_round_to(v32: np.ndarray, dt: str) -> np.ndarray:
+    """v (float32) as stored in dtype dt, widened back to float32."""
+    v32 = np.asarray(v32, np.float32)
+    if dt == "f32":
+        return v32
+    if dt == "f16":
+        return v32.astype(np.float16).astype(np.float32)
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(v32)).to(torch.bfloat16).to(torch.float32).numpy()
+
+
+def _np_widen(x: np.ndarray, dt: str) -> np.ndarray:
+    if dt == "bf16":
+        return (x.astype(np.uint32) << 16).view(np.float32)
+    return x.astype(np.float32)
+
+
+def _np_affine(x: np.ndarray, dt: str, bits: int, gs: int):
+    xf = _np_widen(x, dt)
+    D = xf.shape[-1]
+    g = xf.reshape(-1, D // gs, gs)
+    mn = g.min(-1, keepdims=True)
+    mx = g.max(-1, keepdims=True)
+    n = np.float32((1 << bits) - 1)
+    s32 = (mx - mn) / n
+    eps = _np_round_to(np.float32(1e-7), dt)
+    s32 = np.where(s32 < eps, eps, s32).astype(np.float32)
+    s = _np_round_to(s32, dt)
+    b = _np_round_to(mn, dt)
+    c = np.rint((g - b) / s)
+    c = np.clip(c, np.float32(0), n).astype(np.int64)
+    return c.reshape(xf.shape), s[..., 0].reshape(xf.shape[:-1] + (D // gs,)), \
+        b[..., 0].reshape(xf.shape[:-1] + (D // gs,))
+
+
+def _np_q8_0(x: np.ndarray, dt: str):
+    xf = _np_widen(x, dt)
+    D = xf.shape[-1]
+    g = xf.reshape(-1, D // 32, 32)
+    amax = np.abs(g).max(-1, keepdims=True)
+    d = (amax / np.float32(127)).astype(np.float16).astype(np.float32)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        c = np.clip(np.rint(g / d), np.float32(-127), np.float32(127))
+    c = np.where(d == 0, np.float32(0), c).astype(np.int64)
+    return c.reshape(xf.shape), d[..., 0].reshape(xf.shape[:-1] + (D // 32,))
+
+
+def _adversarial_rows(dt: str, D: int, seed: int) -> np.ndarray:
+    """Rows built to sit on rounding decisions: exact ties (k + 1/2 steps of
+    power-of-two and non-power-of-two scales, with and without a bias),
+    constant rows, tiny and huge ranges, negative-only rows, fp16
+    subnormals."""
+    rng = np.random.default_rng(seed)
+    rows = []
+    for num, den in ((1, 16), (7, 128), (13, 512), (3, 64), (5, 1024)):
+        for bias in (0.0, -2.0, 0.75):
+            k = rng.integers(0, 15, D)
+            half = rng.random(D) < 0.6
+            rows.append(bias + (k + 0.5 * half) * num / den)
+            rows[-1][0], rows[-1][1] = bias, bias + 15 * num / den
+    rows.append(np.full(D, 0.3125))
+    rows.append(np.full(D, -7.0))
+    rows.append(rng.standard_normal(D) * 1e-5)
+    rows.append(rng.standard_normal(D) * 3000.0)
+    rows.append(-1.0 - rng.random(D))
+    rows.append(rng.integers(-3, 4, D) * 2.0 ** -24)          # fp16 subnormal steps
+    rows.append(np.where(rng.random(D) < 0.5, 0.0, 1.0))
+    x = np.stack(rows).astype(np.float32)
+    return W.cast(x, dt)
+
+
+REDERIVE = [("f16", 4, 32), ("f16", 4, 64), ("f16", 8, 64), ("f16", 8, 128), ("f32", 4, 64),
+            ("f32", 8, 32), ("bf16", 4, 128), ("bf16", 8, 64)]
+
+
+@pytest.mark.parametrize("dt,bits,gs", REDERIVE)
+def test_affine_matches_numpy_rederivation(orc, dt, bits, gs):
+    D = 256
+    x = np.concatenate([W.random_case(31 + bits + gs, (600, D), "normal", dt),
+                        W.random_case(32 + bits + gs, (600, D), "uniform", dt),
+                        _adversarial_rows(dt, D, 33 + gs)])
+    codes, s, b = orc.quantize_affine(x, dt, bits, gs)
+    c_np, s_np, b_np = _np_affine(x, dt, bits, gs)
+    assert np.array_equal(_f32(orc, s, dt), s_np.astype(np.float64))
+    assert np.array_equal(_f32(orc, b, dt), b_np.astype(np.float64))
+    c = _unpack(codes, bits, D).astype(np.int64)
+    bad = np.argwhere(c != c_np)
+    assert bad.size == 0, f"{len(bad)} codes differ, first at {tuple(bad[0])}"
+
+
+@pytest.mark.parametrize("dt", ["f16", "f32", "bf16"])
+def test_q8_0_matches_numpy_rederivation(orc, dt):
+    D = 256
+    x = np.concatenate([W.random_case(41, (600, D), "normal", dt),
+                        W.random_case(42, (600, D), "uniform", dt),
+                        _adversarial_rows(dt, D, 43)])
+    x[0, :32] = 0                               # a zero block
+    codes, d = orc.quantize_q8_0(x, dt)
+    c_np, d_np = _np_q8_0(x, dt)
+    assert np.array_equal(orc.to_f32(d, "f16"), d_np)
+    bad = np.argwhere(codes.astype(np.int64) != c_np)
+    assert bad.size == 0, f"{len(bad)} codes differ, first at {tuple(bad[0])}"
+
+
+def test_rederivation_discriminates_rounding_variants():
+    """The inputs above separate the readings that the pages leave open: a
+    reciprocal multiply, or half-up rounding, changes codes on them."""
+    x = _adversarial_rows("f16", 256, 33 + 64)
+    xf = _np_widen(x, "f16").reshape(-1, 4, 64)
+    c, s, b = _np_affine(x, "f16", 4, 64)
+    s = s[..., None]
+    b = b[..., None]
+    recip = np.clip(np.rint((xf - b) * (np.float32(1) / s)), 0, 15).reshape(c.shape)
+    half_up = np.clip(np.floor((xf - b) / s + np.float32(0.5)), 0, 15).reshape(c.shape)
+    assert (recip != c).any() and (half_up != c).any()
