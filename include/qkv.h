@@ -62,7 +62,7 @@
 extern "C" {
 #endif
 
-#define QKV_ABI_VERSION 2
+#define QKV_ABI_VERSION 3
 
 typedef enum {
     QKV_OK = 0,
@@ -135,18 +135,30 @@ qkv_status qkv_update_append(const void* k_new, const void* v_new, int32_t dtype
                              const qkv_pack* k_cache, const qkv_pack* v_cache, void* stream);
 
 /* Bytes of workspace the attention calls need for these sizes (0 when no
- * key partitioning is used): a ticket area (4 bytes per batch x kv head x
- * row tile, rounded up to 256 bytes), then per row tile and split the partial
- * softmax state (m, l) and an unnormalised output row.  The ticket area must
- * hold zeros when the workspace is first used (zero-fill the workspace once
- * after allocating it); every call leaves it zero.  The partial states need no
+ * key partitioning is used): a ticket header of QKV_TICKET_BYTES (one 32-bit
+ * counter per batch x kv head, at the same place for every call), then per
+ * row tile and split the partial softmax state (m, l) and an unnormalised
+ * output row.  The ticket header must hold zeros when the workspace is first
+ * used (zero-fill it after allocating, or call qsdpa_workspace_reset); every
+ * call that completes leaves it zero.  The partial states need no
  * initialisation: a call writes them and either merges them in the same
  * kernel (the last workgroup of each batch x kv head, counted by its ticket)
  * or with the split merge kernel it launches next on the same stream.  Calls
- * that may overlap (different streams) need separate workspaces.  It must be
- * 256-byte aligned. */
+ * that may overlap (different streams) need separate workspaces.  The
+ * workspace must be 256-byte aligned and must not overlap q, out, the packs
+ * or the mask. */
 size_t qsdpa_workspace_bytes(int64_t B, int64_t Hq, int64_t Lq, int64_t D, int64_t L,
                              const qkv_pack* k, int32_t q_dtype, const qkv_attn_opts* opts);
+
+#define QKV_TICKET_BYTES ((size_t)262144)
+
+/* Zero-fills the ticket header of a workspace (its first QKV_TICKET_BYTES)
+ * on 'stream' with a kernel, which a HIP graph may capture: for a workspace
+ * just allocated, or one whose last call did not complete (a ticket left
+ * non-zero would make later calls merge at the wrong moment).  Errors:
+ * EINVAL for a null or misaligned workspace or workspace_bytes below
+ * QKV_TICKET_BYTES; EHIP if the launch fails. */
+qkv_status qsdpa_workspace_reset(void* workspace, size_t workspace_bytes, void* stream);
 
 /* Kernels a plan can name (qkv_attn_plan.kernel). */
 typedef enum {
@@ -184,7 +196,8 @@ qkv_status qsdpa_plan(int64_t B, int64_t Hq, int64_t Lq, int64_t D, int64_t L, c
  * page's fused single-query path, the mask is applied.  A row whose keys are
  * all masked to -inf produces zeros.  out must not overlap q, the packs or
  * the workspace.  Errors: EINVAL (shapes, Hq % Hk != 0, L < 1 or > L_cap,
- * packs mismatch, overlap), EUNSUPPORTED, EWORKSPACE. */
+ * packs mismatch, overlap of out or the workspace with an input),
+ * EUNSUPPORTED, EWORKSPACE. */
 qkv_status qsdpa_decode(const void* q, int32_t q_dtype, int64_t B, int64_t Hq, int64_t D,
                         const qkv_pack* k, const qkv_pack* v, int64_t L, float scale,
                         const void* mask, int32_t mask_dtype, const int64_t mask_strides[4],

@@ -3,8 +3,10 @@
 The compute path is libqkv.so (hand-written HIP kernels for gfx950 behind the
 C ABI in include/qkv.h); this package is its torch-facing binding.
 """
-from .api import (Pack, PreparedAppend, PreparedAttention, PreparedDecode, QKVError, Workspace, empty_pack, qkv_quantize, qkv_update_append,
-                  qsdpa_decode, qsdpa_plan, qsdpa_prefill, qsdpa_workspace_bytes, torch_dtype)
+from .api import (Pack, PreparedAppend, PreparedAttention, PreparedDecode, QKVError, Workspace,
+                  empty_pack, qkv_quantize, qkv_update_append, qsdpa_decode, qsdpa_plan,
+                  qsdpa_prefill, qsdpa_workspace_bytes, qsdpa_workspace_reset, torch_dtype)
 
-__all__ = ["Pack", "PreparedAppend", "PreparedAttention", "PreparedDecode", "QKVError", "Workspace", "empty_pack", "qkv_quantize", "qkv_update_append",
-           "qsdpa_decode", "qsdpa_plan", "qsdpa_prefill", "qsdpa_workspace_bytes", "torch_dtype"]
+__all__ = ["Pack", "PreparedAppend", "PreparedAttention", "PreparedDecode", "QKVError", "Workspace",
+           "empty_pack", "qkv_quantize", "qkv_update_append", "qsdpa_decode", "qsdpa_plan",
+           "qsdpa_prefill", "qsdpa_workspace_bytes", "qsdpa_workspace_reset", "torch_dtype"]

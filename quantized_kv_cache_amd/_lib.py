@@ -17,9 +17,10 @@ QKV_ALGO_AUTO, QKV_ALGO_GENERIC, QKV_ALGO_MATRIX = 0, 1, 2
 QKV_KERNEL_GENERIC, QKV_KERNEL_DECODE, QKV_KERNEL_DECODE_NARROW, QKV_KERNEL_PREFILL = 0, 1, 2, 3
 
 # every symbol include/qkv.h declares
-EXPORTS = ["qkv_quantize", "qkv_update_append", "qsdpa_workspace_bytes", "qsdpa_plan",
-           "qsdpa_decode", "qsdpa_prefill", "qkv_last_error", "qkv_abi_version",
+EXPORTS = ["qkv_quantize", "qkv_update_append", "qsdpa_workspace_bytes", "qsdpa_workspace_reset",
+           "qsdpa_plan", "qsdpa_decode", "qsdpa_prefill", "qkv_last_error", "qkv_abi_version",
            "qkv_measure_read"]
+QKV_TICKET_BYTES = 262144
 
 
 class QkvPack(ctypes.Structure):
@@ -72,6 +73,8 @@ def load():
     L.qkv_update_append.restype = I32
     L.qsdpa_workspace_bytes.argtypes = [I64, I64, I64, I64, I64, PK, I32, OP]
     L.qsdpa_workspace_bytes.restype = SZ
+    L.qsdpa_workspace_reset.argtypes = [P, SZ, P]
+    L.qsdpa_workspace_reset.restype = I32
     L.qsdpa_plan.argtypes = [I64, I64, I64, I64, I64, PK, I32, OP, ctypes.POINTER(QkvAttnPlan)]
     L.qsdpa_plan.restype = I32
     L.qsdpa_decode.argtypes = [P, I32, I64, I64, I64, PK, PK, I64, ctypes.c_float, P, I32, I64P,

@@ -7,7 +7,8 @@ kernels behind the C ABI; there is no CPU path.
 
 The function names are those of the C ABI (include/qkv.h):
 ``qkv_quantize``, ``qkv_update_append``, ``qsdpa_workspace_bytes``,
-``qsdpa_plan``, ``qsdpa_decode``, ``qsdpa_prefill``.
+``qsdpa_workspace_reset``, ``qsdpa_plan``, ``qsdpa_decode``,
+``qsdpa_prefill``.
 """
 from __future__ import annotations
 
@@ -171,22 +172,50 @@ def qsdpa_plan(q: torch.Tensor, k: Pack, L: int, num_splits: int = 0,
 
 
 class Workspace:
-    """Reusable attention workspace (grows on demand), one buffer per device,
-    for calls on one stream.  Buffers start zero-filled (the ticket area at
-    their start must be; the calls leave it zero)."""
+    """Reusable attention workspace (grows on demand): one buffer per (device,
+    stream), so that calls on different streams never share split states or
+    merge tickets.  Buffers start zero-filled (the ticket header at their
+    start must; every call that completes leaves it zero)."""
 
     def __init__(self):
-        self._buf: dict[torch.device, torch.Tensor] = {}
+        self._buf: dict[tuple, torch.Tensor] = {}
 
-    def get(self, nbytes: int, device) -> torch.Tensor | None:
+    @staticmethod
+    def _key(device, stream):
+        device = torch.device(device)
+        if stream is None:
+            stream = torch.cuda.current_stream(device)
+        return device, int(stream.cuda_stream)
+
+    def get(self, nbytes: int, device, stream=None) -> torch.Tensor | None:
+        """The buffer of (device, stream) with at least nbytes (None for 0);
+        stream defaults to the device's current torch stream."""
         if nbytes == 0:
             return None
-        device = torch.device(device)
-        buf = self._buf.get(device)
+        key = self._key(device, stream)
+        buf = self._buf.get(key)
         if buf is None or buf.numel() < nbytes:
-            buf = torch.zeros(((nbytes + 255) // 256) * 256, dtype=torch.uint8, device=device)
-            self._buf[device] = buf
+            buf = torch.zeros(((nbytes + 255) // 256) * 256, dtype=torch.uint8, device=key[0])
+            self._buf[key] = buf
         return buf
+
+    def reset(self, device, stream=None) -> None:
+        """Zero the ticket header of the (device, stream) buffer on that
+        stream (qsdpa_workspace_reset), e.g. after a call that did not
+        complete."""
+        buf = self._buf.get(self._key(device, stream))
+        if buf is not None:
+            qsdpa_workspace_reset(buf, stream)
+
+
+def qsdpa_workspace_reset(buf: torch.Tensor, stream=None) -> None:
+    """Zero-fill the ticket header of a workspace buffer on its device's
+    current (or the given) stream."""
+    if stream is None:
+        stream = torch.cuda.current_stream(buf.device)
+    st = _lib.load().qsdpa_workspace_reset(_ptr(buf), buf.numel() * buf.element_size(),
+                                           ctypes.c_void_p(stream.cuda_stream))
+    _lib.check(st)
 
 
 _default_ws = Workspace()

@@ -21,6 +21,8 @@ hipError_t launch_measure_read(const void* buf, size_t bytes, int workgroups, ui
 }  // namespace qkv
 #include "qkv_merge.hpp"
 
+static_assert(QKV_TICKET_BYTES == qkv::kTicketBytes, "ticket header size of the ABI");
+
 namespace {
 
 thread_local std::string g_last_error;
@@ -160,8 +162,21 @@ struct Plan {
 
 size_t ws_for(int64_t B, int64_t Hk, int n_rt, int S, int RT, int64_t D) {
     if (S <= 1) return 0;
-    return qkv::ticket_bytes(B * Hk * n_rt) +
+    return qkv::kTicketBytes +
            (size_t)(B * Hk * n_rt) * (size_t)S * (size_t)RT * (size_t)(D + 2) * 4;  // ml + o
+}
+
+// Element extent [lo, hi) of a strided 4-d view in bytes.
+Range strided_range(const void* base, size_t esize, const int64_t n[4], const int64_t st[4]) {
+    int64_t last = 0;
+    for (int i = 0; i < 4; ++i) last += (n[i] - 1) * st[i];
+    uintptr_t lo = reinterpret_cast<uintptr_t>(base);
+    return {lo, lo + (uintptr_t)((last + 1) * (int64_t)esize)};
+}
+
+bool overlaps_pack(Range r, const qkv_pack* p) {
+    return overlap(r, codes_range(p)) || overlap(r, scales_range(p, p->scales)) ||
+           (p->biases && overlap(r, scales_range(p, p->biases)));
 }
 
 // Split count: enough workgroups to cover the CUs about twice, each split at
@@ -269,10 +284,13 @@ qkv_status attention(const char* name, const void* q, int32_t q_dtype, int64_t B
     Range rq{reinterpret_cast<uintptr_t>(q), reinterpret_cast<uintptr_t>(q) + qbytes};
     if (overlap(ro, rq)) return fail(QKV_EINVAL, "%s: out overlaps q", name);
     const qkv_pack* packs[2] = {k, v};
-    for (const qkv_pack* p : packs) {
-        if (overlap(ro, codes_range(p)) || overlap(ro, scales_range(p, p->scales)) ||
-            (p->biases && overlap(ro, scales_range(p, p->biases))))
-            return fail(QKV_EINVAL, "%s: out overlaps a pack", name);
+    for (const qkv_pack* p : packs)
+        if (overlaps_pack(ro, p)) return fail(QKV_EINVAL, "%s: out overlaps a pack", name);
+    Range rm{0, 0};
+    if (mask_kind == QKV_MASK_ADDITIVE) {
+        const int64_t mn[4] = {B, Hq, Lq, L};
+        rm = strided_range(mask, dtype_size(mask_dtype), mn, ms);
+        if (overlap(ro, rm)) return fail(QKV_EINVAL, "%s: out overlaps the mask", name);
     }
     if (opts && opts->algo == QKV_ALGO_MATRIX &&
         !qkv::matrix_supported(q_dtype, k->mode, k->bits, k->group_size, (int)D, (int)G, Lq))
@@ -288,6 +306,11 @@ qkv_status attention(const char* name, const void* q, int32_t q_dtype, int64_t B
         if (!aligned(workspace, 256)) return fail(QKV_EINVAL, "%s: workspace not 256-byte aligned", name);
         Range rw{reinterpret_cast<uintptr_t>(workspace), reinterpret_cast<uintptr_t>(workspace) + pl.ws_bytes};
         if (overlap(ro, rw)) return fail(QKV_EINVAL, "%s: out overlaps the workspace", name);
+        if (overlap(rq, rw)) return fail(QKV_EINVAL, "%s: q overlaps the workspace", name);
+        for (const qkv_pack* p : packs)
+            if (overlaps_pack(rw, p)) return fail(QKV_EINVAL, "%s: the workspace overlaps a pack", name);
+        if (mask_kind == QKV_MASK_ADDITIVE && overlap(rm, rw))
+            return fail(QKV_EINVAL, "%s: the mask overlaps the workspace", name);
     }
 
     qkv::AttnLaunch a{};
@@ -317,7 +340,7 @@ qkv_status attention(const char* name, const void* q, int32_t q_dtype, int64_t B
     if (pl.ws_bytes > 0) {
         const int64_t tiles = B * k->H * pl.n_rt;
         a.tickets = static_cast<uint32_t*>(workspace);
-        a.part_ml = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + qkv::ticket_bytes(tiles));
+        a.part_ml = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + qkv::kTicketBytes);
         a.part_o = a.part_ml + (size_t)tiles * (size_t)pl.S * 16 * 2;
     }
     hipStream_t s = static_cast<hipStream_t>(stream);
@@ -428,6 +451,16 @@ qkv_status qsdpa_prefill(const void* q, int32_t q_dtype, int64_t B, int64_t Hq, 
                          size_t workspace_bytes, const qkv_attn_opts* opts, void* stream) {
     return attention("qsdpa_prefill", q, q_dtype, B, Hq, Lq, D, k, v, L, scale, mask_kind, mask,
                      mask_dtype, mask_strides, out, workspace, workspace_bytes, opts, stream);
+}
+
+qkv_status qsdpa_workspace_reset(void* workspace, size_t workspace_bytes, void* stream) {
+    if (!workspace) return fail(QKV_EINVAL, "qsdpa_workspace_reset: null workspace");
+    if (!aligned(workspace, 256)) return fail(QKV_EINVAL, "qsdpa_workspace_reset: workspace not 256-byte aligned");
+    if (workspace_bytes < qkv::kTicketBytes)
+        return fail(QKV_EINVAL, "qsdpa_workspace_reset: %zu bytes is less than the %zu-byte ticket header",
+                    workspace_bytes, qkv::kTicketBytes);
+    return hip_status(qkv::launch_fill_zero(workspace, qkv::kTicketBytes, static_cast<hipStream_t>(stream)),
+                      "qsdpa_workspace_reset");
 }
 
 qkv_status qkv_measure_read(const void* buf, size_t bytes, int32_t workgroups, uint32_t* sink,

@@ -4,6 +4,8 @@
 // states (all its loads issued before it waits: one memory round trip for
 // S <= 128).  States combine online in log2 units, the split groups combine
 // through LDS, and the chunk is written in the query dtype.
+#include <algorithm>
+
 #include "qkv_merge.hpp"
 
 namespace qkv {
@@ -182,6 +184,20 @@ hipError_t launch_merge(int q_dtype, int D, int64_t B, const AttnLaunch& p, hipS
         case DT_BF16: return launch_q<DT_BF16>(D, B, p, stream);
     }
     return hipErrorNotSupported;
+}
+
+// Zero fill of a workspace's ticket header (16-byte stores, grid-stride).
+__global__ __launch_bounds__(256) void fill_zero_kernel(uint4* p, size_t n16) {
+    for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += (size_t)gridDim.x * 256)
+        p[i] = uint4{0u, 0u, 0u, 0u};
+}
+
+hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t stream) {
+    const size_t n16 = bytes / 16;
+    if (n16 == 0) return hipSuccess;
+    const size_t blocks = std::min<size_t>((n16 + 255) / 256, 1024);
+    hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, (uint4*)p, n16);
+    return hipGetLastError();
 }
 
 }  // namespace qkv

@@ -6,8 +6,8 @@
 // "add fast::quantized_kv_update", sdpa_vector.h quant_sdpa_vector, applied
 // across workgroups).  A row with no visible key (every m_s = -inf) gives 0.
 //
-// Workspace of a call: [tickets: one uint32 per tile, padded to 256 bytes]
-// [ml: tiles x S x 16 x 2] [o: tiles x S x 16 x D] (fp32).  Either the
+// Workspace of a call: [tickets: kTicketBytes, one uint32 per (batch, kv
+// head)] [ml: tiles x S x 16 x 2] [o: tiles x S x 16 x D] (fp32).  Either the
 // attention kernel writes the states and merge_splits_kernel, launched next on
 // the same stream, reads them (kernel order is the only synchronisation), or
 // the attention kernel merges them itself (merge_last below): every workgroup
@@ -24,8 +24,17 @@ constexpr int kMaxSplits = 256;
 
 hipError_t launch_merge(int q_dtype, int D, int64_t B, const AttnLaunch& p, hipStream_t stream);
 
-// Bytes of the ticket area at the start of a workspace.
-inline size_t ticket_bytes(int64_t tiles) { return (size_t)((tiles * 4 + 255) / 256 * 256); }
+// The ticket header at the start of every split workspace: one uint32 per
+// (batch, kv head) of the fused-merge decode, whose grid holds fewer than
+// 2^16 of them.  Its size does not depend on the call, so the partial states
+// of one call never lie where a later call on the same workspace keeps its
+// tickets.
+constexpr size_t kTicketWords = 65536;
+constexpr size_t kTicketBytes = kTicketWords * 4;
+
+// Zero-fills 'bytes' (a multiple of 16) at p on 'stream' with a kernel (no
+// memset node, so the call can be captured in a graph).
+hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t stream);
 
 struct SplitState {
     float m, l;

@@ -32,7 +32,7 @@ def test_exports_every_declared_function(L):
     assert set(names) == set(_lib.EXPORTS), names
     for n in names:
         assert hasattr(L, n), n
-    assert L.qkv_abi_version() == 2
+    assert L.qkv_abi_version() == 3
 
 
 def _pack(**kw):
@@ -137,9 +137,9 @@ def test_workspace_bytes(L):
                                    ctypes.byref(one)) == 0
     n = L.qsdpa_workspace_bytes(1, 4, 1, 128, 64, ctypes.byref(kp), _lib.QKV_F16,
                                 ctypes.byref(four))
-    # a 256-byte ticket area, then splits x 16 rows x (m, l, o[D]) floats per
+    # the fixed ticket header, then splits x 16 rows x (m, l, o[D]) floats per
     # (b, kv head, row tile)
-    assert n == 256 + 2 * 2 * 16 * 130 * 4
+    assert n == _lib.QKV_TICKET_BYTES + 2 * 2 * 16 * 130 * 4
     assert L.qsdpa_workspace_bytes(1, 3, 1, 128, 64, ctypes.byref(kp), _lib.QKV_F16, None) == 0
 
 
@@ -193,3 +193,33 @@ def test_measure_read_rejects_bad_arguments(L):
                                   (FAKE, 4096, 0, sink), (FAKE, 4096, 8193, sink)):
         assert L.qkv_measure_read(buf, nbytes, wgs, snk, None) == _lib.QKV_EINVAL, (buf, nbytes, wgs)
         assert L.qkv_last_error()
+
+
+def test_decode_rejects_workspace_overlapping_inputs(L):
+    """The workspace is written by the call: it may not overlap q, either
+    pack or the mask (nor out)."""
+    opts = _lib.QkvAttnOpts(num_splits=4, algo=_lib.QKV_ALGO_GENERIC)
+    need = L.qsdpa_workspace_bytes(1, 4, 1, 128, 64, ctypes.byref(_pack()), _lib.QKV_F16,
+                                   ctypes.byref(opts))
+    good = FAKE + 0x4000000
+    assert need > _lib.QKV_TICKET_BYTES
+    for ws, what in ((FAKE + 0x1000000 - 256 * 1024, "q"),          # runs into q
+                     (FAKE + 0x800000 - 256 * 1024, "pack"),        # runs into V's codes
+                     (FAKE + 0x100000, "pack"),                     # K's scales
+                     (FAKE + 0x2000000, "out")):
+        st = _decode(L, ws=ws, wsb=need, opts=opts)
+        assert st == _lib.QKV_EINVAL and what in L.qkv_last_error().decode(), (hex(ws), what)
+    st = _decode(L, ws=FAKE + 0x3000000 - 4096, wsb=need, opts=opts, mask=FAKE + 0x3000000,
+                 ms=(0, 0, 0, 1))
+    assert st == _lib.QKV_EINVAL and "mask" in L.qkv_last_error().decode()
+    # out may not overlap the mask either
+    st = _decode(L, mask=FAKE + 0x2000000, ms=(0, 0, 0, 1))
+    assert st == _lib.QKV_EINVAL and "mask" in L.qkv_last_error().decode()
+    assert good > 0
+
+
+def test_workspace_reset_rejects(L):
+    assert L.qsdpa_workspace_reset(None, _lib.QKV_TICKET_BYTES, None) == _lib.QKV_EINVAL
+    assert L.qsdpa_workspace_reset(FAKE + 16, _lib.QKV_TICKET_BYTES, None) == _lib.QKV_EINVAL
+    assert L.qsdpa_workspace_reset(FAKE, _lib.QKV_TICKET_BYTES - 256, None) == _lib.QKV_EINVAL
+    assert "ticket header" in L.qkv_last_error().decode()

@@ -15,6 +15,8 @@ from tests._cases import (W, assert_close, assert_pack_equal, err_over_tol, orac
 
 pytestmark = pytest.mark.gpu
 
+TICKETS = qkv._lib.QKV_TICKET_BYTES     # the workspace's ticket header
+
 
 def _seed(*a):
     return zlib.crc32(repr(a).encode()) % 100000
@@ -120,7 +122,7 @@ def test_decode_fused_merge_repeats():
         out = qkv.qsdpa_decode(qd, kp, vp, L, 0.1, num_splits=32, workspace=ws)
         assert torch.equal(out, ref), f"call {i} differs from the first call on its cache"
     torch.cuda.synchronize()
-    assert not ws.get(1, qd.device)[:256].any(), "tickets not back to zero"
+    assert not ws.get(1, qd.device)[:TICKETS].any(), "tickets not back to zero"
 
 
 def test_decode_fused_merge_ignores_stale_states():
@@ -145,7 +147,7 @@ def test_decode_fused_merge_ignores_stale_states():
         assert qkv.qsdpa_plan(qd, kp, L, num_splits=splits)["kernel"] == "attn_decode_narrow"
         first = None
         for fill in ("random", "dominating", "complement"):
-            area = buf[256:]
+            area = buf[TICKETS:]
             if fill == "random":
                 area.copy_(torch.randint(0, 256, (area.numel(),), dtype=torch.uint8,
                                          device=qd.device, generator=gen))
@@ -161,7 +163,7 @@ def test_decode_fused_merge_ignores_stale_states():
             out = qkv.qsdpa_decode(qd, kp, vp, L, 0.1, num_splits=splits, workspace=ws)
             assert torch.equal(out, first), f"splits={splits}: call {i} differs from the first"
     torch.cuda.synchronize()
-    assert not buf[:256].any(), "tickets not back to zero"
+    assert not buf[:TICKETS].any(), "tickets not back to zero"
 
 
 def test_decode_fused_merge_mixed_plans_share_a_workspace():
@@ -182,7 +184,7 @@ def test_decode_fused_merge_mixed_plans_share_a_workspace():
                 out = qkv.qsdpa_decode(qd, kp, vp, L, 0.2, num_splits=splits, workspace=ws)
                 assert_close(out, ref, f"case {ci} splits={splits} rep {rep}")
     torch.cuda.synchronize()
-    assert not ws.get(1, prepared[0][0].device)[:256].any(), "tickets not back to zero"
+    assert not ws.get(1, prepared[0][0].device)[:TICKETS].any(), "tickets not back to zero"
 
 
 @pytest.mark.parametrize("mode,bits,vmean,vstd", [
