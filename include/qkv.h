@@ -204,6 +204,28 @@ qkv_status qsdpa_decode(const void* q, int32_t q_dtype, int64_t B, int64_t Hq, i
                         void* out, void* workspace, size_t workspace_bytes,
                         const qkv_attn_opts* opts, void* stream);
 
+/* qsdpa_decode for callers that cannot allocate (code under HIP graph
+ * capture, serving loops that forbid hipMalloc): the same computation and
+ * kernels, with the split workspace in a device array inside the library
+ * instead of a caller's buffer.  The array holds QKV_STATIC_SCRATCH_BYTES;
+ * each GPU has its own copy, resolved and its ticket header zeroed (with a
+ * kernel on 'stream') at the first call on that device, and kept until the
+ * process ends.  Nothing is allocated or freed by this call.  Every call on a
+ * GPU shares that GPU's array and leaves its contents (tickets zero, split
+ * states of the last call): calls that may overlap on one GPU (different
+ * streams, or host threads) race and must not be issued.  'stream' must
+ * belong to the current device.  Arguments and errors as qsdpa_decode, plus
+ * EWORKSPACE when the call's plan needs more than QKV_STATIC_SCRATCH_BYTES
+ * (then pass fewer splits in opts, or use qsdpa_decode with a workspace),
+ * and EHIP when the device array cannot be resolved. */
+#define QKV_STATIC_SCRATCH_BYTES ((size_t)(QKV_TICKET_BYTES + 16u * 1024u * 1024u))
+
+qkv_status qsdpa_decode_static(const void* q, int32_t q_dtype, int64_t B, int64_t Hq, int64_t D,
+                               const qkv_pack* k, const qkv_pack* v, int64_t L, float scale,
+                               const void* mask, int32_t mask_dtype,
+                               const int64_t mask_strides[4], void* out,
+                               const qkv_attn_opts* opts, void* stream);
+
 /* Prefill: q, out [B,Hq,Lq,D] contiguous; keys [0, L).
  *   out[b,h,i] = softmax_j(scale * q[b,h,i] . K[b,h/(Hq/Hk),j] + m_ij) V
  * for every query row i < Lq: the composition that the MLX page "add

@@ -18,9 +18,10 @@ QKV_KERNEL_GENERIC, QKV_KERNEL_DECODE, QKV_KERNEL_DECODE_NARROW, QKV_KERNEL_PREF
 
 # every symbol include/qkv.h declares
 EXPORTS = ["qkv_quantize", "qkv_update_append", "qsdpa_workspace_bytes", "qsdpa_workspace_reset",
-           "qsdpa_plan", "qsdpa_decode", "qsdpa_prefill", "qkv_last_error", "qkv_abi_version",
-           "qkv_measure_read"]
+           "qsdpa_plan", "qsdpa_decode", "qsdpa_decode_static", "qsdpa_prefill", "qkv_last_error",
+           "qkv_abi_version", "qkv_measure_read"]
 QKV_TICKET_BYTES = 262144
+QKV_STATIC_SCRATCH_BYTES = QKV_TICKET_BYTES + 16 * 1024 * 1024
 
 
 class QkvPack(ctypes.Structure):
@@ -80,6 +81,9 @@ def load():
     L.qsdpa_decode.argtypes = [P, I32, I64, I64, I64, PK, PK, I64, ctypes.c_float, P, I32, I64P,
                                P, P, SZ, OP, P]
     L.qsdpa_decode.restype = I32
+    L.qsdpa_decode_static.argtypes = [P, I32, I64, I64, I64, PK, PK, I64, ctypes.c_float, P, I32,
+                                      I64P, P, OP, P]
+    L.qsdpa_decode_static.restype = I32
     L.qsdpa_prefill.argtypes = [P, I32, I64, I64, I64, I64, PK, PK, I64, ctypes.c_float, I32, P,
                                 I32, I64P, P, P, SZ, OP, P]
     L.qsdpa_prefill.restype = I32

@@ -8,7 +8,7 @@ kernels behind the C ABI; there is no CPU path.
 The function names are those of the C ABI (include/qkv.h):
 ``qkv_quantize``, ``qkv_update_append``, ``qsdpa_workspace_bytes``,
 ``qsdpa_workspace_reset``, ``qsdpa_plan``, ``qsdpa_decode``,
-``qsdpa_prefill``.
+``qsdpa_decode_static``, ``qsdpa_prefill``.
 """
 from __future__ import annotations
 
@@ -255,6 +255,27 @@ def qsdpa_decode(q: torch.Tensor, k: Pack, v: Pack, L: int, scale: float,
                                   ctypes.byref(v.c_struct()), L, float(scale), mp, mdt, ms,
                                   _ptr(out), _ptr(buf), nbytes,
                                   ctypes.byref(_opts(num_splits, algo)), _stream(q.device))
+    _lib.check(st)
+    return out
+
+
+def qsdpa_decode_static(q: torch.Tensor, k: Pack, v: Pack, L: int, scale: float,
+                        mask: torch.Tensor | None = None, num_splits: int = 0,
+                        algo: str = "auto", out: torch.Tensor | None = None) -> torch.Tensor:
+    """qsdpa_decode with the library's static per-GPU workspace: the call
+    itself allocates nothing (``out`` given).  Calls that overlap on one GPU
+    race on that workspace."""
+    B, Hq, Lq, D = q.shape
+    if Lq != 1:
+        raise ValueError("decode takes one query per head")
+    if q.dim() != 4 or not q.is_contiguous():
+        raise ValueError("q must be a contiguous [B,Hq,1,D] tensor")
+    out = torch.empty_like(q) if out is None else out
+    mp, mdt, ms = _mask_args(mask, (B, Hq, 1, L))
+    st = _lib.load().qsdpa_decode_static(_ptr(q), _dt(q), B, Hq, D, ctypes.byref(k.c_struct()),
+                                         ctypes.byref(v.c_struct()), L, float(scale), mp, mdt, ms,
+                                         _ptr(out), ctypes.byref(_opts(num_splits, algo)),
+                                         _stream(q.device))
     _lib.check(st)
     return out
 

@@ -247,7 +247,7 @@ qkv_status attention(const char* name, const void* q, int32_t q_dtype, int64_t B
                      int64_t Lq, int64_t D, const qkv_pack* k, const qkv_pack* v, int64_t L,
                      float scale, int32_t mask_kind, const void* mask, int32_t mask_dtype,
                      const int64_t ms[4], void* out, void* workspace, size_t workspace_bytes,
-                     const qkv_attn_opts* opts, void* stream) {
+                     const qkv_attn_opts* opts, void* stream, bool static_ws = false) {
     qkv_status st;
     if ((st = check_pack(k, "k")) != QKV_OK) return st;
     if ((st = check_pack(v, "v")) != QKV_OK) return st;
@@ -299,7 +299,16 @@ qkv_status attention(const char* name, const void* q, int32_t q_dtype, int64_t B
     Plan pl = make_plan(B, Hq, Lq, D, L, k, q_dtype, opts);
     if (B * k->H > 65535 || (!pl.prefill && pl.n_rt > 65535) || pl.S > 65535)
         return fail(QKV_EUNSUPPORTED, "%s: batch x kv heads or row tiles beyond the launch grid", name);
-    if (pl.ws_bytes > 0) {
+    if (pl.ws_bytes > 0 && static_ws) {
+        // the library's own device array; checked last, since resolving it
+        // may enqueue the zero fill of its ticket header
+        if (pl.ws_bytes > QKV_STATIC_SCRATCH_BYTES)
+            return fail(QKV_EWORKSPACE, "%s: the plan needs %zu bytes of workspace, the static one holds %zu",
+                        name, pl.ws_bytes, (size_t)QKV_STATIC_SCRATCH_BYTES);
+        hipError_t se = qkv::static_scratch(static_cast<hipStream_t>(stream), &workspace);
+        if (se != hipSuccess) return hip_status(se, name);
+        workspace_bytes = QKV_STATIC_SCRATCH_BYTES;
+    } else if (pl.ws_bytes > 0) {
         if (!workspace || workspace_bytes < pl.ws_bytes)
             return fail(QKV_EWORKSPACE, "%s: workspace of %zu bytes needed, %zu given", name,
                         pl.ws_bytes, workspace ? workspace_bytes : (size_t)0);
@@ -442,6 +451,15 @@ qkv_status qsdpa_decode(const void* q, int32_t q_dtype, int64_t B, int64_t Hq, i
     return attention("qsdpa_decode", q, q_dtype, B, Hq, 1, D, k, v, L, scale,
                      mask ? QKV_MASK_ADDITIVE : QKV_MASK_NONE, mask, mask_dtype, mask_strides, out,
                      workspace, workspace_bytes, opts, stream);
+}
+
+qkv_status qsdpa_decode_static(const void* q, int32_t q_dtype, int64_t B, int64_t Hq, int64_t D,
+                               const qkv_pack* k, const qkv_pack* v, int64_t L, float scale,
+                               const void* mask, int32_t mask_dtype, const int64_t mask_strides[4],
+                               void* out, const qkv_attn_opts* opts, void* stream) {
+    return attention("qsdpa_decode_static", q, q_dtype, B, Hq, 1, D, k, v, L, scale,
+                     mask ? QKV_MASK_ADDITIVE : QKV_MASK_NONE, mask, mask_dtype, mask_strides, out,
+                     nullptr, 0, opts, stream, true);
 }
 
 qkv_status qsdpa_prefill(const void* q, int32_t q_dtype, int64_t B, int64_t Hq, int64_t Lq,

@@ -97,4 +97,10 @@ int narrow_decode_key_quantum();
 hipError_t launch_attn_narrow(int mode, int bits, int D, int64_t B, const AttnLaunch& p,
                               hipStream_t stream);
 
+// The device address of this GPU's static split workspace
+// (QKV_STATIC_SCRATCH_BYTES, its ticket header zeroed on 'stream' at the first
+// use on the device).  The stream must belong to the current device
+// (hipErrorInvalidDevice otherwise).
+hipError_t static_scratch(hipStream_t stream, void** addr);
+
 }  // namespace qkv
