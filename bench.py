@@ -121,6 +121,9 @@ def parse():
                          "and the kernel pass launch the attention kernel)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-mib", type=int, default=0)
+    ap.add_argument("--read-sweep", action="store_true",
+                    help="instead: the plain streaming read of the workload's K/V bytes over a "
+                         "grid of load shapes (workgroups, threads, loads in flight, width)")
     return ap.parse_args()
 
 
@@ -208,6 +211,44 @@ def read_ceiling(torch, nbytes, copies, steps, stream):
     ms_big, wg_big = best(lambda i, g: rd(big, g), 3, 20)
     del bufs, big
     return ms, ms_big, wg, wg_big
+
+
+def read_sweep(torch, w, copies, steps):
+    """The plain streaming read (qkv_measure_read_config) of the workload's
+    per-step K/V pack bytes, rotating over 'copies' buffers, for every load
+    shape of a grid; prints one line per shape, fastest first."""
+    import ctypes
+    from quantized_kv_cache_amd import _lib
+    lib = _lib.load()
+    stream = torch.cuda.current_stream()
+    nbytes = (pack_bytes(w, w.L) + 15) // 16 * 16
+    bufs = [torch.ones(nbytes, dtype=torch.uint8, device="cuda") for _ in range(copies)]
+    sink = torch.empty(8192 * 16, dtype=torch.int32, device="cuda")
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    rows = []
+    for width in (16, 8, 4):
+        for threads in (256, 512, 1024):
+            for u in (1, 2, 4, 8, 16):
+                for wgs in (256, 512, 1024, 2048, 4096, 8192):
+                    def rd(i, wgs=wgs, threads=threads, u=u, width=width):
+                        t = bufs[i % copies]
+                        st = lib.qkv_measure_read_config(ctypes.c_void_p(t.data_ptr()), nbytes, wgs,
+                                                         threads, u, width,
+                                                         ctypes.c_void_p(sink.data_ptr()), sp)
+                        if st != _lib.QKV_OK:
+                            raise RuntimeError(lib.qkv_last_error().decode())
+                    for i in range(copies):
+                        rd(i)
+                    ms = time_region(torch, rd, 0, steps, stream)
+                    rows.append((ms * 1e3, wgs, threads, u, width))
+        print(f"# width {width} done", flush=True)
+    rows.sort()
+    print(f"# plain read of {nbytes} bytes per launch ({w.name} K/V packs), rotating over "
+          f"{copies} buffers, {steps} launches per shape; us per launch and TB/s")
+    print(f"{'us':>8} {'TB/s':>6} {'frac_8TB':>8} {'wgs':>5} {'threads':>7} {'in_flight':>9} {'width':>5}")
+    for us, wgs, threads, u, width in rows:
+        print(f"{us:8.2f} {nbytes / us / 1e6:6.3f} {nbytes / us / 1e6 / 8.0:8.3f} {wgs:5d} {threads:7d} "
+              f"{u:9d} {width:5d}")
 
 
 def call_latency(torch, run, first, n, stream):
@@ -308,6 +349,10 @@ def main():
     w = W.WORKLOADS[args.workload]
     torch.cuda.set_device(0)
     stream = torch.cuda.current_stream()
+    if args.read_sweep:
+        per = pack_bytes(w, w.cap)
+        R = args.copies or min(MAX_COPIES, max(1, -(-2 * MALL_BYTES // per)))
+        return read_sweep(torch, w, R, args.steps)
     inp, ks, vs, R = make_caches(w, qkv, W, args.copies)
     ws = qkv.Workspace()
 

@@ -33,6 +33,18 @@ extern "C" {
 qkv_status qkv_measure_read(const void* buf, size_t bytes, int32_t workgroups, uint32_t* sink,
                             void* stream);
 
+/* The same plain read with its shape chosen by the caller, to sweep the
+ * read rate over load shapes: 'threads' per workgroup (64, 128, ..., 1024),
+ * 'in_flight' loads per thread issued before any is used (1, 2, 4, 8 or 16),
+ * each 'width' bytes wide (4, 8 or 16); workgroup w reads the w-th of
+ * 'workgroups' contiguous, equal ranges.  'sink' must hold
+ * workgroups * threads / 64 words.  Errors: EINVAL for null pointers, bytes
+ * = 0 or not a multiple of 'width', 'buf' not 'width'-aligned, or any
+ * parameter outside the sets above (workgroups in [1,
+ * QKV_MEASURE_MAX_WORKGROUPS]); EHIP if the launch fails. */
+qkv_status qkv_measure_read_config(const void* buf, size_t bytes, int32_t workgroups, int32_t threads,
+                                   int32_t in_flight, int32_t width, uint32_t* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

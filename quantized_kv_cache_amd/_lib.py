@@ -13,13 +13,14 @@ STATUS_NAMES = {0: "QKV_OK", 1: "QKV_EINVAL", 2: "QKV_EUNSUPPORTED", 3: "QKV_EWO
 QKV_F32, QKV_F16, QKV_BF16 = 0, 1, 2
 QKV_AFFINE, QKV_Q8_0 = 0, 1
 QKV_MASK_NONE, QKV_MASK_CAUSAL, QKV_MASK_ADDITIVE = 0, 1, 2
-QKV_ALGO_AUTO, QKV_ALGO_GENERIC, QKV_ALGO_MATRIX = 0, 1, 2
+QKV_ALGO_AUTO, QKV_ALGO_GENERIC, QKV_ALGO_MATRIX, QKV_ALGO_UNFUSED = 0, 1, 2, 3
 QKV_KERNEL_GENERIC, QKV_KERNEL_DECODE, QKV_KERNEL_DECODE_NARROW, QKV_KERNEL_PREFILL = 0, 1, 2, 3
+QKV_KERNEL_UNFUSED = 4
 
 # every symbol include/qkv.h declares
 EXPORTS = ["qkv_quantize", "qkv_update_append", "qsdpa_workspace_bytes", "qsdpa_workspace_reset",
            "qsdpa_plan", "qsdpa_decode", "qsdpa_decode_static", "qsdpa_prefill", "qkv_last_error",
-           "qkv_abi_version", "qkv_measure_read"]
+           "qkv_abi_version", "qkv_measure_read", "qkv_measure_read_config"]
 QKV_TICKET_BYTES = 262144
 QKV_STATIC_SCRATCH_BYTES = QKV_TICKET_BYTES + 16 * 1024 * 1024
 
@@ -93,6 +94,8 @@ def load():
     L.qkv_abi_version.restype = I32
     L.qkv_measure_read.argtypes = [P, SZ, I32, P, P]      # include/qkv_measure.h
     L.qkv_measure_read.restype = I32
+    L.qkv_measure_read_config.argtypes = [P, SZ, I32, I32, I32, I32, P, P]
+    L.qkv_measure_read_config.restype = I32
     _lib = L
     return L
 

@@ -18,6 +18,8 @@ namespace qkv {
 // Plain streaming read of a device buffer (qkv_measure.hip).
 hipError_t launch_measure_read(const void* buf, size_t bytes, int workgroups, uint32_t* sink,
                                hipStream_t stream);
+hipError_t launch_measure_read_config(const void* buf, size_t bytes, int workgroups, int threads, int in_flight,
+                                      int width, uint32_t* sink, hipStream_t stream);
 }  // namespace qkv
 #include "qkv_merge.hpp"
 
@@ -151,6 +153,7 @@ qkv_status check_source(const void* x, int32_t dtype, const int64_t xs[3], const
 
 // ---------------------------------------------------------------- attention plans
 struct Plan {
+    bool unfused;                   // the four-kernel composition (QKV_ALGO_UNFUSED)
     bool matrix;
     bool prefill;                   // tiled matrix kernel
     int wg_rows;                    // its rows per workgroup
@@ -179,6 +182,10 @@ bool overlaps_pack(Range r, const qkv_pack* p) {
            (p->biases && overlap(r, scales_range(p, p->biases)));
 }
 
+size_t unfused_scores_bytes(int64_t B, int64_t Hq, int64_t L) {
+    return ((size_t)(B * Hq * L) * 4 + 255) / 256 * 256;
+}
+
 // Split count: enough workgroups to cover the CUs about twice, each split at
 // least min_keys long, and at most kMaxSplits (the merge keeps per-split
 // weights in LDS).
@@ -195,6 +202,17 @@ Plan make_plan(int64_t B, int64_t Hq, int64_t Lq, int64_t D, int64_t L, const qk
     const int G = (int)(Hq / Hk);
     const int algo = opts ? opts->algo : QKV_ALGO_AUTO;
     const int bits = k->bits;
+    if (algo == QKV_ALGO_UNFUSED) {
+        // scores [B Hq][L], then the P V sums of every key chunk
+        pl.unfused = true;
+        pl.RT = 16;
+        pl.n_rt = 1;
+        pl.wg_rows = 0;
+        pl.chunk = qkv::unfused_chunk_keys(B, Hk, L, G);
+        pl.S = (int)((L + pl.chunk - 1) / pl.chunk);
+        pl.ws_bytes = unfused_scores_bytes(B, Hq, L) + (size_t)pl.S * (size_t)(B * Hq * D) * 4;
+        return pl;
+    }
     pl.matrix = false;
     pl.prefill = false;
     pl.narrow = false;
@@ -275,8 +293,11 @@ qkv_status attention(const char* name, const void* q, int32_t q_dtype, int64_t B
     }
     if (mask_kind == QKV_MASK_CAUSAL && L < Lq)
         return fail(QKV_EINVAL, "%s: causal mask needs L >= Lq", name);
-    if (opts && (opts->num_splits < 0 || opts->algo < 0 || opts->algo > QKV_ALGO_MATRIX))
+    if (opts && (opts->num_splits < 0 || opts->algo < 0 || opts->algo > QKV_ALGO_UNFUSED))
         return fail(QKV_EINVAL, "%s: bad options", name);
+    if (opts && opts->algo == QKV_ALGO_UNFUSED && (Lq != 1 || G > 16))
+        return fail(QKV_EUNSUPPORTED, "%s: the unfused composition takes one query per head and a GQA "
+                    "factor of at most 16", name);
     const size_t qe = dtype_size(q_dtype);
     if (!aligned(q, qe) || !aligned(out, qe)) return fail(QKV_EINVAL, "%s: q/out misaligned", name);
     const size_t qbytes = (size_t)(B * Hq * Lq * D) * qe;
@@ -346,7 +367,13 @@ qkv_status attention(const char* name, const void* q, int32_t q_dtype, int64_t B
     a.n_rt = pl.n_rt;
     a.wg_rows = pl.wg_rows;
     a.RT = pl.RT;
-    if (pl.ws_bytes > 0) {
+    if (pl.unfused) {
+        a.un_scores = static_cast<float*>(workspace);
+        a.un_partial = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) +
+                                                unfused_scores_bytes(B, Hq, L));
+        a.un_chunks = pl.S;
+        a.un_chunk = pl.chunk;
+    } else if (pl.ws_bytes > 0) {
         const int64_t tiles = B * k->H * pl.n_rt;
         a.tickets = static_cast<uint32_t*>(workspace);
         a.part_ml = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + qkv::kTicketBytes);
@@ -358,13 +385,14 @@ qkv_status attention(const char* name, const void* q, int32_t q_dtype, int64_t B
         hipError_t te = hipEventRecord(static_cast<hipEvent_t>(opts->timing_events[0]), s);
         if (te != hipSuccess) return hip_status(te, name);
     }
-    hipError_t e = pl.prefill  ? qkv::launch_prefill_matrix(k->mode, k->bits, (int)D, B, a, s)
+    hipError_t e = pl.unfused  ? qkv::launch_attn_unfused(q_dtype, k->mode, k->bits, (int)D, B, a, s)
+                   : pl.prefill  ? qkv::launch_prefill_matrix(k->mode, k->bits, (int)D, B, a, s)
                    : pl.narrow ? qkv::launch_attn_narrow(k->mode, k->bits, (int)D, B, a, s)
                    : pl.matrix ? qkv::launch_attn_matrix(k->mode, k->bits, (int)D, B, a, s)
                                : qkv::launch_attn_generic(q_dtype, k->mode, k->bits, (int)D, B, a, s);
     if (e == hipSuccess && timed) e = hipEventRecord(static_cast<hipEvent_t>(opts->timing_events[1]), s);
     // the narrow decode kernel merges its splits itself
-    if (e == hipSuccess && pl.S > 1 && !pl.narrow) e = qkv::launch_merge(q_dtype, (int)D, B, a, s);
+    if (e == hipSuccess && pl.S > 1 && !pl.narrow && !pl.unfused) e = qkv::launch_merge(q_dtype, (int)D, B, a, s);
     return hip_status(e, name);
 }
 
@@ -431,10 +459,11 @@ qkv_status qsdpa_plan(int64_t B, int64_t Hq, int64_t Lq, int64_t D, int64_t L, c
     if (k->H < 1 || B < 1 || Hq < 1 || Lq < 1 || L < 1 || Hq % k->H)
         return fail(QKV_EINVAL, "qsdpa_plan: bad sizes");
     Plan pl = make_plan(B, Hq, Lq, D, L, k, q_dtype, opts);
-    plan->algo = pl.matrix ? QKV_ALGO_MATRIX : QKV_ALGO_GENERIC;
+    plan->algo = pl.unfused ? QKV_ALGO_UNFUSED : pl.matrix ? QKV_ALGO_MATRIX : QKV_ALGO_GENERIC;
     plan->num_splits = pl.S;
     plan->row_tile = pl.prefill ? pl.wg_rows : pl.RT;
-    plan->kernel = !pl.matrix  ? QKV_KERNEL_GENERIC
+    plan->kernel = pl.unfused   ? QKV_KERNEL_UNFUSED
+                   : !pl.matrix ? QKV_KERNEL_GENERIC
                    : pl.prefill ? QKV_KERNEL_PREFILL
                    : pl.narrow  ? QKV_KERNEL_DECODE_NARROW
                                 : QKV_KERNEL_DECODE;
@@ -491,6 +520,25 @@ qkv_status qkv_measure_read(const void* buf, size_t bytes, int32_t workgroups, u
                     QKV_MEASURE_MAX_WORKGROUPS);
     return hip_status(qkv::launch_measure_read(buf, bytes, workgroups, sink, static_cast<hipStream_t>(stream)),
                       "qkv_measure_read");
+}
+
+qkv_status qkv_measure_read_config(const void* buf, size_t bytes, int32_t workgroups, int32_t threads,
+                                   int32_t in_flight, int32_t width, uint32_t* sink, void* stream) {
+    if (!buf || !sink) return fail(QKV_EINVAL, "qkv_measure_read_config: null pointer");
+    if (width != 4 && width != 8 && width != 16)
+        return fail(QKV_EINVAL, "qkv_measure_read_config: width %d not in {4, 8, 16}", width);
+    if (bytes == 0 || bytes % (size_t)width || !aligned(buf, (size_t)width))
+        return fail(QKV_EINVAL, "qkv_measure_read_config: bytes and buf must be multiples of the width");
+    if (threads < 64 || threads > 1024 || threads % 64)
+        return fail(QKV_EINVAL, "qkv_measure_read_config: threads=%d not a multiple of 64 in [64, 1024]", threads);
+    if (in_flight != 1 && in_flight != 2 && in_flight != 4 && in_flight != 8 && in_flight != 16)
+        return fail(QKV_EINVAL, "qkv_measure_read_config: in_flight=%d not in {1, 2, 4, 8, 16}", in_flight);
+    if (workgroups < 1 || workgroups > QKV_MEASURE_MAX_WORKGROUPS)
+        return fail(QKV_EINVAL, "qkv_measure_read_config: workgroups=%d outside [1, %d]", workgroups,
+                    QKV_MEASURE_MAX_WORKGROUPS);
+    return hip_status(qkv::launch_measure_read_config(buf, bytes, workgroups, threads, in_flight, width, sink,
+                                                      static_cast<hipStream_t>(stream)),
+                      "qkv_measure_read_config");
 }
 
 const char* qkv_last_error(void) { return g_last_error.c_str(); }

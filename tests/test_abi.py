@@ -223,3 +223,17 @@ def test_workspace_reset_rejects(L):
     assert L.qsdpa_workspace_reset(FAKE + 16, _lib.QKV_TICKET_BYTES, None) == _lib.QKV_EINVAL
     assert L.qsdpa_workspace_reset(FAKE, _lib.QKV_TICKET_BYTES - 256, None) == _lib.QKV_EINVAL
     assert "ticket header" in L.qkv_last_error().decode()
+
+
+def test_measure_read_config_rejects_bad_arguments(L):
+    sink = FAKE + 0x400000
+    good = dict(buf=FAKE, nbytes=4096, wgs=64, threads=256, u=4, width=16, snk=sink)
+    bad = [dict(buf=0), dict(snk=0), dict(width=2), dict(nbytes=4100), dict(buf=FAKE + 8),
+           dict(threads=100), dict(threads=2048), dict(u=3), dict(u=32), dict(wgs=0),
+           dict(wgs=8193), dict(nbytes=0)]
+    for b in bad:
+        a = dict(good, **b)
+        st = L.qkv_measure_read_config(a["buf"], a["nbytes"], a["wgs"], a["threads"], a["u"],
+                                       a["width"], a["snk"], None)
+        assert st == _lib.QKV_EINVAL, b
+        assert L.qkv_last_error()
