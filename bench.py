@@ -112,7 +112,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="decode_64k_4bit_gqa4")
-    ap.add_argument("--algo", default="auto", choices=["auto", "generic", "matrix"])
+    ap.add_argument("--algo", default="auto", choices=["auto", "generic", "matrix", "unfused"],
+                    help="kernel choice; 'unfused' times the four-kernel composition and also "
+                         "the fused decode of the same workload in the same job")
     ap.add_argument("--splits", type=int, default=0)
     ap.add_argument("--copies", type=int, default=0, help="cache copies (0 = enough for 512 MB)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -448,6 +450,16 @@ def main():
                            "unit": "TFLOP/s", "frac": round(tf / MFMA_F16_PEAK_TFLOPS, 4),
                            "traffic": traffic, "kernel": kernel,
                            "kernel_us": round(kms * 1e3, 3), "algorithmic_flops": flops}
+    if args.algo == "unfused" and not w.steps:
+        # the fused decode of the same inputs, timed the same way in this job
+        fused = [qkv.PreparedAttention(q0, ks[c], vs[c], w.L, w.scale, torch.empty_like(q0),
+                                       causal=w.causal, workspace=ws) for c in range(R)]
+        for i in range(args.warmup):
+            fused[i % R]()
+        fms = time_region(torch, lambda i: fused[i % R](), 0, args.steps, stream)
+        rec["vs_fused"] = {"fused_us_per_step": round(fms * 1e3, 3),
+                           "fused_kernel": qkv.qsdpa_plan(q0, ks[0], w.L)["kernel"],
+                           "unfused_over_fused": round(ms / fms, 3)}
     if not args.no_extras:
         rd_ms, big_ms, rd_wg, big_wg = read_ceiling(torch, pack_bytes(w, w.L), R, args.steps, stream)
         rd_gbs = pack_bytes(w, w.L) / (rd_ms * 1e-3) / 1e9

@@ -78,8 +78,17 @@ typedef enum { QKV_MASK_NONE = 0, QKV_MASK_CAUSAL = 1, QKV_MASK_ADDITIVE = 2 } q
 
 /* Kernel selection for the attention calls.  AUTO picks the fastest kernel
  * instantiated for the arguments; GENERIC is the plain vector kernel (every
- * supported combination); MATRIX uses the gfx950 matrix cores (fp16 queries). */
-typedef enum { QKV_ALGO_AUTO = 0, QKV_ALGO_GENERIC = 1, QKV_ALGO_MATRIX = 2 } qkv_algo;
+ * supported combination); MATRIX uses the gfx950 matrix cores (fp16 queries).
+ * UNFUSED (decode only, GQA factor <= 16) runs the composition that the MLX
+ * page "add fast::quantized_kv_update" gives as the fallback of
+ * quantized_scaled_dot_product_attention (mlx/fast.cpp) and times against the
+ * fused kernel in sdpa_vector_bench.py (quant_attention): a quantized
+ * matrix-vector product q K^T into an fp32 score buffer, a softmax over each
+ * row, and a quantized vector-matrix product P V split over key chunks
+ * (qvm_split_k on the MLX 1.0.0 Metal host page), then the sum of the
+ * chunks, as four kernels; its workspace holds the scores and the chunk sums. */
+typedef enum { QKV_ALGO_AUTO = 0, QKV_ALGO_GENERIC = 1, QKV_ALGO_MATRIX = 2,
+               QKV_ALGO_UNFUSED = 3 } qkv_algo;
 
 typedef struct {
     int32_t mode;          /* qkv_mode */
@@ -165,13 +174,15 @@ typedef enum {
     QKV_KERNEL_GENERIC = 0,        /* any dtype / format, CUDA-core arithmetic */
     QKV_KERNEL_DECODE = 1,         /* single query, fp16, GQA factor <= 16, 16x16x32 MFMA */
     QKV_KERNEL_DECODE_NARROW = 2,  /* single query, fp16, GQA factor <= 4, 4x4x4 MFMA */
-    QKV_KERNEL_PREFILL = 3         /* 64-row tiles, fp16, K/V dequantized into LDS */
+    QKV_KERNEL_PREFILL = 3,        /* 64-row tiles, fp16, K/V dequantized into LDS */
+    QKV_KERNEL_UNFUSED = 4         /* scores, softmax, P V, chunk sum: four kernels */
 } qkv_kernel;
 
 /* The launch plan an attention call with these arguments would use:
- * the algorithm class (QKV_ALGO_GENERIC or QKV_ALGO_MATRIX) and the kernel
- * (qkv_kernel), the key splits, the (GQA-packed) query rows per workgroup
- * and the workspace size.  Errors: EINVAL for null pointers or shapes that
+ * the algorithm class (QKV_ALGO_GENERIC, QKV_ALGO_MATRIX or
+ * QKV_ALGO_UNFUSED) and the kernel (qkv_kernel), the key splits (for the
+ * unfused composition: the key chunks of its P V product), the (GQA-packed)
+ * query rows per workgroup and the workspace size.  Errors: EINVAL for null pointers or shapes that
  * the attention calls would reject as such. */
 typedef struct {
     int32_t algo;

@@ -23,7 +23,7 @@ from ._lib import QKVError  # noqa: F401
 _DT = {torch.float32: _lib.QKV_F32, torch.float16: _lib.QKV_F16, torch.bfloat16: _lib.QKV_BF16}
 _DT_NAME = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
 _ALGO = {"auto": _lib.QKV_ALGO_AUTO, "generic": _lib.QKV_ALGO_GENERIC,
-         "matrix": _lib.QKV_ALGO_MATRIX}
+         "matrix": _lib.QKV_ALGO_MATRIX, "unfused": _lib.QKV_ALGO_UNFUSED}
 
 
 def torch_dtype(name_or_dtype) -> torch.dtype:
@@ -155,7 +155,7 @@ def qsdpa_workspace_bytes(q: torch.Tensor, k: Pack, L: int, num_splits: int = 0,
 
 # kernel names of qsdpa_plan()["kernel"] (the device function names)
 KERNEL_NAMES = {0: "attn_generic_kernel", 1: "attn_matrix_decode", 2: "attn_decode_narrow",
-                3: "attn_matrix_prefill"}
+                3: "attn_matrix_prefill", 4: "unfused_scores_kernel"}
 
 
 def qsdpa_plan(q: torch.Tensor, k: Pack, L: int, num_splits: int = 0,
@@ -166,7 +166,7 @@ def qsdpa_plan(q: torch.Tensor, k: Pack, L: int, num_splits: int = 0,
     st = _lib.load().qsdpa_plan(B, Hq, Lq, D, L, ctypes.byref(k.c_struct()), _dt(q),
                                 ctypes.byref(_opts(num_splits, algo)), ctypes.byref(pl))
     _lib.check(st)
-    return {"algo": {1: "generic", 2: "matrix"}[pl.algo], "num_splits": pl.num_splits,
+    return {"algo": {1: "generic", 2: "matrix", 3: "unfused"}[pl.algo], "num_splits": pl.num_splits,
             "row_tile": pl.row_tile, "keys_per_split": pl.keys_per_split,
             "workspace_bytes": pl.workspace_bytes, "kernel": KERNEL_NAMES[pl.kernel]}
 

@@ -185,6 +185,9 @@ bool overlaps_pack(Range r, const qkv_pack* p) {
 size_t unfused_scores_bytes(int64_t B, int64_t Hq, int64_t L) {
     return ((size_t)(B * Hq * L) * 4 + 255) / 256 * 256;
 }
+size_t unfused_stats_bytes(int64_t B, int64_t Hq, int64_t L) {
+    return ((size_t)qkv::unfused_stats_floats(B, Hq, L) * 4 + 255) / 256 * 256;
+}
 
 // Split count: enough workgroups to cover the CUs about twice, each split at
 // least min_keys long, and at most kMaxSplits (the merge keeps per-split
@@ -210,7 +213,8 @@ Plan make_plan(int64_t B, int64_t Hq, int64_t Lq, int64_t D, int64_t L, const qk
         pl.wg_rows = 0;
         pl.chunk = qkv::unfused_chunk_keys(B, Hk, L, G);
         pl.S = (int)((L + pl.chunk - 1) / pl.chunk);
-        pl.ws_bytes = unfused_scores_bytes(B, Hq, L) + (size_t)pl.S * (size_t)(B * Hq * D) * 4;
+        pl.ws_bytes = unfused_scores_bytes(B, Hq, L) + unfused_stats_bytes(B, Hq, L) +
+                      (size_t)pl.S * (size_t)(B * Hq * D) * 4;
         return pl;
     }
     pl.matrix = false;
@@ -295,9 +299,9 @@ qkv_status attention(const char* name, const void* q, int32_t q_dtype, int64_t B
         return fail(QKV_EINVAL, "%s: causal mask needs L >= Lq", name);
     if (opts && (opts->num_splits < 0 || opts->algo < 0 || opts->algo > QKV_ALGO_UNFUSED))
         return fail(QKV_EINVAL, "%s: bad options", name);
-    if (opts && opts->algo == QKV_ALGO_UNFUSED && (Lq != 1 || G > 16))
-        return fail(QKV_EUNSUPPORTED, "%s: the unfused composition takes one query per head and a GQA "
-                    "factor of at most 16", name);
+    if (opts && opts->algo == QKV_ALGO_UNFUSED && (Lq != 1 || G > 16 || B * Hq > 65535))
+        return fail(QKV_EUNSUPPORTED, "%s: the unfused composition takes one query per head, a GQA "
+                    "factor of at most 16 and B x Hq below 65536", name);
     const size_t qe = dtype_size(q_dtype);
     if (!aligned(q, qe) || !aligned(out, qe)) return fail(QKV_EINVAL, "%s: q/out misaligned", name);
     const size_t qbytes = (size_t)(B * Hq * Lq * D) * qe;
@@ -368,9 +372,11 @@ qkv_status attention(const char* name, const void* q, int32_t q_dtype, int64_t B
     a.wg_rows = pl.wg_rows;
     a.RT = pl.RT;
     if (pl.unfused) {
-        a.un_scores = static_cast<float*>(workspace);
-        a.un_partial = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) +
-                                                unfused_scores_bytes(B, Hq, L));
+        uint8_t* w8 = static_cast<uint8_t*>(workspace);
+        a.un_scores = reinterpret_cast<float*>(w8);
+        a.un_stats = reinterpret_cast<float*>(w8 + unfused_scores_bytes(B, Hq, L));
+        a.un_partial = reinterpret_cast<float*>(w8 + unfused_scores_bytes(B, Hq, L) +
+                                                unfused_stats_bytes(B, Hq, L));
         a.un_chunks = pl.S;
         a.un_chunk = pl.chunk;
     } else if (pl.ws_bytes > 0) {

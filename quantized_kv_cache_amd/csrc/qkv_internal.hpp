@@ -58,6 +58,12 @@ struct AttnLaunch {
     float* part_ml;                 // [B*Hk*n_rt][S][16][2] (m, l) of each split
     float* part_o;                  // [B*Hk*n_rt][S][16][D] unnormalised o of each split
     uint32_t* tickets;              // [B*Hk*n_rt] fused-merge tickets (zero between calls)
+    // unfused composition (launch_attn_unfused)
+    float* un_scores;               // [B*Hq][L] scores, then probabilities
+    float* un_stats;                // [B*Hq][L/4096 chunks] (m, l) of the softmax
+    float* un_partial;              // [un_chunks][B*Hq][D] P V sums per key chunk
+    int32_t un_chunks;              // key chunks of the P V product
+    int64_t un_chunk;               // keys per chunk
 };
 
 // Launchers (return hipGetLastError() of the launch).
@@ -96,6 +102,16 @@ bool narrow_decode_supported(int q_dtype, int mode, int bits, int group_size, in
 int narrow_decode_key_quantum();
 hipError_t launch_attn_narrow(int mode, int bits, int D, int64_t B, const AttnLaunch& p,
                               hipStream_t stream);
+
+// The unfused composition for one query per head (scores, softmax, P V over
+// key chunks, sum of the chunks): fp32/fp16/bf16 queries, affine 4/8-bit or
+// Q8_0 caches, D in {64, 128, 256}, G <= 16.  unfused_chunk_keys gives the
+// keys per P V chunk (a power of two in [64, 1024], G rounded up to a power
+// of two times it at most 4096).
+int unfused_chunk_keys(int64_t B, int64_t Hk, int64_t L, int G);
+int64_t unfused_stats_floats(int64_t B, int64_t Hq, int64_t L);
+hipError_t launch_attn_unfused(int q_dtype, int mode, int bits, int D, int64_t B, const AttnLaunch& p,
+                               hipStream_t stream);
 
 // The device address of this GPU's static split workspace
 // (QKV_STATIC_SCRATCH_BYTES, its ticket header zeroed on 'stream' at the first
