@@ -59,6 +59,8 @@ METRIC = "qsdpa_decode µs/step + achieved HBM GB/s (% peak), L=64K 4-bit GQA-4"
 def pack_bytes(w, L) -> int:
     """Algorithmic bytes of the K and V packs over L tokens of every (b, kv head)."""
     rows = w.B * w.Hk * L
+    if w.mode == "dense":
+        return 2 * rows * w.D * 2
     if w.mode == "q8_0":
         per = w.D + 2 * (w.D // 32)
     else:
@@ -112,7 +114,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="decode_64k_4bit_gqa4")
-    ap.add_argument("--algo", default="auto", choices=["auto", "generic", "matrix", "unfused"],
+    ap.add_argument("--algo", default="auto",
+                    choices=["auto", "generic", "matrix", "unfused", "dequant_f16"],
                     help="kernel choice; 'unfused' times the four-kernel composition and also "
                          "the fused decode of the same workload in the same job")
     ap.add_argument("--splits", type=int, default=0)
@@ -130,7 +133,8 @@ def parse():
 
 
 def clone_pack(qkv, p):
-    return qkv.Pack(p.mode, p.bits, p.group_size, p.D, p.codes.clone(), p.scales.clone(),
+    return qkv.Pack(p.mode, p.bits, p.group_size, p.D, p.codes.clone(),
+                    None if p.scales is None else p.scales.clone(),
                     None if p.biases is None else p.biases.clone())
 
 
@@ -280,6 +284,22 @@ def cpu_baseline(w, inp, budget_s):
     import oracle as orc
     from tests._cases import oracle_attention, oracle_pack
     from quantized_kv_cache_amd import workloads as W
+    if w.mode == "dense":
+        # the unquantized cache: fp64 attention over its fp16 values
+        n, t0 = 0, time.perf_counter()
+        while True:
+            orc.attention(orc.to_f32(inp["q"], w.dtype), orc.to_f32(inp["k"], w.dtype),
+                          orc.to_f32(inp["v"], w.dtype), w.scale)
+            n += 1
+            el = time.perf_counter() - t0
+            if el >= budget_s or n >= 50:
+                break
+        sec = el / n
+        alg = pack_bytes(w, w.L) + 2 * q_bytes(w)
+        return {"value": round(alg / sec / 1e9, 4), "unit": "GB/s", "cores": orc.num_threads(),
+                "kind": "oracle",
+                "sample": f"{n} x decode step of {w.name}, {sec * 1e3:.1f} ms each; the same "
+                          f"algorithmic bytes per unit of work as the GPU figure"}
     kr = oracle_pack(inp["k"], w.dtype, w.mode, w.bits, w.group_size)
     vr = oracle_pack(inp["v"], w.dtype, w.mode, w.bits, w.group_size)
     q, L, mask, causal = inp["q"], w.L, None, w.causal
@@ -426,7 +446,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f16" if plan["algo"] == "matrix" else "f32",
+        "dtype": "f16" if plan["algo"] in ("matrix", "dequant_f16") else "f32",
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hk": w.Hk, "D": w.D, "L": w.L,
                    "Lq": w.Lq, "mode": w.mode, "bits": w.bits, "group_size": w.group_size,

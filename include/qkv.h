@@ -40,6 +40,12 @@
  *  d == 0); the value is d * c.  Codes are stored one byte per value in a
  *  codes plane, scales in a separate plane (biases == NULL).
  *
+ *  QKV_DENSE: the unquantized cache the pages compare against (the dense
+ *  fp16 K/V of the MLX benchmark's sdpa baseline, sdpa_vector_bench.py; the
+ *  F16 KV cache and the F16 scratch copies of the llama.cpp page): codes hold
+ *  fp16 values, one per element (bits 16, group_size D, scale_dtype QKV_F16,
+ *  scales and biases NULL).  Attention over dense packs takes fp16 queries.
+ *
  *  Layout of a pack with B batches, H heads, capacity L_cap, head size D:
  *    codes  : row r at byte offset r * row_bytes, row_bytes = D*bits/8
  *    scales : row r at element offset r * (D / group_size)
@@ -62,7 +68,7 @@
 extern "C" {
 #endif
 
-#define QKV_ABI_VERSION 3
+#define QKV_ABI_VERSION 4
 
 typedef enum {
     QKV_OK = 0,
@@ -73,7 +79,7 @@ typedef enum {
 } qkv_status;
 
 typedef enum { QKV_F32 = 0, QKV_F16 = 1, QKV_BF16 = 2 } qkv_dtype;
-typedef enum { QKV_AFFINE = 0, QKV_Q8_0 = 1 } qkv_mode;
+typedef enum { QKV_AFFINE = 0, QKV_Q8_0 = 1, QKV_DENSE = 2 } qkv_mode;
 typedef enum { QKV_MASK_NONE = 0, QKV_MASK_CAUSAL = 1, QKV_MASK_ADDITIVE = 2 } qkv_mask_kind;
 
 /* Kernel selection for the attention calls.  AUTO picks the fastest kernel
@@ -86,9 +92,14 @@ typedef enum { QKV_MASK_NONE = 0, QKV_MASK_CAUSAL = 1, QKV_MASK_ADDITIVE = 2 } q
  * matrix-vector product q K^T into an fp32 score buffer, a softmax over each
  * row, and a quantized vector-matrix product P V split over key chunks
  * (qvm_split_k on the MLX 1.0.0 Metal host page), then the sum of the
- * chunks, as four kernels; its workspace holds the scores and the chunk sums. */
+ * chunks, as four kernels; its workspace holds the scores and the chunk sums.
+ * DEQUANT_F16 (fp16 queries, affine caches with fp16 scales or Q8_0) is the
+ * strategy of the llama.cpp page "Metal: Optimize q8_0 KV - #25556" (merged
+ * #27390, kernel_flash_attn_ext_dequant_to_f16): K and V rows [0, L) are
+ * first dequantized into dense fp16 copies in the workspace (qkv_dequantize),
+ * then the dense matrix-core attention runs on them. */
 typedef enum { QKV_ALGO_AUTO = 0, QKV_ALGO_GENERIC = 1, QKV_ALGO_MATRIX = 2,
-               QKV_ALGO_UNFUSED = 3 } qkv_algo;
+               QKV_ALGO_UNFUSED = 3, QKV_ALGO_DEQUANT_F16 = 4 } qkv_algo;
 
 typedef struct {
     int32_t mode;          /* qkv_mode */
@@ -142,6 +153,18 @@ qkv_status qkv_quantize(const void* x, int32_t x_dtype, const int64_t x_strides[
 qkv_status qkv_update_append(const void* k_new, const void* v_new, int32_t dtype,
                              const int64_t new_strides[3], int64_t T, int64_t offset,
                              const qkv_pack* k_cache, const qkv_pack* v_cache, void* stream);
+
+/* Dequantize rows [0, L) of every (b, h) of a quantized pack into a dense
+ * fp16 pack of the same B, H, D (L <= both capacities): element j of a row
+ * becomes fp16(fp32(s) * c + fp32(b)) (affine, the product and the sum each
+ * rounded in fp32, then rounded to fp16) or fp16(fp32(d) * c) (Q8_0) -- the
+ * dequantization of the MLX page "add fast::quantized_kv_update"
+ * (kernels/quantized.h: scale * code + bias) stored as the fp16 copy of the
+ * llama.cpp page "Metal: Optimize q8_0 KV - #25556" (merged #27390,
+ * kernel_flash_attn_ext_dequant_to_f16).  src must be AFFINE with fp16
+ * scales, or Q8_0.  Errors: EINVAL (pack checks, dst not DENSE, shape
+ * mismatch, L outside [0, capacity], src and dst overlapping), EUNSUPPORTED. */
+qkv_status qkv_dequantize(const qkv_pack* src, int64_t L, const qkv_pack* dst, void* stream);
 
 /* Bytes of workspace the attention calls need for these sizes (0 when no
  * key partitioning is used): a ticket header of QKV_TICKET_BYTES (one 32-bit

@@ -11,14 +11,14 @@ QKV_OK, QKV_EINVAL, QKV_EUNSUPPORTED, QKV_EWORKSPACE, QKV_EHIP = range(5)
 STATUS_NAMES = {0: "QKV_OK", 1: "QKV_EINVAL", 2: "QKV_EUNSUPPORTED", 3: "QKV_EWORKSPACE",
                 4: "QKV_EHIP"}
 QKV_F32, QKV_F16, QKV_BF16 = 0, 1, 2
-QKV_AFFINE, QKV_Q8_0 = 0, 1
+QKV_AFFINE, QKV_Q8_0, QKV_DENSE = 0, 1, 2
 QKV_MASK_NONE, QKV_MASK_CAUSAL, QKV_MASK_ADDITIVE = 0, 1, 2
-QKV_ALGO_AUTO, QKV_ALGO_GENERIC, QKV_ALGO_MATRIX, QKV_ALGO_UNFUSED = 0, 1, 2, 3
+QKV_ALGO_AUTO, QKV_ALGO_GENERIC, QKV_ALGO_MATRIX, QKV_ALGO_UNFUSED, QKV_ALGO_DEQUANT_F16 = 0, 1, 2, 3, 4
 QKV_KERNEL_GENERIC, QKV_KERNEL_DECODE, QKV_KERNEL_DECODE_NARROW, QKV_KERNEL_PREFILL = 0, 1, 2, 3
 QKV_KERNEL_UNFUSED = 4
 
 # every symbol include/qkv.h declares
-EXPORTS = ["qkv_quantize", "qkv_update_append", "qsdpa_workspace_bytes", "qsdpa_workspace_reset",
+EXPORTS = ["qkv_quantize", "qkv_update_append", "qkv_dequantize", "qsdpa_workspace_bytes", "qsdpa_workspace_reset",
            "qsdpa_plan", "qsdpa_decode", "qsdpa_decode_static", "qsdpa_prefill", "qkv_last_error",
            "qkv_abi_version", "qkv_measure_read", "qkv_measure_read_config"]
 QKV_TICKET_BYTES = 262144
@@ -73,6 +73,8 @@ def load():
     L.qkv_quantize.restype = I32
     L.qkv_update_append.argtypes = [P, P, I32, I64P, I64, I64, PK, PK, P]
     L.qkv_update_append.restype = I32
+    L.qkv_dequantize.argtypes = [PK, I64, PK, P]
+    L.qkv_dequantize.restype = I32
     L.qsdpa_workspace_bytes.argtypes = [I64, I64, I64, I64, I64, PK, I32, OP]
     L.qsdpa_workspace_bytes.restype = SZ
     L.qsdpa_workspace_reset.argtypes = [P, SZ, P]

@@ -8,7 +8,7 @@ kernels behind the C ABI; there is no CPU path.
 The function names are those of the C ABI (include/qkv.h):
 ``qkv_quantize``, ``qkv_update_append``, ``qsdpa_workspace_bytes``,
 ``qsdpa_workspace_reset``, ``qsdpa_plan``, ``qsdpa_decode``,
-``qsdpa_decode_static``, ``qsdpa_prefill``.
+``qsdpa_decode_static``, ``qsdpa_prefill``, ``qkv_dequantize``.
 """
 from __future__ import annotations
 
@@ -23,7 +23,8 @@ from ._lib import QKVError  # noqa: F401
 _DT = {torch.float32: _lib.QKV_F32, torch.float16: _lib.QKV_F16, torch.bfloat16: _lib.QKV_BF16}
 _DT_NAME = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
 _ALGO = {"auto": _lib.QKV_ALGO_AUTO, "generic": _lib.QKV_ALGO_GENERIC,
-         "matrix": _lib.QKV_ALGO_MATRIX, "unfused": _lib.QKV_ALGO_UNFUSED}
+         "matrix": _lib.QKV_ALGO_MATRIX, "unfused": _lib.QKV_ALGO_UNFUSED,
+         "dequant_f16": _lib.QKV_ALGO_DEQUANT_F16}
 
 
 def torch_dtype(name_or_dtype) -> torch.dtype:
@@ -51,12 +52,13 @@ def _ptr(t: torch.Tensor | None):
 class Pack:
     """A quantized K or V cache: codes, scales and (affine) biases, each
     [B, H, L_cap, *] with rows of one token of one head."""
-    mode: str                      # "affine" | "q8_0"
+    mode: str                      # "affine" | "q8_0" | "dense"
     bits: int
     group_size: int
     D: int
-    codes: torch.Tensor            # affine: int32 words [B,H,L_cap,D*bits/32]; q8_0: int8 [B,H,L_cap,D]
-    scales: torch.Tensor           # [B,H,L_cap,D/group_size]
+    codes: torch.Tensor            # affine: int32 words [B,H,L_cap,D*bits/32]; q8_0: int8 [B,H,L_cap,D];
+                                   # dense: fp16 values [B,H,L_cap,D]
+    scales: torch.Tensor | None    # [B,H,L_cap,D/group_size] (None for dense)
     biases: torch.Tensor | None    # affine only
 
     @property
@@ -73,10 +75,18 @@ class Pack:
 
     @property
     def scale_dtype(self) -> torch.dtype:
-        return self.scales.dtype
+        return self.codes.dtype if self.scales is None else self.scales.dtype
 
     def c_struct(self) -> _lib.QkvPack:
         c, s = self.codes, self.scales
+        if self.mode == "dense":
+            if c.stride(3) != 1 or any(c.stride(i) % c.shape[3] for i in range(3)):
+                raise ValueError("pack rows must be contiguous, strides whole rows")
+            rs = [c.stride(i) // c.shape[3] for i in range(3)]
+            return _lib.QkvPack(mode=_lib.QKV_DENSE, bits=16, group_size=self.D,
+                                scale_dtype=_dt(c), B=c.shape[0], H=c.shape[1], L_cap=c.shape[2],
+                                D=self.D, codes=c.data_ptr(), scales=None, biases=None,
+                                stride_b=rs[0], stride_h=rs[1], stride_l=rs[2])
         if c.stride(3) != 1 or s.stride(3) != 1:
             raise ValueError("pack rows must be contiguous")
         if self.biases is not None and self.biases.stride() != s.stride():
@@ -100,6 +110,9 @@ def empty_pack(B: int, H: int, L_cap: int, D: int, mode: str = "affine", bits: i
                group_size: int = 64, dtype=torch.float16, device="cuda") -> Pack:
     """Allocate a zero-filled dense pack (the caller owns the memory)."""
     dtype = torch_dtype(dtype)
+    if mode == "dense":
+        return Pack("dense", 16, D, D, torch.zeros((B, H, L_cap, D), dtype=torch.float16, device=device),
+                    None, None)
     if mode == "q8_0":
         return Pack("q8_0", 8, 32, D,
                     torch.zeros((B, H, L_cap, D), dtype=torch.int8, device=device),
@@ -142,6 +155,18 @@ def qkv_update_append(k_cache: Pack, v_cache: Pack, k_new: torch.Tensor, v_new: 
     _lib.check(st)
 
 
+def qkv_dequantize(src: Pack, L: int | None = None, out: Pack | None = None) -> Pack:
+    """Rows [0, L) of a quantized pack as a dense fp16 pack (a new one of the
+    source's capacity unless ``out`` is given)."""
+    L = src.L_cap if L is None else L
+    if out is None:
+        out = empty_pack(src.B, src.H, src.L_cap, src.D, "dense", device=src.codes.device)
+    st = _lib.load().qkv_dequantize(ctypes.byref(src.c_struct()), L, ctypes.byref(out.c_struct()),
+                                    _stream(src.codes.device))
+    _lib.check(st)
+    return out
+
+
 def _opts(num_splits: int, algo: str):
     return _lib.QkvAttnOpts(num_splits=int(num_splits), algo=_ALGO[algo])
 
@@ -166,7 +191,7 @@ def qsdpa_plan(q: torch.Tensor, k: Pack, L: int, num_splits: int = 0,
     st = _lib.load().qsdpa_plan(B, Hq, Lq, D, L, ctypes.byref(k.c_struct()), _dt(q),
                                 ctypes.byref(_opts(num_splits, algo)), ctypes.byref(pl))
     _lib.check(st)
-    return {"algo": {1: "generic", 2: "matrix", 3: "unfused"}[pl.algo], "num_splits": pl.num_splits,
+    return {"algo": {1: "generic", 2: "matrix", 3: "unfused", 4: "dequant_f16"}[pl.algo], "num_splits": pl.num_splits,
             "row_tile": pl.row_tile, "keys_per_split": pl.keys_per_split,
             "workspace_bytes": pl.workspace_bytes, "kernel": KERNEL_NAMES[pl.kernel]}
 

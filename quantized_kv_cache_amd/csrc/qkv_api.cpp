@@ -77,19 +77,31 @@ Range codes_range(const qkv_pack* p) {
     return {lo, lo + (uintptr_t)((max_row(p) + 1) * row_bytes(p))};
 }
 Range scales_range(const qkv_pack* p, const void* base) {
+    if (!base) return {0, 0};
     uintptr_t lo = reinterpret_cast<uintptr_t>(base);
     return {lo, lo + (uintptr_t)((max_row(p) + 1) * groups_per_row(p) * dtype_size(p->scale_dtype))};
 }
 
 qkv_status check_pack(const qkv_pack* p, const char* name) {
     if (!p) return fail(QKV_EINVAL, "%s: null pack", name);
-    if (p->mode != QKV_AFFINE && p->mode != QKV_Q8_0)
+    if (p->mode != QKV_AFFINE && p->mode != QKV_Q8_0 && p->mode != QKV_DENSE)
         return fail(QKV_EINVAL, "%s: unknown mode %d", name, p->mode);
     if (p->B < 1 || p->H < 1 || p->L_cap < 1 || p->D < 1)
         return fail(QKV_EINVAL, "%s: B, H, L_cap and D must be >= 1", name);
     if (p->stride_b < 0 || p->stride_h < 0 || p->stride_l < 0)
         return fail(QKV_EINVAL, "%s: negative stride", name);
-    if (!p->codes || !p->scales) return fail(QKV_EINVAL, "%s: null codes or scales", name);
+    if (!p->codes) return fail(QKV_EINVAL, "%s: null codes", name);
+    if (p->mode == QKV_DENSE) {
+        if (p->bits != 16 || p->scale_dtype != QKV_F16 || p->group_size != p->D)
+            return fail(QKV_EINVAL, "%s: a dense pack holds fp16 values (bits 16, group_size D, scale dtype fp16)",
+                        name);
+        if (p->scales || p->biases) return fail(QKV_EINVAL, "%s: a dense pack takes no scales or biases", name);
+        if (p->D != 64 && p->D != 128 && p->D != 256)
+            return fail(QKV_EUNSUPPORTED, "%s: head size D=%lld not in {64, 128, 256}", name, (long long)p->D);
+        if (!aligned(p->codes, 16)) return fail(QKV_EINVAL, "%s: codes not 16-byte aligned", name);
+        return QKV_OK;
+    }
+    if (!p->scales) return fail(QKV_EINVAL, "%s: null scales", name);
     if (p->mode == QKV_AFFINE) {
         if (p->bits != 4 && p->bits != 8) return fail(QKV_EUNSUPPORTED, "%s: bits %d not in {4, 8}", name, p->bits);
         if (p->group_size != 32 && p->group_size != 64 && p->group_size != 128)
@@ -148,12 +160,16 @@ qkv_status check_source(const void* x, int32_t dtype, const int64_t xs[3], const
     if (!aligned(x, 16)) return fail(QKV_EINVAL, "%s: source not 16-byte aligned", name);
     if (p->mode == QKV_AFFINE && dtype != p->scale_dtype)
         return fail(QKV_EUNSUPPORTED, "%s: affine scale dtype must equal the source dtype", name);
+    if (p->mode == QKV_DENSE && dtype != QKV_F16)
+        return fail(QKV_EUNSUPPORTED, "%s: a dense pack takes fp16 values", name);
     return QKV_OK;
 }
 
 // ---------------------------------------------------------------- attention plans
 struct Plan {
     bool unfused;                   // the four-kernel composition (QKV_ALGO_UNFUSED)
+    bool prepass;                   // dense fp16 copies first (QKV_ALGO_DEQUANT_F16)
+    size_t dense_bytes;             // bytes of each dense copy in the workspace
     bool matrix;
     bool prefill;                   // tiled matrix kernel
     int wg_rows;                    // its rows per workgroup
@@ -198,8 +214,61 @@ int auto_splits(int64_t base_wgs, int64_t L, int64_t min_keys, int64_t target) {
     return (int)std::max<int64_t>(1, std::min<int64_t>({want, cap, 256}));
 }
 
+qkv::DequantLaunch dequant_job(const qkv_pack* src, const qkv_pack* dst, int64_t L) {
+    qkv::DequantLaunch j{};
+    j.codes = src->codes;
+    j.scales = src->scales;
+    j.biases = src->biases;
+    j.sb = src->stride_b;
+    j.sh = src->stride_h;
+    j.sl = src->stride_l;
+    j.out = dst->codes;
+    j.db = dst->stride_b;
+    j.dh = dst->stride_h;
+    j.dl = dst->stride_l;
+    j.H = src->H;
+    j.L = L;
+    j.rows = src->B * src->H * L;
+    j.gs = src->mode == QKV_Q8_0 ? 32 : src->group_size;
+    return j;
+}
+
+// A dense fp16 pack of rows [0, L) of every (b, h) of k at 'codes' (the
+// dequantize-first strategy's copies).
+qkv_pack dense_copy_of(const qkv_pack* k, int64_t L, void* codes) {
+    qkv_pack d{};
+    d.mode = QKV_DENSE;
+    d.bits = 16;
+    d.group_size = (int32_t)k->D;
+    d.scale_dtype = QKV_F16;
+    d.B = k->B;
+    d.H = k->H;
+    d.L_cap = L;
+    d.D = k->D;
+    d.codes = codes;
+    d.stride_b = k->H * L;
+    d.stride_h = L;
+    d.stride_l = 1;
+    return d;
+}
+
+size_t dense_copy_bytes(const qkv_pack* k, int64_t L) {
+    return ((size_t)(k->B * k->H * L * k->D) * 2 + 255) / 256 * 256;
+}
+
 Plan make_plan(int64_t B, int64_t Hq, int64_t Lq, int64_t D, int64_t L, const qkv_pack* k,
                int32_t q_dtype, const qkv_attn_opts* opts) {
+    if (opts && opts->algo == QKV_ALGO_DEQUANT_F16) {
+        // the dense plan over the copies, after them in the workspace
+        const qkv_pack d = dense_copy_of(k, L, nullptr);
+        qkv_attn_opts o2 = *opts;
+        o2.algo = QKV_ALGO_AUTO;
+        Plan pl = make_plan(B, Hq, Lq, D, L, &d, q_dtype, &o2);
+        pl.prepass = true;
+        pl.dense_bytes = dense_copy_bytes(k, L);
+        pl.ws_bytes += 2 * pl.dense_bytes;
+        return pl;
+    }
     Plan pl{};
     const int64_t Hk = k->H;
     const int G = (int)(Hq / Hk);
@@ -241,6 +310,12 @@ Plan make_plan(int64_t B, int64_t Hq, int64_t Lq, int64_t D, int64_t L, const qk
     int S;
     if (opts && opts->num_splits > 0) {
         S = std::min(opts->num_splits, 256);
+    } else if (pl.prefill && Lq == 1) {
+        // a decode on the tiled kernel (dense caches, GQA beyond 16): it streams
+        // the cache like the decode kernels, so it wants two workgroups per CU
+        // (the LDS of the tiles allows it) and splits down to two tiles
+        const int64_t wgs = B * Hk * ((n_rows + pl.wg_rows - 1) / pl.wg_rows);
+        S = auto_splits(wgs, L, 128, 512);
     } else if (pl.prefill) {
         // one workgroup per CU fits the largest tiles; split only short row counts
         const int64_t wgs = B * Hk * ((n_rows + pl.wg_rows - 1) / pl.wg_rows);
@@ -297,8 +372,16 @@ qkv_status attention(const char* name, const void* q, int32_t q_dtype, int64_t B
     }
     if (mask_kind == QKV_MASK_CAUSAL && L < Lq)
         return fail(QKV_EINVAL, "%s: causal mask needs L >= Lq", name);
-    if (opts && (opts->num_splits < 0 || opts->algo < 0 || opts->algo > QKV_ALGO_UNFUSED))
+    if (opts && (opts->num_splits < 0 || opts->algo < 0 || opts->algo > QKV_ALGO_DEQUANT_F16))
         return fail(QKV_EINVAL, "%s: bad options", name);
+    const int algo = opts ? opts->algo : QKV_ALGO_AUTO;
+    if (k->mode == QKV_DENSE && (q_dtype != QKV_F16 || (algo != QKV_ALGO_AUTO && algo != QKV_ALGO_MATRIX)))
+        return fail(QKV_EUNSUPPORTED, "%s: attention over dense packs takes fp16 queries on the matrix-core "
+                    "kernel", name);
+    if (algo == QKV_ALGO_DEQUANT_F16 &&
+        (q_dtype != QKV_F16 || k->mode == QKV_DENSE || (k->mode == QKV_AFFINE && k->scale_dtype != QKV_F16)))
+        return fail(QKV_EUNSUPPORTED, "%s: the dequantize-first strategy takes fp16 queries and a quantized "
+                    "cache with fp16 scales", name);
     if (opts && opts->algo == QKV_ALGO_UNFUSED && (Lq != 1 || G > 16 || B * Hq > 65535))
         return fail(QKV_EUNSUPPORTED, "%s: the unfused composition takes one query per head, a GQA "
                     "factor of at most 16 and B x Hq below 65536", name);
@@ -324,6 +407,8 @@ qkv_status attention(const char* name, const void* q, int32_t q_dtype, int64_t B
     Plan pl = make_plan(B, Hq, Lq, D, L, k, q_dtype, opts);
     if (B * k->H > 65535 || (!pl.prefill && pl.n_rt > 65535) || pl.S > 65535)
         return fail(QKV_EUNSUPPORTED, "%s: batch x kv heads or row tiles beyond the launch grid", name);
+    if ((k->mode == QKV_DENSE || pl.prepass) && !pl.prefill)
+        return fail(QKV_EUNSUPPORTED, "%s: no matrix-core kernel for a dense cache of this size", name);
     if (pl.ws_bytes > 0 && static_ws) {
         // the library's own device array; checked last, since resolving it
         // may enqueue the zero fill of its ticket header
@@ -347,17 +432,31 @@ qkv_status attention(const char* name, const void* q, int32_t q_dtype, int64_t B
             return fail(QKV_EINVAL, "%s: the mask overlaps the workspace", name);
     }
 
+    // the dequantize-first strategy attends dense fp16 copies at the start of
+    // the workspace; the split states follow them
+    const qkv_pack* kx = k;
+    const qkv_pack* vx = v;
+    qkv_pack kd{}, vd{};
+    if (pl.prepass) {
+        uint8_t* w8 = static_cast<uint8_t*>(workspace);
+        kd = dense_copy_of(k, L, w8);
+        vd = dense_copy_of(v, L, w8 + pl.dense_bytes);
+        kx = &kd;
+        vx = &vd;
+        workspace = w8 + 2 * pl.dense_bytes;
+    }
+
     qkv::AttnLaunch a{};
     a.q = q;
     a.out = out;
-    a.k = {k->codes, k->scales, k->biases, k->stride_b, k->stride_h, k->stride_l};
-    a.v = {v->codes, v->scales, v->biases, v->stride_b, v->stride_h, v->stride_l};
+    a.k = {kx->codes, kx->scales, kx->biases, kx->stride_b, kx->stride_h, kx->stride_l};
+    a.v = {vx->codes, vx->scales, vx->biases, vx->stride_b, vx->stride_h, vx->stride_l};
     a.Hq = Hq;
     a.Hk = k->H;
     a.Lq = Lq;
     a.L = L;
     a.G = (int32_t)G;
-    a.gs_log2 = ilog2(k->group_size);
+    a.gs_log2 = ilog2(kx->group_size);
     a.scale = scale;
     a.mask_kind = mask_kind;
     a.mask = mask_kind == QKV_MASK_ADDITIVE ? mask : nullptr;
@@ -391,8 +490,18 @@ qkv_status attention(const char* name, const void* q, int32_t q_dtype, int64_t B
         hipError_t te = hipEventRecord(static_cast<hipEvent_t>(opts->timing_events[0]), s);
         if (te != hipSuccess) return hip_status(te, name);
     }
-    hipError_t e = pl.unfused  ? qkv::launch_attn_unfused(q_dtype, k->mode, k->bits, (int)D, B, a, s)
-                   : pl.prefill  ? qkv::launch_prefill_matrix(k->mode, k->bits, (int)D, B, a, s)
+    hipError_t e = hipSuccess;
+    if (pl.prepass) {
+        for (int i = 0; i < 2 && e == hipSuccess; ++i) {
+            const qkv_pack* src = i == 0 ? k : v;
+            const qkv_pack& dst = i == 0 ? kd : vd;
+            e = qkv::launch_dequantize(src->mode, src->bits, src->group_size, (int)D,
+                                       dequant_job(src, &dst, L), s);
+        }
+    }
+    if (e == hipSuccess)
+        e = pl.unfused     ? qkv::launch_attn_unfused(q_dtype, k->mode, k->bits, (int)D, B, a, s)
+                   : pl.prefill  ? qkv::launch_prefill_matrix(kx->mode, kx->bits, (int)D, B, a, s)
                    : pl.narrow ? qkv::launch_attn_narrow(k->mode, k->bits, (int)D, B, a, s)
                    : pl.matrix ? qkv::launch_attn_matrix(k->mode, k->bits, (int)D, B, a, s)
                                : qkv::launch_attn_generic(q_dtype, k->mode, k->bits, (int)D, B, a, s);
@@ -453,6 +562,26 @@ qkv_status qkv_update_append(const void* k_new, const void* v_new, int32_t dtype
     return hip_status(e, "qkv_update_append");
 }
 
+qkv_status qkv_dequantize(const qkv_pack* src, int64_t L, const qkv_pack* dst, void* stream) {
+    qkv_status st;
+    if ((st = check_pack(src, "qkv_dequantize(src)")) != QKV_OK) return st;
+    if ((st = check_pack(dst, "qkv_dequantize(dst)")) != QKV_OK) return st;
+    if (src->mode == QKV_DENSE) return fail(QKV_EINVAL, "qkv_dequantize: the source is not quantized");
+    if (dst->mode != QKV_DENSE) return fail(QKV_EINVAL, "qkv_dequantize: the destination must be a dense pack");
+    if (src->mode == QKV_AFFINE && src->scale_dtype != QKV_F16)
+        return fail(QKV_EUNSUPPORTED, "qkv_dequantize: affine packs with fp16 scales only");
+    if (src->B != dst->B || src->H != dst->H || src->D != dst->D)
+        return fail(QKV_EINVAL, "qkv_dequantize: source and destination differ in B, H or D");
+    if (L < 0 || L > src->L_cap || L > dst->L_cap)
+        return fail(QKV_EINVAL, "qkv_dequantize: L=%lld outside [0, capacity]", (long long)L);
+    if (overlaps_pack(codes_range(dst), src))
+        return fail(QKV_EINVAL, "qkv_dequantize: source and destination overlap");
+    if (L == 0) return ok();
+    return hip_status(qkv::launch_dequantize(src->mode, src->bits, src->group_size, (int)src->D,
+                                             dequant_job(src, dst, L), static_cast<hipStream_t>(stream)),
+                      "qkv_dequantize");
+}
+
 size_t qsdpa_workspace_bytes(int64_t B, int64_t Hq, int64_t Lq, int64_t D, int64_t L,
                              const qkv_pack* k, int32_t q_dtype, const qkv_attn_opts* opts) {
     if (!k || k->H < 1 || B < 1 || Hq < 1 || Lq < 1 || L < 1 || Hq % k->H) return 0;
@@ -465,7 +594,10 @@ qkv_status qsdpa_plan(int64_t B, int64_t Hq, int64_t Lq, int64_t D, int64_t L, c
     if (k->H < 1 || B < 1 || Hq < 1 || Lq < 1 || L < 1 || Hq % k->H)
         return fail(QKV_EINVAL, "qsdpa_plan: bad sizes");
     Plan pl = make_plan(B, Hq, Lq, D, L, k, q_dtype, opts);
-    plan->algo = pl.unfused ? QKV_ALGO_UNFUSED : pl.matrix ? QKV_ALGO_MATRIX : QKV_ALGO_GENERIC;
+    plan->algo = pl.unfused   ? QKV_ALGO_UNFUSED
+                 : pl.prepass ? QKV_ALGO_DEQUANT_F16
+                 : pl.matrix  ? QKV_ALGO_MATRIX
+                              : QKV_ALGO_GENERIC;
     plan->num_splits = pl.S;
     plan->row_tile = pl.prefill ? pl.wg_rows : pl.RT;
     plan->kernel = pl.unfused   ? QKV_KERNEL_UNFUSED

@@ -9,7 +9,7 @@
 namespace qkv {
 
 enum DType { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2 };
-enum Mode { MODE_AFFINE = 0, MODE_Q8_0 = 1 };
+enum Mode { MODE_AFFINE = 0, MODE_Q8_0 = 1, MODE_DENSE = 2 };
 enum MaskKind { MASK_NONE = 0, MASK_CAUSAL = 1, MASK_ADDITIVE = 2 };
 
 // One tensor's worth of rows to quantize: source rows [B,H,T,D] with element
@@ -65,6 +65,21 @@ struct AttnLaunch {
     int32_t un_chunks;              // key chunks of the P V product
     int64_t un_chunk;               // keys per chunk
 };
+
+// Rows [0, L) of every (b, h) of a quantized pack (src) -> a dense fp16 pack
+// (dst codes, same B, H, D), one launch.
+struct DequantLaunch {
+    const void* codes;
+    const void* scales;
+    const void* biases;
+    int64_t sb, sh, sl;             // src strides in rows
+    void* out;
+    int64_t db, dh, dl;             // dst strides in rows
+    int64_t H, L, rows;             // rows = B * H * L
+    int32_t gs;                     // group size (32 for Q8_0)
+};
+hipError_t launch_dequantize(int mode, int bits, int group_size, int D, const DequantLaunch& p,
+                             hipStream_t stream);
 
 // Launchers (return hipGetLastError() of the launch).
 hipError_t launch_quantize(int x_dtype, int mode, int bits, int group_size, int D,

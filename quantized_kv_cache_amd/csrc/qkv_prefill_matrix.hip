@@ -34,6 +34,9 @@
 //    cross a row's last visible key; fully hidden tiles are skipped.
 //  * With several key splits the rows' (m, l, o) go to the workspace for the
 //    split merge kernel.
+//  * A dense fp16 cache (the unquantized baseline, or the fp16 copies of the
+//    dequantize-first strategy of the llama.cpp page) takes the same path
+//    with its rows staged into LDS as loaded.
 #include "qkv_internal.hpp"
 #include "qkv_mfma.hpp"
 
@@ -139,7 +142,10 @@ __global__ __launch_bounds__(PNTHR) void attn_matrix_prefill(AttnLaunch p) {
     const int G = p.G;
     const float sl = p.scale * kLog2e;
 
-    // this lane's row (the B column of S^T and of O^T)
+    // this lane's row (the B column of S^T and of O^T); a wave whose 16-row
+    // block lies past the last row (decode, ragged last tile) only loads and
+    // stages tiles for the others
+    const bool rb_live = rt * BMR + rb * 16 < p.n_rows;
     const int row = rt * BMR + rb * 16 + n;
     const bool row_ok = row < p.n_rows;
     const int rowc = row_ok ? row : p.n_rows - 1;
@@ -222,8 +228,12 @@ __global__ __launch_bounds__(PNTHR) void attn_matrix_prefill(AttnLaunch p) {
                 R.vc[c] = uint4{y[0], y[1], 0u, 0u};
             }
         }
-        R.ks = buf16(rows_rsrc(ksb, r0, j_end, BN, kss, SROWB), o_ks);
-        R.vs = buf16(rows_rsrc(vsb, r0, j_end, BN, vss, SROWB), o_vs);
+        if constexpr (MODE == MODE_DENSE) {
+            R.ks = R.vs = 0u;
+        } else {
+            R.ks = buf16(rows_rsrc(ksb, r0, j_end, BN, kss, SROWB), o_ks);
+            R.vs = buf16(rows_rsrc(vsb, r0, j_end, BN, vss, SROWB), o_vs);
+        }
         if constexpr (MODE == MODE_AFFINE) {
             R.kbias = buf16(rows_rsrc(kbb, r0, j_end, BN, kss, SROWB), o_ks);
             R.vbias = buf16(rows_rsrc(vbb, r0, j_end, BN, vss, SROWB), o_vs);
@@ -250,6 +260,24 @@ __global__ __launch_bounds__(PNTHR) void attn_matrix_prefill(AttnLaunch p) {
     };
     // the K (or V) half of a tile: the slice's codes -> fp16 rows in LDS
     auto store_half = [&](const uint4* codes, uint32_t sc, uint32_t bi, _Float16* dst) {
+        if constexpr (MODE == MODE_DENSE) {
+            // fp16 values: the chunks as loaded, the pair's order swapped on
+            // swapping rows as for the dequantized chunks
+            // (a mask, not a select: a select of the two chunks becomes an
+            // indexed access through scratch memory)
+            const uint32_t m = swap ? 0xffffffffu : 0u;
+#pragma unroll
+            for (int c16 = 0; c16 < DPT / 16; ++c16) {
+                const uint4 a = codes[2 * c16], c = codes[2 * c16 + 1];
+                const uint4 x = {a.x ^ c.x, a.y ^ c.y, a.z ^ c.z, a.w ^ c.w};
+                const uint4 first = {a.x ^ (x.x & m), a.y ^ (x.y & m), a.z ^ (x.z & m), a.w ^ (x.w & m)};
+                const uint4 second = {c.x ^ (x.x & m), c.y ^ (x.y & m), c.z ^ (x.z & m), c.w ^ (x.w & m)};
+                const int c0 = 2 * c16 + (swap ? 1 : 0), c1 = 2 * c16 + (swap ? 0 : 1);
+                *(uint4*)(dst + 8 * c0) = first;
+                *(uint4*)(dst + 8 * c1) = second;
+            }
+            return;
+        }
         const uint32_t s2 = sc | (sc << 16), b2 = bi | (bi << 16);
 #pragma unroll
         for (int c16 = 0; c16 < DPT / 16; ++c16) {
@@ -294,6 +322,7 @@ __global__ __launch_bounds__(PNTHR) void attn_matrix_prefill(AttnLaunch p) {
         const int64_t j0 = j_begin + (int64_t)t * BN + KPW * kh;  // first key of this wave's part
         const _Float16* kt = s_k[buf];
         const _Float16* vt = s_v[buf];
+        if (rb_live) {
 
         // S^T for the part's subtiles of 16 keys: lane holds keys 16 u + 4 kb + jj of row n
         float sc[NSUB][4];
@@ -380,6 +409,7 @@ __global__ __launch_bounds__(PNTHR) void attn_matrix_prefill(AttnLaunch p) {
                     va[0], va[1], va[2], va[3], vb[0], vb[1], vb[2], vb[3]});
                 acc[t2] = mfma16(aop, pb, acc[t2]);
             }
+        }
         }
         // next tile -> the other buffer, then one barrier per tile
         if (t + 1 < ntile && dq_on) {
@@ -480,6 +510,14 @@ hipError_t by_d(int D, int64_t B, const AttnLaunch& p, hipStream_t s) {
 hipError_t launch_prefill_matrix(int mode, int bits, int D, int64_t B, const AttnLaunch& p,
                                  hipStream_t stream) {
     const int gs = 1 << p.gs_log2;
+    if (mode == MODE_DENSE) {
+        switch (D) {
+            case 64: return launch_p<MODE_DENSE, 16, 64, 64>(B, p, stream);
+            case 128: return launch_p<MODE_DENSE, 16, 128, 128>(B, p, stream);
+            case 256: return launch_p<MODE_DENSE, 16, 256, 256>(B, p, stream);
+        }
+        return hipErrorNotSupported;
+    }
     if (mode == MODE_Q8_0) return by_d<MODE_Q8_0, 8, 32>(D, B, p, stream);
     if (bits == 4) {
         if (gs == 32) return by_d<MODE_AFFINE, 4, 32>(D, B, p, stream);

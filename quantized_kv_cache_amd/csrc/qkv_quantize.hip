@@ -15,6 +15,8 @@
 // the wave is contiguous.  Each lane writes one packed word (4-bit) or two
 // (8-bit, Q8_0); the first lane of a group writes its scale and bias.
 //
+// A dense fp16 pack (the unquantized cache) takes the fp16 values as they are.
+//
 // Bit-exactness: min/max are exact; the scale division, the subtract and the
 // code division are IEEE fp32 (no fused multiply-add is possible in these
 // expressions); codes round half to even (v_rndne_f32); scale and bias are
@@ -81,6 +83,12 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(QuantLaunch p) {
     const int64_t src = b * job.xs0 + h * job.xs1 + t * job.xs2 + (int64_t)lr * 8;
     const int64_t dst = b * job.sb + h * job.sh + (p.offset + t) * job.sl;
 
+    if constexpr (MODE == MODE_DENSE) {
+        // a dense fp16 cache stores the values themselves
+        const uint4 raw = *(const uint4*)((const uint16_t*)job.x + src);
+        ((uint4*)((uint8_t*)job.codes + dst * (int64_t)(D * 2)))[lr] = raw;
+        return;
+    } else {
     float v[8];
     load8<DT>(job.x, src, v);
 
@@ -145,6 +153,7 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(QuantLaunch p) {
         ((uint2*)crow)[lr] = w;
         if (lr % LPG == 0) ((uint16_t*)job.scales)[dst * NG + lr / LPG] = dh;
     }
+    }
 }
 
 template <int DT, int MODE, int BITS, int GS, int D>
@@ -172,6 +181,10 @@ template <int DT>
 hipError_t dispatch_fmt(int mode, int bits, int gs, int D, const QuantLaunch& p, int njobs,
                         hipStream_t s) {
     if (mode == MODE_Q8_0) return dispatch_d<DT, MODE_Q8_0, 8, 32>(D, p, njobs, s);
+    if (mode == MODE_DENSE) {
+        if constexpr (DT == DT_F16) return dispatch_d<DT, MODE_DENSE, 16, 32>(D, p, njobs, s);
+        return hipErrorNotSupported;
+    }
     if (bits == 4) {
         if (gs == 32) return dispatch_d<DT, MODE_AFFINE, 4, 32>(D, p, njobs, s);
         if (gs == 64) return dispatch_d<DT, MODE_AFFINE, 4, 64>(D, p, njobs, s);

@@ -64,6 +64,13 @@ WORKLOADS = {
                                   "q8_0", 8, 32, 1.0 / 16.0, False, 404),
     "q8_0_prefill_512": Workload("q8_0_prefill_512", 1, 32, 2, 256, 20480, 512, "f16", "normal",
                                  "q8_0", 8, 32, 1.0 / 16.0, True, 505),
+    # the unquantized baseline at the shapes of the two decode workloads: dense
+    # fp16 K/V (the sdpa baseline of the MLX benchmark; the F16 cache of the
+    # llama.cpp page), same distributions as the quantized workloads
+    "dense_decode_64k_gqa4": Workload("dense_decode_64k_gqa4", 1, 32, 8, 128, 65536, 1, "f16",
+                                      "uniform", "dense", 16, 128, 1.0, False, 3),
+    "dense_decode_20k_gqa16": Workload("dense_decode_20k_gqa16", 1, 32, 2, 256, 20480, 1, "f16",
+                                       "normal", "dense", 16, 256, 1.0 / 16.0, False, 404),
 }
 
 

@@ -32,7 +32,7 @@ def test_exports_every_declared_function(L):
     assert set(names) == set(_lib.EXPORTS), names
     for n in names:
         assert hasattr(L, n), n
-    assert L.qkv_abi_version() == 3
+    assert L.qkv_abi_version() == 4
 
 
 def _pack(**kw):
@@ -237,3 +237,56 @@ def test_measure_read_config_rejects_bad_arguments(L):
                                        a["width"], a["snk"], None)
         assert st == _lib.QKV_EINVAL, b
         assert L.qkv_last_error()
+
+
+def _dense(**kw):
+    d = dict(mode=_lib.QKV_DENSE, bits=16, group_size=128, scale_dtype=_lib.QKV_F16, B=1, H=2,
+             L_cap=64, D=128, codes=FAKE + 0x3000000, scales=None, biases=None,
+             stride_b=128, stride_h=64, stride_l=1)
+    d.update(kw)
+    return _lib.QkvPack(**d)
+
+
+@pytest.mark.parametrize("kw,msg", [(dict(bits=8), "fp16"), (dict(group_size=64), "fp16"),
+                                    (dict(scale_dtype=_lib.QKV_F32), "fp16"),
+                                    (dict(scales=FAKE), "no scales"), (dict(codes=FAKE + 8), "aligned")])
+def test_dense_pack_rules(L, kw, msg):
+    st = L.qkv_dequantize(ctypes.byref(_pack()), 8, ctypes.byref(_dense(**kw)), None)
+    assert st == _lib.QKV_EINVAL and msg in L.qkv_last_error().decode(), L.qkv_last_error()
+
+
+def test_dequantize_rejects(L):
+    src, dst = _pack(), _dense()
+    assert L.qkv_dequantize(ctypes.byref(dst), 8, ctypes.byref(dst), None) == _lib.QKV_EINVAL
+    assert L.qkv_dequantize(ctypes.byref(src), 8, ctypes.byref(_pack(codes=FAKE + 0x3000000)),
+                            None) == _lib.QKV_EINVAL                            # dst not dense
+    assert L.qkv_dequantize(ctypes.byref(src), 65, ctypes.byref(dst), None) == _lib.QKV_EINVAL
+    assert L.qkv_dequantize(ctypes.byref(src), 8, ctypes.byref(_dense(H=3)), None) == _lib.QKV_EINVAL
+    assert L.qkv_dequantize(ctypes.byref(src), 8, ctypes.byref(_dense(codes=FAKE)), None) == \
+        _lib.QKV_EINVAL                                                          # overlap
+    assert L.qkv_dequantize(ctypes.byref(_pack(scale_dtype=_lib.QKV_F32)), 8, ctypes.byref(dst),
+                            None) == _lib.QKV_EUNSUPPORTED
+    assert L.qkv_dequantize(ctypes.byref(src), 0, ctypes.byref(dst), None) == _lib.QKV_OK
+
+
+def test_dense_and_dequant_first_plans(L):
+    dense = _dense(L_cap=4096, stride_b=8192, stride_h=4096)
+    pl = _lib.QkvAttnPlan()
+    assert L.qsdpa_plan(1, 8, 1, 128, 4096, ctypes.byref(dense), _lib.QKV_F16, None,
+                        ctypes.byref(pl)) == 0
+    assert pl.kernel == _lib.QKV_KERNEL_PREFILL
+    q8 = _lib.QkvPack(mode=_lib.QKV_Q8_0, bits=8, group_size=32, scale_dtype=_lib.QKV_F16, B=1,
+                      H=2, L_cap=4096, D=128, codes=FAKE, scales=FAKE + 0x10000000, biases=None,
+                      stride_b=8192, stride_h=4096, stride_l=1)
+    opts = _lib.QkvAttnOpts(num_splits=0, algo=_lib.QKV_ALGO_DEQUANT_F16)
+    assert L.qsdpa_plan(1, 32, 64, 128, 4000, ctypes.byref(q8), _lib.QKV_F16, ctypes.byref(opts),
+                        ctypes.byref(pl)) == 0
+    assert pl.algo == _lib.QKV_ALGO_DEQUANT_F16 and pl.kernel == _lib.QKV_KERNEL_PREFILL
+    # two dense fp16 copies of the 4000 attended rows come first in the workspace
+    assert pl.workspace_bytes >= 2 * 2 * 4000 * 128 * 2
+    # dense packs need fp16 queries
+    st = L.qsdpa_decode(ctypes.c_void_p(FAKE + 0x1000000), _lib.QKV_F32, 1, 8, 128,
+                        ctypes.byref(dense), ctypes.byref(_dense(codes=FAKE + 0x5000000, L_cap=4096,
+                                                                 stride_b=8192, stride_h=4096)),
+                        64, 1.0, None, 0, None, ctypes.c_void_p(FAKE + 0x2000000), None, 0, None, None)
+    assert st == _lib.QKV_EUNSUPPORTED
