@@ -5,8 +5,9 @@ TEST INFRASTRUCTURE ONLY (tests, smoke check, CPU-baseline timing).
 Array conventions (numpy, C-contiguous):
   * ``"f32"`` values are ``np.float32``; ``"f16"`` values are ``np.float16``;
     ``"bf16"`` values are ``np.uint16`` bit patterns.
-  * affine codes are ``np.uint32`` words, LSB-first; Q8_0 codes are ``np.int8``
-    and Q8_0 scales are fp16 bit patterns (``np.uint16``).
+  * affine and symmetric 4/5-bit ("qsym") codes are ``np.uint32`` words
+    holding each row's least-significant-bit-first code stream; Q8_0 codes are
+    ``np.int8``; Q8_0 and qsym scales are fp16 bit patterns (``np.uint16``).
 
 Every wrapper only marshals arrays; the arithmetic is in the C file, where
 each function cites the page passage it follows.
@@ -30,7 +31,8 @@ __all__ = [
     "build", "lib", "num_threads", "DTYPE_CODE",
     "f16_bits_from_f32", "f32_from_f16_bits", "bf16_bits_from_f32", "f32_from_bf16_bits",
     "to_f32", "affine_eps",
-    "quantize_affine", "dequant_affine", "quantize_q8_0", "dequant_q8_0",
+    "quantize_affine", "dequant_affine", "quantize_q8_0", "dequant_q8_0", "quantize_qsym",
+    "dequant_qsym",
     "append_rows", "attention", "quantize", "dequant",
 ]
 
@@ -72,6 +74,10 @@ def lib():
         L.orc_quantize_q8_0.restype = None
         L.orc_dequant_q8_0.argtypes = [P, P, I64, I64, P]
         L.orc_dequant_q8_0.restype = None
+        L.orc_quantize_qsym.argtypes = [P, I, I64, I64, I, P, P]
+        L.orc_quantize_qsym.restype = None
+        L.orc_dequant_qsym.argtypes = [P, P, I64, I64, I, P]
+        L.orc_dequant_qsym.restype = None
         L.orc_attention.argtypes = [P, P, P, I64, I64, I64, I64, I64, I64, ctypes.c_double,
                                     P, P, I, P]
         L.orc_attention.restype = None
@@ -191,9 +197,36 @@ def dequant_q8_0(codes, d):
     return out
 
 
+def quantize_qsym(x: np.ndarray, dtype: str, bits: int):
+    """Symmetric 32-blocks at 4 or 5 bits.  Returns (codes as uint32 words of
+    the rows' bit streams, d fp16 bit patterns)."""
+    x = _c(x, _NP_STORAGE[dtype])
+    D = x.shape[-1]
+    if D % 32 or (D * bits) % 32:
+        raise ValueError("D must be a multiple of 32")
+    rows = x.size // D
+    codes = np.zeros(x.shape[:-1] + (D * bits // 32,), np.uint32)
+    d = np.zeros(x.shape[:-1] + (D // 32,), np.uint16)
+    lib().orc_quantize_qsym(_ptr(x), DTYPE_CODE[dtype], rows, D, bits, _ptr(codes), _ptr(d))
+    return codes, d
+
+
+def dequant_qsym(codes, d, bits: int):
+    codes = _c(codes, np.uint32)
+    d = _c(d, np.uint16)
+    D = codes.shape[-1] * 32 // bits
+    rows = codes.size // codes.shape[-1]
+    out = np.zeros(codes.shape[:-1] + (D,), np.float32)
+    lib().orc_dequant_qsym(_ptr(codes), _ptr(d), rows, D, bits, _ptr(out))
+    return out
+
+
 def quantize(x: np.ndarray, dtype: str, mode: str, bits: int = 8, group_size: int = 64,
              scale_dtype: str | None = None):
     """Uniform front end: returns dict(codes=..., scales=..., biases=... or None)."""
+    if mode == "qsym":
+        c, d = quantize_qsym(x, dtype, bits)
+        return {"codes": c, "scales": d, "biases": None}
     if mode == "affine":
         c, s, b = quantize_affine(x, dtype, bits, group_size, scale_dtype)
         return {"codes": c, "scales": s, "biases": b}
@@ -208,6 +241,8 @@ def dequant(pack: dict, mode: str, bits: int = 8, group_size: int = 64,
     if mode == "affine":
         return dequant_affine(pack["codes"], pack["scales"], pack["biases"], scale_dtype,
                               bits, group_size)
+    if mode == "qsym":
+        return dequant_qsym(pack["codes"], pack["scales"], bits)
     return dequant_q8_0(pack["codes"], pack["scales"])
 
 

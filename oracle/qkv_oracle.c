@@ -20,6 +20,10 @@
  *              (Q8_0 KV blocks: 32 signed int8 codes, one fp16 scale)
  *
  * Readings taken where the pages are silent:
+ *   - codes of a row form one least-significant-bit-first stream (the 2/4/8-bit
+ *     layout of the pages, continued through the 3/5/6-bit packs);
+ *   - the Q4_0 / Q5_0 caches the llama.cpp page names: the Q8_0 rule with the
+ *     code range of 4 / 5 bits (symmetric blocks of 32, one fp16 scale);
  *   - codes are rounded half-to-even from the STORED (dtype-rounded) scale
  *     and bias, with IEEE fp32 subtract and divide, no fused multiply-add;
  *   - the scale is floored at eps = T(1e-7) before it is stored;
@@ -147,27 +151,51 @@ static long rne_int(float v) {
 float orc_affine_eps(int scale_dtype) { return round_to_dtype(1e-7f, scale_dtype); }
 
 /* ------------------------------------------------------------------------ */
+/* Code packing.  The codes of a row form one little-endian bit stream:      */
+/* element j occupies bits [j*bits, (j+1)*bits), least significant bit      */
+/* first.  For 2, 4 and 8 bits this is element j at bits                    */
+/* [(j mod (32/bits))*bits, +bits) of uint32 word j / (32/bits)             */
+/* ([MLX-KVU] sdpa_vector.h load_keys masks 0x000f, 0x00f0, 0x0f00, 0xf000; */
+/* [MLX-WIP] qmm.cu load_quantized shifts); for 3, 5 and 6 bits it packs 8,  */
+/* 8 and 4 values into 3, 5 and 3 bytes ([MLX-WIP] quantized_utils.cuh     */
+/* get_pack_factor / get_bytes_per_pack), their bit order within a pack     */
+/* taken to continue the same least-significant-first stream.               */
+/* ------------------------------------------------------------------------ */
+static void put_code(uint8_t* row, int64_t j, int bits, uint32_t c) {
+    for (int k = 0; k < bits; ++k) {
+        int64_t bit = j * bits + k;
+        if ((c >> k) & 1u) row[bit >> 3] |= (uint8_t)(1u << (bit & 7));
+    }
+}
+
+static uint32_t get_code(const uint8_t* row, int64_t j, int bits) {
+    uint32_t c = 0;
+    for (int k = 0; k < bits; ++k) {
+        int64_t bit = j * bits + k;
+        c |= (uint32_t)((row[bit >> 3] >> (bit & 7)) & 1u) << k;
+    }
+    return c;
+}
+
+/* ------------------------------------------------------------------------ */
 /* Group-wise affine quantization ([MLX-KVU] quantized.h affine_quantize;   */
 /* [MLX-WIP] quantized.cu affine_quantize).  Per group of gs elements:       */
 /*   s = max((max - min) / (2^bits - 1), eps) stored in T, b = min in T,    */
-/*   c = clamp(rne((x - b) / s), 0, 2^bits - 1), packed LSB-first into      */
-/*   little-endian uint32 words: element j sits at bits [j*bits, +bits) of  */
-/*   word j / (32/bits) ([MLX-KVU] sdpa_vector.h load_keys masks 0x000f,    */
-/*   0x00f0, 0x0f00, 0xf000; [MLX-WIP] qmm.cu load_quantized shifts).       */
-/* x: rows x D in x_dtype.  codes: rows x (D*bits/32) words.                */
-/* scales, biases: rows x (D/gs) in scale_dtype.                            */
+/*   c = clamp(rne((x - b) / s), 0, 2^bits - 1), packed as above.           */
+/* x: rows x D in x_dtype.  codes: rows x (D*bits/8) bytes (D*bits/32       */
+/* little-endian words).  scales, biases: rows x (D/gs) in scale_dtype.     */
 /* ------------------------------------------------------------------------ */
 void orc_quantize_affine(const void* x, int x_dtype, int64_t rows, int64_t D,
                          int bits, int gs, int scale_dtype,
                          uint32_t* codes, void* scales, void* biases) {
-    const int64_t words_per_row = D * bits / 32;
+    const int64_t bytes_per_row = D * bits / 8;
     const int64_t groups = D / gs;
     const float n_levels = (float)((1 << bits) - 1);
     const float eps = orc_affine_eps(scale_dtype);
     float* xs = (float*)malloc(sizeof(float) * (size_t)gs);
     for (int64_t r = 0; r < rows; ++r) {
-        uint32_t* crow = codes + r * words_per_row;
-        memset(crow, 0, sizeof(uint32_t) * (size_t)words_per_row);
+        uint8_t* crow = (uint8_t*)codes + r * bytes_per_row;
+        memset(crow, 0, (size_t)bytes_per_row);
         for (int64_t g = 0; g < groups; ++g) {
             /* 1. widen the group to fp32 (exact for all three dtypes) */
             for (int i = 0; i < gs; ++i) xs[i] = load_elem(x, x_dtype, r * D + g * gs + i);
@@ -191,10 +219,7 @@ void orc_quantize_affine(const void* x, int x_dtype, int64_t rows, int64_t D,
                 long c = rne_int(t);
                 if (c < 0) c = 0;
                 if (c > (long)n_levels) c = (long)n_levels;
-                int64_t j = g * gs + i;               /* element index in row */
-                int64_t w = j / (32 / bits);
-                int sh = (int)(j % (32 / bits)) * bits;
-                crow[w] |= ((uint32_t)c) << sh;
+                put_code(crow, g * gs + i, bits, (uint32_t)c);
             }
         }
     }
@@ -207,14 +232,13 @@ void orc_quantize_affine(const void* x, int x_dtype, int64_t rows, int64_t D,
 void orc_dequant_affine(const uint32_t* codes, const void* scales, const void* biases,
                         int scale_dtype, int64_t rows, int64_t D, int bits, int gs,
                         float* out) {
-    const int64_t words_per_row = D * bits / 32;
+    const int64_t bytes_per_row = D * bits / 8;
     const int64_t groups = D / gs;
-    const uint32_t mask = (uint32_t)((1u << bits) - 1u);
     for (int64_t r = 0; r < rows; ++r) {
+        const uint8_t* crow = (const uint8_t*)codes + r * bytes_per_row;
         for (int64_t j = 0; j < D; ++j) {
             int64_t g = j / gs;
-            uint32_t w = codes[r * words_per_row + j / (32 / bits)];
-            uint32_t c = (w >> ((j % (32 / bits)) * bits)) & mask;
+            uint32_t c = get_code(crow, j, bits);
             float s = load_elem(scales, scale_dtype, r * groups + g);
             float b = load_elem(biases, scale_dtype, r * groups + g);
             float prod = s * (float)c;            /* two roundings, no fma */
@@ -255,6 +279,58 @@ void orc_quantize_q8_0(const void* x, int x_dtype, int64_t rows, int64_t D,
             }
         }
     }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Symmetric blocks of 32 at b = 4 or 5 bits: the Q8_0 rule with the code    */
+/* range of b bits (the reading taken for the Q4_0 / Q5_0 caches that the   */
+/* llama.cpp page names): qmax = 2^(b-1) - 1, d = fp16(amax / qmax),        */
+/* c = clamp(rne(x / d), -qmax, qmax) (0 when d == 0), stored as b-bit two's */
+/* complement in the row's bit stream.  codes: rows x (D*b/8) bytes.        */
+/* ------------------------------------------------------------------------ */
+void orc_quantize_qsym(const void* x, int x_dtype, int64_t rows, int64_t D, int bits,
+                       uint8_t* codes, uint16_t* dscale) {
+    const int64_t blocks = D / 32;
+    const int64_t bytes_per_row = D * bits / 8;
+    const long qmax = (1L << (bits - 1)) - 1;
+    for (int64_t r = 0; r < rows; ++r) {
+        uint8_t* crow = codes + r * bytes_per_row;
+        memset(crow, 0, (size_t)bytes_per_row);
+        for (int64_t k = 0; k < blocks; ++k) {
+            float xs[32];
+            float amax = 0.0f;
+            for (int i = 0; i < 32; ++i) {
+                xs[i] = load_elem(x, x_dtype, r * D + k * 32 + i);
+                float a = fabsf(xs[i]);
+                if (a > amax) amax = a;
+            }
+            float d32 = amax / (float)qmax;
+            uint16_t dh = orc_f32_to_f16(d32);
+            dscale[r * blocks + k] = dh;
+            float d = orc_f16_to_f32(dh);
+            for (int i = 0; i < 32; ++i) {
+                long c = 0;
+                if (d != 0.0f) {
+                    c = rne_int(xs[i] / d);
+                    if (c < -qmax) c = -qmax;
+                    if (c > qmax) c = qmax;
+                }
+                put_code(crow, k * 32 + i, bits, (uint32_t)c & ((1u << bits) - 1u));
+            }
+        }
+    }
+}
+
+void orc_dequant_qsym(const uint8_t* codes, const uint16_t* dscale, int64_t rows, int64_t D,
+                      int bits, float* out) {
+    const int64_t blocks = D / 32;
+    const int64_t bytes_per_row = D * bits / 8;
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t j = 0; j < D; ++j) {
+            uint32_t u = get_code(codes + r * bytes_per_row, j, bits);
+            long c = (u >> (bits - 1)) ? (long)u - (1L << bits) : (long)u;   /* two's complement */
+            out[r * D + j] = orc_f16_to_f32(dscale[r * blocks + j / 32]) * (float)c;
+        }
 }
 
 /* Q8_0 dequantization x^ = d * c in fp32. */

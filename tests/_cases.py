@@ -72,12 +72,14 @@ def assert_pack_equal(gpu: dict, ref: dict, rows=None):
 def dequant(pk: dict, mode: str, bits: int, gs: int, scale_dtype: str) -> np.ndarray:
     if mode == "q8_0":
         return orc.dequant_q8_0(pk["codes"], pk["scales"])
+    if mode == "qsym":
+        return orc.dequant_qsym(pk["codes"], pk["scales"], bits)
     return orc.dequant_affine(pk["codes"], pk["scales"], pk["biases"], scale_dtype, bits, gs)
 
 
 def oracle_attention(q: np.ndarray, qdt: str, kp: dict, vp: dict, L: int, mode: str, bits: int,
                      gs: int, scale: float, mask=None, causal=False) -> np.ndarray:
-    sdt = "f16" if mode == "q8_0" else qdt
+    sdt = "f16" if mode in ("q8_0", "qsym") else qdt
     kh = dequant({k: (None if v is None else v[:, :, :L]) for k, v in kp.items()}, mode, bits, gs, sdt)
     vh = dequant({k: (None if v is None else v[:, :, :L]) for k, v in vp.items()}, mode, bits, gs, sdt)
     return orc.attention(orc.to_f32(q, qdt), kh, vh, scale, mask=mask, causal=causal)
@@ -107,7 +109,7 @@ def assert_close(gpu: torch.Tensor, ref: np.ndarray, what: str = "", report: boo
 
 
 def scale_dtype_of(mode: str, dtype: str) -> str:
-    return "f16" if mode == "q8_0" else dtype
+    return "f16" if mode in ("q8_0", "qsym") else dtype
 
 
 __all__ = ["ATOL", "RTOL", "TORCH_DT", "to_dev", "from_dev", "pack_numpy", "oracle_pack",
