@@ -40,6 +40,22 @@
  *  d == 0); the value is d * c.  Codes are stored one byte per value in a
  *  codes plane, scales in a separate plane (biases == NULL).
  *
+ *  Affine codes of 2, 3, 5 and 6 bits follow the pack factors and bytes per
+ *  pack of the MLX CUDA page "Fixed mma and working dequant"
+ *  (quantized_utils.cuh: 3 and 5 bits pack 8 values into 3 and 5 bytes, 6
+ *  bits 4 values into 3 bytes): the codes of a row form one
+ *  least-significant-bit-first stream, element j at bits [j*bits,
+ *  (j+1)*bits), which for 2, 4 and 8 bits is the word layout above.
+ *
+ *  QKV_QSYM: symmetric blocks of 32 values at 4 or 5 bits, the rule of Q8_0
+ *  with the code range of the width -- the reading taken for the Q4_0 and
+ *  Q5_0 caches that the llama.cpp page names: d = fp16(amax / qmax) with
+ *  qmax = 2^(bits-1) - 1, c = clamp(round_half_even(x / d), -qmax, qmax) (0
+ *  when d == 0), the value d * c; codes are bits-wide two's complement in the
+ *  row's bit stream, scales fp16 (group_size 32, biases NULL).  The affine
+ *  4-bit and 5-bit formats with group_size 32 and fp16 scales play the role
+ *  of Q4_1 and Q5_1 (a scale and a minimum per block of 32).
+ *
  *  QKV_DENSE: the unquantized cache the pages compare against (the dense
  *  fp16 K/V of the MLX benchmark's sdpa baseline, sdpa_vector_bench.py; the
  *  F16 KV cache and the F16 scratch copies of the llama.cpp page): codes hold
@@ -53,10 +69,13 @@
  *  where r = b*stride_b + h*stride_h + l*stride_l (strides in ROWS; the
  *  dense layout [B,H,L_cap] is {H*L_cap, L_cap, 1}).
  *  Requirements: codes 16-byte aligned; scales/biases aligned to one row
- *  of scales (min(16, (D / group_size) * element size) bytes); D in
- *  {64, 128, 256}; bits in {4, 8} with group_size in
- *  {32, 64, 128} dividing D (affine), bits 8 and group_size 32 (Q8_0);
+ *  of scales (min(16, (D / group_size) * element size) bytes, a power of
+ *  two); D in {64, 96, 128, 256} (96: affine, Q8_0 and QSYM); bits in
+ *  {2, 3, 4, 5, 6, 8} with group_size in {32, 64, 128} dividing D (affine),
+ *  bits 8 and group_size 32 (Q8_0), bits 4 or 5 and group_size 32 (QSYM);
  *  affine scale_dtype equal to the dtype of the values it was made from.
+ *  The matrix-core kernels take affine 4/8-bit and Q8_0 packs with D in
+ *  {64, 128, 256}; every other format runs on the generic kernel.
  */
 #ifndef QKV_H
 #define QKV_H
@@ -79,7 +98,7 @@ typedef enum {
 } qkv_status;
 
 typedef enum { QKV_F32 = 0, QKV_F16 = 1, QKV_BF16 = 2 } qkv_dtype;
-typedef enum { QKV_AFFINE = 0, QKV_Q8_0 = 1, QKV_DENSE = 2 } qkv_mode;
+typedef enum { QKV_AFFINE = 0, QKV_Q8_0 = 1, QKV_DENSE = 2, QKV_QSYM = 3 } qkv_mode;
 typedef enum { QKV_MASK_NONE = 0, QKV_MASK_CAUSAL = 1, QKV_MASK_ADDITIVE = 2 } qkv_mask_kind;
 
 /* Kernel selection for the attention calls.  AUTO picks the fastest kernel

@@ -11,7 +11,7 @@ QKV_OK, QKV_EINVAL, QKV_EUNSUPPORTED, QKV_EWORKSPACE, QKV_EHIP = range(5)
 STATUS_NAMES = {0: "QKV_OK", 1: "QKV_EINVAL", 2: "QKV_EUNSUPPORTED", 3: "QKV_EWORKSPACE",
                 4: "QKV_EHIP"}
 QKV_F32, QKV_F16, QKV_BF16 = 0, 1, 2
-QKV_AFFINE, QKV_Q8_0, QKV_DENSE = 0, 1, 2
+QKV_AFFINE, QKV_Q8_0, QKV_DENSE, QKV_QSYM = 0, 1, 2, 3
 QKV_MASK_NONE, QKV_MASK_CAUSAL, QKV_MASK_ADDITIVE = 0, 1, 2
 QKV_ALGO_AUTO, QKV_ALGO_GENERIC, QKV_ALGO_MATRIX, QKV_ALGO_UNFUSED, QKV_ALGO_DEQUANT_F16 = 0, 1, 2, 3, 4
 QKV_KERNEL_GENERIC, QKV_KERNEL_DECODE, QKV_KERNEL_DECODE_NARROW, QKV_KERNEL_PREFILL = 0, 1, 2, 3

@@ -52,11 +52,12 @@ def _ptr(t: torch.Tensor | None):
 class Pack:
     """A quantized K or V cache: codes, scales and (affine) biases, each
     [B, H, L_cap, *] with rows of one token of one head."""
-    mode: str                      # "affine" | "q8_0" | "dense"
+    mode: str                      # "affine" | "q8_0" | "qsym" | "dense"
     bits: int
     group_size: int
     D: int
-    codes: torch.Tensor            # affine: int32 words [B,H,L_cap,D*bits/32]; q8_0: int8 [B,H,L_cap,D];
+    codes: torch.Tensor            # affine, qsym: int32 words [B,H,L_cap,D*bits/32] (each row's
+                                   # least-significant-first code stream); q8_0: int8 [B,H,L_cap,D];
                                    # dense: fp16 values [B,H,L_cap,D]
     scales: torch.Tensor | None    # [B,H,L_cap,D/group_size] (None for dense)
     biases: torch.Tensor | None    # affine only
@@ -98,7 +99,7 @@ class Pack:
         if rs != ss:
             raise ValueError("codes and scales must share row strides")
         return _lib.QkvPack(
-            mode=_lib.QKV_AFFINE if self.mode == "affine" else _lib.QKV_Q8_0,
+            mode={"affine": _lib.QKV_AFFINE, "q8_0": _lib.QKV_Q8_0, "qsym": _lib.QKV_QSYM}[self.mode],
             bits=self.bits, group_size=self.group_size, scale_dtype=_dt(s),
             B=c.shape[0], H=c.shape[1], L_cap=c.shape[2], D=self.D,
             codes=c.data_ptr(), scales=s.data_ptr(),
@@ -113,6 +114,10 @@ def empty_pack(B: int, H: int, L_cap: int, D: int, mode: str = "affine", bits: i
     if mode == "dense":
         return Pack("dense", 16, D, D, torch.zeros((B, H, L_cap, D), dtype=torch.float16, device=device),
                     None, None)
+    if mode == "qsym":
+        return Pack("qsym", bits, 32, D,
+                    torch.zeros((B, H, L_cap, D * bits // 32), dtype=torch.int32, device=device),
+                    torch.zeros((B, H, L_cap, D // 32), dtype=torch.float16, device=device), None)
     if mode == "q8_0":
         return Pack("q8_0", 8, 32, D,
                     torch.zeros((B, H, L_cap, D), dtype=torch.int8, device=device),

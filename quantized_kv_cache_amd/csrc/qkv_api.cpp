@@ -84,7 +84,7 @@ Range scales_range(const qkv_pack* p, const void* base) {
 
 qkv_status check_pack(const qkv_pack* p, const char* name) {
     if (!p) return fail(QKV_EINVAL, "%s: null pack", name);
-    if (p->mode != QKV_AFFINE && p->mode != QKV_Q8_0 && p->mode != QKV_DENSE)
+    if (p->mode != QKV_AFFINE && p->mode != QKV_Q8_0 && p->mode != QKV_DENSE && p->mode != QKV_QSYM)
         return fail(QKV_EINVAL, "%s: unknown mode %d", name, p->mode);
     if (p->B < 1 || p->H < 1 || p->L_cap < 1 || p->D < 1)
         return fail(QKV_EINVAL, "%s: B, H, L_cap and D must be >= 1", name);
@@ -103,7 +103,8 @@ qkv_status check_pack(const qkv_pack* p, const char* name) {
     }
     if (!p->scales) return fail(QKV_EINVAL, "%s: null scales", name);
     if (p->mode == QKV_AFFINE) {
-        if (p->bits != 4 && p->bits != 8) return fail(QKV_EUNSUPPORTED, "%s: bits %d not in {4, 8}", name, p->bits);
+        if (p->bits != 2 && p->bits != 3 && p->bits != 4 && p->bits != 5 && p->bits != 6 && p->bits != 8)
+            return fail(QKV_EUNSUPPORTED, "%s: bits %d not in {2, 3, 4, 5, 6, 8}", name, p->bits);
         if (p->group_size != 32 && p->group_size != 64 && p->group_size != 128)
             return fail(QKV_EUNSUPPORTED, "%s: group_size %d not in {32, 64, 128}", name, p->group_size);
         if (p->D % p->group_size)
@@ -111,6 +112,12 @@ qkv_status check_pack(const qkv_pack* p, const char* name) {
                         (long long)p->D, p->group_size);
         if (!valid_dtype(p->scale_dtype)) return fail(QKV_EINVAL, "%s: bad scale dtype", name);
         if (!p->biases) return fail(QKV_EINVAL, "%s: affine pack needs biases", name);
+    } else if (p->mode == QKV_QSYM) {
+        if ((p->bits != 4 && p->bits != 5) || p->group_size != 32)
+            return fail(QKV_EINVAL, "%s: symmetric blocks need bits 4 or 5, group_size 32", name);
+        if (p->scale_dtype != QKV_F16) return fail(QKV_EINVAL, "%s: symmetric block scales are fp16", name);
+        if (p->biases) return fail(QKV_EINVAL, "%s: symmetric blocks take no biases", name);
+        if (p->D % 32) return fail(QKV_EINVAL, "%s: D must be a multiple of 32", name);
     } else {
         if (p->bits != 8 || p->group_size != 32)
             return fail(QKV_EINVAL, "%s: Q8_0 needs bits=8, group_size=32", name);
@@ -118,13 +125,15 @@ qkv_status check_pack(const qkv_pack* p, const char* name) {
         if (p->biases) return fail(QKV_EINVAL, "%s: Q8_0 pack takes no biases", name);
         if (p->D % 32) return fail(QKV_EINVAL, "%s: D must be a multiple of 32", name);
     }
-    if (p->D != 64 && p->D != 128 && p->D != 256)
-        return fail(QKV_EUNSUPPORTED, "%s: head size D=%lld not in {64, 128, 256}", name, (long long)p->D);
+    if (p->D != 64 && p->D != 96 && p->D != 128 && p->D != 256)
+        return fail(QKV_EUNSUPPORTED, "%s: head size D=%lld not in {64, 96, 128, 256}", name, (long long)p->D);
     if (!aligned(p->codes, 16)) return fail(QKV_EINVAL, "%s: codes not 16-byte aligned", name);
-    // scale and bias planes: aligned to one row of them (up to 16 bytes), the
-    // width of the kernels' row loads
+    // scale and bias planes: for the matrix-core formats aligned to one row of
+    // them (up to 16 bytes), the width of those kernels' row loads; the
+    // general paths read them one element at a time
     const size_t ss = dtype_size(p->scale_dtype);
-    const size_t ra = std::min<size_t>(16, (size_t)(p->D / p->group_size) * ss);
+    const size_t ra = qkv::fast_format(p->mode, p->bits, (int)p->D)
+                          ? std::min<size_t>(16, (size_t)(p->D / p->group_size) * ss) : ss;
     if (!aligned(p->scales, ra) || (p->biases && !aligned(p->biases, ra)))
         return fail(QKV_EINVAL, "%s: scales/biases misaligned (need %zu-byte alignment)", name, ra);
     return QKV_OK;
@@ -382,6 +391,10 @@ qkv_status attention(const char* name, const void* q, int32_t q_dtype, int64_t B
         (q_dtype != QKV_F16 || k->mode == QKV_DENSE || (k->mode == QKV_AFFINE && k->scale_dtype != QKV_F16)))
         return fail(QKV_EUNSUPPORTED, "%s: the dequantize-first strategy takes fp16 queries and a quantized "
                     "cache with fp16 scales", name);
+    if ((algo == QKV_ALGO_UNFUSED || algo == QKV_ALGO_DEQUANT_F16 || algo == QKV_ALGO_MATRIX) &&
+        k->mode != QKV_DENSE && !qkv::fast_format(k->mode, k->bits, (int)D))
+        return fail(QKV_EUNSUPPORTED, "%s: this algorithm takes affine 4/8-bit or Q8_0 caches with D a "
+                    "multiple of 64", name);
     if (opts && opts->algo == QKV_ALGO_UNFUSED && (Lq != 1 || G > 16 || B * Hq > 65535))
         return fail(QKV_EUNSUPPORTED, "%s: the unfused composition takes one query per head, a GQA "
                     "factor of at most 16 and B x Hq below 65536", name);
@@ -568,8 +581,10 @@ qkv_status qkv_dequantize(const qkv_pack* src, int64_t L, const qkv_pack* dst, v
     if ((st = check_pack(dst, "qkv_dequantize(dst)")) != QKV_OK) return st;
     if (src->mode == QKV_DENSE) return fail(QKV_EINVAL, "qkv_dequantize: the source is not quantized");
     if (dst->mode != QKV_DENSE) return fail(QKV_EINVAL, "qkv_dequantize: the destination must be a dense pack");
-    if (src->mode == QKV_AFFINE && src->scale_dtype != QKV_F16)
-        return fail(QKV_EUNSUPPORTED, "qkv_dequantize: affine packs with fp16 scales only");
+    if ((src->mode == QKV_AFFINE && src->scale_dtype != QKV_F16) ||
+        !qkv::fast_format(src->mode, src->bits, (int)src->D))
+        return fail(QKV_EUNSUPPORTED, "qkv_dequantize: affine 4/8-bit packs with fp16 scales, or Q8_0, "
+                    "with D a multiple of 64");
     if (src->B != dst->B || src->H != dst->H || src->D != dst->D)
         return fail(QKV_EINVAL, "qkv_dequantize: source and destination differ in B, H or D");
     if (L < 0 || L > src->L_cap || L > dst->L_cap)

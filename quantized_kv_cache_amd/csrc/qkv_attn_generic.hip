@@ -25,6 +25,8 @@
 // workspace and the split merge kernel combines them with the log-sum-exp
 // rule and writes the output.  This kernel favours generality over
 // speed; the matrix-core kernels cover the fp16 hot shapes.
+#include <type_traits>
+
 #include "qkv_device.hpp"
 #include "qkv_internal.hpp"
 #include "qkv_merge.hpp"
@@ -58,9 +60,41 @@ __device__ __forceinline__ float slice_elem(const uint32_t* w, float s, float b,
     }
 }
 
+// The general formats (affine 2/3/5/6-bit, symmetric 4/5-bit blocks, head
+// size 96): the words of a row's bit stream that cover the slice's
+// DPK * BITS bits, funnel-shifted so that the slice starts at bit 0 (the
+// element offsets are then compile-time constants), and the scale / bias of
+// the slice's first and last quantization group (a slice of D / 8 <= 32
+// elements spans at most two groups of >= 32).
+template <int MODE, int BITS, int D>
+struct StreamSlice {
+    static constexpr int DPK = D / 8;
+    static constexpr int W = (DPK * BITS + 31) / 32;     // words of the aligned slice
+    uint32_t k[W], v[W];
+    float ks[2], kb[2], vs[2], vb[2];
+    int split;                                           // first element of the second group
+};
+
+template <int MODE, int BITS>
+__device__ __forceinline__ float stream_elem(const uint32_t* w, const float* s, const float* b, int split,
+                                             int e) {
+    const int bit = e * BITS;
+    uint32_t u = w[bit >> 5] >> (bit & 31);
+    if ((bit & 31) + BITS > 32) u |= w[(bit >> 5) + 1] << (32 - (bit & 31));
+    u &= (1u << BITS) - 1u;
+    const int gi = e >= split ? 1 : 0;
+    if constexpr (MODE == MODE_AFFINE) {
+        return s[gi] * (float)u + b[gi];
+    } else {
+        const int c = (int)(u << (32 - BITS)) >> (32 - BITS);   // two's complement
+        return s[gi] * (float)c;
+    }
+}
+
 template <int QT, int MODE, int BITS, int D>
 __global__ __launch_bounds__(256) void attn_generic_kernel(AttnLaunch p) {
-    constexpr int ST = (MODE == MODE_Q8_0) ? DT_F16 : QT;   // scale dtype
+    constexpr bool STREAM = !fast_format(MODE, BITS, D);
+    constexpr int ST = (MODE == MODE_AFFINE) ? QT : DT_F16;  // scale dtype
     constexpr int DPK = D / 8;                               // d per lane (scores)
     constexpr int DPO = D / 16;                              // d per lane (output)
     __shared__ float qs[RTG][D];
@@ -90,8 +124,9 @@ __global__ __launch_bounds__(256) void attn_generic_kernel(AttnLaunch p) {
     const uint8_t* kc = (const uint8_t*)p.k.codes;
     const uint8_t* vc = (const uint8_t*)p.v.codes;
 
-    // this thread's key of a block and d slice (one quantization group)
-    using Raw = RawSlice<MODE, BITS, D>;
+    // this thread's key of a block and d slice (one quantization group, or
+    // up to two for the general formats)
+    using Raw = std::conditional_t<STREAM, StreamSlice<MODE, BITS, D>, RawSlice<MODE, BITS, D>>;
     constexpr int ROWB = D * BITS / 8;
     const int kk = tid / 8, part = tid % 8;
     const int NGr = D >> p.gs_log2;
@@ -99,9 +134,43 @@ __global__ __launch_bounds__(256) void attn_generic_kernel(AttnLaunch p) {
     // rows past the range load the range's last row (never used: their scores
     // are -inf and their V entries 0), so the loads need no branch
     const int64_t j_last = max(j_end - 1, (int64_t)0);
+    // general formats: the slice's first bit, word and groups
+    constexpr int RW = D * BITS / 32;                    // words per row
+    const int fbit = part * Raw::DPK * BITS;
+    const int w0 = fbit >> 5, sh0 = fbit & 31;
+    const int g0 = (part * Raw::DPK) >> p.gs_log2;
+    const int g1 = (part * Raw::DPK + Raw::DPK - 1) >> p.gs_log2;
+    const int gsplit = ((g0 + 1) << p.gs_log2) - part * Raw::DPK;
+    auto load_stream = [&](const uint8_t* base, int64_t r, uint32_t* out) {
+        const uint32_t* rw = (const uint32_t*)(base + r * ROWB);
+        uint32_t x[Raw::W + 1];
+#pragma unroll
+        for (int i = 0; i <= Raw::W; ++i) x[i] = rw[min(w0 + i, RW - 1)];
+#pragma unroll
+        for (int i = 0; i < Raw::W; ++i)
+            out[i] = sh0 ? (x[i] >> sh0) | (x[i + 1] << (32 - sh0)) : x[i];
+    };
     auto load_raw = [&](int64_t jb, Raw& R) {
         const int64_t j = min(jb + kk, j_last);
         const int64_t kr = krow0 + j * p.k.sl, vr = vrow0 + j * p.v.sl;
+        if constexpr (STREAM) {
+            load_stream(kc, kr, R.k);
+            load_stream(vc, vr, R.v);
+            R.split = gsplit;
+#pragma unroll
+            for (int t2 = 0; t2 < 2; ++t2) {
+                const int gg = t2 ? g1 : g0;
+                R.ks[t2] = load_as_f32<ST>(p.k.scales, kr * NGr + gg);
+                R.vs[t2] = load_as_f32<ST>(p.v.scales, vr * NGr + gg);
+                if constexpr (MODE == MODE_AFFINE) {
+                    R.kb[t2] = load_as_f32<ST>(p.k.biases, kr * NGr + gg);
+                    R.vb[t2] = load_as_f32<ST>(p.v.biases, vr * NGr + gg);
+                } else {
+                    R.kb[t2] = R.vb[t2] = 0.0f;
+                }
+            }
+            return;
+        } else {
         const uint32_t* kw = (const uint32_t*)(kc + kr * ROWB) + part * Raw::W;
         const uint32_t* vw = (const uint32_t*)(vc + vr * ROWB) + part * Raw::W;
 #pragma unroll
@@ -114,6 +183,15 @@ __global__ __launch_bounds__(256) void attn_generic_kernel(AttnLaunch p) {
             R.kb = load_as_f32<ST>(p.k.biases, kr * NGr + gsl);
             R.vb = load_as_f32<ST>(p.v.biases, vr * NGr + gsl);
         }
+        }
+    };
+    auto k_elem = [&](const Raw& R, int e) -> float {
+        if constexpr (STREAM) return stream_elem<MODE, BITS>(R.k, R.ks, R.kb, R.split, e);
+        else return slice_elem<MODE, BITS>(R.k, R.ks, R.kb, e);
+    };
+    auto v_elem = [&](const Raw& R, int e) -> float {
+        if constexpr (STREAM) return stream_elem<MODE, BITS>(R.v, R.vs, R.vb, R.split, e);
+        else return slice_elem<MODE, BITS>(R.v, R.vs, R.vb, e);
     };
     Raw cur, nxt;
     load_raw(j_begin, cur);
@@ -151,7 +229,7 @@ __global__ __launch_bounds__(256) void attn_generic_kernel(AttnLaunch p) {
 #pragma unroll
                 for (int e = 0; e < DPK; ++e) {
                     const int d = part * DPK + e;
-                    const float kv = slice_elem<MODE, BITS>(cur.k, cur.ks, cur.kb, e);
+                    const float kv = k_elem(cur, e);
 #pragma unroll
                     for (int r = 0; r < RTG; ++r) acc[r] += qs[r][d] * kv;
                 }
@@ -211,7 +289,7 @@ __global__ __launch_bounds__(256) void attn_generic_kernel(AttnLaunch p) {
         // ---- V block -> LDS (fp32; keys past the range hold zeros)
 #pragma unroll
         for (int e = 0; e < DPK; ++e)
-            vt[kk][part * DPK + e] = (jb + kk < j_end) ? slice_elem<MODE, BITS>(cur.v, cur.vs, cur.vb, e) : 0.0f;
+            vt[kk][part * DPK + e] = (jb + kk < j_end) ? v_elem(cur, e) : 0.0f;
         __syncthreads();
         // ---- o = o * alpha + P V
         {
@@ -269,6 +347,7 @@ template <int QT, int MODE, int BITS>
 hipError_t dispatch_d(int D, int64_t B, const AttnLaunch& p, hipStream_t s) {
     switch (D) {
         case 64: return launch_g<QT, MODE, BITS, 64>(B, p, s);
+        case 96: return launch_g<QT, MODE, BITS, 96>(B, p, s);
         case 128: return launch_g<QT, MODE, BITS, 128>(B, p, s);
         case 256: return launch_g<QT, MODE, BITS, 256>(B, p, s);
     }
@@ -279,8 +358,20 @@ template <int QT>
 hipError_t dispatch_fmt(int mode, int bits, int D, int64_t B, const AttnLaunch& p,
                         hipStream_t s) {
     if (mode == MODE_Q8_0) return dispatch_d<QT, MODE_Q8_0, 8>(D, B, p, s);
-    if (bits == 4) return dispatch_d<QT, MODE_AFFINE, 4>(D, B, p, s);
-    if (bits == 8) return dispatch_d<QT, MODE_AFFINE, 8>(D, B, p, s);
+    if (mode == MODE_QSYM) {
+        if (bits == 4) return dispatch_d<QT, MODE_QSYM, 4>(D, B, p, s);
+        if (bits == 5) return dispatch_d<QT, MODE_QSYM, 5>(D, B, p, s);
+        return hipErrorNotSupported;
+    }
+    if (mode != MODE_AFFINE) return hipErrorNotSupported;
+    switch (bits) {
+        case 2: return dispatch_d<QT, MODE_AFFINE, 2>(D, B, p, s);
+        case 3: return dispatch_d<QT, MODE_AFFINE, 3>(D, B, p, s);
+        case 4: return dispatch_d<QT, MODE_AFFINE, 4>(D, B, p, s);
+        case 5: return dispatch_d<QT, MODE_AFFINE, 5>(D, B, p, s);
+        case 6: return dispatch_d<QT, MODE_AFFINE, 6>(D, B, p, s);
+        case 8: return dispatch_d<QT, MODE_AFFINE, 8>(D, B, p, s);
+    }
     return hipErrorNotSupported;
 }
 

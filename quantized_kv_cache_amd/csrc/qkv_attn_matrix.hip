@@ -830,7 +830,9 @@ hipError_t by_d(int D, int64_t B, const AttnLaunch& p, hipStream_t s) {
 bool matrix_supported(int q_dtype, int mode, int bits, int group_size, int D, int G, int64_t Lq) {
     if (q_dtype != DT_F16 || Lq < 1 || G < 1) return false;
     if (D != 64 && D != 128 && D != 256) return false;
-    if (mode == MODE_Q8_0 || mode == MODE_DENSE) return true;
+    if (mode == MODE_DENSE) return true;
+    if (!fast_format(mode, bits, D)) return false;
+    if (mode == MODE_Q8_0) return true;
     if (bits != 4 && bits != 8) return false;
     if (group_size != 32 && group_size != 64 && group_size != 128) return false;
     return D % group_size == 0;

@@ -566,7 +566,7 @@ hipError_t by_d(int D, int64_t B, const AttnLaunch& p, hipStream_t s) {
 
 bool narrow_decode_supported(int q_dtype, int mode, int bits, int group_size, int D, int G,
                              int64_t Lq) {
-    if (q_dtype != DT_F16 || Lq != 1 || G < 1 || G > 4 || mode == MODE_DENSE) return false;
+    if (q_dtype != DT_F16 || Lq != 1 || G < 1 || G > 4 || !fast_format(mode, bits, D)) return false;
     if (D != 64 && D != 128) return false;
     const int gs = mode == MODE_Q8_0 ? 32 : group_size;
     if (mode == MODE_AFFINE && (bits != 4 && bits != 8)) return false;

@@ -9,7 +9,15 @@
 namespace qkv {
 
 enum DType { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2 };
-enum Mode { MODE_AFFINE = 0, MODE_Q8_0 = 1, MODE_DENSE = 2 };
+enum Mode { MODE_AFFINE = 0, MODE_Q8_0 = 1, MODE_DENSE = 2, MODE_QSYM = 3 };
+
+// Formats of the matrix-core and fast quantize kernels: affine 4/8-bit and
+// Q8_0 with D a multiple of 64.  Every other format (affine 2/3/5/6-bit, the
+// symmetric 4/5-bit blocks, head size 96) takes the general paths, which
+// read codes as a bit stream.
+constexpr bool fast_format(int mode, int bits, int D) {
+    return (mode == MODE_Q8_0 || (mode == MODE_AFFINE && (bits == 4 || bits == 8))) && D % 64 == 0;
+}
 enum MaskKind { MASK_NONE = 0, MASK_CAUSAL = 1, MASK_ADDITIVE = 2 };
 
 // One tensor's worth of rows to quantize: source rows [B,H,T,D] with element

@@ -56,11 +56,12 @@ __global__ __launch_bounds__(256) void merge_splits_kernel(AttnLaunch p) {
     const int f = blockIdx.z * MC + threadIdx.x % MC;   // float4 column of the row
     const int sg = threadIdx.x / MC;
     const int S = p.S;
+    const bool f_ok = f < F4;                     // D = 96: the last chunk is 32 d wide
 
     const float2* ml = (const float2*)p.part_ml + (tile * S * 16 + r);
     const float4* po = (const float4*)p.part_o + ((tile * S * 16 + r) * F4 + f);
     State st{-INFINITY, 0.0f, {0.f, 0.f, 0.f, 0.f}};
-    for (int s0 = sg; s0 < S; s0 += U * SG) {
+    for (int s0 = sg; s0 < S && f_ok; s0 += U * SG) {
         float2 a[U];
         float4 o[U];
 #pragma unroll
@@ -77,7 +78,7 @@ __global__ __launch_bounds__(256) void merge_splits_kernel(AttnLaunch p) {
     }
     red[threadIdx.x] = st;
     __syncthreads();
-    if (sg != 0) return;
+    if (sg != 0 || !f_ok) return;
 #pragma unroll
     for (int g = 1; g < SG; ++g) {
         const State& o = red[g * MC + threadIdx.x];
@@ -102,7 +103,9 @@ __global__ __launch_bounds__(256) void merge_splits_small(AttnLaunch p) {
     constexpr int RPW = 256 / F4;                 // rows per workgroup
     pin_args(p);
     const int64_t tile = blockIdx.x;
+    if (threadIdx.x >= RPW * F4) return;          // D = 96: 240 of the 256 threads
     const int r = blockIdx.y * RPW + threadIdx.x / F4;
+    if (r >= 16) return;
     const Row rw = locate(p, (uint32_t)tile, r);
     if (rw.pr >= p.n_rows) return;
     const int64_t b = rw.b, kvh = rw.kvh, i = rw.i, h = rw.h;
@@ -158,6 +161,7 @@ hipError_t launch_q(int D, int64_t B, const AttnLaunch& p, hipStream_t s) {
     if (p.S <= kSmallS) {
         switch (D) {
             case 64: return launch_small<QT, 64>(B, p, s);
+            case 96: return launch_small<QT, 96>(B, p, s);
             case 128: return launch_small<QT, 128>(B, p, s);
             case 256: return launch_small<QT, 256>(B, p, s);
             default: return hipErrorNotSupported;
@@ -165,9 +169,10 @@ hipError_t launch_q(int D, int64_t B, const AttnLaunch& p, hipStream_t s) {
     }
     // rows of a tile that exist: all 16 unless the (single) tile is short
     const unsigned rows = (unsigned)(p.n_rows < 16 ? p.n_rows : 16);
-    dim3 grid((unsigned)(B * p.Hk * p.n_rt), rows, (unsigned)(D / (4 * MC)));
+    dim3 grid((unsigned)(B * p.Hk * p.n_rt), rows, (unsigned)((D + 4 * MC - 1) / (4 * MC)));
     switch (D) {
         case 64: hipLaunchKernelGGL((merge_splits_kernel<QT, 64>), grid, dim3(256), 0, s, p); break;
+        case 96: hipLaunchKernelGGL((merge_splits_kernel<QT, 96>), grid, dim3(256), 0, s, p); break;
         case 128: hipLaunchKernelGGL((merge_splits_kernel<QT, 128>), grid, dim3(256), 0, s, p); break;
         case 256: hipLaunchKernelGGL((merge_splits_kernel<QT, 256>), grid, dim3(256), 0, s, p); break;
         default: return hipErrorNotSupported;

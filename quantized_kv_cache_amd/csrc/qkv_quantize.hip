@@ -156,6 +156,122 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(QuantLaunch p) {
     }
 }
 
+// The general path: affine codes of any width, symmetric 4/5-bit blocks, and
+// head size 96.  One thread per quantization group (per 32-block for the
+// symmetric formats): two passes over the group's values (its range, then
+// its codes), the codes packed into the group's words of the row's bit
+// stream (a group of GS values at BITS bits starts on a word boundary since
+// GS * BITS is a multiple of 32).  The arithmetic is that of the fast kernel
+// above.
+template <int DT>
+__device__ __forceinline__ float load1(const void* base, int64_t off) {
+    return load_as_f32<DT>(base, off);
+}
+
+template <int DT, int MODE, int BITS, int GS>
+__global__ __launch_bounds__(256) void quantize_groups_kernel(QuantLaunch p, int D) {
+    const QuantJob& job = p.job[blockIdx.y];
+    const int ng = D / GS;
+    const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t row = gid / ng;
+    const int g = (int)(gid % ng);
+    if (row >= p.rows) return;
+    const int64_t t = row % p.T;
+    const int64_t bh = row / p.T;
+    const int64_t h = bh % p.H;
+    const int64_t b = bh / p.H;
+    const int64_t src = b * job.xs0 + h * job.xs1 + t * job.xs2 + (int64_t)g * GS;
+    const int64_t dst = b * job.sb + h * job.sh + (p.offset + t) * job.sl;
+    uint32_t* wout = (uint32_t*)((uint8_t*)job.codes + dst * (int64_t)(D * BITS / 8)) + g * (GS * BITS / 32);
+
+    uint64_t acc = 0;
+    int nacc = 0, wi = 0;
+    auto put = [&](uint32_t c) {
+        acc |= (uint64_t)c << nacc;
+        nacc += BITS;
+        if (nacc >= 32) {
+            wout[wi++] = (uint32_t)acc;
+            acc >>= 32;
+            nacc -= 32;
+        }
+    };
+    if constexpr (MODE == MODE_AFFINE) {
+        constexpr float NL = (float)((1 << BITS) - 1);
+        float mn = load1<DT>(job.x, src), mx = mn;
+        for (int i = 1; i < GS; ++i) {
+            const float v = load1<DT>(job.x, src + i);
+            mn = fminf(mn, v);
+            mx = fmaxf(mx, v);
+        }
+        const float eps = round_to<DT>(1e-7f);
+        float s32 = (mx - mn) / NL;
+        if (s32 < eps) s32 = eps;
+        const float s = round_to<DT>(s32);
+        const float bias = round_to<DT>(mn);
+        for (int i = 0; i < GS; ++i) {
+            float q = __builtin_rintf((load1<DT>(job.x, src + i) - bias) / s);
+            q = fminf(fmaxf(q, 0.0f), NL);
+            put((uint32_t)q);
+        }
+        store_from_f32<DT>(job.scales, dst * ng + g, s32);
+        store_from_f32<DT>(job.biases, dst * ng + g, mn);
+    } else {
+        constexpr float QM = (float)((1 << (BITS - 1)) - 1);
+        float amax = 0.0f;
+        for (int i = 0; i < GS; ++i) amax = fmaxf(amax, fabsf(load1<DT>(job.x, src + i)));
+        const uint16_t dh = f32_to_f16(amax / QM);
+        const float d = f16_to_f32(dh);
+        for (int i = 0; i < GS; ++i) {
+            float q = 0.0f;
+            if (d != 0.0f) {
+                q = __builtin_rintf(load1<DT>(job.x, src + i) / d);
+                q = fminf(fmaxf(q, -QM), QM);
+            }
+            put((uint32_t)(int32_t)q & ((1u << BITS) - 1u));
+        }
+        ((uint16_t*)job.scales)[dst * ng + g] = dh;
+    }
+}
+
+template <int DT, int MODE, int BITS, int GS>
+hipError_t launch_groups(int D, const QuantLaunch& p, int njobs, hipStream_t stream) {
+    if (D % GS) return hipErrorNotSupported;
+    const int64_t n = p.rows * (D / GS);
+    const int64_t blocks = (n + 255) / 256;
+    if (blocks == 0) return hipSuccess;
+    hipLaunchKernelGGL((quantize_groups_kernel<DT, MODE, BITS, GS>), dim3((unsigned)blocks, njobs), dim3(256),
+                       0, stream, p, D);
+    return hipGetLastError();
+}
+
+template <int DT, int BITS>
+hipError_t groups_by_gs(int gs, int D, const QuantLaunch& p, int njobs, hipStream_t s) {
+    if (gs == 32) return launch_groups<DT, MODE_AFFINE, BITS, 32>(D, p, njobs, s);
+    if (gs == 64) return launch_groups<DT, MODE_AFFINE, BITS, 64>(D, p, njobs, s);
+    if (gs == 128) return launch_groups<DT, MODE_AFFINE, BITS, 128>(D, p, njobs, s);
+    return hipErrorNotSupported;
+}
+
+template <int DT>
+hipError_t dispatch_groups(int mode, int bits, int gs, int D, const QuantLaunch& p, int njobs, hipStream_t s) {
+    if (mode == MODE_QSYM) {
+        if (bits == 4) return launch_groups<DT, MODE_QSYM, 4, 32>(D, p, njobs, s);
+        if (bits == 5) return launch_groups<DT, MODE_QSYM, 5, 32>(D, p, njobs, s);
+        return hipErrorNotSupported;
+    }
+    if (mode == MODE_Q8_0) return launch_groups<DT, MODE_QSYM, 8, 32>(D, p, njobs, s);
+    if (mode != MODE_AFFINE) return hipErrorNotSupported;
+    switch (bits) {
+        case 2: return groups_by_gs<DT, 2>(gs, D, p, njobs, s);
+        case 3: return groups_by_gs<DT, 3>(gs, D, p, njobs, s);
+        case 4: return groups_by_gs<DT, 4>(gs, D, p, njobs, s);
+        case 5: return groups_by_gs<DT, 5>(gs, D, p, njobs, s);
+        case 6: return groups_by_gs<DT, 6>(gs, D, p, njobs, s);
+        case 8: return groups_by_gs<DT, 8>(gs, D, p, njobs, s);
+    }
+    return hipErrorNotSupported;
+}
+
 template <int DT, int MODE, int BITS, int GS, int D>
 hipError_t launch_q(const QuantLaunch& p, int njobs, hipStream_t stream) {
     constexpr int RPW = 64 / (D / 8);
@@ -201,6 +317,14 @@ hipError_t dispatch_fmt(int mode, int bits, int gs, int D, const QuantLaunch& p,
 
 hipError_t launch_quantize(int x_dtype, int mode, int bits, int group_size, int D,
                            const QuantLaunch& p, int njobs, hipStream_t stream) {
+    if (mode != MODE_DENSE && !fast_format(mode, bits, D)) {
+        switch (x_dtype) {
+            case DT_F32: return dispatch_groups<DT_F32>(mode, bits, group_size, D, p, njobs, stream);
+            case DT_F16: return dispatch_groups<DT_F16>(mode, bits, group_size, D, p, njobs, stream);
+            case DT_BF16: return dispatch_groups<DT_BF16>(mode, bits, group_size, D, p, njobs, stream);
+        }
+        return hipErrorNotSupported;
+    }
     switch (x_dtype) {
         case DT_F32: return dispatch_fmt<DT_F32>(mode, bits, group_size, D, p, njobs, stream);
         case DT_F16: return dispatch_fmt<DT_F16>(mode, bits, group_size, D, p, njobs, stream);

@@ -50,9 +50,11 @@ def _quant(L, pk, x=FAKE + 0x400000, dt=_lib.QKV_F16, strides=(16384, 8192, 128)
 
 
 @pytest.mark.parametrize("kw,status,msg", [
-    (dict(bits=3), _lib.QKV_EUNSUPPORTED, "bits"),
+    (dict(bits=7), _lib.QKV_EUNSUPPORTED, "bits"),
     (dict(group_size=48), _lib.QKV_EUNSUPPORTED, "group_size"),
-    (dict(D=96, group_size=32), _lib.QKV_EUNSUPPORTED, "head size"),
+    (dict(D=160, group_size=32), _lib.QKV_EUNSUPPORTED, "head size"),
+    (dict(mode=_lib.QKV_QSYM, bits=6, group_size=32, biases=None), _lib.QKV_EINVAL, "bits 4 or 5"),
+    (dict(mode=_lib.QKV_QSYM, bits=4, group_size=32), _lib.QKV_EINVAL, "biases"),
     (dict(D=160, group_size=64), _lib.QKV_EINVAL, "multiple"),
     (dict(codes=FAKE + 4), _lib.QKV_EINVAL, "aligned"),
     (dict(scales=FAKE + 0x100001), _lib.QKV_EINVAL, "misaligned"),

@@ -1,0 +1,99 @@
+"""The wider format set on the GPU: affine codes of 2, 3, 5 and 6 bits, head
+size 96, and the symmetric 4/5-bit blocks (the Q4_0/Q5_0 reading), plus Q8_0
+and affine 4/8-bit at head size 96.  Quantize and append must give the
+oracle's bits; decode and prefill (on the generic kernel, with key splits
+and the merge kernels) must be within the attention tolerance of the
+oracle."""
+import math
+import zlib
+
+import numpy as np
+import pytest
+
+import quantized_kv_cache_amd as qkv
+from tests._cases import (W, assert_close, assert_pack_equal, oracle_attention, oracle_pack,
+                          pack_numpy, to_dev)
+
+pytestmark = pytest.mark.gpu
+
+FORMATS = [
+    # mode, bits, gs, D, dtype
+    ("affine", 2, 32, 128, "f16"),
+    ("affine", 3, 64, 128, "f16"),
+    ("affine", 3, 32, 96, "bf16"),
+    ("affine", 5, 32, 256, "f16"),
+    ("affine", 5, 128, 128, "f32"),
+    ("affine", 6, 64, 64, "f16"),
+    ("affine", 6, 32, 96, "f16"),
+    ("affine", 2, 64, 256, "bf16"),
+    ("affine", 4, 32, 96, "f16"),
+    ("affine", 8, 32, 96, "f32"),
+    ("q8_0", 8, 32, 96, "f16"),
+    ("qsym", 4, 32, 128, "f16"),
+    ("qsym", 5, 32, 96, "f16"),
+    ("qsym", 4, 32, 256, "bf16"),
+    ("qsym", 5, 32, 64, "f32"),
+]
+
+
+def _seed(*a):
+    return zlib.crc32(repr(a).encode()) % 100000
+
+
+def _case(fmt, B, Hq, Hk, Lq, L, dist="normal"):
+    mode, bits, gs, D, dt = fmt
+    s = _seed(fmt, B, Hq, Hk, Lq, L)
+    q = W.random_case(s, (B, Hq, Lq, D), dist, dt)
+    k = W.random_case(s + 1, (B, Hk, L, D), dist, dt)
+    v = W.random_case(s + 2, (B, Hk, L, D), dist, dt)
+    kp = qkv.qkv_quantize(to_dev(k, dt), mode, bits, gs)
+    vp = qkv.qkv_quantize(to_dev(v, dt), mode, bits, gs)
+    kr, vr = oracle_pack(k, dt, mode, bits, gs), oracle_pack(v, dt, mode, bits, gs)
+    assert_pack_equal(pack_numpy(kp), kr)
+    assert_pack_equal(pack_numpy(vp), vr)
+    return q, kp, vp, kr, vr
+
+
+@pytest.mark.parametrize("fmt", FORMATS, ids=lambda f: "-".join(map(str, f)))
+def test_formats_quantize_append_and_decode(fmt):
+    mode, bits, gs, D, dt = fmt
+    q, kp, vp, kr, vr = _case(fmt, 2, 8, 2, 1, 517)
+    scale = 1.0 / math.sqrt(D)
+    ref = oracle_attention(q, dt, kr, vr, 517, mode, bits, gs, scale)
+    qd = to_dev(q, dt)
+    assert qkv.qsdpa_plan(qd, kp, 517)["kernel"] == "attn_generic_kernel"
+    for splits in (0, 1, 5, 17):
+        out = qkv.qsdpa_decode(qd, kp, vp, 517, scale, num_splits=splits)
+        assert_close(out, ref, f"decode {fmt} splits={splits}")
+    # append three tokens at an offset: bit-exact rows, the rest untouched
+    new_k = W.random_case(_seed(fmt, "k"), (2, 2, 3, D), "normal", dt)
+    new_v = W.random_case(_seed(fmt, "v"), (2, 2, 3, D), "normal", dt)
+    before_k = pack_numpy(kp)
+    qkv.qkv_update_append(kp, vp, to_dev(new_k, dt), to_dev(new_v, dt), 200)
+    after_k = pack_numpy(kp)
+    nk = oracle_pack(new_k, dt, mode, bits, gs)
+    for name, a in nk.items():
+        if a is None:
+            continue
+        g, r = after_k[name][:, :, 200:203], a
+        assert np.array_equal(np.ascontiguousarray(g).view(np.uint8), np.ascontiguousarray(r).view(np.uint8)), name
+        keep = np.r_[0:200, 203:517]
+        assert np.array_equal(np.ascontiguousarray(after_k[name][:, :, keep]).view(np.uint8),
+                              np.ascontiguousarray(before_k[name][:, :, keep]).view(np.uint8)), name
+
+
+@pytest.mark.parametrize("fmt", FORMATS[::2], ids=lambda f: "-".join(map(str, f)))
+def test_formats_prefill(fmt):
+    mode, bits, gs, D, dt = fmt
+    q, kp, vp, kr, vr = _case(fmt, 1, 8, 2, 21, 300)
+    ref = oracle_attention(q, dt, kr, vr, 300, mode, bits, gs, 0.1, causal=True)
+    for splits in (0, 3):
+        out = qkv.qsdpa_prefill(to_dev(q, dt), kp, vp, 300, 0.1, causal=True, num_splits=splits)
+        assert_close(out, ref, f"prefill {fmt} splits={splits}")
+
+
+def test_formats_rejected_by_matrix_only_algorithms():
+    q, kp, vp, _, _ = _case(("affine", 3, 32, 128, "f16"), 1, 8, 2, 1, 100)
+    for algo in ("matrix", "unfused", "dequant_f16"):
+        with pytest.raises(qkv.QKVError):
+            qkv.qsdpa_decode(to_dev(q, "f16"), kp, vp, 100, 0.1, algo=algo)

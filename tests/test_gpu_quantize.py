@@ -29,7 +29,7 @@ def test_quantize_fuzz_bitexact(dtype, mode, bits, gs, D):
     assert_pack_equal(pack_numpy(pk), oracle_pack(x, dtype, mode, bits, gs))
 
 
-@pytest.mark.parametrize("name", list(W.WORKLOADS))
+@pytest.mark.parametrize("name", [n for n, w in W.WORKLOADS.items() if w.mode != "dense"])
 def test_quantize_workload_bitexact(name):
     w = W.WORKLOADS[name]
     inp = W.make_inputs(w)
