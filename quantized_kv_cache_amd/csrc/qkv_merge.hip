@@ -1,9 +1,11 @@
 // Split merge kernels.  Many splits: one workgroup per (row tile, row, 64-d
 // chunk of the output row): grid x = tile, y = row, z = chunk.  Its 256 threads are 16
-// float4 columns x 16 split groups, so a thread combines at most S/16 split
+// float4 columns x 16 split groups, so a thread reads at most S/16 split
 // states (all its loads issued before it waits: one memory round trip for
-// S <= 128).  States combine online in log2 units, the split groups combine
-// through LDS, and the chunk is written in the query dtype.
+// S <= 128).  The row's maximum M over the splits' m (log2 units) comes
+// first, then every state is weighted by 2^(m_s - M) and the weighted sums
+// of the split groups are added through LDS, so no split waits on another's
+// rescaling; the chunk is written in the query dtype.
 #include <algorithm>
 
 #include "qkv_merge.hpp"
@@ -11,10 +13,6 @@
 namespace qkv {
 
 namespace {
-
-using State = SplitState;
-
-__device__ __forceinline__ void combine(State& a, float m, float l, float4 o) { combine_state(a, m, l, o); }
 
 // Every argument the merge reads, fetched in one round trip at the start.
 __device__ __forceinline__ void pin_args(const AttnLaunch& p) {
@@ -45,7 +43,9 @@ constexpr int U = 8;            // loads in flight per batch
 template <int QT, int D>
 __global__ __launch_bounds__(256) void merge_splits_kernel(AttnLaunch p) {
     constexpr int F4 = D / 4;
-    __shared__ State red[256];
+    __shared__ float red_m[256];
+    __shared__ float red_l[256];
+    __shared__ float4 red_o[256];
 
     pin_args(p);
     const int64_t tile = blockIdx.x;
@@ -58,38 +58,74 @@ __global__ __launch_bounds__(256) void merge_splits_kernel(AttnLaunch p) {
     const int S = p.S;
     const bool f_ok = f < F4;                     // D = 96: the last chunk is 32 d wide
 
+    // The row's maximum first (its m values only), then the sums weighted by
+    // 2^(m_s - M): no rescaling chain between splits.
     const float2* ml = (const float2*)p.part_ml + (tile * S * 16 + r);
     const float4* po = (const float4*)p.part_o + ((tile * S * 16 + r) * F4 + f);
-    State st{-INFINITY, 0.0f, {0.f, 0.f, 0.f, 0.f}};
-    for (int s0 = sg; s0 < S && f_ok; s0 += U * SG) {
-        float2 a[U];
-        float4 o[U];
+    float mx = -INFINITY;
+    for (int s0 = sg; s0 < S; s0 += U * SG) {
+        float a[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int s = s0 + u * SG;
-            if (s < S) {
-                a[u] = ml[(int64_t)s * 16];
-                o[u] = po[(int64_t)s * 16 * F4];
-            }
+            a[u] = s < S ? ml[(int64_t)s * 16].x : -INFINITY;
         }
 #pragma unroll
-        for (int u = 0; u < U; ++u)
-            if (s0 + u * SG < S) combine(st, a[u].x, a[u].y, o[u]);
+        for (int u = 0; u < U; ++u) mx = fmaxf(mx, a[u]);
     }
-    red[threadIdx.x] = st;
+    red_m[threadIdx.x] = mx;
+    __syncthreads();
+    float M = red_m[threadIdx.x % MC];
+#pragma unroll
+    for (int g = 1; g < SG; ++g) M = fmaxf(M, red_m[g * MC + threadIdx.x % MC]);
+    float l = 0.0f;
+    float4 o = {0.f, 0.f, 0.f, 0.f};
+    if (M != -INFINITY && f_ok) {
+        for (int s0 = sg; s0 < S; s0 += U * SG) {
+            float2 a[U];
+            float4 x[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int s = s0 + u * SG;
+                if (s < S) {
+                    a[u] = ml[(int64_t)s * 16];
+                    x[u] = po[(int64_t)s * 16 * F4];
+                } else {
+                    a[u] = float2{-INFINITY, 0.0f};
+                    x[u] = float4{0.f, 0.f, 0.f, 0.f};
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const float w = a[u].x == -INFINITY ? 0.0f : fast_exp2(a[u].x - M);
+                l += w * a[u].y;
+                o.x += w * x[u].x;
+                o.y += w * x[u].y;
+                o.z += w * x[u].z;
+                o.w += w * x[u].w;
+            }
+        }
+    }
+    red_l[threadIdx.x] = l;
+    red_o[threadIdx.x] = o;
     __syncthreads();
     if (sg != 0 || !f_ok) return;
 #pragma unroll
     for (int g = 1; g < SG; ++g) {
-        const State& o = red[g * MC + threadIdx.x];
-        combine(st, o.m, o.l, o.o);
+        const int t = g * MC + threadIdx.x;
+        l += red_l[t];
+        const float4 y = red_o[t];
+        o.x += y.x;
+        o.y += y.y;
+        o.z += y.z;
+        o.w += y.w;
     }
-    const float inv = st.l > 0.0f ? 1.0f / st.l : 0.0f;
+    const float inv = l > 0.0f ? 1.0f / l : 0.0f;
     const int64_t ob = ((b * p.Hq + h) * p.Lq + i) * D + 4 * f;
-    store_from_f32<QT>(p.out, ob, st.o.x * inv);
-    store_from_f32<QT>(p.out, ob + 1, st.o.y * inv);
-    store_from_f32<QT>(p.out, ob + 2, st.o.z * inv);
-    store_from_f32<QT>(p.out, ob + 3, st.o.w * inv);
+    store_from_f32<QT>(p.out, ob, o.x * inv);
+    store_from_f32<QT>(p.out, ob + 1, o.y * inv);
+    store_from_f32<QT>(p.out, ob + 2, o.z * inv);
+    store_from_f32<QT>(p.out, ob + 3, o.w * inv);
 }
 
 // Few splits (S <= kSmallS, the prefill case): one thread per float4 column

@@ -7,7 +7,9 @@
 // across workgroups).  A row with no visible key (every m_s = -inf) gives 0.
 //
 // Workspace of a call: [tickets: kTicketBytes, one uint32 per (batch, kv
-// head)] [ml: tiles x S x 16 x 2] [o: tiles x S x 16 x D] (fp32).  Either the
+// head)] [ml: tiles x S x 16 x 2] [o: tiles x S x 16 x D] (fp32).  The
+// merges take the row's maximum over its splits first and then add the
+// states weighted by 2^(m_s - M).  Either the
 // attention kernel writes the states and merge_splits_kernel, launched next on
 // the same stream, reads them (kernel order is the only synchronisation), or
 // the attention kernel merges them itself (merge_last below): every workgroup
@@ -35,25 +37,6 @@ constexpr size_t kTicketBytes = kTicketWords * 4;
 // Zero-fills 'bytes' (a multiple of 16) at p on 'stream' with a kernel (no
 // memset node, so the call can be captured in a graph).
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t stream);
-
-struct SplitState {
-    float m, l;
-    float4 o;
-};
-
-// Online combination of two partial softmax states (log2 units).
-__device__ __forceinline__ void combine_state(SplitState& a, float m, float l, float4 o) {
-    if (m == -INFINITY) return;
-    const float mm = fmaxf(a.m, m);
-    const float fa = (a.m == -INFINITY) ? 0.0f : fast_exp2(a.m - mm);
-    const float fb = fast_exp2(m - mm);
-    a.l = a.l * fa + l * fb;
-    a.o.x = a.o.x * fa + o.x * fb;
-    a.o.y = a.o.y * fa + o.y * fb;
-    a.o.z = a.o.z * fa + o.z * fb;
-    a.o.w = a.o.w * fa + o.w * fb;
-    a.m = mm;
-}
 
 // Cache policy bits of a buffer access: sc1 = device scope.  A store with it
 // is performed in memory shared by all XCDs (not only in the writer's L2)
@@ -84,10 +67,13 @@ __device__ __forceinline__ void wait_stores() {
 
 // The fused merge for single-query tiles (rows = the G <= GP query heads of a
 // kv head), run by all NTHR threads of the last workgroup: thread -> (float4
-// column c of the GP x D outputs, split group sg); it combines splits sg,
-// sg + SGN, ... (loads issued 8 at a time), the SGN group states combine
-// through 'lds' (>= 6 NTHR floats) in group order, and column c's 4 fp16
-// outputs are stored.  Same result for any workgroup that runs it.
+// column c of the GP x D outputs, split group sg); it reads splits sg,
+// sg + SGN, ... (loads issued 8 at a time): their m values first, for the
+// row's maximum M (combined over the split groups through 'lds', >= 6 NTHR
+// floats), then the states weighted by 2^(m_s - M), whose sums the split
+// groups add through 'lds' in group order; column c's 4 fp16 outputs are
+// stored.  No split waits on another's rescaling, and any workgroup that
+// runs it gets the same result.
 template <int NTHR, int D, int GP>
 __device__ __forceinline__ void merge_last(const AttnLaunch& p, int64_t b, int64_t kvh, int64_t bk,
                                            float* lds) {
@@ -102,42 +88,80 @@ __device__ __forceinline__ void merge_last(const AttnLaunch& p, int64_t b, int64
     const int S = p.S, G = p.G;
     const auto rml = flat_rsrc(p.part_ml + bk * S * 32, (uint32_t)S * 32 * 4);
     const auto ro = flat_rsrc(p.part_o + bk * S * 16 * D, (uint32_t)S * 16 * D * 4);
-    SplitState st{-INFINITY, 0.0f, {0.f, 0.f, 0.f, 0.f}};
+    float mx = -INFINITY;
     if (h < G) {
         for (int s0 = sg; s0 < S; s0 += U * SGN) {
-            float m[U], l[U];
-            float4 o[U];
+            float m[U];
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const uint32_t s = (uint32_t)(s0 + u * SGN);
-                const auto a = __builtin_amdgcn_raw_buffer_load_b64(rml, (int)((s * 32 + 2 * h) * 4), 0,
-                                                                    kScopeDevice);
-                const auto x = __builtin_amdgcn_raw_buffer_load_b128(
-                    ro, (int)(((s * 16 + h) * D + 4 * f) * 4), 0, kScopeDevice);
-                m[u] = __uint_as_float(a[0]);
-                l[u] = __uint_as_float(a[1]);
-                o[u] = float4{__uint_as_float(x[0]), __uint_as_float(x[1]), __uint_as_float(x[2]),
-                              __uint_as_float(x[3])};
+                m[u] = s < (uint32_t)S ? __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+                                              rml, (int)((s * 32 + 2 * h) * 4), 0, kScopeDevice))
+                                       : -INFINITY;
             }
 #pragma unroll
-            for (int u = 0; u < U; ++u)
-                if (s0 + u * SGN < S) combine_state(st, m[u], l[u], o[u]);
+            for (int u = 0; u < U; ++u) mx = fmaxf(mx, m[u]);
         }
     }
-    lds[tid] = st.m;
-    lds[NTHR + tid] = st.l;
-    *(float4*)&lds[2 * NTHR + 4 * tid] = st.o;
+    lds[tid] = mx;
+    __syncthreads();
+    float M = lds[c];
+#pragma unroll
+    for (int g = 1; g < SGN; ++g) M = fmaxf(M, lds[g * NC + c]);
+    float l = 0.0f;
+    float4 o = {0.f, 0.f, 0.f, 0.f};
+    if (h < G && M != -INFINITY) {
+        for (int s0 = sg; s0 < S; s0 += U * SGN) {
+            float m[U], ls[U];
+            float4 x[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const uint32_t s = (uint32_t)(s0 + u * SGN);
+                if (s < (uint32_t)S) {
+                    const auto a = __builtin_amdgcn_raw_buffer_load_b64(rml, (int)((s * 32 + 2 * h) * 4), 0,
+                                                                        kScopeDevice);
+                    const auto y = __builtin_amdgcn_raw_buffer_load_b128(
+                        ro, (int)(((s * 16 + h) * D + 4 * f) * 4), 0, kScopeDevice);
+                    m[u] = __uint_as_float(a[0]);
+                    ls[u] = __uint_as_float(a[1]);
+                    x[u] = float4{__uint_as_float(y[0]), __uint_as_float(y[1]), __uint_as_float(y[2]),
+                                  __uint_as_float(y[3])};
+                } else {
+                    m[u] = -INFINITY;
+                    ls[u] = 0.0f;
+                    x[u] = float4{0.f, 0.f, 0.f, 0.f};
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const float w = m[u] == -INFINITY ? 0.0f : fast_exp2(m[u] - M);
+                l += w * ls[u];
+                o.x += w * x[u].x;
+                o.y += w * x[u].y;
+                o.z += w * x[u].z;
+                o.w += w * x[u].w;
+            }
+        }
+    }
+    __syncthreads();                              // every thread has read the maxima
+    lds[tid] = l;
+    *(float4*)&lds[2 * NTHR + 4 * tid] = o;
     __syncthreads();
     if (sg != 0 || h >= G) return;
 #pragma unroll
     for (int g = 1; g < SGN; ++g) {
         const int t = g * NC + c;
-        combine_state(st, lds[t], lds[NTHR + t], *(const float4*)&lds[2 * NTHR + 4 * t]);
+        l += lds[t];
+        const float4 y = *(const float4*)&lds[2 * NTHR + 4 * t];
+        o.x += y.x;
+        o.y += y.y;
+        o.z += y.z;
+        o.w += y.w;
     }
-    const float inv = st.l > 0.0f ? 1.0f / st.l : 0.0f;
+    const float inv = l > 0.0f ? 1.0f / l : 0.0f;
     uint16_t* dst = (uint16_t*)p.out + (b * p.Hq + kvh * G + h) * D + 4 * f;
-    const uint16_t hv[4] = {f32_to_f16(st.o.x * inv), f32_to_f16(st.o.y * inv), f32_to_f16(st.o.z * inv),
-                            f32_to_f16(st.o.w * inv)};
+    const uint16_t hv[4] = {f32_to_f16(o.x * inv), f32_to_f16(o.y * inv), f32_to_f16(o.z * inv),
+                            f32_to_f16(o.w * inv)};
     if ((reinterpret_cast<uintptr_t>(p.out) & 7) == 0) {
         *(uint2*)dst = uint2{(uint32_t)hv[0] | ((uint32_t)hv[1] << 16), (uint32_t)hv[2] | ((uint32_t)hv[3] << 16)};
     } else {
