@@ -126,6 +126,9 @@ def parse():
                          "and the kernel pass launch the attention kernel)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-mib", type=int, default=0)
+    ap.add_argument("--op", default="attention", choices=["attention", "quantize"],
+                    help="'quantize' times qkv_quantize of the workload's K and V caches "
+                         "(alternating) instead of the attention step")
     ap.add_argument("--read-sweep", action="store_true",
                     help="instead: the plain streaming read of the workload's K/V bytes over a "
                          "grid of load shapes (workgroups, threads, loads in flight, width)")
@@ -343,6 +346,30 @@ def cpu_baseline(w, inp, budget_s):
                       f"algorithmic bytes per unit of work as the GPU figure"}
 
 
+def quantize_mode(args, w, torch, qkv, W, stream):
+    """qkv_quantize of the workload's K and V (fp16/fp32 [B,Hk,L,D] -> packs),
+    alternating, back to back: the bytes read and written per call over its
+    time, against the HBM peak."""
+    inp = W.make_inputs(w)
+    xs = [W.to_tensor(inp["k"], w.dtype), W.to_tensor(inp["v"], w.dtype)]
+    packs = [qkv.qkv_quantize(x, w.mode, w.bits, w.group_size) for x in xs]
+    for i in range(args.warmup):
+        qkv.qkv_quantize(xs[i % 2], out=packs[i % 2])
+    ms = time_region(torch, lambda i: qkv.qkv_quantize(xs[i % 2], out=packs[i % 2]), 0, args.steps,
+                     stream)
+    src = xs[0].numel() * xs[0].element_size()
+    dst = pack_bytes(w, w.L) // 2
+    gbs = (src + dst) / (ms * 1e-3) / 1e9
+    print(json.dumps({"metric": f"qkv_quantize {w.name} K/V GB/s (read + written)", "value": round(gbs, 1),
+                      "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+                      "us_per_call": round(ms * 1e3, 3), "bytes_read": src, "bytes_written": dst,
+                      "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                                   "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                                   "kernel": "quantize_rows_kernel"},
+                      "config": {"workload": w.name, "mode": w.mode, "bits": w.bits,
+                                 "group_size": w.group_size, "dtype": w.dtype}}), flush=True)
+
+
 def copy_mode(args):
     import torch
     n = args.copy_mib * 2 ** 20
@@ -375,6 +402,8 @@ def main():
         per = pack_bytes(w, w.cap)
         R = args.copies or min(MAX_COPIES, max(1, -(-2 * MALL_BYTES // per)))
         return read_sweep(torch, w, R, args.steps)
+    if args.op == "quantize":
+        return quantize_mode(args, w, torch, qkv, W, stream)
     inp, ks, vs, R = make_caches(w, qkv, W, args.copies)
     ws = qkv.Workspace()
 
