@@ -63,6 +63,8 @@ def pack_bytes(w, L) -> int:
         return 2 * rows * w.D * 2
     if w.mode == "q8_0":
         per = w.D + 2 * (w.D // 32)
+    elif w.mode == "qsym":
+        per = w.D * w.bits // 8 + 2 * (w.D // 32)
     else:
         ss = 4 if w.dtype == "f32" else 2
         per = w.D * w.bits // 8 + 2 * (w.D // w.group_size) * ss

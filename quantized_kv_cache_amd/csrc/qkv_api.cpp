@@ -332,9 +332,11 @@ Plan make_plan(int64_t B, int64_t Hq, int64_t Lq, int64_t D, int64_t L, const qk
     } else {
         // the generic kernel walks a split serially in 32-key blocks (one
         // memory round trip each), so even single-block splits pay off for
-        // small caches (256 keys: 10.5 us with 8 splits, 12.9 us with 4)
+        // small caches (256 keys: 10.5 us with 8 splits, 12.9 us with 4), and
+        // long ones want four workgroups per CU (64K keys, 3-bit, 8 kv heads:
+        // 199 us with 64 splits, 136 us with 128)
         S = pl.matrix ? auto_splits(B * Hk * pl.n_rt, L, 256, 256)
-                      : auto_splits(B * Hk * pl.n_rt, L, 32, 512);
+                      : auto_splits(B * Hk * pl.n_rt, L, 32, 1024);
     }
     int64_t chunk = (L + S - 1) / S;
     const int64_t gran = !pl.matrix ? 32

@@ -36,7 +36,7 @@ namespace qkv {
 namespace {
 
 constexpr int KB = 32;      // keys per block
-constexpr int RTG = 16;     // rows per tile
+constexpr int WS_ROWS = 16; // rows per tile in the split workspace (the merge kernels' layout)
 
 // The packed words of one d slice (DPK = D / 8 consecutive d, inside one
 // quantization group) of one K row and one V row, with their scale / bias.
@@ -91,12 +91,20 @@ __device__ __forceinline__ float stream_elem(const uint32_t* w, const float* s, 
     }
 }
 
-template <int QT, int MODE, int BITS, int D>
+// RTG rows per tile: 16, or 4 for a single query of at most 4 heads per kv
+// head (a decode with G <= 4), which then costs a quarter of the arithmetic.
+template <int QT, int MODE, int BITS, int D, int RTG>
 __global__ __launch_bounds__(256) void attn_generic_kernel(AttnLaunch p) {
     constexpr bool STREAM = !fast_format(MODE, BITS, D);
     constexpr int ST = (MODE == MODE_AFFINE) ? QT : DT_F16;  // scale dtype
     constexpr int DPK = D / 8;                               // d per lane (scores)
-    constexpr int DPO = D / 16;                              // d per lane (output)
+    // output: OC chunks of DPO d per row, RTG * OC <= 256 threads
+    constexpr int OC = D % (256 / RTG) == 0 ? 256 / RTG : 256 / RTG / 2;
+    constexpr int DPO = D / OC;
+    static_assert(D % OC == 0 && RTG * OC <= 256, "output mapping");
+    // softmax: TPR threads per row, KPT keys per thread
+    constexpr int KPT = KB * RTG / 256 >= 1 ? KB * RTG / 256 : 1;
+    constexpr int TPR = KB / KPT;
     __shared__ float qs[RTG][D];
     __shared__ float sc[RTG][KB];
     __shared__ float vt[KB][D];
@@ -199,9 +207,7 @@ __global__ __launch_bounds__(256) void attn_generic_kernel(AttnLaunch p) {
     // queries of the tile, pre-multiplied by the softmax scale (fp32); rows
     // past the tile's last read row 0 and store zeros, so every load is
     // issued before the first wait
-#pragma unroll
-    for (int it = 0; it < RTG * D / 256; ++it) {
-        const int idx = tid + 256 * it;
+    for (int idx = tid; idx < RTG * D; idx += 256) {
         const int r = idx / D, d = idx % D;
         const int pr = r0 + (r < nr ? r : 0);
         const int64_t i = pr / p.G, h = kvh * p.G + pr % p.G;
@@ -210,7 +216,8 @@ __global__ __launch_bounds__(256) void attn_generic_kernel(AttnLaunch p) {
     }
     if (tid < RTG) { m_s[tid] = -INFINITY; l_s[tid] = 0.0f; }
 
-    const int orow = tid / 16, ochunk = tid % 16;
+    const int orow = tid / OC, ochunk = tid % OC;
+    const int orow_c = min(orow, RTG - 1);              // threads past the rows read row RTG - 1
     float o[DPO];
 #pragma unroll
     for (int i = 0; i < DPO; ++i) o[i] = 0.0f;
@@ -260,27 +267,35 @@ __global__ __launch_bounds__(256) void attn_generic_kernel(AttnLaunch p) {
             }
         }
         __syncthreads();
-        // ---- online softmax update: 16 lanes per row, 2 keys per lane
-        {
-            const int r = tid / 16, l16 = tid % 16;
-            const float z0 = sc[r][l16], z1 = sc[r][l16 + 16];
-            float mb = fmaxf(z0, z1);
+        // ---- online softmax update: TPR lanes per row, KPT keys per lane
+        if (tid < RTG * TPR) {                         // whole waves
+            const int r = tid / TPR, lt = tid % TPR;
+            float z[KPT];
+            float mb = -INFINITY;
 #pragma unroll
-            for (int o2 = 1; o2 < 16; o2 <<= 1) mb = fmaxf(mb, __shfl_xor(mb, o2, 64));
+            for (int k = 0; k < KPT; ++k) {
+                z[k] = sc[r][lt + k * TPR];
+                mb = fmaxf(mb, z[k]);
+            }
+#pragma unroll
+            for (int o2 = 1; o2 < TPR; o2 <<= 1) mb = fmaxf(mb, __shfl_xor(mb, o2, 64));
             const float m_old = m_s[r];
             const float m_new = fmaxf(m_old, mb);
-            float p0 = 0.0f, p1 = 0.0f, alpha = 1.0f;
+            float pk[KPT], alpha = 1.0f, ps = 0.0f;
+#pragma unroll
+            for (int k = 0; k < KPT; ++k) pk[k] = 0.0f;
             if (m_new != -INFINITY) {
                 alpha = (m_old == -INFINITY) ? 0.0f : fast_exp2((m_old - m_new) * kLog2e);
-                p0 = (z0 == -INFINITY) ? 0.0f : fast_exp2((z0 - m_new) * kLog2e);
-                p1 = (z1 == -INFINITY) ? 0.0f : fast_exp2((z1 - m_new) * kLog2e);
-            }
-            float ps = p0 + p1;
 #pragma unroll
-            for (int o2 = 1; o2 < 16; o2 <<= 1) ps += __shfl_xor(ps, o2, 64);
-            sc[r][l16] = p0;
-            sc[r][l16 + 16] = p1;
-            if (l16 == 0) {
+                for (int k = 0; k < KPT; ++k) pk[k] = (z[k] == -INFINITY) ? 0.0f : fast_exp2((z[k] - m_new) * kLog2e);
+            }
+#pragma unroll
+            for (int k = 0; k < KPT; ++k) ps += pk[k];
+#pragma unroll
+            for (int o2 = 1; o2 < TPR; o2 <<= 1) ps += __shfl_xor(ps, o2, 64);
+#pragma unroll
+            for (int k = 0; k < KPT; ++k) sc[r][lt + k * TPR] = pk[k];
+            if (lt == 0) {
                 m_s[r] = m_new;
                 l_s[r] = l_s[r] * alpha + ps;
                 a_s[r] = alpha;
@@ -293,11 +308,11 @@ __global__ __launch_bounds__(256) void attn_generic_kernel(AttnLaunch p) {
         __syncthreads();
         // ---- o = o * alpha + P V
         {
-            const float alpha = a_s[orow];
+            const float alpha = a_s[orow_c];
 #pragma unroll
             for (int i = 0; i < DPO; ++i) o[i] *= alpha;
             for (int key = 0; key < KB; ++key) {
-                const float pk = sc[orow][key];
+                const float pk = sc[orow_c][key];
 #pragma unroll
                 for (int i = 0; i < DPO; ++i) o[i] += pk * vt[key][ochunk * DPO + i];
             }
@@ -306,7 +321,7 @@ __global__ __launch_bounds__(256) void attn_generic_kernel(AttnLaunch p) {
         cur = nxt;
     }
 
-    const bool row_ok = orow < nr;
+    const bool row_ok = orow < nr;                       // (nr <= RTG)
     const int pr = r0 + orow;
     const int64_t oi = row_ok ? (int64_t)(pr / p.G) : 0;
     const int64_t oh = row_ok ? kvh * p.G + pr % p.G : 0;
@@ -314,7 +329,7 @@ __global__ __launch_bounds__(256) void attn_generic_kernel(AttnLaunch p) {
 
     if (p.S == 1) {
         if (row_ok) {
-            const float l = l_s[orow];
+            const float l = l_s[orow_c];
             const float inv = l > 0.0f ? 1.0f / l : 0.0f;
 #pragma unroll
             for (int i = 0; i < DPO; ++i) store_from_f32<QT>(p.out, obase + i, o[i] * inv);
@@ -324,8 +339,8 @@ __global__ __launch_bounds__(256) void attn_generic_kernel(AttnLaunch p) {
 
     // ---- partial state -> workspace, then the last workgroup merges
     const int64_t tile = bk * p.n_rt + rt;
-    float* ml = p.part_ml + (tile * p.S + split) * RTG * 2;
-    float* po = p.part_o + (tile * p.S + split) * RTG * D;
+    float* ml = p.part_ml + (tile * p.S + split) * WS_ROWS * 2;
+    float* po = p.part_o + (tile * p.S + split) * WS_ROWS * D;
     if (row_ok) {
 #pragma unroll
         for (int i = 0; i < DPO; ++i) po[orow * D + ochunk * DPO + i] = o[i];
@@ -339,7 +354,10 @@ __global__ __launch_bounds__(256) void attn_generic_kernel(AttnLaunch p) {
 template <int QT, int MODE, int BITS, int D>
 hipError_t launch_g(int64_t B, const AttnLaunch& p, hipStream_t stream) {
     dim3 grid(p.S, p.n_rt, (unsigned)(B * p.Hk));
-    hipLaunchKernelGGL((attn_generic_kernel<QT, MODE, BITS, D>), grid, dim3(256), 0, stream, p);
+    if (p.n_rows <= 4)   // one tile of at most 4 rows (a decode with G <= 4)
+        hipLaunchKernelGGL((attn_generic_kernel<QT, MODE, BITS, D, 4>), grid, dim3(256), 0, stream, p);
+    else
+        hipLaunchKernelGGL((attn_generic_kernel<QT, MODE, BITS, D, 16>), grid, dim3(256), 0, stream, p);
     return hipGetLastError();
 }
 

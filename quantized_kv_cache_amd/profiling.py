@@ -33,6 +33,7 @@ KERNEL_SOURCES = {
     "merge_splits_kernel": ["qkv_merge.hip", "qkv_merge.hpp", "qkv_device.hpp", "qkv_internal.hpp"],
     "merge_splits_small": ["qkv_merge.hip", "qkv_merge.hpp", "qkv_device.hpp", "qkv_internal.hpp"],
     "quantize_rows_kernel": ["qkv_quantize.hip", "qkv_device.hpp", "qkv_internal.hpp"],
+    "unfused_scores_kernel": ["qkv_unfused.hip", "qkv_device.hpp", "qkv_internal.hpp"],
 }
 
 
@@ -72,6 +73,27 @@ def short_name(name: str) -> str:
     return s.split("::")[-1].split(" ")[-1]
 
 
+def trace_table(path: str, skip: int) -> str:
+    """Per-kernel durations from a --kernel-trace CSV, leaving out each
+    kernel's first `skip` dispatches (warm-up launches)."""
+    per = {}
+    for r in csv.DictReader(open(path)):
+        name = short_name(r["Kernel_Name"])
+        per.setdefault(name, []).append((int(r["Dispatch_Id"]),
+                                         (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3))
+    total = sum(d for v in per.values() for _, d in sorted(v)[skip:])
+    lines = [f"{'kernel':<34} {'calls':>6} {'avg_us':>10} {'median_us':>10} {'min_us':>10} "
+             f"{'max_us':>10} {'pct':>6}"]
+    for name, v in sorted(per.items(), key=lambda kv: -sum(d for _, d in sorted(kv[1])[skip:])):
+        ds = [d for _, d in sorted(v)[skip:]]
+        if not ds:
+            continue
+        lines.append(f"{name[:34]:<34} {len(ds):>6} {statistics.fmean(ds):>10.3f} "
+                     f"{statistics.median(ds):>10.3f} {min(ds):>10.3f} {max(ds):>10.3f} "
+                     f"{100.0 * sum(ds) / total:>6.2f}")
+    return "\n".join(lines)
+
+
 def stats_table(path: str) -> str:
     rows = list(csv.DictReader(open(path)))
     lines = [f"{'kernel':<34} {'calls':>6} {'avg_us':>10} {'min_us':>10} {'max_us':>10} {'pct':>6}"]
@@ -107,17 +129,31 @@ def main(argv=None):
     a = sub.add_parser("stats")
     a.add_argument("csv")
     a.add_argument("--command", action="append", default=[])
+    t = sub.add_parser("trace")
+    t.add_argument("csv")
+    t.add_argument("--skip", type=int, default=10)
+    t.add_argument("--command", action="append", default=[])
     b = sub.add_parser("counters")
     for k in ("kernel", "workload", "fetch", "write", "copy_fetch", "copy_write"):
         b.add_argument("--" + k.replace("_", "-"), required=True)
     b.add_argument("--copy-bytes", type=int, required=True)
     b.add_argument("--command", action="append", default=[])
+    b.add_argument("--dram", help="--pmc TCC_EA0_RDREQ_DRAM TCC_EA0_WRREQ_DRAM run of the workload")
+    b.add_argument("--copy-dram", help="the same counters for the copy")
+    b.add_argument("--sq", help="--pmc run of SQ/GRBM counters (MFMA, LDS, VALU activity)")
     args = ap.parse_args(argv)
     if args.cmd == "stats":
         print("# rocprofv3 kernel durations")
         for c in args.command:
             print(f"# command: {c}")
         print(stats_table(args.csv))
+        return
+    if args.cmd == "trace":
+        print(f"# rocprofv3 kernel durations, steady state (each kernel's first {args.skip} "
+              f"dispatches left out)")
+        for c in args.command:
+            print(f"# command: {c}")
+        print(trace_table(args.csv, args.skip))
         return
     fetch = counter_means(args.fetch, "FETCH_SIZE")
     write = counter_means(args.write, "WRITE_SIZE")
@@ -145,6 +181,26 @@ def main(argv=None):
     print(f"fetch_bytes_per_launch = {f_kib * f_scale:.0f}")
     print(f"write_bytes_per_launch = {w_kib * w_scale:.0f}")
     print(f"hbm_bytes_per_launch = {hbm:.0f}")
+    if args.dram and args.copy_dram:
+        # requests the L2 sends to the memory side (DRAM or its memory-side
+        # cache), per dispatch, scaled by bytes per request of the copy
+        rd = counter_means(args.dram, "TCC_EA0_RDREQ_DRAM")[k][0]
+        wr = counter_means(args.dram, "TCC_EA0_WRREQ_DRAM")[k][0]
+        crd = copy_kernel_mean(args.copy_dram, "TCC_EA0_RDREQ_DRAM")
+        cwr = copy_kernel_mean(args.copy_dram, "TCC_EA0_WRREQ_DRAM")
+        print(f"dram_read_requests_per_dispatch = {rd:.0f}")
+        print(f"dram_write_requests_per_dispatch = {wr:.0f}")
+        print(f"dram_read_bytes_per_request = {args.copy_bytes / crd:.2f}")
+        print(f"dram_write_bytes_per_request = {args.copy_bytes / cwr:.2f}")
+        print(f"dram_read_bytes_per_launch = {rd * args.copy_bytes / crd:.0f}")
+        print(f"dram_write_bytes_per_launch = {wr * args.copy_bytes / cwr:.0f}")
+    if args.sq:
+        for cname in ("SQ_BUSY_CYCLES", "GRBM_GUI_ACTIVE", "SQ_VALU_MFMA_BUSY_CYCLES",
+                      "SQ_INSTS_VALU_MFMA_MOPS_F16", "SQ_ACTIVE_INST_VALU", "SQ_INSTS_VALU",
+                      "SQ_LDS_IDX_ACTIVE", "SQ_LDS_BANK_CONFLICT"):
+            m = counter_means(args.sq, cname).get(k)
+            if m is not None:
+                print(f"{cname.lower()}_per_dispatch = {m[0]:.0f}")
     print(f"kernel_source_hash = {kernel_hash(k)}")
 
 

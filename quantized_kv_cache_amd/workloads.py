@@ -64,6 +64,15 @@ WORKLOADS = {
                                   "q8_0", 8, 32, 1.0 / 16.0, False, 404),
     "q8_0_prefill_512": Workload("q8_0_prefill_512", 1, 32, 2, 256, 20480, 512, "f16", "normal",
                                  "q8_0", 8, 32, 1.0 / 16.0, True, 505),
+    # the wider formats at the 64K GQA-4 decode shape (and head size 96 at a
+    # 16K context): affine 3-bit (8 codes in 3 bytes), the symmetric 4-bit
+    # blocks (the Q4_0 reading), affine 4-bit group 32 at D = 96
+    "decode_64k_3bit_gqa4": Workload("decode_64k_3bit_gqa4", 1, 32, 8, 128, 65536, 1, "f16",
+                                     "uniform", "affine", 3, 64, 1.0, False, 3),
+    "decode_64k_qsym4_gqa4": Workload("decode_64k_qsym4_gqa4", 1, 32, 8, 128, 65536, 1, "f16",
+                                      "normal", "qsym", 4, 32, 1.0 / math.sqrt(128.0), False, 7),
+    "decode_16k_d96_gqa4": Workload("decode_16k_d96_gqa4", 1, 32, 8, 96, 16384, 1, "f16", "normal",
+                                    "affine", 4, 32, 1.0 / math.sqrt(96.0), False, 9),
     # the unquantized baseline at the shapes of the two decode workloads: dense
     # fp16 K/V (the sdpa baseline of the MLX benchmark; the F16 cache of the
     # llama.cpp page), same distributions as the quantized workloads

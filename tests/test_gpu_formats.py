@@ -97,3 +97,19 @@ def test_formats_rejected_by_matrix_only_algorithms():
     for algo in ("matrix", "unfused", "dequant_f16"):
         with pytest.raises(qkv.QKVError):
             qkv.qsdpa_decode(to_dev(q, "f16"), kp, vp, 100, 0.1, algo=algo)
+
+
+@pytest.mark.parametrize("name", ["decode_64k_3bit_gqa4", "decode_64k_qsym4_gqa4", "decode_16k_d96_gqa4"])
+def test_format_workload_full(name):
+    w = W.WORKLOADS[name]
+    print(f"[format] {name}", flush=True)
+    inp = W.make_inputs(w)
+    kp = qkv.qkv_quantize(to_dev(inp["k"], w.dtype), w.mode, w.bits, w.group_size)
+    vp = qkv.qkv_quantize(to_dev(inp["v"], w.dtype), w.mode, w.bits, w.group_size)
+    kr = oracle_pack(inp["k"], w.dtype, w.mode, w.bits, w.group_size)
+    vr = oracle_pack(inp["v"], w.dtype, w.mode, w.bits, w.group_size)
+    assert_pack_equal(pack_numpy(kp), kr)
+    assert_pack_equal(pack_numpy(vp), vr)
+    out = qkv.qsdpa_decode(to_dev(inp["q"], w.dtype), kp, vp, w.L, w.scale)
+    ref = oracle_attention(inp["q"], w.dtype, kr, vr, w.L, w.mode, w.bits, w.group_size, w.scale)
+    assert_close(out, ref, name, report=True)
