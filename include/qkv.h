@@ -155,7 +155,8 @@ typedef struct {
  * block of the llama.cpp page "Metal: Optimize q8_0 KV - #25556" (32 signed
  * int8 codes with one fp16 scale); the exact arithmetic is stated under
  * "Cache format" above.  L = 0 enqueues nothing.  dst rows >= L are not
- * touched.
+ * touched.  The values must be finite: a NaN or an infinity in a group gives
+ * unspecified codes and scale for that group (the other groups are exact).
  * Errors: EINVAL (null pointers, L > L_cap, misalignment, shape mismatch),
  * EUNSUPPORTED (format outside the instantiated set). */
 qkv_status qkv_quantize(const void* x, int32_t x_dtype, const int64_t x_strides[3], int64_t L,

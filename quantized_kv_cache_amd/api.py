@@ -332,6 +332,22 @@ def qsdpa_prefill(q: torch.Tensor, k: Pack, v: Pack, L: int, scale: float, causa
     return out
 
 
+class PreparedQuantize:
+    """A qkv_quantize call with its arguments marshalled once: calling it
+    quantizes the same x[B,H,L,D] into rows [0, L) of the same pack."""
+
+    def __init__(self, x: torch.Tensor, out: Pack):
+        self._keep = (x, out)
+        self._c = out.c_struct()
+        self._fn = _lib.load().qkv_quantize
+        self._args = (_ptr(x), _dt(x), _src_strides(x), x.shape[2], ctypes.byref(self._c), _stream(x.device))
+
+    def __call__(self) -> None:
+        st = self._fn(*self._args)
+        if st:
+            _lib.check(st)
+
+
 class PreparedAppend:
     """A qkv_update_append call with its arguments marshalled once; calling it
     with an offset quantizes the same k_new/v_new into rows [offset, offset+T)."""

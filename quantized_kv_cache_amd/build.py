@@ -34,10 +34,16 @@ FLAGS = [
 ]
 
 
+# per-source additions: the quantize kernels take finite inputs (a NaN or an
+# infinity in a group gives unspecified codes for it), which lets min/max
+# reductions skip NaN quieting and fold their DPP lane moves into the min/max
+FILE_FLAGS = {"qkv_quantize.hip": ["-fno-honor-nans"]}
+
+
 def _compile(src: str) -> str:
     out = os.path.join(OBJ, os.path.basename(src) + ".o")
     lang = ["-x", "hip"]
-    cmd = [HIPCC, *lang, *FLAGS, "-c", os.path.join(CSRC, src), "-o", out]
+    cmd = [HIPCC, *lang, *FLAGS, *FILE_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", out]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

@@ -543,7 +543,8 @@ qkv_status qkv_quantize(const void* x, int32_t x_dtype, const int64_t x_strides[
     p.H = dst->H;
     p.T = L;
     p.offset = 0;
-    p.rows = dst->B * dst->H * L;
+    p.BH = dst->B * dst->H;
+    p.rows = p.BH * L;
     hipError_t e = qkv::launch_quantize(x_dtype, dst->mode, dst->bits, dst->group_size, (int)dst->D, p,
                                         1, static_cast<hipStream_t>(stream));
     return hip_status(e, "qkv_quantize");
@@ -571,7 +572,8 @@ qkv_status qkv_update_append(const void* k_new, const void* v_new, int32_t dtype
     p.H = k_cache->H;
     p.T = T;
     p.offset = offset;
-    p.rows = k_cache->B * k_cache->H * T;
+    p.BH = k_cache->B * k_cache->H;
+    p.rows = p.BH * T;
     hipError_t e = qkv::launch_quantize(dtype, k_cache->mode, k_cache->bits, k_cache->group_size,
                                         (int)k_cache->D, p, 2, static_cast<hipStream_t>(stream));
     return hip_status(e, "qkv_update_append");

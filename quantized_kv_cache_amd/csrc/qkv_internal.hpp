@@ -34,6 +34,7 @@ struct QuantJob {
 struct QuantLaunch {
     QuantJob job[2];                // K (and V for append)
     int64_t H, T, offset;
+    int64_t BH;                     // B*H
     int64_t rows;                   // B*H*T
 };
 

@@ -10,17 +10,34 @@
 //
 // Mapping (wave64): each lane owns 8 consecutive values of a row (one 16-byte
 // load for fp16/bf16, two for fp32); a group of gs values is gs/8 adjacent
-// lanes, so its min/max (or absmax) is a butterfly over at most 16 lanes; a
-// row is D/8 lanes, so one wave covers 512/D rows and every load and store of
-// the wave is contiguous.  Each lane writes one packed word (4-bit) or two
-// (8-bit, Q8_0); the first lane of a group writes its scale and bias.
+// lanes, so its min/max (or absmax) is a DPP reduction over at most 16 lanes;
+// a row is D/8 lanes, so one wave covers 512/D rows per pass and every load
+// and store of the wave is contiguous.  A workgroup takes a run of rows of
+// one (batch, head), which it finds from the grid's y coordinate, so no
+// 64-bit index division is needed; each wave makes two passes whose loads are
+// issued together.  Each lane writes one packed word (4-bit) or two (8-bit,
+// Q8_0); the first lane of a group writes its scale and bias.
 //
 // A dense fp16 pack (the unquantized cache) takes the fp16 values as they are.
 //
-// Bit-exactness: min/max are exact; the scale division, the subtract and the
-// code division are IEEE fp32 (no fused multiply-add is possible in these
-// expressions); codes round half to even (v_rndne_f32); scale and bias are
-// rounded to their dtype before the codes are computed from them.
+// Bit-exactness: min/max are exact; the subtract is IEEE fp32; scale and
+// bias are rounded to their dtype before the codes are computed from them;
+// codes round half to even.  The two divisions are exact IEEE fp32 quotients
+// reached without a division instruction per element: with y = RN(1/b) and
+// q = RN(a y), the residual r = a - b q is exact in one fused multiply-add
+// and RN(q + r y) is the correctly rounded a / b (Markstein's correction
+// step).  For fp16 and bf16 divisors y is the hardware reciprocal refined by
+// one Newton step.  Both steps were checked on the CPU against the IEEE
+// operations: the reciprocal for every fp16 and bf16 divisor from every start
+// within one ulp; the quotient for (max - min) / (2^bits - 1) and amax / 127
+// over a dense sample of all non-negative fp32 values, and for the code
+// quotients over every fp16 and bf16 divisor at every numerator within four
+// ulps of each half-integer quotient up to 300 (where a one-ulp difference
+// could move a code).  fp32 sources keep the IEEE division for the codes.
+// The file is compiled for finite inputs (a NaN or an infinity in a group
+// gives unspecified codes for that group), so min/max need no NaN handling.
+#include <algorithm>
+
 #include "qkv_device.hpp"
 #include "qkv_internal.hpp"
 
@@ -47,112 +64,161 @@ __device__ __forceinline__ void load8(const void* base, int64_t off, float v[8])
     }
 }
 
-template <int LANES>
-__device__ __forceinline__ float group_min(float x) {
-#pragma unroll
-    for (int o = 1; o < LANES; o <<= 1) x = fminf(x, __shfl_xor(x, o, 64));
-    return x;
+// Reduction over LANES adjacent lanes (aligned, a power of two <= 16), every
+// lane receiving the result: DPP quad permutations for the first two steps,
+// then half-row and row mirrors (lane i of 8 or 16 meets lane 7 - i or 15 - i,
+// which lies in the other half once the halves are reduced).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
 }
-template <int LANES>
-__device__ __forceinline__ float group_max(float x) {
-#pragma unroll
-    for (int o = 1; o < LANES; o <<= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
+template <int LANES, bool MAX>
+__device__ __forceinline__ float group_reduce(float x) {
+    auto op = [](float a, float b) { return MAX ? fmaxf(a, b) : fminf(a, b); };
+    if constexpr (LANES >= 2) x = op(x, dpp_f32<0xB1>(x));    // quad_perm [1,0,3,2]
+    if constexpr (LANES >= 4) x = op(x, dpp_f32<0x4E>(x));    // quad_perm [2,3,0,1]
+    if constexpr (LANES >= 8) x = op(x, dpp_f32<0x141>(x));   // row_half_mirror
+    if constexpr (LANES >= 16) x = op(x, dpp_f32<0x140>(x));  // row_mirror
     return x;
 }
 
-// DT: source (and, for affine, scale) dtype.  MODE: affine / Q8_0.
+// RN(1 / b) for a divisor b with a 16-bit (fp16 or bf16) significand: the
+// hardware reciprocal (within one ulp) and one Newton step.  Every fp16 divisor
+// and every bf16 divisor >= 1e-7 was checked on the CPU from each starting
+// value within one ulp of 1 / b: the step lands on the correctly rounded
+// reciprocal.
+__device__ __forceinline__ float recip_rn16(float b) {
+    const float y0 = __builtin_amdgcn_rcpf(b);
+    const float e = __builtin_fmaf(-b, y0, 1.0f);
+    return __builtin_fmaf(e, y0, y0);
+}
+
+// RN(a / b) from y = RN(1 / b): one product and two fused multiply-adds.
+__device__ __forceinline__ float div_by_recip(float a, float b, float y) {
+    const float q = a * y;
+    const float r = __builtin_fmaf(-q, b, a);
+    return __builtin_fmaf(r, y, q);
+}
+
+// round_half_even(x) for |x| < 2^22 as an integer in the low bits of the
+// result's bit pattern (1.5 * 2^23 + n), clamped to [lo, hi].
+__device__ __forceinline__ int32_t rne_clamp(float x, int lo, int hi) {
+    const int32_t u = __float_as_int(x + 12582912.0f);
+    return min(max(u, 0x4B400000 + lo), 0x4B400000 + hi) - 0x4B400000;
+}
+
+constexpr int kQuantPasses = 2;   // row passes per wave, loads issued together
+
+// DT: source (and, for affine, scale) dtype.  MODE: affine / Q8_0 / dense.
 template <int DT, int MODE, int BITS, int GS, int D>
 __global__ __launch_bounds__(256) void quantize_rows_kernel(QuantLaunch p) {
+#pragma clang fp contract(off)
     constexpr int LPR = D / 8;                 // lanes per row
-    constexpr int RPW = 64 / LPR;              // rows per wave
+    constexpr int RPW = 64 / LPR;              // rows per wave and pass
+    constexpr int U = kQuantPasses;
+    constexpr int RPB = 4 * RPW * U;           // rows per workgroup
     constexpr int GSZ = (MODE == MODE_Q8_0) ? 32 : GS;
     constexpr int LPG = GSZ / 8;               // lanes per group
     constexpr int NG = D / GSZ;                // groups per row
-    const QuantJob& job = p.job[blockIdx.y];
+    const QuantJob& job = p.job[blockIdx.z];
+    pin_sgpr(job.x); pin_sgpr(job.codes); pin_sgpr(job.scales); pin_sgpr(job.biases);
 
     const int lane = threadIdx.x & 63;
-    const int64_t wave = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    const int64_t row = wave * RPW + lane / LPR;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lr = lane % LPR;
-    if (row >= p.rows) return;                 // whole rows (hence groups) leave together
-
-    const int64_t t = row % p.T;
-    const int64_t bh = row / p.T;
-    const int64_t h = bh % p.H;
-    const int64_t b = bh / p.H;
-    const int64_t src = b * job.xs0 + h * job.xs1 + t * job.xs2 + (int64_t)lr * 8;
-    const int64_t dst = b * job.sb + h * job.sh + (p.offset + t) * job.sl;
-
-    if constexpr (MODE == MODE_DENSE) {
-        // a dense fp16 cache stores the values themselves
-        const uint4 raw = *(const uint4*)((const uint16_t*)job.x + src);
-        ((uint4*)((uint8_t*)job.codes + dst * (int64_t)(D * 2)))[lr] = raw;
-        return;
-    } else {
-    float v[8];
-    load8<DT>(job.x, src, v);
-
-    if constexpr (MODE == MODE_AFFINE) {
-        constexpr float NL = (float)((1 << BITS) - 1);
-        float mn = v[0], mx = v[0];
+    // the rows of this lane: t0 + u * RPW of every (batch, head) bh of the grid's y stride
+    const int64_t t0 = (int64_t)blockIdx.x * RPB + wave * RPW * U + lane / LPR;
+    const uint32_t H = (uint32_t)p.H;
+    for (uint32_t bh = blockIdx.y; bh < (uint32_t)p.BH; bh += gridDim.y) {
+        const uint32_t b = bh / H;
+        const uint32_t h = bh - b * H;
+        const int64_t xbase = (int64_t)b * job.xs0 + (int64_t)h * job.xs1 + (int64_t)lr * 8;
+        const int64_t rbase = (int64_t)b * job.sb + (int64_t)h * job.sh;
+        bool ok[U];
+        int64_t dst[U];
+        uint4 raw[U];
+        float v[U][8];
+        // every pass loads (rows past the end load the last row and store
+        // nothing), so that the passes' loads are in flight together
 #pragma unroll
-        for (int i = 1; i < 8; ++i) { mn = fminf(mn, v[i]); mx = fmaxf(mx, v[i]); }
-        mn = group_min<LPG>(mn);
-        mx = group_max<LPG>(mx);
-        const float eps = round_to<DT>(1e-7f);
-        float s32 = (mx - mn) / NL;
-        if (s32 < eps) s32 = eps;
-        const float s = round_to<DT>(s32);
-        const float bias = round_to<DT>(mn);
-        uint32_t c[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            float q = __builtin_rintf((v[i] - bias) / s);
-            q = fminf(fmaxf(q, 0.0f), NL);
-            c[i] = (uint32_t)q;
+        for (int u = 0; u < U; ++u) {
+            const int64_t t = t0 + u * RPW;
+            ok[u] = t < p.T;                   // whole rows (hence groups) agree
+            dst[u] = rbase + (p.offset + t) * job.sl;
+            const int64_t src = xbase + (ok[u] ? t : p.T - 1) * job.xs2;
+            if constexpr (MODE == MODE_DENSE) raw[u] = *(const uint4*)((const uint16_t*)job.x + src);
+            else load8<DT>(job.x, src, v[u]);
         }
-        uint8_t* crow = (uint8_t*)job.codes + dst * (int64_t)(D * BITS / 8);
-        if constexpr (BITS == 4) {
-            uint32_t w = 0;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) w |= c[i] << (4 * i);
-            ((uint32_t*)crow)[lr] = w;
-        } else {
-            uint2 w;
-            w.x = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
-            w.y = c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24);
-            ((uint2*)crow)[lr] = w;
-        }
-        if (lr % LPG == 0) {
-            const int64_t si = dst * NG + lr / LPG;
-            store_from_f32<DT>(job.scales, si, s32);
-            store_from_f32<DT>(job.biases, si, mn);
-        }
-    } else {
-        float amax = 0.0f;
+        for (int u = 0; u < U; ++u) {
+            if constexpr (MODE == MODE_DENSE) {
+                // a dense fp16 cache stores the values themselves
+                if (ok[u]) ((uint4*)((uint8_t*)job.codes + dst[u] * (int64_t)(D * 2)))[lr] = raw[u];
+            } else if constexpr (MODE == MODE_AFFINE) {
+                constexpr int NL = (1 << BITS) - 1;
+                float mn = v[u][0], mx = v[u][0];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
-        amax = group_max<LPG>(amax);
-        const float d32 = amax / 127.0f;
-        const uint16_t dh = f32_to_f16(d32);
-        const float d = f16_to_f32(dh);
-        uint32_t c[8];
+                for (int i = 1; i < 8; ++i) { mn = fminf(mn, v[u][i]); mx = fmaxf(mx, v[u][i]); }
+                mn = group_reduce<LPG, false>(mn);
+                mx = group_reduce<LPG, true>(mx);
+                const float eps = round_to<DT>(1e-7f);
+                float s32 = div_by_recip(mx - mn, (float)NL, 1.0f / (float)NL);
+                if (s32 < eps) s32 = eps;
+                const float s = round_to<DT>(s32);
+                const float bias = round_to<DT>(mn);
+                const float y = DT == DT_F32 ? 1.0f : recip_rn16(s);
+                int32_t c[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            float q = 0.0f;
-            if (d != 0.0f) {
-                q = __builtin_rintf(v[i] / d);
-                q = fminf(fmaxf(q, -127.0f), 127.0f);
+                for (int i = 0; i < 8; ++i) {
+                    const float a = v[u][i] - bias;
+                    const float qt = DT == DT_F32 ? a / s : div_by_recip(a, s, y);
+                    c[i] = rne_clamp(qt, 0, NL);
+                }
+                if (!ok[u]) continue;
+                uint8_t* crow = (uint8_t*)job.codes + dst[u] * (int64_t)(D * BITS / 8);
+                if constexpr (BITS == 4) {
+                    uint32_t w = 0;
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) w |= (uint32_t)c[i] << (4 * i);
+                    ((uint32_t*)crow)[lr] = w;
+                } else {
+                    uint2 w;
+                    w.x = (uint32_t)c[0] | ((uint32_t)c[1] << 8) | ((uint32_t)c[2] << 16) | ((uint32_t)c[3] << 24);
+                    w.y = (uint32_t)c[4] | ((uint32_t)c[5] << 8) | ((uint32_t)c[6] << 16) | ((uint32_t)c[7] << 24);
+                    ((uint2*)crow)[lr] = w;
+                }
+                if (lr % LPG == 0) {
+                    const int64_t si = dst[u] * NG + lr / LPG;
+                    store_from_f32<DT>(job.scales, si, s32);
+                    store_from_f32<DT>(job.biases, si, mn);
+                }
+            } else {
+                float amax = 0.0f;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[u][i]));
+                amax = group_reduce<LPG, true>(amax);
+                const float d32 = div_by_recip(amax, 127.0f, 1.0f / 127.0f);
+                const uint16_t dh = f32_to_f16(d32);
+                const float d = f16_to_f32(dh);
+                // d = 0 (an all-zero block) gives codes 0: y = 0 makes every quotient 0
+                const float y = d != 0.0f ? recip_rn16(d) : 0.0f;
+                int32_t c[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const float qt = DT == DT_F32 ? (d != 0.0f ? v[u][i] / d : 0.0f) : div_by_recip(v[u][i], d, y);
+                    c[i] = rne_clamp(qt, -127, 127);
+                }
+                if (!ok[u]) continue;
+                uint8_t* crow = (uint8_t*)job.codes + dst[u] * (int64_t)D;
+                uint2 w;
+                w.x = ((uint32_t)c[0] & 0xffu) | (((uint32_t)c[1] & 0xffu) << 8) |
+                      (((uint32_t)c[2] & 0xffu) << 16) | ((uint32_t)c[3] << 24);
+                w.y = ((uint32_t)c[4] & 0xffu) | (((uint32_t)c[5] & 0xffu) << 8) |
+                      (((uint32_t)c[6] & 0xffu) << 16) | ((uint32_t)c[7] << 24);
+                ((uint2*)crow)[lr] = w;
+                if (lr % LPG == 0) ((uint16_t*)job.scales)[dst[u] * NG + lr / LPG] = dh;
             }
-            c[i] = (uint32_t)(int32_t)q & 0xffu;
         }
-        uint8_t* crow = (uint8_t*)job.codes + dst * (int64_t)D;
-        uint2 w;
-        w.x = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
-        w.y = c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24);
-        ((uint2*)crow)[lr] = w;
-        if (lr % LPG == 0) ((uint16_t*)job.scales)[dst * NG + lr / LPG] = dh;
-    }
     }
 }
 
@@ -274,11 +340,12 @@ hipError_t dispatch_groups(int mode, int bits, int gs, int D, const QuantLaunch&
 
 template <int DT, int MODE, int BITS, int GS, int D>
 hipError_t launch_q(const QuantLaunch& p, int njobs, hipStream_t stream) {
-    constexpr int RPW = 64 / (D / 8);
-    const int64_t waves = (p.rows + RPW - 1) / RPW;
-    const int64_t blocks = (waves + 3) / 4;
-    if (blocks == 0) return hipSuccess;
-    hipLaunchKernelGGL((quantize_rows_kernel<DT, MODE, BITS, GS, D>), dim3((unsigned)blocks, njobs),
+    constexpr int RPB = 4 * (64 / (D / 8)) * kQuantPasses;
+    const int64_t bx = (p.T + RPB - 1) / RPB;
+    if (bx == 0 || p.BH == 0) return hipSuccess;
+    if (bx > 0x7fffffff || p.BH > 0x7fffffff) return hipErrorInvalidValue;
+    const unsigned by = (unsigned)std::min<int64_t>(p.BH, 65535);
+    hipLaunchKernelGGL((quantize_rows_kernel<DT, MODE, BITS, GS, D>), dim3((unsigned)bx, by, njobs),
                        dim3(256), 0, stream, p);
     return hipGetLastError();
 }
