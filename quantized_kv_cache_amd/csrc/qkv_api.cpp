@@ -300,10 +300,13 @@ Plan make_plan(int64_t B, int64_t Hq, int64_t Lq, int64_t D, int64_t L, const qk
     pl.narrow = false;
     // the matrix kernels address a kv head's rows with 32-bit offsets
     const int64_t span = (k->L_cap - 1) * k->stride_l * row_bytes(k) + row_bytes(k);
+    // the narrow decode also takes the symmetric 4-bit blocks, which the
+    // other matrix kernels do not
+    const bool narrow_ok = qkv::narrow_decode_supported(q_dtype, k->mode, bits, k->group_size, (int)D, G, Lq);
     if (algo != QKV_ALGO_GENERIC && span < (int64_t(1) << 31) &&
-        qkv::matrix_supported(q_dtype, k->mode, bits, k->group_size, (int)D, G, Lq)) {
+        (narrow_ok || qkv::matrix_supported(q_dtype, k->mode, bits, k->group_size, (int)D, G, Lq))) {
         pl.matrix = true;
-        pl.narrow = qkv::narrow_decode_supported(q_dtype, k->mode, bits, k->group_size, (int)D, G, Lq);
+        pl.narrow = narrow_ok;
         pl.prefill = !pl.narrow &&
                      !qkv::decode_matrix_supported(q_dtype, k->mode, bits, k->group_size, (int)D, G, Lq);
     }

@@ -22,6 +22,11 @@
 //    pre-divided by 16; Q8_0 codes have the sign bit flipped, c + 128); each
 //    step lies in one quantization group and the groups have separate
 //    accumulators, so  z = sum_g s_g 2^24 acc_g + b_g sum_{d in g} q_d.
+//    The symmetric 4-bit blocks (the q4_0 reading of the llama.cpp page's
+//    merged #27390 text: d c with c a 4-bit two's complement code) are the
+//    affine 4-bit form of the same block: flipping each nibble's top bit
+//    gives c + 8, and d c = d (c + 8) + (-8 d), so they run as affine codes
+//    with the bias -8 d derived from the scale (no bias plane).
 //  * Online softmax with a lazy maximum: the running maxima change (and the
 //    wave reduces, rescales) only when a tile holds a score 8 (log2 units)
 //    above them, or any larger score for keys with a large value scale.
@@ -55,7 +60,10 @@ constexpr int NTH = NW * 64;
 constexpr float kLazy = 8.0f;                  // running-maximum slack (log2 units)
 constexpr uint32_t kLazyBigScale = 0x5800u;    // fp16 128 = 2^(15 - kLazy)
 
-template <int MODE, int BITS, int GS, int D, bool MASK, int GP>
+// SA: the scale (and bias) rows are aligned to their size (up to 16 bytes),
+// so a row is read in dwords; otherwise (possible only for the symmetric blocks, whose scale
+// planes need 2-byte alignment) it is read in 16-bit pieces.
+template <int MODE, int BITS, int GS, int D, bool MASK, int GP, bool SA>
 __global__ __launch_bounds__(NTH) void attn_decode_narrow(AttnLaunch p) {
     constexpr int NG = D / GS;
     constexpr int ROWB = D * BITS / 8;            // code bytes of a row
@@ -69,6 +77,11 @@ __global__ __launch_bounds__(NTH) void attn_decode_narrow(AttnLaunch p) {
     constexpr int NSW = SROWB >= 4 ? SROWB / 4 : 1;
     static_assert(NG <= 4 && NBANK >= 1, "narrow kernel: <= 4 groups, D >= 64");
     static_assert(GP * NG <= 16, "P' has 16 columns");
+    static_assert(MODE != MODE_QSYM || (BITS == 4 && GS == 32), "symmetric blocks: 4-bit codes, blocks of 32");
+    // symmetric codes: the nibbles' top bits flipped (c + 8) and the bias -8 d;
+    // Q8_0: the bias of its sign-flipped codes (c + 128) is -128 d
+    constexpr uint32_t kFlip = MODE == MODE_QSYM ? 0x88888888u : 0u;
+    constexpr float kCodeBias = MODE == MODE_QSYM ? -8.0f : -128.0f;
 
     // Per-wave LDS: the P' rows of its tiles while it streams, then its
     // output state for the workgroup merge (a wave writes the latter only
@@ -160,8 +173,17 @@ __global__ __launch_bounds__(NTH) void attn_decode_narrow(AttnLaunch p) {
     const uint32_t o_ks = (uint32_t)lane * kss, o_vs = (uint32_t)lane * vss;
     const uint32_t o_v = (uint32_t)(8 * kb) * vcs + (uint32_t)n * VB;
     auto load_rows16 = [&](__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t* dst) {
-        if constexpr (NG == 1) dst[0] = buf16(r, off);
-        else bufn(r, off, dst, NSW);
+        if constexpr (NG == 1) {
+            dst[0] = buf16(r, off);
+        } else if constexpr (!SA) {
+            uint32_t h[NG];
+#pragma unroll
+            for (int g = 0; g < NG; ++g) h[g] = buf16(r, off + 2 * g);
+#pragma unroll
+            for (int w = 0; w < NSW; ++w) dst[w] = h[2 * w] | (h[2 * w + 1] << 16);
+        } else {
+            bufn(r, off, dst, NSW);
+        }
     };
     auto load_tile = [&](int tt, Tile& T) {
         const int64_t row0 = j0 + (int64_t)tt * NTK;
@@ -258,7 +280,7 @@ __global__ __launch_bounds__(NTH) void attn_decode_narrow(AttnLaunch p) {
             constexpr int u = decltype(uc)::value;
             uint32_t b0, b1;
             if constexpr (BITS == 4) {
-                const uint32_t x = T.k[u >> 1];
+                const uint32_t x = T.k[u >> 1] ^ kFlip;
                 if constexpr (u & 1) {
                     const uint32_t t = perm_b(0u, x, 0x0C030C01u);
                     b0 = t & 0x000F000Fu;
@@ -290,7 +312,7 @@ __global__ __launch_bounds__(NTH) void attn_decode_narrow(AttnLaunch p) {
 #pragma unroll
                 for (int h = 0; h < 4; ++h) z[h] = __builtin_fmaf(bb, qs[h][g], __builtin_fmaf(acc[g][h], S, z[h]));
             } else {
-                const float Tq = -128.0f * s;
+                const float Tq = kCodeBias * s;
 #pragma unroll
                 for (int h = 0; h < 4; ++h) z[h] = __builtin_fmaf(Tq, qs[h][g], __builtin_fmaf(acc[g][h], S, z[h]));
             }
@@ -363,7 +385,7 @@ __global__ __launch_bounds__(NTH) void attn_decode_narrow(AttnLaunch p) {
                 const uint32_t bw = T.vbias[g >> 1];
                 bv = (g & 1) ? hi_f16(bw) : lo_f16(bw);
             } else {
-                bv = -128.0f * (float)sv;
+                bv = kCodeBias * (float)sv;
             }
 #pragma unroll
             for (int h = 0; h < GP; ++h) prow[h + GP * g] = (_Float16)pr[h] * sv;
@@ -395,7 +417,18 @@ __global__ __launch_bounds__(NTH) void attn_decode_narrow(AttnLaunch p) {
                 uint32_t a[4];
 #pragma unroll
                 for (int q2 = 0; q2 < 4; ++q2) {
-                    uint32_t x = pair_sub_byte<BITS>(T.v[c][2 * q2], T.v[c][2 * q2 + 1], t);
+                    uint32_t x;
+                    if constexpr (MODE == MODE_QSYM) {
+                        uint32_t wa[VW], wb[VW];
+#pragma unroll
+                        for (int i = 0; i < VW; ++i) {
+                            wa[i] = T.v[c][2 * q2][i] ^ kFlip;
+                            wb[i] = T.v[c][2 * q2 + 1][i] ^ kFlip;
+                        }
+                        x = pair_sub_byte<BITS>(wa, wb, t);
+                    } else {
+                        x = pair_sub_byte<BITS>(T.v[c][2 * q2], T.v[c][2 * q2 + 1], t);
+                    }
                     if constexpr (MODE == MODE_Q8_0) x ^= 0x00800080u;
                     a[q2] = x;
                 }
@@ -533,10 +566,25 @@ __global__ __launch_bounds__(NTH) void attn_decode_narrow(AttnLaunch p) {
 template <int MODE, int BITS, int GS, int D, int GP>
 hipError_t launch_g(int64_t B, const AttnLaunch& p, hipStream_t stream) {
     dim3 grid(p.S, (unsigned)p.Hk, (unsigned)B);
+    constexpr int SROWB = D / GS * 2;
+    constexpr uintptr_t kAlign = (SROWB >= 16 ? 16 : SROWB) - 1;   // a scale row's own alignment
+    const bool sa = SROWB < 4 ||
+                    ((reinterpret_cast<uintptr_t>(p.k.scales) | reinterpret_cast<uintptr_t>(p.v.scales)) & kAlign) == 0;
+    if constexpr (MODE == MODE_QSYM) {
+        if (!sa) {
+            if (p.mask_kind == MASK_ADDITIVE)
+                hipLaunchKernelGGL((attn_decode_narrow<MODE, BITS, GS, D, true, GP, false>), grid, dim3(NTH), 0, stream, p);
+            else
+                hipLaunchKernelGGL((attn_decode_narrow<MODE, BITS, GS, D, false, GP, false>), grid, dim3(NTH), 0, stream, p);
+            return hipGetLastError();
+        }
+    } else if (!sa) {
+        return hipErrorInvalidValue;               // the host checks guarantee aligned rows
+    }
     if (p.mask_kind == MASK_ADDITIVE)
-        hipLaunchKernelGGL((attn_decode_narrow<MODE, BITS, GS, D, true, GP>), grid, dim3(NTH), 0, stream, p);
+        hipLaunchKernelGGL((attn_decode_narrow<MODE, BITS, GS, D, true, GP, true>), grid, dim3(NTH), 0, stream, p);
     else
-        hipLaunchKernelGGL((attn_decode_narrow<MODE, BITS, GS, D, false, GP>), grid, dim3(NTH), 0, stream, p);
+        hipLaunchKernelGGL((attn_decode_narrow<MODE, BITS, GS, D, false, GP, true>), grid, dim3(NTH), 0, stream, p);
     return hipGetLastError();
 }
 
@@ -566,8 +614,10 @@ hipError_t by_d(int D, int64_t B, const AttnLaunch& p, hipStream_t s) {
 
 bool narrow_decode_supported(int q_dtype, int mode, int bits, int group_size, int D, int G,
                              int64_t Lq) {
-    if (q_dtype != DT_F16 || Lq != 1 || G < 1 || G > 4 || !fast_format(mode, bits, D)) return false;
+    if (q_dtype != DT_F16 || Lq != 1 || G < 1 || G > 4) return false;
     if (D != 64 && D != 128) return false;
+    if (mode == MODE_QSYM) return bits == 4 && group_size == 32;
+    if (!fast_format(mode, bits, D)) return false;
     const int gs = mode == MODE_Q8_0 ? 32 : group_size;
     if (mode == MODE_AFFINE && (bits != 4 && bits != 8)) return false;
     if (gs != 32 && gs != 64 && gs != 128) return false;
@@ -582,6 +632,7 @@ hipError_t launch_attn_narrow(int mode, int bits, int D, int64_t B, const AttnLa
                               hipStream_t stream) {
     const int gs = 1 << p.gs_log2;
     if (mode == MODE_Q8_0) return by_d<MODE_Q8_0, 8, 32>(D, B, p, stream);
+    if (mode == MODE_QSYM) return bits == 4 && gs == 32 ? by_d<MODE_QSYM, 4, 32>(D, B, p, stream) : hipErrorNotSupported;
     if (bits == 4) {
         if (gs == 32) return by_d<MODE_AFFINE, 4, 32>(D, B, p, stream);
         if (gs == 64) return by_d<MODE_AFFINE, 4, 64>(D, B, p, stream);

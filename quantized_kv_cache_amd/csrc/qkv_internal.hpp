@@ -14,7 +14,8 @@ enum Mode { MODE_AFFINE = 0, MODE_Q8_0 = 1, MODE_DENSE = 2, MODE_QSYM = 3 };
 // Formats of the matrix-core and fast quantize kernels: affine 4/8-bit and
 // Q8_0 with D a multiple of 64.  Every other format (affine 2/3/5/6-bit, the
 // symmetric 4/5-bit blocks, head size 96) takes the general paths, which
-// read codes as a bit stream.
+// read codes as a bit stream; the narrow decode also takes the symmetric
+// 4-bit blocks (narrow_decode_supported).
 constexpr bool fast_format(int mode, int bits, int D) {
     return (mode == MODE_Q8_0 || (mode == MODE_AFFINE && (bits == 4 || bits == 8))) && D % 64 == 0;
 }

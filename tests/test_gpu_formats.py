@@ -2,13 +2,15 @@
 size 96, and the symmetric 4/5-bit blocks (the Q4_0/Q5_0 reading), plus Q8_0
 and affine 4/8-bit at head size 96.  Quantize and append must give the
 oracle's bits; decode and prefill (on the generic kernel, with key splits
-and the merge kernels) must be within the attention tolerance of the
-oracle."""
+and the merge kernels; the symmetric 4-bit blocks with fp16 queries, D 64 or
+128 and at most 4 heads per kv head also on the narrow matrix-core decode)
+must be within the attention tolerance of the oracle."""
 import math
 import zlib
 
 import numpy as np
 import pytest
+import torch
 
 import quantized_kv_cache_amd as qkv
 from tests._cases import (W, assert_close, assert_pack_equal, oracle_attention, oracle_pack,
@@ -61,10 +63,13 @@ def test_formats_quantize_append_and_decode(fmt):
     scale = 1.0 / math.sqrt(D)
     ref = oracle_attention(q, dt, kr, vr, 517, mode, bits, gs, scale)
     qd = to_dev(q, dt)
-    assert qkv.qsdpa_plan(qd, kp, 517)["kernel"] == "attn_generic_kernel"
-    for splits in (0, 1, 5, 17):
-        out = qkv.qsdpa_decode(qd, kp, vp, 517, scale, num_splits=splits)
-        assert_close(out, ref, f"decode {fmt} splits={splits}")
+    narrow = mode == "qsym" and bits == 4 and D in (64, 128) and dt == "f16"
+    assert qkv.qsdpa_plan(qd, kp, 517)["kernel"] == ("attn_decode_narrow" if narrow else "attn_generic_kernel")
+    assert qkv.qsdpa_plan(qd, kp, 517, algo="generic")["kernel"] == "attn_generic_kernel"
+    for algo in (("auto", "generic") if narrow else ("auto",)):
+        for splits in (0, 1, 5, 17):
+            out = qkv.qsdpa_decode(qd, kp, vp, 517, scale, num_splits=splits, algo=algo)
+            assert_close(out, ref, f"decode {fmt} {algo} splits={splits}")
     # append three tokens at an offset: bit-exact rows, the rest untouched
     new_k = W.random_case(_seed(fmt, "k"), (2, 2, 3, D), "normal", dt)
     new_v = W.random_case(_seed(fmt, "v"), (2, 2, 3, D), "normal", dt)
@@ -113,3 +118,67 @@ def test_format_workload_full(name):
     out = qkv.qsdpa_decode(to_dev(inp["q"], w.dtype), kp, vp, w.L, w.scale)
     ref = oracle_attention(inp["q"], w.dtype, kr, vr, w.L, w.mode, w.bits, w.group_size, w.scale)
     assert_close(out, ref, name, report=True)
+
+
+# the symmetric 4-bit blocks on the narrow matrix-core decode: GQA factors 1-4,
+# both head sizes, ragged lengths, an additive mask, split counts, and the
+# same bits on a repeated call
+QSYM_NARROW = [
+    # B, Hq, Hk, D, L, mask
+    (2, 8, 2, 128, 1000, False),
+    (1, 3, 3, 64, 777, False),
+    (1, 6, 2, 128, 4099, True),
+    (2, 4, 2, 64, 130, False),
+    (1, 32, 8, 128, 2113, True),
+]
+
+
+@pytest.mark.parametrize("case", QSYM_NARROW, ids=lambda c: "-".join(map(str, c)))
+def test_qsym4_narrow_decode(case):
+    B, Hq, Hk, D, L, use_mask = case
+    fmt = ("qsym", 4, 32, D, "f16")
+    q, kp, vp, kr, vr = _case(fmt, B, Hq, Hk, 1, L)
+    scale = 1.0 / math.sqrt(D)
+    mask = None
+    if use_mask:
+        rng = np.random.default_rng(_seed(case, "mask"))
+        mask = np.where(rng.random((B, Hq, 1, L)) < 0.2, -np.inf, rng.normal(0, 1, (B, Hq, 1, L))).astype(np.float32)
+        mask[..., 0] = 0.0                        # every row sees a key
+    ref = oracle_attention(q, "f16", kr, vr, L, "qsym", 4, 32, scale, mask=mask)
+    qd = to_dev(q, "f16")
+    md = None if mask is None else to_dev(mask, "f32")
+    assert qkv.qsdpa_plan(qd, kp, L)["kernel"] == "attn_decode_narrow"
+    first = None
+    for splits in (0, 1, 3, 9):
+        out = qkv.qsdpa_decode(qd, kp, vp, L, scale, mask=md, num_splits=splits)
+        assert_close(out, ref, f"qsym4 narrow {case} splits={splits}", report=splits == 0)
+        if splits == 0:
+            first = out.clone()
+    again = qkv.qsdpa_decode(qd, kp, vp, L, scale, mask=md)
+    assert torch.equal(again, first)
+
+
+def _offset_scales(p):
+    """The pack with its scale plane copied to storage 2 bytes past an aligned
+    address (the symmetric formats only require 2-byte alignment)."""
+    n = p.scales.numel()
+    flat = torch.zeros(n + 8, dtype=p.scales.dtype, device=p.scales.device)
+    view = flat[1:1 + n].view(p.scales.shape)
+    view.copy_(p.scales)
+    assert view.data_ptr() % 4 == 2
+    return qkv.Pack(p.mode, p.bits, p.group_size, p.D, p.codes, view, None)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_qsym4_narrow_unaligned_scales(D):
+    fmt = ("qsym", 4, 32, D, "f16")
+    q, kp, vp, kr, vr = _case(fmt, 1, 8, 2, 1, 1500)
+    qd = to_dev(q, "f16")
+    scale = 1.0 / math.sqrt(D)
+    ref = oracle_attention(q, "f16", kr, vr, 1500, "qsym", 4, 32, scale)
+    aligned = qkv.qsdpa_decode(qd, kp, vp, 1500, scale)
+    ku, vu = _offset_scales(kp), _offset_scales(vp)
+    assert qkv.qsdpa_plan(qd, ku, 1500)["kernel"] == "attn_decode_narrow"
+    out = qkv.qsdpa_decode(qd, ku, vu, 1500, scale)
+    assert_close(out, ref, f"qsym4 narrow D={D}, 2-byte aligned scales")
+    assert torch.equal(out, aligned)
