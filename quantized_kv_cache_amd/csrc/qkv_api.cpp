@@ -174,6 +174,15 @@ qkv_status check_source(const void* x, int32_t dtype, const int64_t xs[3], const
     return QKV_OK;
 }
 
+// The quantize kernels address a pass of rows with 32-bit offsets from a
+// per-pass base: a source row stride and a pack row stride below 2^27 bytes.
+qkv_status check_row_strides(const int64_t xs[3], int32_t dtype, const qkv_pack* p, const char* name) {
+    const int64_t lim = int64_t(1) << 27;
+    if (xs[2] * (int64_t)dtype_size(dtype) >= lim || p->stride_l * row_bytes(p) >= lim)
+        return fail(QKV_EUNSUPPORTED, "%s: a row stride of 2^27 bytes or more is not supported", name);
+    return QKV_OK;
+}
+
 // ---------------------------------------------------------------- attention plans
 struct Plan {
     bool unfused;                   // the four-kernel composition (QKV_ALGO_UNFUSED)
@@ -540,6 +549,7 @@ qkv_status qkv_quantize(const void* x, int32_t x_dtype, const int64_t x_strides[
     if ((st = check_source(x, x_dtype, x_strides, dst, "qkv_quantize")) != QKV_OK) return st;
     if (L < 0 || L > dst->L_cap) return fail(QKV_EINVAL, "qkv_quantize: L=%lld outside [0, L_cap]", (long long)L);
     if (L == 0) return ok();
+    if ((st = check_row_strides(x_strides, x_dtype, dst, "qkv_quantize")) != QKV_OK) return st;
     qkv::QuantLaunch p{};
     p.job[0] = make_job(x, x_strides, dst);
     p.job[1] = p.job[0];
@@ -569,6 +579,8 @@ qkv_status qkv_update_append(const void* k_new, const void* v_new, int32_t dtype
                     (long long)(offset + T));
     if (overlap(codes_range(k_cache), codes_range(v_cache)))
         return fail(QKV_EINVAL, "qkv_update_append: K and V codes overlap");
+    if ((st = check_row_strides(new_strides, dtype, k_cache, "qkv_update_append(k)")) != QKV_OK) return st;
+    if ((st = check_row_strides(new_strides, dtype, v_cache, "qkv_update_append(v)")) != QKV_OK) return st;
     qkv::QuantLaunch p{};
     p.job[0] = make_job(k_new, new_strides, k_cache);
     p.job[1] = make_job(v_new, new_strides, v_cache);

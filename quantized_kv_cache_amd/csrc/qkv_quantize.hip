@@ -45,24 +45,8 @@ namespace qkv {
 
 namespace {
 
-template <int DT>
-__device__ __forceinline__ void load8(const void* base, int64_t off, float v[8]) {
-    if constexpr (DT == DT_F32) {
-        const float4* p = (const float4*)((const float*)base + off);
-        float4 a = p[0], b = p[1];
-        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-        v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-    } else {
-        uint4 w = *(const uint4*)((const uint16_t*)base + off);
-        uint32_t ws[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            uint16_t lo = (uint16_t)(ws[i] & 0xffffu), hi = (uint16_t)(ws[i] >> 16);
-            if constexpr (DT == DT_F16) { v[2 * i] = f16_to_f32(lo); v[2 * i + 1] = f16_to_f32(hi); }
-            else { v[2 * i] = bf16_to_f32(lo); v[2 * i + 1] = bf16_to_f32(hi); }
-        }
-    }
-}
+typedef uint32_t u2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 
 // Reduction over LANES adjacent lanes (aligned, a power of two <= 16), every
 // lane receiving the result: DPP quad permutations for the first two steps,
@@ -109,7 +93,49 @@ __device__ __forceinline__ int32_t rne_clamp(float x, int lo, int hi) {
 
 constexpr int kQuantPasses = 2;   // row passes per wave, loads issued together
 
+// A raw buffer resource over `rows` rows (0 .. RPW) of a plane starting at
+// base, rows `stride` bytes apart and `row_bytes` long: loads past the last
+// row read zeros and stores there are dropped, so a pass needs no bounds
+// branch.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t pass_rsrc(const uint8_t* base, int64_t rows, uint32_t stride,
+                                                              uint32_t row_bytes) {
+    const uint32_t bytes = rows > 0 ? (uint32_t)(rows - 1) * stride + row_bytes : 0u;
+    return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)bytes, 0x00020000);
+}
+
+// 8 consecutive source values as fp32 (fp32: two 16-byte loads, else one).
+template <int DT>
+__device__ __forceinline__ void load8_buf(__amdgpu_buffer_rsrc_t r, uint32_t off, float v[8]) {
+    if constexpr (DT == DT_F32) {
+        const auto a = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+        const auto b = __builtin_amdgcn_raw_buffer_load_b128(r, (int)(off + 16), 0, 0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            v[i] = __uint_as_float(a[i]);
+            v[4 + i] = __uint_as_float(b[i]);
+        }
+    } else {
+        const auto w = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint16_t lo = (uint16_t)(w[i] & 0xffffu), hi = (uint16_t)(w[i] >> 16);
+            if constexpr (DT == DT_F16) { v[2 * i] = f16_to_f32(lo); v[2 * i + 1] = f16_to_f32(hi); }
+            else { v[2 * i] = bf16_to_f32(lo); v[2 * i + 1] = bf16_to_f32(hi); }
+        }
+    }
+}
+
+template <int DT>
+__device__ __forceinline__ void store_scale_buf(__amdgpu_buffer_rsrc_t r, uint32_t off, float v) {
+    if constexpr (DT == DT_F32) __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, (int)off, 0, 0);
+    else if constexpr (DT == DT_F16) __builtin_amdgcn_raw_buffer_store_b16(f32_to_f16(v), r, (int)off, 0, 0);
+    else __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(v), r, (int)off, 0, 0);
+}
+
 // DT: source (and, for affine, scale) dtype.  MODE: affine / Q8_0 / dense.
+// Every address is a wave-uniform base (scalar, 64-bit) plus a lane offset
+// that does not change between passes (32-bit): the host keeps a source row
+// stride and a pack row stride below 2^27 bytes.
 template <int DT, int MODE, int BITS, int GS, int D>
 __global__ __launch_bounds__(256) void quantize_rows_kernel(QuantLaunch p) {
 #pragma clang fp contract(off)
@@ -120,40 +146,61 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(QuantLaunch p) {
     constexpr int GSZ = (MODE == MODE_Q8_0) ? 32 : GS;
     constexpr int LPG = GSZ / 8;               // lanes per group
     constexpr int NG = D / GSZ;                // groups per row
+    constexpr int ES = DT == DT_F32 ? 4 : 2;   // source element bytes
+    constexpr int ROWB = MODE == MODE_DENSE ? 2 * D : D * BITS / 8;   // code bytes of a row
+    constexpr int SS = MODE == MODE_AFFINE ? ES : 2;                  // scale element bytes
+    constexpr int SROWB = NG * SS;
     const QuantJob& job = p.job[blockIdx.z];
     pin_sgpr(job.x); pin_sgpr(job.codes); pin_sgpr(job.scales); pin_sgpr(job.biases);
+    pin_sgpr(job.xs0); pin_sgpr(job.xs1); pin_sgpr(job.xs2);
+    pin_sgpr(job.sb); pin_sgpr(job.sh); pin_sgpr(job.sl);
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lr = lane % LPR;
-    // the rows of this lane: t0 + u * RPW of every (batch, head) bh of the grid's y stride
-    const int64_t t0 = (int64_t)blockIdx.x * RPB + wave * RPW * U + lane / LPR;
+    const int lrow = lane / LPR;               // the lane's row within a pass
+    const uint32_t xstride = (uint32_t)(job.xs2 * ES);
+    const uint32_t cstride = (uint32_t)(job.sl * ROWB);
+    const uint32_t sstride = (uint32_t)(job.sl * SROWB);
+    const uint32_t o_x = (uint32_t)lrow * xstride + (uint32_t)lr * 8 * ES;
+    const uint32_t o_c = (uint32_t)lrow * cstride + (uint32_t)lr * (ROWB / LPR);
+    const uint32_t o_s = (uint32_t)lrow * sstride + (uint32_t)(lr / LPG) * SS;
+    const bool leader = lr % LPG == 0;
+    // first row of each pass of this wave, relative to the (batch, head)
+    const int64_t tw = (int64_t)blockIdx.x * RPB + wave * RPW * U;
     const uint32_t H = (uint32_t)p.H;
     for (uint32_t bh = blockIdx.y; bh < (uint32_t)p.BH; bh += gridDim.y) {
         const uint32_t b = bh / H;
         const uint32_t h = bh - b * H;
-        const int64_t xbase = (int64_t)b * job.xs0 + (int64_t)h * job.xs1 + (int64_t)lr * 8;
-        const int64_t rbase = (int64_t)b * job.sb + (int64_t)h * job.sh;
-        bool ok[U];
-        int64_t dst[U];
+        const int64_t xrow0 = (int64_t)b * job.xs0 + (int64_t)h * job.xs1;    // elements
+        const int64_t prow0 = (int64_t)b * job.sb + (int64_t)h * job.sh + p.offset;   // pack rows
+        __amdgpu_buffer_rsrc_t rc[U], rs[U], rb[U];
         uint4 raw[U];
         float v[U][8];
-        // every pass loads (rows past the end load the last row and store
-        // nothing), so that the passes' loads are in flight together
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int64_t t = t0 + u * RPW;
-            ok[u] = t < p.T;                   // whole rows (hence groups) agree
-            dst[u] = rbase + (p.offset + t) * job.sl;
-            const int64_t src = xbase + (ok[u] ? t : p.T - 1) * job.xs2;
-            if constexpr (MODE == MODE_DENSE) raw[u] = *(const uint4*)((const uint16_t*)job.x + src);
-            else load8<DT>(job.x, src, v[u]);
+            const int64_t t = tw + u * RPW;
+            const int64_t rows = min((int64_t)RPW, p.T - t);
+            const auto rx = pass_rsrc((const uint8_t*)job.x + (xrow0 + t * job.xs2) * ES, rows, xstride, D * ES);
+            rc[u] = pass_rsrc((const uint8_t*)job.codes + (prow0 + t * job.sl) * ROWB, rows, cstride, ROWB);
+            if constexpr (MODE != MODE_DENSE) {
+                rs[u] = pass_rsrc((const uint8_t*)job.scales + (prow0 + t * job.sl) * SROWB, rows, sstride, SROWB);
+                if constexpr (MODE == MODE_AFFINE)
+                    rb[u] = pass_rsrc((const uint8_t*)job.biases + (prow0 + t * job.sl) * SROWB, rows, sstride, SROWB);
+            }
+            if constexpr (MODE == MODE_DENSE) {
+                const auto w = __builtin_amdgcn_raw_buffer_load_b128(rx, (int)o_x, 0, 0);
+                raw[u] = uint4{w[0], w[1], w[2], w[3]};
+            } else {
+                load8_buf<DT>(rx, o_x, v[u]);
+            }
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             if constexpr (MODE == MODE_DENSE) {
                 // a dense fp16 cache stores the values themselves
-                if (ok[u]) ((uint4*)((uint8_t*)job.codes + dst[u] * (int64_t)(D * 2)))[lr] = raw[u];
+                const u4 w = {raw[u].x, raw[u].y, raw[u].z, raw[u].w};
+                __builtin_amdgcn_raw_buffer_store_b128(w, rc[u], (int)o_c, 0, 0);
             } else if constexpr (MODE == MODE_AFFINE) {
                 constexpr int NL = (1 << BITS) - 1;
                 float mn = v[u][0], mx = v[u][0];
@@ -174,23 +221,19 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(QuantLaunch p) {
                     const float qt = DT == DT_F32 ? a / s : div_by_recip(a, s, y);
                     c[i] = rne_clamp(qt, 0, NL);
                 }
-                if (!ok[u]) continue;
-                uint8_t* crow = (uint8_t*)job.codes + dst[u] * (int64_t)(D * BITS / 8);
                 if constexpr (BITS == 4) {
                     uint32_t w = 0;
 #pragma unroll
                     for (int i = 0; i < 8; ++i) w |= (uint32_t)c[i] << (4 * i);
-                    ((uint32_t*)crow)[lr] = w;
+                    __builtin_amdgcn_raw_buffer_store_b32(w, rc[u], (int)o_c, 0, 0);
                 } else {
-                    uint2 w;
-                    w.x = (uint32_t)c[0] | ((uint32_t)c[1] << 8) | ((uint32_t)c[2] << 16) | ((uint32_t)c[3] << 24);
-                    w.y = (uint32_t)c[4] | ((uint32_t)c[5] << 8) | ((uint32_t)c[6] << 16) | ((uint32_t)c[7] << 24);
-                    ((uint2*)crow)[lr] = w;
+                    const u2 w = {(uint32_t)c[0] | ((uint32_t)c[1] << 8) | ((uint32_t)c[2] << 16) | ((uint32_t)c[3] << 24),
+                                  (uint32_t)c[4] | ((uint32_t)c[5] << 8) | ((uint32_t)c[6] << 16) | ((uint32_t)c[7] << 24)};
+                    __builtin_amdgcn_raw_buffer_store_b64(w, rc[u], (int)o_c, 0, 0);
                 }
-                if (lr % LPG == 0) {
-                    const int64_t si = dst[u] * NG + lr / LPG;
-                    store_from_f32<DT>(job.scales, si, s32);
-                    store_from_f32<DT>(job.biases, si, mn);
+                if (leader) {
+                    store_scale_buf<DT>(rs[u], o_s, s32);
+                    store_scale_buf<DT>(rb[u], o_s, mn);
                 }
             } else {
                 float amax = 0.0f;
@@ -208,15 +251,12 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(QuantLaunch p) {
                     const float qt = DT == DT_F32 ? (d != 0.0f ? v[u][i] / d : 0.0f) : div_by_recip(v[u][i], d, y);
                     c[i] = rne_clamp(qt, -127, 127);
                 }
-                if (!ok[u]) continue;
-                uint8_t* crow = (uint8_t*)job.codes + dst[u] * (int64_t)D;
-                uint2 w;
-                w.x = ((uint32_t)c[0] & 0xffu) | (((uint32_t)c[1] & 0xffu) << 8) |
-                      (((uint32_t)c[2] & 0xffu) << 16) | ((uint32_t)c[3] << 24);
-                w.y = ((uint32_t)c[4] & 0xffu) | (((uint32_t)c[5] & 0xffu) << 8) |
-                      (((uint32_t)c[6] & 0xffu) << 16) | ((uint32_t)c[7] << 24);
-                ((uint2*)crow)[lr] = w;
-                if (lr % LPG == 0) ((uint16_t*)job.scales)[dst[u] * NG + lr / LPG] = dh;
+                const u2 w = {((uint32_t)c[0] & 0xffu) | (((uint32_t)c[1] & 0xffu) << 8) |
+                                  (((uint32_t)c[2] & 0xffu) << 16) | ((uint32_t)c[3] << 24),
+                              ((uint32_t)c[4] & 0xffu) | (((uint32_t)c[5] & 0xffu) << 8) |
+                                  (((uint32_t)c[6] & 0xffu) << 16) | ((uint32_t)c[7] << 24)};
+                __builtin_amdgcn_raw_buffer_store_b64(w, rc[u], (int)o_c, 0, 0);
+                if (leader) __builtin_amdgcn_raw_buffer_store_b16(dh, rs[u], (int)o_s, 0, 0);
             }
         }
     }

@@ -81,6 +81,9 @@ def test_quantize_rejects_bad_sources(L):
     assert _quant(L, _pack(), dt=_lib.QKV_F32)[0] == _lib.QKV_EUNSUPPORTED      # scale != src
     st, _ = _quant(L, _pack(), n=0)                                             # nothing to do
     assert st == _lib.QKV_OK
+    # a source row stride of 2^27 bytes or more
+    st, err = _quant(L, _pack(), strides=(16384, 8192, 1 << 26))
+    assert st == _lib.QKV_EUNSUPPORTED and "2^27" in err, (st, err)
 
 
 def _append(L, kp, vp, T=1, offset=0, k=FAKE + 0x400000, v=FAKE + 0x500000):
