@@ -158,7 +158,8 @@ typedef struct {
  * touched.  The values must be finite: a NaN or an infinity in a group gives
  * unspecified codes and scale for that group (the other groups are exact).
  * Errors: EINVAL (null pointers, L > L_cap, misalignment, shape mismatch),
- * EUNSUPPORTED (format outside the instantiated set). */
+ * EUNSUPPORTED (format outside the instantiated set, or a source row stride
+ * x_strides[2] * element size or a pack row stride of 2^27 bytes or more). */
 qkv_status qkv_quantize(const void* x, int32_t x_dtype, const int64_t x_strides[3], int64_t L,
                         const qkv_pack* dst, void* stream);
 
