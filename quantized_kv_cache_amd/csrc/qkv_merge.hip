@@ -58,43 +58,33 @@ __global__ __launch_bounds__(256) void merge_splits_kernel(AttnLaunch p) {
     const int S = p.S;
     const bool f_ok = f < F4;                     // D = 96: the last chunk is 32 d wide
 
-    // The row's maximum first (its m values only), then the sums weighted by
-    // 2^(m_s - M): no rescaling chain between splits.
+    // The row's maximum first, then the sums weighted by 2^(m_s - M): no
+    // rescaling chain between splits.  With at most U SG splits every state
+    // of the thread is loaded in one round trip before the maximum is
+    // reduced; more splits take a pass for the maxima and one for the sums.
+    // Both forms add in the same order, so they give the same bits.
     const float2* ml = (const float2*)p.part_ml + (tile * S * 16 + r);
     const float4* po = (const float4*)p.part_o + ((tile * S * 16 + r) * F4 + f);
-    float mx = -INFINITY;
-    for (int s0 = sg; s0 < S; s0 += U * SG) {
-        float a[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int s = s0 + u * SG;
-            a[u] = s < S ? ml[(int64_t)s * 16].x : -INFINITY;
-        }
-#pragma unroll
-        for (int u = 0; u < U; ++u) mx = fmaxf(mx, a[u]);
-    }
-    red_m[threadIdx.x] = mx;
-    __syncthreads();
-    float M = red_m[threadIdx.x % MC];
-#pragma unroll
-    for (int g = 1; g < SG; ++g) M = fmaxf(M, red_m[g * MC + threadIdx.x % MC]);
     float l = 0.0f;
     float4 o = {0.f, 0.f, 0.f, 0.f};
-    if (M != -INFINITY && f_ok) {
-        for (int s0 = sg; s0 < S; s0 += U * SG) {
-            float2 a[U];
-            float4 x[U];
+    if (S <= U * SG) {
+        float2 a[U];
+        float4 x[U];
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int s = s0 + u * SG;
-                if (s < S) {
-                    a[u] = ml[(int64_t)s * 16];
-                    x[u] = po[(int64_t)s * 16 * F4];
-                } else {
-                    a[u] = float2{-INFINITY, 0.0f};
-                    x[u] = float4{0.f, 0.f, 0.f, 0.f};
-                }
-            }
+        for (int u = 0; u < U; ++u) {
+            const int s = sg + u * SG;
+            a[u] = s < S ? ml[(int64_t)s * 16] : float2{-INFINITY, 0.0f};
+            x[u] = (s < S && f_ok) ? po[(int64_t)s * 16 * F4] : float4{0.f, 0.f, 0.f, 0.f};
+        }
+        float mx = -INFINITY;
+#pragma unroll
+        for (int u = 0; u < U; ++u) mx = fmaxf(mx, a[u].x);
+        red_m[threadIdx.x] = mx;
+        __syncthreads();
+        float M = red_m[threadIdx.x % MC];
+#pragma unroll
+        for (int g = 1; g < SG; ++g) M = fmaxf(M, red_m[g * MC + threadIdx.x % MC]);
+        if (M != -INFINITY && f_ok) {
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const float w = a[u].x == -INFINITY ? 0.0f : fast_exp2(a[u].x - M);
@@ -103,6 +93,49 @@ __global__ __launch_bounds__(256) void merge_splits_kernel(AttnLaunch p) {
                 o.y += w * x[u].y;
                 o.z += w * x[u].z;
                 o.w += w * x[u].w;
+            }
+        }
+    } else {
+        float mx = -INFINITY;
+        for (int s0 = sg; s0 < S; s0 += U * SG) {
+            float a[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int s = s0 + u * SG;
+                a[u] = s < S ? ml[(int64_t)s * 16].x : -INFINITY;
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) mx = fmaxf(mx, a[u]);
+        }
+        red_m[threadIdx.x] = mx;
+        __syncthreads();
+        float M = red_m[threadIdx.x % MC];
+#pragma unroll
+        for (int g = 1; g < SG; ++g) M = fmaxf(M, red_m[g * MC + threadIdx.x % MC]);
+        if (M != -INFINITY && f_ok) {
+            for (int s0 = sg; s0 < S; s0 += U * SG) {
+                float2 a[U];
+                float4 x[U];
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const int s = s0 + u * SG;
+                    if (s < S) {
+                        a[u] = ml[(int64_t)s * 16];
+                        x[u] = po[(int64_t)s * 16 * F4];
+                    } else {
+                        a[u] = float2{-INFINITY, 0.0f};
+                        x[u] = float4{0.f, 0.f, 0.f, 0.f};
+                    }
+                }
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const float w = a[u].x == -INFINITY ? 0.0f : fast_exp2(a[u].x - M);
+                    l += w * a[u].y;
+                    o.x += w * x[u].x;
+                    o.y += w * x[u].y;
+                    o.z += w * x[u].z;
+                    o.w += w * x[u].w;
+                }
             }
         }
     }
