@@ -107,3 +107,41 @@ def test_quantize_rejects_bad_arguments():
     with pytest.raises(qkv.QKVError):
         qkv.qkv_update_append(pk, pk, x[:, :, :2], x[:, :, :2], 3)   # rows 3..5 > cap
     assert_pack_equal(pack_numpy(pk), before)
+
+
+# exact ties on the GPU: rows whose quotients are exactly k + 1/2 (the
+# hand-derived fixtures under tests/golden/), repeated over rows, heads and
+# both halves of a D = 128 row, so every lane position of the kernel meets
+# them; codes, scales and biases must be the fixtures' own values
+def _unpack_codes(words: np.ndarray, bits: int, D: int) -> np.ndarray:
+    w = np.ascontiguousarray(words).view(np.uint32).astype(np.uint64)
+    per = 32 // bits
+    j = np.arange(D)
+    return ((w[..., j // per] >> ((j % per) * bits).astype(np.uint64)) & ((1 << bits) - 1)).astype(np.int64)
+
+
+@pytest.mark.parametrize("name,D", [("affine_ties_4bit_g32.txt", 64), ("affine_ties_4bit_g32.txt", 128),
+                                    ("affine_ties_8bit_g32.txt", 64), ("affine_ties_8bit_g32.txt", 128),
+                                    ("q8_0_ties.txt", 64), ("q8_0_ties.txt", 256)])
+def test_quantize_exact_ties_match_golden(name, D):
+    from tests import _golden
+    g = _golden.load(name)
+    row = np.asarray(g["x"], np.float16)
+    assert np.array_equal(row.astype(np.float64), np.asarray(g["x"], np.float64))
+    reps = D // row.size
+    x = np.tile(row, (2, 3, 37, reps))                        # [B, H, L, D]
+    xd = to_dev(x, "f16")
+    if name.startswith("q8_0"):
+        pk = pack_numpy(qkv.qkv_quantize(xd, "q8_0", 8, 32))
+        codes = pk["codes"].astype(np.int64)
+        assert np.array_equal(codes, np.broadcast_to(np.tile(np.asarray(g["codes"]), reps), codes.shape))
+        d = pk["scales"].view(np.float16).astype(np.float64)
+        assert np.array_equal(d, np.broadcast_to(np.tile(np.asarray(g["d"], np.float64), reps), d.shape))
+    else:
+        bits = g["bits"]
+        pk = pack_numpy(qkv.qkv_quantize(xd, "affine", bits, 32))
+        codes = _unpack_codes(pk["codes"], bits, D)
+        assert np.array_equal(codes, np.broadcast_to(np.tile(np.asarray(g["codes_unpacked"]), reps), codes.shape))
+        for key in ("scales", "biases"):
+            got = pk[key].astype(np.float64)
+            assert np.array_equal(got, np.broadcast_to(np.tile(np.asarray(g[key], np.float64), reps), got.shape)), key
