@@ -87,7 +87,7 @@
 extern "C" {
 #endif
 
-#define QKV_ABI_VERSION 4
+#define QKV_ABI_VERSION 5
 
 typedef enum {
     QKV_OK = 0,
@@ -219,12 +219,16 @@ typedef enum {
     QKV_KERNEL_DECODE = 1,         /* single query, fp16, GQA factor <= 16, 16x16x32 MFMA */
     QKV_KERNEL_DECODE_NARROW = 2,  /* single query, fp16, GQA factor <= 4, 4x4x4 MFMA */
     QKV_KERNEL_PREFILL = 3,        /* 64-row tiles, fp16, K/V dequantized into LDS */
-    QKV_KERNEL_UNFUSED = 4         /* scores, softmax, P V, chunk sum: four kernels */
+    QKV_KERNEL_UNFUSED = 4,        /* scores, softmax, P V, chunk sum: four kernels */
+    QKV_KERNEL_DECODE_STREAM = 5   /* single query, fp16, GQA factor <= 4, the formats without a
+                                      matrix-core kernel (bit-stream codes, symmetric blocks,
+                                      D = 96), VALU arithmetic; chosen under QKV_ALGO_AUTO */
 } qkv_kernel;
 
 /* The launch plan an attention call with these arguments would use:
- * the algorithm class (QKV_ALGO_GENERIC, QKV_ALGO_MATRIX or
- * QKV_ALGO_UNFUSED) and the kernel (qkv_kernel), the key splits (for the
+ * the algorithm class (QKV_ALGO_GENERIC for the VALU kernels -- the generic
+ * kernel and the bit-stream decode --, QKV_ALGO_MATRIX, QKV_ALGO_UNFUSED or
+ * QKV_ALGO_DEQUANT_F16) and the kernel (qkv_kernel), the key splits (for the
  * unfused composition: the key chunks of its P V product), the (GQA-packed)
  * query rows per workgroup and the workspace size.  Errors: EINVAL for null pointers or shapes that
  * the attention calls would reject as such. */

@@ -16,6 +16,7 @@ QKV_MASK_NONE, QKV_MASK_CAUSAL, QKV_MASK_ADDITIVE = 0, 1, 2
 QKV_ALGO_AUTO, QKV_ALGO_GENERIC, QKV_ALGO_MATRIX, QKV_ALGO_UNFUSED, QKV_ALGO_DEQUANT_F16 = 0, 1, 2, 3, 4
 QKV_KERNEL_GENERIC, QKV_KERNEL_DECODE, QKV_KERNEL_DECODE_NARROW, QKV_KERNEL_PREFILL = 0, 1, 2, 3
 QKV_KERNEL_UNFUSED = 4
+QKV_KERNEL_DECODE_STREAM = 5
 
 # every symbol include/qkv.h declares
 EXPORTS = ["qkv_quantize", "qkv_update_append", "qkv_dequantize", "qsdpa_workspace_bytes", "qsdpa_workspace_reset",

@@ -185,7 +185,7 @@ def qsdpa_workspace_bytes(q: torch.Tensor, k: Pack, L: int, num_splits: int = 0,
 
 # kernel names of qsdpa_plan()["kernel"] (the device function names)
 KERNEL_NAMES = {0: "attn_generic_kernel", 1: "attn_matrix_decode", 2: "attn_decode_narrow",
-                3: "attn_matrix_prefill", 4: "unfused_scores_kernel"}
+                3: "attn_matrix_prefill", 4: "unfused_scores_kernel", 5: "attn_decode_stream"}
 
 
 def qsdpa_plan(q: torch.Tensor, k: Pack, L: int, num_splits: int = 0,

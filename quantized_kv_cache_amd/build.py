@@ -18,7 +18,7 @@ ROOT = os.path.dirname(HERE)
 
 SOURCES = ["qkv_api.cpp", "qkv_quantize.hip", "qkv_attn_generic.hip", "qkv_attn_matrix.hip",
            "qkv_attn_narrow.hip", "qkv_prefill_matrix.hip", "qkv_merge.hip", "qkv_measure.hip", "qkv_static.hip",
-           "qkv_unfused.hip", "qkv_dequant.hip"]
+           "qkv_unfused.hip", "qkv_dequant.hip", "qkv_attn_stream.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -192,6 +192,7 @@ struct Plan {
     bool prefill;                   // tiled matrix kernel
     int wg_rows;                    // its rows per workgroup
     bool narrow;                    // single-query kernel for GQA factors <= 4
+    bool stream;                    // single-query VALU kernel for the bit-stream formats
     int RT, n_rt, S;
     int64_t chunk;
     size_t ws_bytes;
@@ -307,6 +308,7 @@ Plan make_plan(int64_t B, int64_t Hq, int64_t Lq, int64_t D, int64_t L, const qk
     pl.matrix = false;
     pl.prefill = false;
     pl.narrow = false;
+    pl.stream = false;
     // the matrix kernels address a kv head's rows with 32-bit offsets
     const int64_t span = (k->L_cap - 1) * k->stride_l * row_bytes(k) + row_bytes(k);
     // the narrow decode also takes the symmetric 4-bit blocks, which the
@@ -319,6 +321,9 @@ Plan make_plan(int64_t B, int64_t Hq, int64_t Lq, int64_t D, int64_t L, const qk
         pl.prefill = !pl.narrow &&
                      !qkv::decode_matrix_supported(q_dtype, k->mode, bits, k->group_size, (int)D, G, Lq);
     }
+    if (!pl.matrix && algo != QKV_ALGO_GENERIC && algo != QKV_ALGO_MATRIX && span < (int64_t(1) << 31) &&
+        qkv::stream_decode_supported(q_dtype, k->mode, bits, k->group_size, k->scale_dtype, (int)D, G, Lq))
+        pl.stream = true;
     const int64_t n_rows = (int64_t)G * Lq;
     pl.wg_rows = n_rows >= qkv::kPrefillWideMinRows ? qkv::kPrefillRowsWide : qkv::kPrefillRows;
     if (pl.prefill) {
@@ -347,11 +352,15 @@ Plan make_plan(int64_t B, int64_t Hq, int64_t Lq, int64_t D, int64_t L, const qk
         // small caches (256 keys: 10.5 us with 8 splits, 12.9 us with 4), and
         // long ones want four workgroups per CU (64K keys, 3-bit, 8 kv heads:
         // 199 us with 64 splits, 136 us with 128)
+        // the bit-stream decode: a workgroup of 4 waves takes at least one
+        // 64-key tile per wave, about 1024 workgroups in all
         S = pl.matrix ? auto_splits(B * Hk * pl.n_rt, L, 256, 256)
-                      : auto_splits(B * Hk * pl.n_rt, L, 32, 1024);
+            : pl.stream ? auto_splits(B * Hk, L, qkv::stream_decode_key_quantum(), 1024)
+                        : auto_splits(B * Hk * pl.n_rt, L, 32, 1024);
     }
     int64_t chunk = (L + S - 1) / S;
-    const int64_t gran = !pl.matrix ? 32
+    const int64_t gran = pl.stream ? qkv::stream_decode_key_quantum()
+                         : !pl.matrix ? 32
                          : pl.prefill ? 64
                          : pl.narrow  ? qkv::narrow_decode_key_quantum()
                                       : qkv::decode_matrix_key_quantum();
@@ -531,6 +540,7 @@ qkv_status attention(const char* name, const void* q, int32_t q_dtype, int64_t B
                    : pl.prefill  ? qkv::launch_prefill_matrix(kx->mode, kx->bits, (int)D, B, a, s)
                    : pl.narrow ? qkv::launch_attn_narrow(k->mode, k->bits, (int)D, B, a, s)
                    : pl.matrix ? qkv::launch_attn_matrix(k->mode, k->bits, (int)D, B, a, s)
+                   : pl.stream ? qkv::launch_attn_stream(k->mode, k->bits, (int)D, B, a, s)
                                : qkv::launch_attn_generic(q_dtype, k->mode, k->bits, (int)D, B, a, s);
     if (e == hipSuccess && timed) e = hipEventRecord(static_cast<hipEvent_t>(opts->timing_events[1]), s);
     // the narrow decode kernel merges its splits itself
@@ -635,6 +645,7 @@ qkv_status qsdpa_plan(int64_t B, int64_t Hq, int64_t Lq, int64_t D, int64_t L, c
     plan->num_splits = pl.S;
     plan->row_tile = pl.prefill ? pl.wg_rows : pl.RT;
     plan->kernel = pl.unfused   ? QKV_KERNEL_UNFUSED
+                   : pl.stream  ? QKV_KERNEL_DECODE_STREAM
                    : !pl.matrix ? QKV_KERNEL_GENERIC
                    : pl.prefill ? QKV_KERNEL_PREFILL
                    : pl.narrow  ? QKV_KERNEL_DECODE_NARROW

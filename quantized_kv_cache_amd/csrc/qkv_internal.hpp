@@ -125,6 +125,16 @@ int decode_matrix_key_quantum();
 bool narrow_decode_supported(int q_dtype, int mode, int bits, int group_size, int D, int G,
                              int64_t Lq);
 int narrow_decode_key_quantum();
+
+// Single-query decode (fp16 queries, G <= 4) for the formats without a
+// matrix-core kernel: the bit-stream codes, the symmetric blocks and head
+// size 96 (launch_attn_stream; its split states use the 16-row layout of
+// the merge kernels).
+bool stream_decode_supported(int q_dtype, int mode, int bits, int group_size, int scale_dtype, int D,
+                             int G, int64_t Lq);
+int stream_decode_key_quantum();
+hipError_t launch_attn_stream(int mode, int bits, int D, int64_t B, const AttnLaunch& p,
+                              hipStream_t stream);
 hipError_t launch_attn_narrow(int mode, int bits, int D, int64_t B, const AttnLaunch& p,
                               hipStream_t stream);
 

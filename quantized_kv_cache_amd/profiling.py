@@ -34,6 +34,7 @@ KERNEL_SOURCES = {
     "merge_splits_small": ["qkv_merge.hip", "qkv_merge.hpp", "qkv_device.hpp", "qkv_internal.hpp"],
     "quantize_rows_kernel": ["qkv_quantize.hip", "qkv_device.hpp", "qkv_internal.hpp"],
     "unfused_scores_kernel": ["qkv_unfused.hip", "qkv_device.hpp", "qkv_internal.hpp"],
+    "attn_decode_stream": ["qkv_attn_stream.hip", "qkv_mfma.hpp", "qkv_device.hpp", "qkv_internal.hpp"],
 }
 
 

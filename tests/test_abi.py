@@ -32,7 +32,7 @@ def test_exports_every_declared_function(L):
     assert set(names) == set(_lib.EXPORTS), names
     for n in names:
         assert hasattr(L, n), n
-    assert L.qkv_abi_version() == 4
+    assert L.qkv_abi_version() == 5
 
 
 def _pack(**kw):
@@ -157,20 +157,24 @@ def test_workspace_bytes(L):
     ((1, 32, 2, 512, 256, 20480, "f16", "q8_0", 8, 32), _lib.QKV_KERNEL_PREFILL),
     ((1, 64, 2, 1, 128, 700, "f16", "affine", 4, 64), _lib.QKV_KERNEL_PREFILL),   # G = 32
     ((1, 8, 2, 1, 128, 700, "bf16", "affine", 4, 64), _lib.QKV_KERNEL_GENERIC),
+    ((1, 32, 8, 1, 128, 65536, "f16", "affine", 3, 64), _lib.QKV_KERNEL_DECODE_STREAM),
+    ((1, 32, 8, 1, 96, 16384, "f16", "affine", 4, 32), _lib.QKV_KERNEL_DECODE_STREAM),
+    ((1, 32, 8, 1, 128, 65536, "f16", "qsym", 5, 32), _lib.QKV_KERNEL_DECODE_STREAM),
+    ((1, 32, 4, 1, 128, 4096, "f16", "affine", 3, 64), _lib.QKV_KERNEL_GENERIC),   # G = 8
 ])
 def test_plan_kernel_choice(L, shape, kernel):
     """The plan names the kernel each workload shape runs on (host logic only)."""
     B, Hq, Hk, Lq, D, Lk, qdt, mode, bits, gs = shape
     dt = {"f32": _lib.QKV_F32, "f16": _lib.QKV_F16, "bf16": _lib.QKV_BF16}[qdt]
-    kp = _lib.QkvPack(mode=_lib.QKV_AFFINE if mode == "affine" else _lib.QKV_Q8_0, bits=bits,
-                      group_size=gs, scale_dtype=dt if mode == "affine" else _lib.QKV_F16,
+    kp = _lib.QkvPack(mode={"affine": _lib.QKV_AFFINE, "q8_0": _lib.QKV_Q8_0, "qsym": _lib.QKV_QSYM}[mode],
+                      bits=bits, group_size=gs, scale_dtype=dt if mode == "affine" else _lib.QKV_F16,
                       B=B, H=Hk, L_cap=Lk, D=D, codes=FAKE, scales=FAKE + 0x10000000,
                       biases=FAKE + 0x20000000 if mode == "affine" else None,
                       stride_b=Hk * Lk, stride_h=Lk, stride_l=1)
     pl = _lib.QkvAttnPlan()
     assert L.qsdpa_plan(B, Hq, Lq, D, Lk, ctypes.byref(kp), dt, None, ctypes.byref(pl)) == 0
     assert pl.kernel == kernel
-    assert pl.algo == (_lib.QKV_ALGO_GENERIC if kernel == _lib.QKV_KERNEL_GENERIC
+    assert pl.algo == (_lib.QKV_ALGO_GENERIC if kernel in (_lib.QKV_KERNEL_GENERIC, _lib.QKV_KERNEL_DECODE_STREAM)
                        else _lib.QKV_ALGO_MATRIX)
     assert 1 <= pl.num_splits <= 256 and pl.num_splits * pl.keys_per_split >= Lk
     if kernel == _lib.QKV_KERNEL_PREFILL:

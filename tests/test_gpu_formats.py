@@ -2,9 +2,10 @@
 size 96, and the symmetric 4/5-bit blocks (the Q4_0/Q5_0 reading), plus Q8_0
 and affine 4/8-bit at head size 96.  Quantize and append must give the
 oracle's bits; decode and prefill (on the generic kernel, with key splits
-and the merge kernels; the symmetric 4-bit blocks with fp16 queries, D 64 or
-128 and at most 4 heads per kv head also on the narrow matrix-core decode)
-must be within the attention tolerance of the oracle."""
+and the merge kernels; with fp16 queries and at most 4 heads per kv head the
+decode also runs on the bit-stream decode kernel, or for the symmetric 4-bit
+blocks at D 64 or 128 on the narrow matrix-core decode) must be within the
+attention tolerance of the oracle."""
 import math
 import zlib
 
@@ -64,9 +65,10 @@ def test_formats_quantize_append_and_decode(fmt):
     ref = oracle_attention(q, dt, kr, vr, 517, mode, bits, gs, scale)
     qd = to_dev(q, dt)
     narrow = mode == "qsym" and bits == 4 and D in (64, 128) and dt == "f16"
-    assert qkv.qsdpa_plan(qd, kp, 517)["kernel"] == ("attn_decode_narrow" if narrow else "attn_generic_kernel")
+    expect = "attn_decode_narrow" if narrow else "attn_decode_stream" if dt == "f16" else "attn_generic_kernel"
+    assert qkv.qsdpa_plan(qd, kp, 517)["kernel"] == expect
     assert qkv.qsdpa_plan(qd, kp, 517, algo="generic")["kernel"] == "attn_generic_kernel"
-    for algo in (("auto", "generic") if narrow else ("auto",)):
+    for algo in (("auto", "generic") if dt == "f16" else ("auto",)):
         for splits in (0, 1, 5, 17):
             out = qkv.qsdpa_decode(qd, kp, vp, 517, scale, num_splits=splits, algo=algo)
             assert_close(out, ref, f"decode {fmt} {algo} splits={splits}")
@@ -182,3 +184,44 @@ def test_qsym4_narrow_unaligned_scales(D):
     out = qkv.qsdpa_decode(qd, ku, vu, 1500, scale)
     assert_close(out, ref, f"qsym4 narrow D={D}, 2-byte aligned scales")
     assert torch.equal(out, aligned)
+
+
+# the bit-stream decode kernel: GQA factors 1-4, every head size, ragged
+# lengths, an additive mask, split counts (one split writes the output itself,
+# several go through the merge kernel), repeat bits
+STREAM_CASES = [
+    # mode, bits, gs, D, B, Hq, Hk, L, mask
+    ("affine", 3, 64, 128, 1, 8, 2, 1999, False),
+    ("affine", 2, 128, 256, 2, 3, 3, 700, True),
+    ("affine", 5, 32, 96, 1, 8, 4, 333, False),
+    ("affine", 6, 64, 64, 2, 4, 1, 4097, True),
+    ("qsym", 5, 32, 128, 1, 32, 8, 1500, False),
+    ("qsym", 4, 32, 96, 1, 6, 2, 64, False),
+    ("q8_0", 8, 32, 96, 1, 4, 2, 1025, True),
+    ("affine", 8, 32, 96, 1, 2, 2, 1, False),          # a single key
+]
+
+
+@pytest.mark.parametrize("case", STREAM_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_stream_decode(case):
+    mode, bits, gs, D, B, Hq, Hk, L, use_mask = case
+    fmt = (mode, bits, gs, D, "f16")
+    q, kp, vp, kr, vr = _case(fmt, B, Hq, Hk, 1, L)
+    scale = 1.0 / math.sqrt(D)
+    mask = None
+    if use_mask:
+        rng = np.random.default_rng(_seed(case, "mask"))
+        mask = np.where(rng.random((B, Hq, 1, L)) < 0.25, -np.inf, rng.normal(0, 1, (B, Hq, 1, L))).astype(np.float32)
+        mask[..., L // 2] = 0.0                       # every row sees a key
+        mask[0, 0, 0, :] = -np.inf                    # a fully masked row -> zeros
+    ref = oracle_attention(q, "f16", kr, vr, L, mode, bits, gs, scale, mask=mask)
+    qd = to_dev(q, "f16")
+    md = None if mask is None else to_dev(mask, "f32")
+    assert qkv.qsdpa_plan(qd, kp, L)["kernel"] == "attn_decode_stream"
+    first = None
+    for splits in (0, 1, 2, 7):
+        out = qkv.qsdpa_decode(qd, kp, vp, L, scale, mask=md, num_splits=splits)
+        assert_close(out, ref, f"stream decode {case} splits={splits}", report=splits == 0)
+        if splits == 0:
+            first = out.clone()
+    assert torch.equal(qkv.qsdpa_decode(qd, kp, vp, L, scale, mask=md), first)
