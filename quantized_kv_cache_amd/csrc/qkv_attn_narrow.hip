@@ -481,50 +481,56 @@ __global__ __launch_bounds__(NTH) void attn_decode_narrow(AttnLaunch p) {
     __syncthreads();
 
     // ------------------------------------------------------------ output
-    // Item i -> (jj, head oh, kbb, tc), jj fastest: the P V values of the 4
+    // Item -> (jj, head oh, kbb, tc), jj fastest: the P V values of the 4
     // consecutive d = DPT (4 kbb + jj) + 4 tc + 0..3 sit in lane
     // 16 kbb + (oh + GP g), register jj, of tiles 4 tc .. 4 tc + 3
-    // (DPT = D / 16).  Consecutive threads read consecutive LDS words; each
-    // item is one 16-byte (or 8-byte) store.
+    // (DPT = D / 16).  The 4 lanes of a quad share an item: lane 'sub' of the
+    // quad combines waves sub and sub + 4, and two quad exchanges add the
+    // lanes' sums in a fixed order.  Consecutive quads read consecutive LDS
+    // words; each item is one 16-byte (or 8-byte) store.
     constexpr int DPT = D / 16;
     static_assert(DPT % 4 == 0, "4 consecutive d per output item");
+    static_assert(NW == 8, "two waves per quad lane");
     // with several splits: this split's state, stored at device scope for the
     // fused merge ([16 rows][D] o and [16 rows][2] (m, l); rows = heads)
     const auto rml = flat_rsrc(p.part_ml + (bk * p.S + split) * 32, 32 * 4);
     const auto rpo = flat_rsrc(p.part_o + (bk * p.S + split) * 16 * D, 16 * D * 4);
     const int64_t obase = (b * p.Hq + kvh * G) * D;
-    for (int i = tid; i < G * D / 4; i += NTH) {
-        const int jj = i & 3;
-        const int oh = (i >> 2) % G;
-        const int rest = (i >> 2) / G;
+    for (int i = tid; i < G * D; i += NTH) {          // G D is a multiple of 4: whole quads
+        const int sub = i & 3;
+        const int item = i >> 2;
+        const int jj = item & 3;
+        const int oh = (item >> 2) % G;
+        const int rest = (item >> 2) / G;
         const int kbb = rest & 3, tc = rest >> 2;
         const int d0 = DPT * (4 * kbb + jj) + 4 * tc;
         const int g = d0 / GS;                        // 4 consecutive d share a group
-        float fw[NW];
-        float Mh = -INFINITY;
-#pragma unroll
-        for (int w = 0; w < NW; ++w) Mh = fmaxf(Mh, s_ml[w][0][oh]);
-        float Lh = 0.0f, bias = 0.0f;
-#pragma unroll
-        for (int w = 0; w < NW; ++w) {
-            const float mw = s_ml[w][0][oh];
-            fw[w] = (mw == -INFINITY) ? 0.0f : fast_exp2(mw - Mh);
-            Lh += fw[w] * s_ml[w][1][oh];
-            bias += fw[w] * s_bias[w][oh][g];
-        }
+        const int w0 = sub, w1 = sub + 4;
+        const float m0 = s_ml[w0][0][oh], m1 = s_ml[w1][0][oh];
+        float Mh = fmaxf(m0, m1);
+        Mh = fmaxf(Mh, dpp_f<0xB1>(Mh));
+        Mh = fmaxf(Mh, dpp_f<0x4E>(Mh));
+        const float f0 = (m0 == -INFINITY) ? 0.0f : fast_exp2(m0 - Mh);
+        const float f1 = (m1 == -INFINITY) ? 0.0f : fast_exp2(m1 - Mh);
+        float part[6];
+        part[4] = f0 * s_ml[w0][1][oh] + f1 * s_ml[w1][1][oh];
+        part[5] = f0 * s_bias[w0][oh][g] + f1 * s_bias[w1][oh][g];
         const int slot = (kbb * 16 + oh + GP * g) * 4 + jj;
-        float v[4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            v[q] = 0.0f;
+        for (int q = 0; q < 4; ++q)
+            part[q] = f0 * s_wave[w0][(4 * tc + q) * 256 + slot] + f1 * s_wave[w1][(4 * tc + q) * 256 + slot];
 #pragma unroll
-            for (int w = 0; w < NW; ++w) v[q] += fw[w] * s_wave[w][(4 * tc + q) * 256 + slot];
+        for (int k = 0; k < 6; ++k) {
+            part[k] += dpp_f<0xB1>(part[k]);          // quad_perm [1, 0, 3, 2]
+            part[k] += dpp_f<0x4E>(part[k]);          // quad_perm [2, 3, 0, 1]
         }
+        if (sub != 0) continue;
+        const float Lh = part[4], bias = part[5];
         float o[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             // 4-bit odd d: the tile of its code's whole byte minus the even d's tile
-            const float x = (BITS == 4 && (q & 1)) ? (v[q] - v[q - 1]) * 0.0625f : v[q];
+            const float x = (BITS == 4 && (q & 1)) ? (part[q] - part[q - 1]) * 0.0625f : part[q];
             o[q] = x * 16777216.0f + bias;
         }
         if (p.S == 1) {

@@ -67,12 +67,15 @@ __device__ __forceinline__ void wait_stores() {
 
 // The fused merge for single-query tiles (rows = the G <= GP query heads of a
 // kv head), run by all NTHR threads of the last workgroup: thread -> (float4
-// column c of the GP x D outputs, split group sg); it reads splits sg,
-// sg + SGN, ... (loads issued 8 at a time): their m values first, for the
-// row's maximum M (combined over the split groups through 'lds', >= 6 NTHR
-// floats), then the states weighted by 2^(m_s - M), whose sums the split
-// groups add through 'lds' in group order; column c's 4 fp16 outputs are
-// stored.  No split waits on another's rescaling, and any workgroup that
+// column c of the GP x D outputs, split group sg); it combines splits sg,
+// sg + SGN, ...  When a thread has at most U splits (S <= U SGN) their m, l
+// and o are all requested at once, so the merge costs one round trip to
+// memory: the row's maximum M is then reduced over the split groups through
+// 'lds' (>= 6 NTHR floats).  With more splits the m values are read first
+// (U loads in flight at a time) and the states after M is known.  Either way
+// the states are weighted by 2^(m_s - M) in split order, the split groups'
+// sums are added through 'lds' in group order, and column c's 4 fp16 outputs
+// are stored.  No split waits on another's rescaling, and any workgroup that
 // runs it gets the same result.
 template <int NTHR, int D, int GP>
 __device__ __forceinline__ void merge_last(const AttnLaunch& p, int64_t b, int64_t kvh, int64_t bk,
@@ -88,58 +91,80 @@ __device__ __forceinline__ void merge_last(const AttnLaunch& p, int64_t b, int64
     const int S = p.S, G = p.G;
     const auto rml = flat_rsrc(p.part_ml + bk * S * 32, (uint32_t)S * 32 * 4);
     const auto ro = flat_rsrc(p.part_o + bk * S * 16 * D, (uint32_t)S * 16 * D * 4);
-    float mx = -INFINITY;
-    if (h < G) {
-        for (int s0 = sg; s0 < S; s0 += U * SGN) {
-            float m[U];
+    // states of splits s0 + u SGN, u < U (absent ones: m = -inf, l = 0, o = 0)
+    auto load_states = [&](int s0, float* m, float* ls, float4* x) {
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const uint32_t s = (uint32_t)(s0 + u * SGN);
-                m[u] = s < (uint32_t)S ? __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
-                                              rml, (int)((s * 32 + 2 * h) * 4), 0, kScopeDevice))
-                                       : -INFINITY;
+        for (int u = 0; u < U; ++u) {
+            const uint32_t s = (uint32_t)(s0 + u * SGN);
+            if (h < G && s < (uint32_t)S) {
+                const auto a = __builtin_amdgcn_raw_buffer_load_b64(rml, (int)((s * 32 + 2 * h) * 4), 0,
+                                                                    kScopeDevice);
+                const auto y = __builtin_amdgcn_raw_buffer_load_b128(
+                    ro, (int)(((s * 16 + h) * D + 4 * f) * 4), 0, kScopeDevice);
+                m[u] = __uint_as_float(a[0]);
+                ls[u] = __uint_as_float(a[1]);
+                x[u] = float4{__uint_as_float(y[0]), __uint_as_float(y[1]), __uint_as_float(y[2]),
+                              __uint_as_float(y[3])};
+            } else {
+                m[u] = -INFINITY;
+                ls[u] = 0.0f;
+                x[u] = float4{0.f, 0.f, 0.f, 0.f};
             }
-#pragma unroll
-            for (int u = 0; u < U; ++u) mx = fmaxf(mx, m[u]);
         }
-    }
-    lds[tid] = mx;
-    __syncthreads();
-    float M = lds[c];
+    };
+    auto accumulate = [&](float M, const float* m, const float* ls, const float4* x, float& l, float4& o) {
 #pragma unroll
-    for (int g = 1; g < SGN; ++g) M = fmaxf(M, lds[g * NC + c]);
+        for (int u = 0; u < U; ++u) {
+            const float w = m[u] == -INFINITY ? 0.0f : fast_exp2(m[u] - M);
+            l += w * ls[u];
+            o.x += w * x[u].x;
+            o.y += w * x[u].y;
+            o.z += w * x[u].z;
+            o.w += w * x[u].w;
+        }
+    };
+    auto row_max = [&](float mx) {
+        lds[tid] = mx;
+        __syncthreads();
+        float M = lds[c];
+#pragma unroll
+        for (int g = 1; g < SGN; ++g) M = fmaxf(M, lds[g * NC + c]);
+        return M;
+    };
     float l = 0.0f;
     float4 o = {0.f, 0.f, 0.f, 0.f};
-    if (h < G && M != -INFINITY) {
-        for (int s0 = sg; s0 < S; s0 += U * SGN) {
-            float m[U], ls[U];
-            float4 x[U];
+    if (S <= U * SGN) {
+        float m[U], ls[U];
+        float4 x[U];
+        load_states(sg, m, ls, x);
+        float mx = -INFINITY;
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const uint32_t s = (uint32_t)(s0 + u * SGN);
-                if (s < (uint32_t)S) {
-                    const auto a = __builtin_amdgcn_raw_buffer_load_b64(rml, (int)((s * 32 + 2 * h) * 4), 0,
-                                                                        kScopeDevice);
-                    const auto y = __builtin_amdgcn_raw_buffer_load_b128(
-                        ro, (int)(((s * 16 + h) * D + 4 * f) * 4), 0, kScopeDevice);
-                    m[u] = __uint_as_float(a[0]);
-                    ls[u] = __uint_as_float(a[1]);
-                    x[u] = float4{__uint_as_float(y[0]), __uint_as_float(y[1]), __uint_as_float(y[2]),
-                                  __uint_as_float(y[3])};
-                } else {
-                    m[u] = -INFINITY;
-                    ls[u] = 0.0f;
-                    x[u] = float4{0.f, 0.f, 0.f, 0.f};
+        for (int u = 0; u < U; ++u) mx = fmaxf(mx, m[u]);
+        const float M = row_max(mx);
+        if (M != -INFINITY) accumulate(M, m, ls, x, l, o);
+    } else {
+        float mx = -INFINITY;
+        if (h < G) {
+            for (int s0 = sg; s0 < S; s0 += U * SGN) {
+                float m[U];
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const uint32_t s = (uint32_t)(s0 + u * SGN);
+                    m[u] = s < (uint32_t)S ? __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+                                                  rml, (int)((s * 32 + 2 * h) * 4), 0, kScopeDevice))
+                                           : -INFINITY;
                 }
-            }
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const float w = m[u] == -INFINITY ? 0.0f : fast_exp2(m[u] - M);
-                l += w * ls[u];
-                o.x += w * x[u].x;
-                o.y += w * x[u].y;
-                o.z += w * x[u].z;
-                o.w += w * x[u].w;
+                for (int u = 0; u < U; ++u) mx = fmaxf(mx, m[u]);
+            }
+        }
+        const float M = row_max(mx);
+        if (h < G && M != -INFINITY) {
+            for (int s0 = sg; s0 < S; s0 += U * SGN) {
+                float m[U], ls[U];
+                float4 x[U];
+                load_states(s0, m, ls, x);
+                accumulate(M, m, ls, x, l, o);
             }
         }
     }
