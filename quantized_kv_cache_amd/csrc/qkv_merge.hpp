@@ -70,8 +70,9 @@ __device__ __forceinline__ void wait_stores() {
 // column c of the GP x D outputs, split group sg); it combines splits sg,
 // sg + SGN, ...  When a thread has at most U splits (S <= U SGN) their m, l
 // and o are all requested at once, so the merge costs one round trip to
-// memory: the row's maximum M is then reduced over the split groups through
-// 'lds' (>= 6 NTHR floats).  With more splits the m values are read first
+// memory: each (m, l) pair is read once, by one thread, and shared through
+// 'lds' (>= 6 NTHR + 256 floats), where every thread then finds the row's
+// maximum M.  With more splits the m values are read first
 // (U loads in flight at a time) and the states after M is known.  Either way
 // the states are weighted by 2^(m_s - M) in split order, the split groups'
 // sums are added through 'lds' in group order, and column c's 4 fp16 outputs
@@ -134,13 +135,45 @@ __device__ __forceinline__ void merge_last(const AttnLaunch& p, int64_t b, int64
     float l = 0.0f;
     float4 o = {0.f, 0.f, 0.f, 0.f};
     if (S <= U * SGN) {
-        float m[U], ls[U];
+        // (m, l) of every (split, head) with one 8-byte load each (thread
+        // s G + h), shared through LDS; the o of this thread's splits
+        float* mlds = lds + 6 * NTHR;                 // [S][GP][2]
+        float2 mlv = {0.0f, 0.0f};
+        if (tid < S * G) {
+            const int s = tid / G, hh = tid - (tid / G) * G;
+            const auto a = __builtin_amdgcn_raw_buffer_load_b64(rml, (int)((s * 32 + 2 * hh) * 4), 0, kScopeDevice);
+            mlv = float2{__uint_as_float(a[0]), __uint_as_float(a[1])};
+        }
         float4 x[U];
-        load_states(sg, m, ls, x);
-        float mx = -INFINITY;
 #pragma unroll
-        for (int u = 0; u < U; ++u) mx = fmaxf(mx, m[u]);
-        const float M = row_max(mx);
+        for (int u = 0; u < U; ++u) {
+            const uint32_t s = (uint32_t)(sg + u * SGN);
+            if (h < G && s < (uint32_t)S) {
+                const auto y = __builtin_amdgcn_raw_buffer_load_b128(
+                    ro, (int)(((s * 16 + h) * D + 4 * f) * 4), 0, kScopeDevice);
+                x[u] = float4{__uint_as_float(y[0]), __uint_as_float(y[1]), __uint_as_float(y[2]),
+                              __uint_as_float(y[3])};
+            } else {
+                x[u] = float4{0.f, 0.f, 0.f, 0.f};
+            }
+        }
+        if (tid < S * G) {
+            const int s = tid / G, hh = tid - (tid / G) * G;
+            *(float2*)&mlds[(s * GP + hh) * 2] = mlv;
+        }
+        __syncthreads();
+        float m[U], ls[U];
+        float M = -INFINITY;
+        if (h < G) {
+            for (int s = 0; s < S; ++s) M = fmaxf(M, mlds[(s * GP + h) * 2]);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int s = sg + u * SGN;
+            const bool ok = h < G && s < S;
+            m[u] = ok ? mlds[(s * GP + h) * 2] : -INFINITY;
+            ls[u] = ok ? mlds[(s * GP + h) * 2 + 1] : 0.0f;
+        }
         if (M != -INFINITY) accumulate(M, m, ls, x, l, o);
     } else {
         float mx = -INFINITY;
