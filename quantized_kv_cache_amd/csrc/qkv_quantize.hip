@@ -214,21 +214,36 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(QuantLaunch p) {
                 const float s = round_to<DT>(s32);
                 const float bias = round_to<DT>(mn);
                 const float y = DT == DT_F32 ? 1.0f : recip_rn16(s);
-                int32_t c[8];
+                // code i = clamp(round_half_even(qt_i), 0, NL): v_cvt_pk_u8_f32
+                // rounds half to even, saturates to [0, 255] and inserts the
+                // byte into a register in one instruction (checked on the GPU
+                // against rint with saturation on ties, their neighbours,
+                // negative values and values past 255); 4-bit quotients are
+                // first limited to 15, which commutes with the rounding
+                float qt[8];
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
                     const float a = v[u][i] - bias;
-                    const float qt = DT == DT_F32 ? a / s : div_by_recip(a, s, y);
-                    c[i] = rne_clamp(qt, 0, NL);
+                    qt[i] = DT == DT_F32 ? a / s : div_by_recip(a, s, y);
+                    if constexpr (BITS == 4) qt[i] = fminf(qt[i], (float)NL);
                 }
                 if constexpr (BITS == 4) {
-                    uint32_t w = 0;
+                    // byte k of the word holds codes 2k (low nibble) and 2k + 1
+                    uint32_t ev = 0, od = 0;
 #pragma unroll
-                    for (int i = 0; i < 8; ++i) w |= (uint32_t)c[i] << (4 * i);
-                    __builtin_amdgcn_raw_buffer_store_b32(w, rc[u], (int)o_c, 0, 0);
+                    for (int k = 0; k < 4; ++k) {
+                        ev = __builtin_amdgcn_cvt_pk_u8_f32(qt[2 * k], (uint32_t)k, ev);
+                        od = __builtin_amdgcn_cvt_pk_u8_f32(qt[2 * k + 1], (uint32_t)k, od);
+                    }
+                    __builtin_amdgcn_raw_buffer_store_b32(ev | (od << 4), rc[u], (int)o_c, 0, 0);
                 } else {
-                    const u2 w = {(uint32_t)c[0] | ((uint32_t)c[1] << 8) | ((uint32_t)c[2] << 16) | ((uint32_t)c[3] << 24),
-                                  (uint32_t)c[4] | ((uint32_t)c[5] << 8) | ((uint32_t)c[6] << 16) | ((uint32_t)c[7] << 24)};
+                    uint32_t lo = 0, hi = 0;
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        lo = __builtin_amdgcn_cvt_pk_u8_f32(qt[k], (uint32_t)k, lo);
+                        hi = __builtin_amdgcn_cvt_pk_u8_f32(qt[4 + k], (uint32_t)k, hi);
+                    }
+                    const u2 w = {lo, hi};
                     __builtin_amdgcn_raw_buffer_store_b64(w, rc[u], (int)o_c, 0, 0);
                 }
                 if (leader) {
