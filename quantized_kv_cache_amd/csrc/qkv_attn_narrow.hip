@@ -632,7 +632,12 @@ bool narrow_decode_supported(int q_dtype, int mode, int bits, int group_size, in
     return ng <= 4 && (bits == 4 || ng <= 2);
 }
 
-int narrow_decode_key_quantum() { return NTK * 8; }
+// Splits are whole tiles, not whole rounds of the 8 waves: with a key count
+// that is not a multiple of 8 tiles per split the spare tiles fall to the
+// first waves of every workgroup, instead of a shorter last split idling the
+// XCDs that hold it (16,448 keys in 4 splits: 65/65/65/62 tiles against
+// 72/72/72/41).
+int narrow_decode_key_quantum() { return NTK; }
 
 hipError_t launch_attn_narrow(int mode, int bits, int D, int64_t B, const AttnLaunch& p,
                               hipStream_t stream) {
