@@ -1,0 +1,99 @@
+"""Attention calls captured in a HIP graph (torch.cuda.CUDAGraph on ROCm) and
+replayed: the decode with the in-kernel split merge (its merge tickets must
+be back at zero after every replay), the 16-row decode followed by the split
+merge kernel, the causal prefill, and qsdpa_decode_static (the entry point
+for callers that cannot allocate).  Between replays the captured query
+tensor is rewritten and the same call runs eagerly on the same workspace;
+every replay must equal the eager call bit for bit, and the first of them
+the oracle within the attention tolerance."""
+import numpy as np
+import pytest
+import torch
+
+import quantized_kv_cache_amd as qkv
+from tests._cases import assert_close, oracle_attention, oracle_pack, to_dev, W
+
+pytestmark = pytest.mark.gpu
+
+CASES = {
+    # name: (B, Hq, Hk, Lq, L, D, mode, bits, gs, causal)
+    "narrow_fused_merge": (1, 16, 4, 1, 9000, 128, "affine", 4, 64, False),
+    "sixteen_row_merge_kernel": (1, 32, 2, 1, 6000, 256, "q8_0", 8, 32, False),
+    "prefill_causal": (1, 8, 2, 40, 3000, 128, "q8_0", 8, 32, True),
+}
+
+
+def _inputs(seed, B, Hq, Hk, Lq, L, D, mode, bits, gs):
+    k = W.random_case(seed + 1, (B, Hk, L, D), "normal", "f16")
+    v = W.random_case(seed + 2, (B, Hk, L, D), "normal", "f16")
+    kp = qkv.qkv_quantize(to_dev(k, "f16"), mode, bits, gs)
+    vp = qkv.qkv_quantize(to_dev(v, "f16"), mode, bits, gs)
+    qs = [W.random_case(seed + 10 + r, (B, Hq, Lq, D), "normal", "f16") for r in range(2)]
+    return k, v, kp, vp, qs
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_graph_replays_equal_eager_calls(name):
+    B, Hq, Hk, Lq, L, D, mode, bits, gs, causal = CASES[name]
+    scale = 1.0 / np.sqrt(D)
+    k, v, kp, vp, qs = _inputs(71, B, Hq, Hk, Lq, L, D, mode, bits, gs)
+    print(f"[graph] {name}", flush=True)
+    s = torch.cuda.Stream()
+    ws = qkv.Workspace()
+    with torch.cuda.stream(s):
+        q = to_dev(qs[0], "f16")
+        out = torch.empty_like(q)
+        call = qkv.PreparedAttention(q, kp, vp, L, scale, out, causal=causal, workspace=ws)
+        call()
+        call()
+    s.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        call()
+    for rep in range(4):
+        qn = qs[rep % 2]
+        q.copy_(to_dev(qn, "f16"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = out.clone()
+        with torch.cuda.stream(s):
+            call()                      # the same launch, eagerly, on the same workspace
+        s.synchronize()
+        assert torch.equal(got, out), f"{name}: replay {rep} differs from the eager call"
+        if rep < 2:
+            ref = oracle_attention(qn, "f16", oracle_pack(k, "f16", mode, bits, gs),
+                                   oracle_pack(v, "f16", mode, bits, gs), L, mode, bits, gs,
+                                   scale, causal=causal)
+            assert_close(got, ref, f"{name} replay {rep}")
+    plan = qkv.qsdpa_plan(q, kp, L)
+    assert plan["num_splits"] > 1, plan           # the split states and merge are exercised
+
+
+def test_graph_replays_of_the_static_decode():
+    B, Hq, Hk, Lq, L, D, mode, bits, gs, _ = CASES["narrow_fused_merge"]
+    scale = 1.0 / np.sqrt(D)
+    k, v, kp, vp, qs = _inputs(83, B, Hq, Hk, Lq, L, D, mode, bits, gs)
+    print("[graph] static decode", flush=True)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        q = to_dev(qs[0], "f16")
+        out = torch.empty_like(q)
+        qkv.qsdpa_decode_static(q, kp, vp, L, scale, out=out)   # first call on the device: set-up
+    s.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        qkv.qsdpa_decode_static(q, kp, vp, L, scale, out=out)
+    for rep in range(4):
+        q.copy_(to_dev(qs[rep % 2], "f16"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = out.clone()
+        with torch.cuda.stream(s):
+            qkv.qsdpa_decode_static(q, kp, vp, L, scale, out=out)
+        s.synchronize()
+        assert torch.equal(got, out), f"static decode: replay {rep} differs from the eager call"
+        want = qkv.qsdpa_decode(q, kp, vp, L, scale)
+        torch.cuda.synchronize()
+        assert torch.equal(got, want), f"static decode: replay {rep} differs from qsdpa_decode"
