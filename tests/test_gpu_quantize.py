@@ -145,3 +145,57 @@ def test_quantize_exact_ties_match_golden(name, D):
         for key in ("scales", "biases"):
             got = pk[key].astype(np.float64)
             assert np.array_equal(got, np.broadcast_to(np.tile(np.asarray(g[key], np.float64), reps), got.shape)), key
+
+
+# rows whose rounding decisions are the hard ones: exact k + 1/2 quotients,
+# constant rows, and groups of fp16 subnormal steps (values o + k 2^-24 with
+# a range of R steps).  With R steps the scale R/15 (R/255) is stored as an
+# fp16 multiple of 2^-24, so for R below a few hundred its rounding moves the
+# top quotient well past the last code (R = 36: scale 2 steps, quotient 18);
+# the codes must then saturate exactly as the oracle clamps them.
+SUBNORMAL_RANGES = (6, 20, 36, 37, 45, 100, 250, 600, 1000)
+
+
+def _hard_rows(D: int, seed: int) -> np.ndarray:
+    rng = np.random.default_rng(seed)
+    rows = []
+    for num, den in ((1, 16), (7, 128), (3, 64)):
+        for bias in (0.0, -2.0):
+            k = rng.integers(0, 15, D)
+            rows.append(bias + (k + 0.5 * (rng.random(D) < 0.6)) * num / den)
+            rows[-1][0], rows[-1][1] = bias, bias + 15 * num / den
+    rows.append(np.full(D, 0.3125))
+    rows.append(np.full(D, 2.0 ** -24))
+    step = 2.0 ** -24
+    for R in SUBNORMAL_RANGES:
+        for off in (0.0, -R * step, 2.0 ** -14):
+            r = off + rng.integers(0, R + 1, D) * step
+            r[0::32], r[1::32] = off, off + R * step        # every 32-block spans R steps
+            rows.append(r)
+    return np.stack(rows).astype(np.float32)
+
+
+def _top_quotients_f16(x: np.ndarray, bits: int, gs: int) -> np.ndarray:
+    """(max - min) / fp16(max(range / (2^bits - 1), fp16(1e-7))) per group,
+    in fp32: where this exceeds 2^bits - 1/2 the code has to saturate."""
+    g = x.astype(np.float32).reshape(x.shape[0], -1, gs)
+    mn, mx = g.min(-1), g.max(-1)
+    s = np.maximum((mx - mn) / np.float32(2 ** bits - 1), np.float32(np.float16(1e-7)))
+    s = s.astype(np.float16).astype(np.float32)
+    return (mx - mn) / s
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16", "f32"])
+@pytest.mark.parametrize("mode,bits,gs", FORMATS)
+@pytest.mark.parametrize("D", [64, 256])
+def test_quantize_hard_rows_bitexact(dtype, mode, bits, gs, D):
+    if mode == "affine" and D % gs:
+        pytest.skip("group does not divide D")
+    rows = _hard_rows(D, 50 + D + gs)
+    x = W.cast(rows, dtype)
+    if dtype == "f16" and mode == "affine":
+        top = _top_quotients_f16(x.astype(np.float32), bits, gs)
+        assert (top > 2 ** bits - 0.5).any(), "no group reaches the saturating codes"
+    x = np.broadcast_to(x, (2, 3) + x.shape).copy()          # [B, H, L, D]
+    pk = qkv.qkv_quantize(to_dev(x, dtype), mode, bits, gs)
+    assert_pack_equal(pack_numpy(pk), oracle_pack(x, dtype, mode, bits, gs))
