@@ -11,9 +11,9 @@
 //
 //  * One workgroup (8 waves) per (key split, batch x kv head) streams its
 //    chunk of packed K/V exactly once; the G query heads of the kv head are
-//    the 16 rows of the matrix tiles (rows >= G are zero), read once per
-//    workgroup (one 16-byte load per thread) and shared through LDS.  Each
-//    wave takes every 8th tile of 32 keys.
+//    the 16 rows of the matrix tiles (rows >= G are zero); each wave reads
+//    the query values of its lanes itself, so no wave waits for another
+//    before its first tile.  Each wave takes every 8th tile of 32 keys.
 //  * A wave's K tile goes straight into LDS (buffer_load ... lds) with loads
 //    that read whole key rows, into rows whose 16-byte chunks are
 //    XOR-swizzled so that the 16 rows of one fragment read start on distinct
@@ -238,8 +238,6 @@ __global__ __launch_bounds__(NTHR) void attn_matrix_decode(AttnLaunch p) {
     constexpr int WAVE_FLOATS = 64 * (D / 4) > KSTAGE + TK * ROWB / 4 ? 64 * (D / 4) : KSTAGE + TK * ROWB / 4;
     static_assert(NCH >= 2 && NCH <= 16 && TK % KPI == 0, "K stage layout");
     __shared__ __attribute__((aligned(16))) float s_wave[NWAVE][WAVE_FLOATS];
-    __shared__ __attribute__((aligned(16))) uint16_t s_q[16 * D];   // the 16 query rows (rows >= G zero)
-    __shared__ float s_qsum[16][NG];
     __shared__ float s_ml[NWAVE][2][16];
     __shared__ float s_bias[NWAVE][16][2];
 
@@ -297,13 +295,17 @@ __global__ __launch_bounds__(NTHR) void attn_matrix_decode(AttnLaunch p) {
     // cooperatively (lane l: key l % 32) and lanes fetch the rows they need
     // with cross-lane shuffles.
     constexpr bool COOP = FOLD;
+    // 16-bit loads stay 16-bit here: widened at their use, after the wait
+    // for the tile (a widening of the first tile's values would otherwise be
+    // placed before the loop and wait for every load of the tile).
+    typedef typename std::conditional<NG == 1, uint16_t, uint32_t>::type srow_t;
     struct Tile {
         uint32_t ks[2][NSW];          // key scales (fp16)
         uint32_t kbias[2][NSW];
         uint32_t vw[8][VW];           // P V codes: keys 8 kb + e
-        uint32_t vs[8];               // value scale / bias of key 8 kb + e (dequantized form)
-        uint32_t vb[8];
-        uint32_t ksr, kbr, vsr, vbr;  // cooperative scale / bias rows (folded form)
+        uint16_t vs[8];               // value scale / bias of key 8 kb + e (dequantized form)
+        uint16_t vb[8];
+        srow_t ksr, kbr, vsr, vbr;    // cooperative scale / bias rows (folded form)
     };
     // K stage: chunk position of chunk c in row r is c ^ kswz(r); the shift
     // makes the 16 rows that one LDS read spans start on distinct banks
@@ -351,8 +353,8 @@ __global__ __launch_bounds__(NTHR) void attn_matrix_decode(AttnLaunch p) {
     auto ld32 = [](__amdgpu_buffer_rsrc_t r, uint32_t off) -> uint32_t {
         return __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0);
     };
-    auto ld16 = [](__amdgpu_buffer_rsrc_t r, uint32_t off) -> uint32_t {
-        return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, 0);
+    auto ld16 = [](__amdgpu_buffer_rsrc_t r, uint32_t off) -> uint16_t {
+        return __builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, 0);
     };
     auto ldn = [&](__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t* dst, int nw) {
         if (nw == 1) {
@@ -380,14 +382,14 @@ __global__ __launch_bounds__(NTHR) void attn_matrix_decode(AttnLaunch p) {
         for (int i = 0; i < NKI; ++i)
             mf::buf_to_lds16(rk, kstage + 1024 * i, o_kl[i]);
         if constexpr (COOP) {
-            T.ksr = (NG == 1) ? ld16(rsrc(ksc, row0, kss, F::SROWB), o_kr)
-                              : ld32(rsrc(ksc, row0, kss, F::SROWB), o_kr);
-            T.kbr = (NG == 1) ? ld16(rsrc(kbi, row0, kss, F::SROWB), o_kr)
-                              : ld32(rsrc(kbi, row0, kss, F::SROWB), o_kr);
-            T.vsr = (NG == 1) ? ld16(rsrc(vsc, row0, vss, F::SROWB), o_vr)
-                              : ld32(rsrc(vsc, row0, vss, F::SROWB), o_vr);
-            T.vbr = (NG == 1) ? ld16(rsrc(vbi, row0, vss, F::SROWB), o_vr)
-                              : ld32(rsrc(vbi, row0, vss, F::SROWB), o_vr);
+            auto ldrow = [&](__amdgpu_buffer_rsrc_t r, uint32_t off) -> srow_t {
+                if constexpr (NG == 1) return ld16(r, off);
+                else return ld32(r, off);
+            };
+            T.ksr = ldrow(rsrc(ksc, row0, kss, F::SROWB), o_kr);
+            T.kbr = ldrow(rsrc(kbi, row0, kss, F::SROWB), o_kr);
+            T.vsr = ldrow(rsrc(vsc, row0, vss, F::SROWB), o_vr);
+            T.vbr = ldrow(rsrc(vbi, row0, vss, F::SROWB), o_vr);
         } else {
             const auto rks = rsrc(ksc, row0, kss, F::SROWB);
             load_scales(rks, o_ks0, T.ks[0]);
@@ -415,42 +417,47 @@ __global__ __launch_bounds__(NTHR) void attn_matrix_decode(AttnLaunch p) {
         }
     };
 
-    // the workgroup's G query rows are read once (wave w: bytes 1024 w ..
-    // 1024 w + 1023 of the 16 x D block, zeros past row G), then the first
-    // tiles are requested before anything waits
-    constexpr int QB = 16 * D * 2;
+    // Each wave reads the query values its lanes need (row n, the 8
+    // consecutive d of every K-step; mostly cache hits, since every wave and
+    // workgroup of the kv head reads the same 16 x D block) before it requests
+    // its first tile, and nothing in the prologue waits on another wave: a
+    // wave starts on its tile as soon as that tile has arrived.  Rows past G
+    // read as zeros (the buffer's size stops at row G).
     const auto rq = flat_rsrc((const uint16_t*)p.q + (b * p.Hq + kvh * G) * D, (uint32_t)(G * D * 2));
-    u4 qv = {0u, 0u, 0u, 0u};
-    if (1024 * wave < QB) {
-        const uint32_t off = 1024 * wave + 16 * lane;
-        if ((reinterpret_cast<uintptr_t>(p.q) & 15) == 0) {   // q only needs 2-byte alignment
-            qv = __builtin_amdgcn_raw_buffer_load_b128(rq, (int)off, 0, 0);
-        } else {
+    const bool q_al16 = (reinterpret_cast<uintptr_t>(p.q) & 15) == 0;   // q only needs 2-byte alignment
+    u4 qraw[STEPS];
+    auto q_off = [&](int st) {
+        const int g = st / F::SPG, u = st % F::SPG;
+        return 2u * (uint32_t)(n * D + g * GS + kb * (GS / 4) + 8 * u);
+    };
+    if (q_al16) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                qv[i] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rq, (int)(off + 4 * i), 0, 0) |
-                        ((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rq, (int)(off + 4 * i + 2), 0, 0) << 16);
-        }
+        for (int st = 0; st < STEPS; ++st)
+            qraw[st] = __builtin_amdgcn_raw_buffer_load_b128(rq, (int)q_off(st), 0, 0);
+    } else {
+#pragma unroll
+        for (int st = 0; st < STEPS; ++st)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const uint32_t h = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rq, (int)(q_off(st) + 2 * i), 0, 0);
+                qraw[st][i >> 1] = (i & 1) ? (qraw[st][i >> 1] | (h << 16)) : h;
+            }
     }
-    // keep the query load ahead of the tile loads (waiting for q must not
+    // keep the query loads ahead of the tile loads (waiting for q must not
     // wait for the tile)
     __builtin_amdgcn_sched_barrier(0);
     const int my_tiles = wave < ntiles ? (ntiles - wave + NWAVE - 1) / NWAVE : 0;
     Tile cur;
     load_tile(wave, cur);
     __builtin_amdgcn_sched_barrier(0);
-    if (1024 * wave < QB) *(u4*)((uint8_t*)s_q + 1024 * wave + 16 * lane) = qv;
-    __syncthreads();
-    uint4 qraw[STEPS];
-#pragma unroll
-    for (int st = 0; st < STEPS; ++st) {
-        const int g = st / F::SPG, u = st % F::SPG;
-        qraw[st] = *(const uint4*)(s_q + n * D + g * GS + kb * (GS / 4) + 8 * u);   // 8 consecutive halves
-    }
 
     // ---------------------------------------------------------------- queries
-    // A operand of q K^T for every K-step, and per-(head, group) sums of q.
+    // A operand of q K^T for every K-step; in the folded form also the
+    // per-(head, group) sums of q of the lane's output rows 4 kb + j, taken
+    // with lane reads (no LDS access: an LDS access here would wait for the
+    // tile's direct-to-LDS loads).
     h8 qa[STEPS];
+    float qs[4][NG];                    // (scale log2e) sum q of output rows 4kb + j
     {
         float part[NG];
 #pragma unroll
@@ -458,8 +465,8 @@ __global__ __launch_bounds__(NTHR) void attn_matrix_decode(AttnLaunch p) {
 #pragma unroll
         for (int st = 0; st < STEPS; ++st) {
             const int g = st / F::SPG;
-            const uint4 raw = qraw[st];
-            const uint32_t hw[4] = {raw.x, raw.y, raw.z, raw.w};
+            const u4 raw = qraw[st];
+            const uint32_t hw[4] = {raw[0], raw[1], raw[2], raw[3]};
             _Float16 hv[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e)
@@ -468,28 +475,33 @@ __global__ __launch_bounds__(NTHR) void attn_matrix_decode(AttnLaunch p) {
 #pragma unroll
             for (int hh = 0; hh < 4; ++hh) {
                 _Float16 v0 = hv[qpos<BITS>(2 * hh)], v1 = hv[qpos<BITS>(2 * hh + 1)];
-                part[g] += (float)v0 + (float)v1;
+                if constexpr (FOLD) part[g] += (float)v0 + (float)v1;
                 if constexpr (BITS == 4 && FOLD) {   // raw odd nibbles arrive as 16 c
                     if (hh & 1) { v0 = v0 * (_Float16)0.0625f; v1 = v1 * (_Float16)0.0625f; }
                 }
-                w[hh] = n < G ? ((uint32_t)__builtin_bit_cast(uint16_t, v0) |
-                                 ((uint32_t)__builtin_bit_cast(uint16_t, v1) << 16))
-                              : 0u;
+                w[hh] = (uint32_t)__builtin_bit_cast(uint16_t, v0) |
+                        ((uint32_t)__builtin_bit_cast(uint16_t, v1) << 16);
             }
             qa[st] = to_h8(w[0], w[1], w[2], w[3]);
         }
 #pragma unroll
         for (int g = 0; g < NG; ++g) {
-            const float s = sum4(part[g]);
-            if (wave == 0 && kb == 0) s_qsum[n][g] = n < G ? s * sl : 0.0f;
+            if constexpr (FOLD) {
+                const float s = sum4(part[g]) * sl;          // head n's group sum, in lanes n + 16 kb
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, s), j));
+                    const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, s), 4 + j));
+                    const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, s), 8 + j));
+                    const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, s), 12 + j));
+                    qs[j][g] = kb == 0 ? r0 : kb == 1 ? r1 : kb == 2 ? r2 : r3;
+                }
+            } else {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) qs[j][g] = 0.0f;
+            }
         }
     }
-    __syncthreads();
-    float qs[4][NG];                    // (scale log2e) sum q of output rows 4kb + j
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int g = 0; g < NG; ++g) qs[j][g] = s_qsum[4 * kb + j][g];
 
     // ---------------------------------------------------------------- main loop
     f4 acc_o[NT];
