@@ -625,10 +625,12 @@ __global__ __launch_bounds__(NTHR) void attn_matrix_decode(AttnLaunch p) {
         }
         float pf[8];
         float ps = 0.0f;
-        const bool live = m_run != -INFINITY;
+        // while the head has seen no visible key (m_run = -inf) all its scores
+        // are -inf, and 2^(-inf - 0) = 0: one select per lane, not per score
+        const float m_sub = m_run == -INFINITY ? 0.0f : m_run;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            pf[e] = live ? fast_exp2(zz[e] - m_run) : 0.0f;
+            pf[e] = fast_exp2(zz[e] - m_sub);
             ps += pf[e];
         }
         l_run += ps;

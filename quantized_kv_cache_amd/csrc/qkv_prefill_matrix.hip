@@ -372,7 +372,9 @@ __global__ __launch_bounds__(PNTHR) void attn_matrix_prefill(AttnLaunch p) {
             for (int t2 = 0; t2 < NT; ++t2) acc[t2] *= alpha;
             m_run = m_new;
         }
-        const bool live = m_run != -INFINITY;
+        // while the row has seen no visible key (m_run = -inf) all its scores
+        // are -inf, and 2^(-inf - 0) = 0: one select per lane, not per score
+        const float m_sub = m_run == -INFINITY ? 0.0f : m_run;
         uint32_t pp[NSUB][2];     // P^T operand halves: keys (16u + 4kb + jj) in pairs
         float ps = 0.0f;
 #pragma unroll
@@ -380,7 +382,7 @@ __global__ __launch_bounds__(PNTHR) void attn_matrix_prefill(AttnLaunch p) {
             float e[4];
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) {
-                e[jj] = live ? fast_exp2(sc[u][jj] - m_run) : 0.0f;
+                e[jj] = fast_exp2(sc[u][jj] - m_sub);
                 ps += e[jj];
             }
             h2 a = {(_Float16)e[0], (_Float16)e[1]}, c = {(_Float16)e[2], (_Float16)e[3]};
