@@ -358,6 +358,9 @@ Plan make_plan(int64_t B, int64_t Hq, int64_t Lq, int64_t D, int64_t L, const qk
             : pl.stream ? auto_splits(B * Hk, L, qkv::stream_decode_key_quantum(), 1024)
                         : auto_splits(B * Hk * pl.n_rt, L, 32, 1024);
     }
+    // the narrow decode's in-kernel merge keeps one ticket per (batch, kv
+    // head) in the fixed header: a batch beyond it runs unsplit
+    if (pl.narrow && B * Hk > (int64_t)qkv::kTicketWords) S = 1;
     int64_t chunk = (L + S - 1) / S;
     const int64_t gran = pl.stream ? qkv::stream_decode_key_quantum()
                          : !pl.matrix ? 32

@@ -182,6 +182,28 @@ def test_plan_kernel_choice(L, shape, kernel):
         assert pl.row_tile == (128 if (Hq // Hk) * Lq >= 256 else 64)
 
 
+def test_plan_narrow_decode_tickets_fit_header(L):
+    """The narrow decode merges its key splits in the kernel with one ticket
+    per (batch, kv head) in the fixed ticket header: a call with more (batch,
+    kv head) pairs than the header holds runs unsplit, even when splits are
+    asked for."""
+    words = _lib.QKV_TICKET_BYTES // 4
+    for B, splits in ((words // 4, 8), (words // 4 + 1, 8), (words // 4 + 1, 0)):
+        Hk, Hq, Lk, D = 4, 16, 4096, 128
+        kp = _lib.QkvPack(mode=_lib.QKV_AFFINE, bits=4, group_size=64, scale_dtype=_lib.QKV_F16,
+                          B=B, H=Hk, L_cap=Lk, D=D, codes=FAKE, scales=FAKE + 0x10000000,
+                          biases=FAKE + 0x20000000, stride_b=Hk * Lk, stride_h=Lk, stride_l=1)
+        opts = _lib.QkvAttnOpts(num_splits=splits)
+        pl = _lib.QkvAttnPlan()
+        assert L.qsdpa_plan(B, Hq, 1, D, Lk, ctypes.byref(kp), _lib.QKV_F16, ctypes.byref(opts),
+                            ctypes.byref(pl)) == 0
+        assert pl.kernel == _lib.QKV_KERNEL_DECODE_NARROW
+        if B * Hk > words:
+            assert pl.num_splits == 1
+        else:
+            assert pl.num_splits == splits
+
+
 @pytest.mark.parametrize("Lq,rows", [(15, 64), (16, 128), (100, 128)])
 def test_prefill_row_tile(L, Lq, rows):
     """Prefill row tiles: 64 rows below 256 GQA-packed rows per (batch, kv
