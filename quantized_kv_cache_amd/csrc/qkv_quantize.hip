@@ -141,6 +141,13 @@ __device__ __forceinline__ void store_scale_buf(__amdgpu_buffer_rsrc_t r, uint32
     else if constexpr (DT == DT_F16) __builtin_amdgcn_raw_buffer_store_b16(f32_to_f16(v), r, (int)off, 0, 0);
     else __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(v), r, (int)off, 0, 0);
 }
+// The same value written to LDS at byte offset off of a staging block.
+template <int DT>
+__device__ __forceinline__ void stage_scale(uint8_t* blk, uint32_t off, float v) {
+    if constexpr (DT == DT_F32) *(uint32_t*)(blk + off) = __float_as_uint(v);
+    else if constexpr (DT == DT_F16) *(uint16_t*)(blk + off) = f32_to_f16(v);
+    else *(uint16_t*)(blk + off) = f32_to_bf16(v);
+}
 
 // DT: source (and, for affine, scale) dtype.  MODE: affine / Q8_0 / dense.
 // Every address is a wave-uniform base (scalar, 64-bit) plus a lane offset
@@ -177,13 +184,28 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(QuantLaunch p) {
     const uint32_t o_s = (uint32_t)lrow * sstride + (uint32_t)(lr / LPG) * SS;
     const bool leader = lr % LPG == 0;
     // first row of each pass of this wave, relative to the (batch, head)
-    const int64_t tw = (int64_t)blockIdx.x * RPB + wave * RPW * U;
+    const int64_t t0 = (int64_t)blockIdx.x * RPB;
+    const int64_t tw = t0 + wave * RPW * U;
     const uint32_t H = (uint32_t)p.H;
+    // Scale (and bias) rows of the workgroup's RPB pack rows, gathered: when
+    // the rows are consecutive (row stride 1), all inside [0, T) and their
+    // scale block is 16-byte aligned, the group leaders put their values into
+    // an LDS copy of the block, which whole 16-byte non-temporal stores then
+    // write: full lines reach memory and none stay dirty in the L2s for the
+    // end of the kernel.  Otherwise each leader stores its own value.
+    constexpr int SBLK = RPB * SROWB;           // bytes of the block's scales
+    constexpr bool CAN_GATHER = MODE != MODE_DENSE && SBLK > 0 && SBLK % 16 == 0 && SBLK / 16 <= 128;
+    __shared__ __attribute__((aligned(16))) uint8_t s_blk[2][CAN_GATHER ? SBLK : 16];
+    const uint32_t o_blk = (uint32_t)(wave * RPW * U + lrow) * SROWB + (uint32_t)(lr / LPG) * SS;
     for (uint32_t bh = blockIdx.y; bh < (uint32_t)p.BH; bh += gridDim.y) {
         const uint32_t b = bh / H;
         const uint32_t h = bh - b * H;
         const int64_t xrow0 = (int64_t)b * job.xs0 + (int64_t)h * job.xs1;    // elements
         const int64_t prow0 = (int64_t)b * job.sb + (int64_t)h * job.sh + p.offset;   // pack rows
+        uint8_t* sblk = (uint8_t*)job.scales + (prow0 + t0) * SROWB;
+        uint8_t* bblk = MODE == MODE_AFFINE ? (uint8_t*)job.biases + (prow0 + t0) * SROWB : sblk;
+        const bool gather = CAN_GATHER && job.sl == 1 && t0 + RPB <= p.T &&
+                            ((reinterpret_cast<uintptr_t>(sblk) | reinterpret_cast<uintptr_t>(bblk)) & 15) == 0;
         __amdgpu_buffer_rsrc_t rc[U], rs[U], rb[U];
         uint4 raw[U];
         float v[U][8];
@@ -257,8 +279,13 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(QuantLaunch p) {
                     __builtin_amdgcn_raw_buffer_store_b64(w, rc[u], (int)o_c, 0, kStream);
                 }
                 if (leader) {
-                    store_scale_buf<DT>(rs[u], o_s, s32);
-                    store_scale_buf<DT>(rb[u], o_s, mn);
+                    if (gather) {
+                        stage_scale<DT>(s_blk[0], o_blk + u * RPW * SROWB, s32);
+                        stage_scale<DT>(s_blk[1], o_blk + u * RPW * SROWB, mn);
+                    } else {
+                        store_scale_buf<DT>(rs[u], o_s, s32);
+                        store_scale_buf<DT>(rb[u], o_s, mn);
+                    }
                 }
             } else {
                 float amax = 0.0f;
@@ -281,7 +308,25 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(QuantLaunch p) {
                               ((uint32_t)c[4] & 0xffu) | (((uint32_t)c[5] & 0xffu) << 8) |
                                   (((uint32_t)c[6] & 0xffu) << 16) | ((uint32_t)c[7] << 24)};
                 __builtin_amdgcn_raw_buffer_store_b64(w, rc[u], (int)o_c, 0, kStream);
-                if (leader) __builtin_amdgcn_raw_buffer_store_b16(dh, rs[u], (int)o_s, 0, 0);
+                if (leader) {
+                    if (gather) *(uint16_t*)(s_blk[0] + o_blk + u * RPW * SROWB) = dh;
+                    else __builtin_amdgcn_raw_buffer_store_b16(dh, rs[u], (int)o_s, 0, 0);
+                }
+            }
+        }
+        if constexpr (CAN_GATHER) {
+            if (gather) {                      // uniform over the workgroup
+                __syncthreads();
+                constexpr int NB = MODE == MODE_AFFINE ? 2 : 1;
+                if ((int)threadIdx.x < NB * SBLK / 16) {
+                    const int k = (int)threadIdx.x / (SBLK / 16);
+                    const uint32_t off = 16u * ((uint32_t)threadIdx.x % (SBLK / 16));
+                    const uint4 x = *(const uint4*)(s_blk[k] + off);
+                    const u4 w = {x.x, x.y, x.z, x.w};
+                    __builtin_amdgcn_raw_buffer_store_b128(w, pass_rsrc(k ? bblk : sblk, 1, 0, SBLK), (int)off, 0,
+                                                           kStream);
+                }
+                __syncthreads();               // the block is read before the next (batch, head) fills it
             }
         }
     }
