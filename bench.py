@@ -131,6 +131,9 @@ def parse():
     ap.add_argument("--op", default="attention", choices=["attention", "quantize"],
                     help="'quantize' times qkv_quantize of the workload's K and V caches "
                          "(alternating) instead of the attention step")
+    ap.add_argument("--separate-append", action="store_true",
+                    help="append workload: qkv_update_append and qsdpa_decode as two calls per step "
+                         "instead of qsdpa_decode_append")
     ap.add_argument("--read-sweep", action="store_true",
                     help="instead: the plain streaming read of the workload's K/V bytes over a "
                          "grid of load shapes (workgroups, threads, loads in flight, width)")
@@ -426,19 +429,29 @@ def main():
         vn = [W.to_tensor(s["v_new"], w.dtype) for s in per_step]
         qs = [W.to_tensor(s["q"], w.dtype) for s in per_step]
         out = torch.empty_like(qs[0])
-        appends = [[qkv.PreparedAppend(ks[c], vs[c], kn[t], vn[t]) for t in range(w.steps)]
-                   for c in range(R)]
-        calls = [[qkv.PreparedAttention(qs[t], ks[c], vs[c], w.L + t + 1, w.scale, out,
-                                        num_splits=args.splits, algo=args.algo, workspace=ws)
-                  for t in range(w.steps)] for c in range(R)]
+        if args.separate_append:
+            # qkv_update_append, then qsdpa_decode: two launches per step
+            appends = [[qkv.PreparedAppend(ks[c], vs[c], kn[t], vn[t]) for t in range(w.steps)]
+                       for c in range(R)]
+            calls = [[qkv.PreparedAttention(qs[t], ks[c], vs[c], w.L + t + 1, w.scale, out,
+                                            num_splits=args.splits, algo=args.algo, workspace=ws)
+                      for t in range(w.steps)] for c in range(R)]
+
+            def run(i):
+                t = i % w.steps
+                appends[i % R][t](w.L + t)
+                calls[i % R][t]()
+        else:
+            # qsdpa_decode_append: the append and the decode in one call
+            calls = [[qkv.PreparedDecodeAppend(qs[t], ks[c], vs[c], kn[t], vn[t], w.L + t, w.scale, out,
+                                               num_splits=args.splits, algo=args.algo, workspace=ws)
+                      for t in range(w.steps)] for c in range(R)]
+
+            def run(i):
+                calls[i % R][i % w.steps]()
 
         def attn_of(i):
             return calls[i % R][i % w.steps]
-
-        def run(i):
-            t = i % w.steps
-            appends[i % R][t](w.L + t)
-            calls[i % R][t]()
         L_mean = w.L + (w.steps + 1) / 2.0
         step_bytes = pack_bytes(w, L_mean) + 2 * q_bytes(w) + append_bytes(w)
         plan_L = w.L + w.steps
@@ -467,7 +480,8 @@ def main():
     if kernel == "attn_decode_narrow" or plan["num_splits"] == 1:
         # the attention call is one kernel launch: its mean duration is the time of a
         # back-to-back pass of the calls alone (for the append workload: the same
-        # calls, on the caches the timed pass left, without the appends)
+        # calls, on the caches the timed pass left; the one-call form rewrites the
+        # step's row with the same bits)
         kms = time_region(torch, lambda i: attn_of(i)(), args.warmup + args.steps, args.steps, stream)
     else:
         kms = kernel_pass(torch, run, attn_of, args.warmup + args.steps, args.steps, stream)
@@ -492,11 +506,15 @@ def main():
                    "cache_dtype": w.dtype, "cache_copies": R, "algo": args.algo,
                    "kernel": kernel, "num_splits": plan["num_splits"]},
     }
+    if w.steps:
+        rec["config"]["append"] = "separate launch" if args.separate_append else "in the decode call"
     traffic = stored_traffic(kernel, w.name)
     if w.Lq == 1:
         # per launch: the K/V pack bytes of the attended keys, q, and out when unsplit
         kb = pack_bytes(w, w.L if not w.steps else L_mean) + q_bytes(w) * (
             1 if plan["num_splits"] > 1 else 2)
+        if w.steps and not args.separate_append:
+            kb += append_bytes(w)          # the kernel also reads the new tokens and writes their rows
         ach = kb / (kms * 1e-3) / 1e9
         rec["roofline"] = {"bound": "hbm", "achieved": round(ach, 2), "peak": HBM_PEAK_GBS,
                            "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),

@@ -87,7 +87,7 @@
 extern "C" {
 #endif
 
-#define QKV_ABI_VERSION 5
+#define QKV_ABI_VERSION 6
 
 typedef enum {
     QKV_OK = 0,
@@ -262,6 +262,29 @@ qkv_status qsdpa_decode(const void* q, int32_t q_dtype, int64_t B, int64_t Hq, i
                         const void* mask, int32_t mask_dtype, const int64_t mask_strides[4],
                         void* out, void* workspace, size_t workspace_bytes,
                         const qkv_attn_opts* opts, void* stream);
+
+/* Decode with append: qkv_update_append of one new token per (batch, kv
+ * head) at row 'offset' (k_new, v_new [B,Hk,1,D] in q_dtype, element strides
+ * new_strides = {b, h, t}), then qsdpa_decode over keys [0, offset + 1) --
+ * one step of a decoding loop over a quantized cache: the MLX page "add
+ * fast::quantized_kv_update" appends the step's keys and values with
+ * fast::quantized_kv_update (kv_update) and then attends the updated cache
+ * with quantized_scaled_dot_product_attention.  The cache rows written are
+ * the bits qkv_update_append writes, and out is what qsdpa_decode returns on
+ * the updated packs with the same options.  On the narrow matrix-core decode
+ * (fp16 queries, GQA factor <= 4, affine or Q8_0 codes, no mask) it is one
+ * launch: the wave that loads the tile holding row 'offset' quantizes the two
+ * new rows first; otherwise the append kernel runs before the decode.
+ * Arguments and errors as qkv_update_append (T = 1, dtype = q_dtype) and
+ * qsdpa_decode (L = offset + 1); size the workspace with qsdpa_plan or
+ * qsdpa_workspace_bytes for L = offset + 1.  timing_events in opts bracket
+ * the attention kernel (the fused one, or the decode after the append). */
+qkv_status qsdpa_decode_append(const void* q, int32_t q_dtype, int64_t B, int64_t Hq, int64_t D,
+                               const void* k_new, const void* v_new, const int64_t new_strides[3],
+                               int64_t offset, const qkv_pack* k_cache, const qkv_pack* v_cache,
+                               float scale, const void* mask, int32_t mask_dtype,
+                               const int64_t mask_strides[4], void* out, void* workspace,
+                               size_t workspace_bytes, const qkv_attn_opts* opts, void* stream);
 
 /* qsdpa_decode for callers that cannot allocate (code under HIP graph
  * capture, serving loops that forbid hipMalloc): the same computation and

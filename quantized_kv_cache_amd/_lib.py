@@ -20,7 +20,8 @@ QKV_KERNEL_DECODE_STREAM = 5
 
 # every symbol include/qkv.h declares
 EXPORTS = ["qkv_quantize", "qkv_update_append", "qkv_dequantize", "qsdpa_workspace_bytes", "qsdpa_workspace_reset",
-           "qsdpa_plan", "qsdpa_decode", "qsdpa_decode_static", "qsdpa_prefill", "qkv_last_error",
+           "qsdpa_plan", "qsdpa_decode", "qsdpa_decode_static", "qsdpa_decode_append", "qsdpa_prefill",
+           "qkv_last_error",
            "qkv_abi_version", "qkv_measure_read", "qkv_measure_read_config"]
 QKV_TICKET_BYTES = 262144
 QKV_STATIC_SCRATCH_BYTES = QKV_TICKET_BYTES + 16 * 1024 * 1024
@@ -88,6 +89,9 @@ def load():
     L.qsdpa_decode_static.argtypes = [P, I32, I64, I64, I64, PK, PK, I64, ctypes.c_float, P, I32,
                                       I64P, P, OP, P]
     L.qsdpa_decode_static.restype = I32
+    L.qsdpa_decode_append.argtypes = [P, I32, I64, I64, I64, P, P, I64P, I64, PK, PK, ctypes.c_float, P, I32,
+                                      I64P, P, P, SZ, OP, P]
+    L.qsdpa_decode_append.restype = I32
     L.qsdpa_prefill.argtypes = [P, I32, I64, I64, I64, I64, PK, PK, I64, ctypes.c_float, I32, P,
                                 I32, I64P, P, P, SZ, OP, P]
     L.qsdpa_prefill.restype = I32

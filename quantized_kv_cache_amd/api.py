@@ -289,6 +289,34 @@ def qsdpa_decode(q: torch.Tensor, k: Pack, v: Pack, L: int, scale: float,
     return out
 
 
+def qsdpa_decode_append(q: torch.Tensor, k: Pack, v: Pack, k_new: torch.Tensor, v_new: torch.Tensor,
+                        offset: int, scale: float, mask: torch.Tensor | None = None,
+                        num_splits: int = 0, algo: str = "auto", out: torch.Tensor | None = None,
+                        workspace: Workspace | None = None) -> torch.Tensor:
+    """One decoding step: k_new/v_new [B,Hk,1,D] (q's dtype) quantized into
+    row ``offset`` of the packs, then softmax(scale q K^T + mask) V over keys
+    [0, offset + 1) -- qkv_update_append followed by qsdpa_decode, as one
+    launch where the narrow decode kernel takes the call."""
+    B, Hq, Lq, D = q.shape
+    if Lq != 1:
+        raise ValueError("decode takes one query per head")
+    if k_new.shape != v_new.shape or k_new.stride() != v_new.stride() or k_new.dtype != v_new.dtype:
+        raise ValueError("k_new and v_new must share shape, strides and dtype")
+    if k_new.shape[2] != 1:
+        raise ValueError("a decode step appends one token per (batch, kv head)")
+    L = offset + 1
+    out = torch.empty_like(q) if out is None else out
+    buf, nbytes = _attn_common(q, k, v, num_splits, algo, workspace, L)
+    mp, mdt, ms = _mask_args(mask, (B, Hq, 1, L))
+    st = _lib.load().qsdpa_decode_append(_ptr(q), _dt(q), B, Hq, D, _ptr(k_new), _ptr(v_new),
+                                         _src_strides(k_new), offset, ctypes.byref(k.c_struct()),
+                                         ctypes.byref(v.c_struct()), float(scale), mp, mdt, ms,
+                                         _ptr(out), _ptr(buf), nbytes,
+                                         ctypes.byref(_opts(num_splits, algo)), _stream(q.device))
+    _lib.check(st)
+    return out
+
+
 def qsdpa_decode_static(q: torch.Tensor, k: Pack, v: Pack, L: int, scale: float,
                         mask: torch.Tensor | None = None, num_splits: int = 0,
                         algo: str = "auto", out: torch.Tensor | None = None) -> torch.Tensor:
@@ -407,6 +435,45 @@ class PreparedAttention:
         """Have later calls record `begin` / `end` (timing-enabled events that
         have been recorded once, so that their HIP handles exist) around the
         attention kernel alone; None stops it."""
+        if begin is None or end is None:
+            self._opts.timing_events[0] = self._opts.timing_events[1] = None
+            return
+        self._opts.timing_events[0] = begin.cuda_event
+        self._opts.timing_events[1] = end.cuda_event
+
+    def __call__(self) -> torch.Tensor:
+        st = self._fn(*self._args)
+        if st:
+            _lib.check(st)
+        return self.out
+
+
+class PreparedDecodeAppend:
+    """A qsdpa_decode_append call (no mask) with its arguments marshalled
+    once: calling it appends the same k_new/v_new at the same offset and
+    attends keys [0, offset + 1).  The tensors must stay alive."""
+
+    def __init__(self, q: torch.Tensor, k: Pack, v: Pack, k_new: torch.Tensor, v_new: torch.Tensor,
+                 offset: int, scale: float, out: torch.Tensor, num_splits: int = 0, algo: str = "auto",
+                 workspace: Workspace | None = None):
+        B, Hq, Lq, D = q.shape
+        if Lq != 1 or not q.is_contiguous() or out.shape != q.shape or not out.is_contiguous():
+            raise ValueError("decode with append takes contiguous q, out of one shape [B,Hq,1,D]")
+        if k_new.shape != v_new.shape or k_new.stride() != v_new.stride() or k_new.dtype != v_new.dtype:
+            raise ValueError("k_new and v_new must share shape, strides and dtype")
+        buf, nbytes = _attn_common(q, k, v, num_splits, algo, workspace, offset + 1)
+        self._keep = (q, k, v, k_new, v_new, out, buf)
+        self._kc, self._vc = k.c_struct(), v.c_struct()
+        self._opts = _opts(num_splits, algo)
+        self._strides = _src_strides(k_new)
+        self._fn = _lib.load().qsdpa_decode_append
+        self._args = (_ptr(q), _dt(q), B, Hq, D, _ptr(k_new), _ptr(v_new), self._strides, offset,
+                      ctypes.byref(self._kc), ctypes.byref(self._vc), float(scale), None, 0, None,
+                      _ptr(out), _ptr(buf), nbytes, ctypes.byref(self._opts), _stream(q.device))
+        self.out = out
+
+    def set_timing(self, begin: torch.cuda.Event | None, end: torch.cuda.Event | None) -> None:
+        """As PreparedAttention.set_timing: events around the attention kernel."""
         if begin is None or end is None:
             self._opts.timing_events[0] = self._opts.timing_events[1] = None
             return

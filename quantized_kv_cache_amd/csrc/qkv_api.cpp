@@ -183,6 +183,48 @@ qkv_status check_row_strides(const int64_t xs[3], int32_t dtype, const qkv_pack*
     return QKV_OK;
 }
 
+// One append of T new K/V tokens at row offset (qkv_update_append's checks).
+qkv_status check_append(const char* name, const void* k_new, const void* v_new, int32_t dtype,
+                        const int64_t new_strides[3], int64_t T, int64_t offset, const qkv_pack* k_cache,
+                        const qkv_pack* v_cache) {
+    qkv_status st;
+    if ((st = check_pack(k_cache, name)) != QKV_OK) return st;
+    if ((st = check_pack(v_cache, name)) != QKV_OK) return st;
+    if (!same_format(k_cache, v_cache)) return fail(QKV_EINVAL, "%s: K and V packs differ in format or shape", name);
+    if ((st = check_source(k_new, dtype, new_strides, k_cache, name)) != QKV_OK) return st;
+    if ((st = check_source(v_new, dtype, new_strides, v_cache, name)) != QKV_OK) return st;
+    if (T < 1) return fail(QKV_EINVAL, "%s: T must be >= 1", name);
+    if (offset < 0 || offset + T > k_cache->L_cap || offset + T > v_cache->L_cap)
+        return fail(QKV_EINVAL, "%s: rows [%lld, %lld) exceed the capacity", name, (long long)offset,
+                    (long long)(offset + T));
+    if (overlap(codes_range(k_cache), codes_range(v_cache)))
+        return fail(QKV_EINVAL, "%s: K and V codes overlap", name);
+    if ((st = check_row_strides(new_strides, dtype, k_cache, name)) != QKV_OK) return st;
+    if ((st = check_row_strides(new_strides, dtype, v_cache, name)) != QKV_OK) return st;
+    return QKV_OK;
+}
+
+qkv::QuantLaunch append_launch(const void* k_new, const void* v_new, const int64_t new_strides[3], int64_t T,
+                               int64_t offset, const qkv_pack* k_cache, const qkv_pack* v_cache) {
+    qkv::QuantLaunch p{};
+    p.job[0] = make_job(k_new, new_strides, k_cache);
+    p.job[1] = make_job(v_new, new_strides, v_cache);
+    p.H = k_cache->H;
+    p.T = T;
+    p.offset = offset;
+    p.BH = k_cache->B * k_cache->H;
+    p.rows = p.BH * T;
+    return p;
+}
+
+// The new token of a decode with append (one row per (batch, kv head), in the
+// query dtype, written at row L - 1 before the decode attends rows [0, L)).
+struct AppendArgs {
+    const void* k_new;
+    const void* v_new;
+    const int64_t* strides;
+};
+
 // ---------------------------------------------------------------- attention plans
 struct Plan {
     bool unfused;                   // the four-kernel composition (QKV_ALGO_UNFUSED)
@@ -379,7 +421,8 @@ qkv_status attention(const char* name, const void* q, int32_t q_dtype, int64_t B
                      int64_t Lq, int64_t D, const qkv_pack* k, const qkv_pack* v, int64_t L,
                      float scale, int32_t mask_kind, const void* mask, int32_t mask_dtype,
                      const int64_t ms[4], void* out, void* workspace, size_t workspace_bytes,
-                     const qkv_attn_opts* opts, void* stream, bool static_ws = false) {
+                     const qkv_attn_opts* opts, void* stream, bool static_ws = false,
+                     const AppendArgs* app = nullptr) {
     qkv_status st;
     if ((st = check_pack(k, "k")) != QKV_OK) return st;
     if ((st = check_pack(v, "v")) != QKV_OK) return st;
@@ -524,12 +567,30 @@ qkv_status attention(const char* name, const void* q, int32_t q_dtype, int64_t B
         a.part_o = a.part_ml + (size_t)tiles * (size_t)pl.S * 16 * 2;
     }
     hipStream_t s = static_cast<hipStream_t>(stream);
+    // a decode with append: on the narrow decode (affine or Q8_0 codes, no
+    // additive mask) the kernel quantizes the new rows itself; otherwise the
+    // append kernel runs first
+    hipError_t e = hipSuccess;
+    if (app) {
+        const bool fused = pl.narrow && !pl.unfused && mask_kind != QKV_MASK_ADDITIVE &&
+                           (k->mode == QKV_AFFINE || k->mode == QKV_Q8_0);
+        if (fused) {
+            a.append = 1;
+            a.k_new = app->k_new;
+            a.v_new = app->v_new;
+            a.ns0 = app->strides[0];
+            a.ns1 = app->strides[1];
+        } else {
+            e = qkv::launch_quantize(q_dtype, k->mode, k->bits, k->group_size, (int)D,
+                                     append_launch(app->k_new, app->v_new, app->strides, 1, L - 1, k, v), 2, s);
+            if (e != hipSuccess) return hip_status(e, name);
+        }
+    }
     const bool timed = opts && opts->timing_events[0] && opts->timing_events[1];
     if (timed) {
         hipError_t te = hipEventRecord(static_cast<hipEvent_t>(opts->timing_events[0]), s);
         if (te != hipSuccess) return hip_status(te, name);
     }
-    hipError_t e = hipSuccess;
     if (pl.prepass) {
         for (int i = 0; i < 2 && e == hipSuccess; ++i) {
             const qkv_pack* src = i == 0 ? k : v;
@@ -580,30 +641,13 @@ qkv_status qkv_update_append(const void* k_new, const void* v_new, int32_t dtype
                              const int64_t new_strides[3], int64_t T, int64_t offset,
                              const qkv_pack* k_cache, const qkv_pack* v_cache, void* stream) {
     qkv_status st;
-    if ((st = check_pack(k_cache, "qkv_update_append(k)")) != QKV_OK) return st;
-    if ((st = check_pack(v_cache, "qkv_update_append(v)")) != QKV_OK) return st;
-    if (!same_format(k_cache, v_cache))
-        return fail(QKV_EINVAL, "qkv_update_append: K and V packs differ in format or shape");
-    if ((st = check_source(k_new, dtype, new_strides, k_cache, "qkv_update_append(k_new)")) != QKV_OK) return st;
-    if ((st = check_source(v_new, dtype, new_strides, v_cache, "qkv_update_append(v_new)")) != QKV_OK) return st;
-    if (T < 1) return fail(QKV_EINVAL, "qkv_update_append: T must be >= 1");
-    if (offset < 0 || offset + T > k_cache->L_cap || offset + T > v_cache->L_cap)
-        return fail(QKV_EINVAL, "qkv_update_append: rows [%lld, %lld) exceed the capacity", (long long)offset,
-                    (long long)(offset + T));
-    if (overlap(codes_range(k_cache), codes_range(v_cache)))
-        return fail(QKV_EINVAL, "qkv_update_append: K and V codes overlap");
-    if ((st = check_row_strides(new_strides, dtype, k_cache, "qkv_update_append(k)")) != QKV_OK) return st;
-    if ((st = check_row_strides(new_strides, dtype, v_cache, "qkv_update_append(v)")) != QKV_OK) return st;
-    qkv::QuantLaunch p{};
-    p.job[0] = make_job(k_new, new_strides, k_cache);
-    p.job[1] = make_job(v_new, new_strides, v_cache);
-    p.H = k_cache->H;
-    p.T = T;
-    p.offset = offset;
-    p.BH = k_cache->B * k_cache->H;
-    p.rows = p.BH * T;
+    if ((st = check_append("qkv_update_append", k_new, v_new, dtype, new_strides, T, offset, k_cache, v_cache)) !=
+        QKV_OK)
+        return st;
     hipError_t e = qkv::launch_quantize(dtype, k_cache->mode, k_cache->bits, k_cache->group_size,
-                                        (int)k_cache->D, p, 2, static_cast<hipStream_t>(stream));
+                                        (int)k_cache->D,
+                                        append_launch(k_new, v_new, new_strides, T, offset, k_cache, v_cache), 2,
+                                        static_cast<hipStream_t>(stream));
     return hip_status(e, "qkv_update_append");
 }
 
@@ -675,6 +719,21 @@ qkv_status qsdpa_decode_static(const void* q, int32_t q_dtype, int64_t B, int64_
     return attention("qsdpa_decode_static", q, q_dtype, B, Hq, 1, D, k, v, L, scale,
                      mask ? QKV_MASK_ADDITIVE : QKV_MASK_NONE, mask, mask_dtype, mask_strides, out,
                      nullptr, 0, opts, stream, true);
+}
+
+qkv_status qsdpa_decode_append(const void* q, int32_t q_dtype, int64_t B, int64_t Hq, int64_t D,
+                               const void* k_new, const void* v_new, const int64_t new_strides[3],
+                               int64_t offset, const qkv_pack* k_cache, const qkv_pack* v_cache, float scale,
+                               const void* mask, int32_t mask_dtype, const int64_t mask_strides[4], void* out,
+                               void* workspace, size_t workspace_bytes, const qkv_attn_opts* opts, void* stream) {
+    qkv_status st;
+    if ((st = check_append("qsdpa_decode_append", k_new, v_new, q_dtype, new_strides, 1, offset, k_cache,
+                           v_cache)) != QKV_OK)
+        return st;
+    const AppendArgs app{k_new, v_new, new_strides};
+    return attention("qsdpa_decode_append", q, q_dtype, B, Hq, 1, D, k_cache, v_cache, offset + 1, scale,
+                     mask ? QKV_MASK_ADDITIVE : QKV_MASK_NONE, mask, mask_dtype, mask_strides, out, workspace,
+                     workspace_bytes, opts, stream, false, &app);
 }
 
 qkv_status qsdpa_prefill(const void* q, int32_t q_dtype, int64_t B, int64_t Hq, int64_t Lq,

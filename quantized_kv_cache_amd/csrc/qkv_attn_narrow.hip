@@ -47,6 +47,7 @@
 #include "qkv_internal.hpp"
 #include "qkv_merge.hpp"
 #include "qkv_mfma.hpp"
+#include "qkv_quant_math.hpp"
 
 namespace qkv {
 
@@ -63,7 +64,7 @@ constexpr uint32_t kLazyBigScale = 0x5800u;    // fp16 128 = 2^(15 - kLazy)
 // SA: the scale (and bias) rows are aligned to their size (up to 16 bytes),
 // so a row is read in dwords; otherwise (possible only for the symmetric blocks, whose scale
 // planes need 2-byte alignment) it is read in 16-bit pieces.
-template <int MODE, int BITS, int GS, int D, bool MASK, int GP, bool SA>
+template <int MODE, int BITS, int GS, int D, bool MASK, int GP, bool SA, bool APPEND = false>
 __global__ __launch_bounds__(NTH) void attn_decode_narrow(AttnLaunch p) {
     constexpr int NG = D / GS;
     constexpr int ROWB = D * BITS / 8;            // code bytes of a row
@@ -205,7 +206,53 @@ __global__ __launch_bounds__(NTH) void attn_decode_narrow(AttnLaunch p) {
                 else bufn(rv, off, T.v[c][e], VW);
             }
     };
+    // Decode with append: the new K/V token of this (batch, kv head) is pack
+    // row L - 1, in the last tile of the last split.  The wave that loads
+    // that tile first quantizes the two new rows with the quantize kernel's
+    // arithmetic (lanes [0, D/8) the K row, lanes 32 + [0, D/8) the V row, 8
+    // values each), writes them into the packs and waits for its stores, so
+    // its load of the tile returns them.  No other workgroup reads the row.
+    auto append_here = [&](int t) { return APPEND && split == p.S - 1 && t == ntiles - 1; };
+    auto append_row = [&]() {
+        if constexpr (APPEND && (MODE == MODE_AFFINE || MODE == MODE_Q8_0)) {
+            constexpr int LPR = D / 8;                                  // lanes per row
+            constexpr int LPG = (MODE == MODE_Q8_0 ? 32 : GS) / 8;      // lanes per group
+            const bool is_v = lane >= 32;
+            const int lr = lane & 31;
+            const bool on = lr < LPR;
+            const uint16_t* src = (const uint16_t*)(is_v ? p.v_new : p.k_new) + b * p.ns0 + kvh * p.ns1 + 8 * lr;
+            uint4 x = uint4{0u, 0u, 0u, 0u};
+            if (on) x = *(const uint4*)src;
+            const uint32_t xw[4] = {x.x, x.y, x.z, x.w};
+            float vals[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) vals[i] = f16_to_f32((uint16_t)(xw[i >> 1] >> (16 * (i & 1))));
+            uint32_t w[2];
+            float s32 = 0.0f, mn = 0.0f;
+            uint16_t dh = 0;
+            if constexpr (MODE == MODE_Q8_0) qm::quantize_q8_0_8<DT_F16, LPG>(vals, w, dh);
+            else qm::quantize_affine8<DT_F16, BITS, LPG>(vals, w, s32, mn);
+            const uint32_t row = (uint32_t)(p.L - 1);
+            if (on) {
+                uint8_t* codes = (uint8_t*)(is_v ? vc : kc) + row * (is_v ? vcs : kcs) + lr * (ROWB / LPR);
+                if constexpr (BITS == 4) *(uint32_t*)codes = w[0];
+                else *(uint2*)codes = uint2{w[0], w[1]};
+                if (lr % LPG == 0) {
+                    const uint32_t so = row * (is_v ? vss : kss) + (lr / LPG) * 2;
+                    uint8_t* sc = (uint8_t*)(is_v ? vsc : ksc) + so;
+                    if constexpr (MODE == MODE_Q8_0) {
+                        *(uint16_t*)sc = dh;
+                    } else {
+                        *(uint16_t*)sc = f32_to_f16(s32);
+                        *(uint16_t*)((uint8_t*)(is_v ? vbi : kbi) + so) = f32_to_f16(mn);
+                    }
+                }
+            }
+            wait_stores();
+        }
+    };
     Tile cur;
+    if (append_here(wave)) append_row();
     load_tile(wave, cur);
     __builtin_amdgcn_sched_barrier(0);
     // An opaque zero, defined after the tile loads (the memory clobber keeps
@@ -452,7 +499,10 @@ __global__ __launch_bounds__(NTH) void attn_decode_narrow(AttnLaunch p) {
         __builtin_amdgcn_sched_barrier(0);
         // no loads after the last tile: they would hold the wave (and the
         // workgroup merge behind it) until the CU's memory queue drains
-        if (nxt < ntiles) load_tile(nxt, cur);
+        if (nxt < ntiles) {
+            if (append_here(nxt)) append_row();
+            load_tile(nxt, cur);
+        }
         __builtin_amdgcn_sched_barrier(0);
         tt = nxt;
     }
@@ -586,6 +636,17 @@ hipError_t launch_g(int64_t B, const AttnLaunch& p, hipStream_t stream) {
         }
     } else if (!sa) {
         return hipErrorInvalidValue;               // the host checks guarantee aligned rows
+    }
+    if (p.append) {
+        // the decode with append: affine and Q8_0 codes, no additive mask
+        if constexpr (MODE == MODE_AFFINE || MODE == MODE_Q8_0) {
+            if (p.mask_kind == MASK_ADDITIVE) return hipErrorNotSupported;
+            hipLaunchKernelGGL((attn_decode_narrow<MODE, BITS, GS, D, false, GP, true, true>), grid, dim3(NTH), 0,
+                               stream, p);
+            return hipGetLastError();
+        } else {
+            return hipErrorNotSupported;
+        }
     }
     if (p.mask_kind == MASK_ADDITIVE)
         hipLaunchKernelGGL((attn_decode_narrow<MODE, BITS, GS, D, true, GP, true>), grid, dim3(NTH), 0, stream, p);

@@ -68,6 +68,13 @@ struct AttnLaunch {
     float* part_ml;                 // [B*Hk*n_rt][S][16][2] (m, l) of each split
     float* part_o;                  // [B*Hk*n_rt][S][16][D] unnormalised o of each split
     uint32_t* tickets;              // [B*Hk*n_rt] fused-merge tickets (zero between calls)
+    // decode with append (narrow decode): the new fp16 K/V token of each
+    // (batch, kv head) at element offset b ns0 + h ns1 is quantized into pack
+    // row L - 1 before the tile holding it is loaded
+    int32_t append;
+    const void* k_new;
+    const void* v_new;
+    int64_t ns0, ns1;
     // unfused composition (launch_attn_unfused)
     float* un_scores;               // [B*Hq][L] scores, then probabilities
     float* un_stats;                // [B*Hq][L/4096 chunks] (m, l) of the softmax

@@ -40,6 +40,7 @@
 
 #include "qkv_device.hpp"
 #include "qkv_internal.hpp"
+#include "qkv_quant_math.hpp"
 
 namespace qkv {
 
@@ -48,48 +49,7 @@ namespace {
 typedef uint32_t u2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 
-// Reduction over LANES adjacent lanes (aligned, a power of two <= 16), every
-// lane receiving the result: DPP quad permutations for the first two steps,
-// then half-row and row mirrors (lane i of 8 or 16 meets lane 7 - i or 15 - i,
-// which lies in the other half once the halves are reduced).
-template <int CTRL>
-__device__ __forceinline__ float dpp_f32(float x) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
-}
-template <int LANES, bool MAX>
-__device__ __forceinline__ float group_reduce(float x) {
-    auto op = [](float a, float b) { return MAX ? fmaxf(a, b) : fminf(a, b); };
-    if constexpr (LANES >= 2) x = op(x, dpp_f32<0xB1>(x));    // quad_perm [1,0,3,2]
-    if constexpr (LANES >= 4) x = op(x, dpp_f32<0x4E>(x));    // quad_perm [2,3,0,1]
-    if constexpr (LANES >= 8) x = op(x, dpp_f32<0x141>(x));   // row_half_mirror
-    if constexpr (LANES >= 16) x = op(x, dpp_f32<0x140>(x));  // row_mirror
-    return x;
-}
-
-// RN(1 / b) for a divisor b with a 16-bit (fp16 or bf16) significand: the
-// hardware reciprocal (within one ulp) and one Newton step.  Every fp16 divisor
-// and every bf16 divisor >= 1e-7 was checked on the CPU from each starting
-// value within one ulp of 1 / b: the step lands on the correctly rounded
-// reciprocal.
-__device__ __forceinline__ float recip_rn16(float b) {
-    const float y0 = __builtin_amdgcn_rcpf(b);
-    const float e = __builtin_fmaf(-b, y0, 1.0f);
-    return __builtin_fmaf(e, y0, y0);
-}
-
-// RN(a / b) from y = RN(1 / b): one product and two fused multiply-adds.
-__device__ __forceinline__ float div_by_recip(float a, float b, float y) {
-    const float q = a * y;
-    const float r = __builtin_fmaf(-q, b, a);
-    return __builtin_fmaf(r, y, q);
-}
-
-// round_half_even(x) for |x| < 2^22 as an integer in the low bits of the
-// result's bit pattern (1.5 * 2^23 + n), clamped to [lo, hi].
-__device__ __forceinline__ int32_t rne_clamp(float x, int lo, int hi) {
-    const int32_t u = __float_as_int(x + 12582912.0f);
-    return min(max(u, 0x4B400000 + lo), 0x4B400000 + hi) - 0x4B400000;
-}
+using namespace qm;
 
 constexpr int kQuantPasses = 2;   // row passes per wave, loads issued together
 
@@ -234,49 +194,14 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(QuantLaunch p) {
                 const u4 w = {raw[u].x, raw[u].y, raw[u].z, raw[u].w};
                 __builtin_amdgcn_raw_buffer_store_b128(w, rc[u], (int)o_c, 0, kStream);
             } else if constexpr (MODE == MODE_AFFINE) {
-                constexpr int NL = (1 << BITS) - 1;
-                float mn = v[u][0], mx = v[u][0];
-#pragma unroll
-                for (int i = 1; i < 8; ++i) { mn = fminf(mn, v[u][i]); mx = fmaxf(mx, v[u][i]); }
-                mn = group_reduce<LPG, false>(mn);
-                mx = group_reduce<LPG, true>(mx);
-                const float eps = round_to<DT>(1e-7f);
-                float s32 = div_by_recip(mx - mn, (float)NL, 1.0f / (float)NL);
-                if (s32 < eps) s32 = eps;
-                const float s = round_to<DT>(s32);
-                const float bias = round_to<DT>(mn);
-                const float y = DT == DT_F32 ? 1.0f : recip_rn16(s);
-                // code i = clamp(round_half_even(qt_i), 0, NL): v_cvt_pk_u8_f32
-                // rounds half to even, saturates to [0, 255] and inserts the
-                // byte into a register in one instruction (checked on the GPU
-                // against rint with saturation on ties, their neighbours,
-                // negative values and values past 255); 4-bit quotients are
-                // first limited to 15, which commutes with the rounding
-                float qt[8];
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const float a = v[u][i] - bias;
-                    qt[i] = DT == DT_F32 ? a / s : div_by_recip(a, s, y);
-                    if constexpr (BITS == 4) qt[i] = fminf(qt[i], (float)NL);
-                }
+                uint32_t w[2];
+                float s32, mn;
+                quantize_affine8<DT, BITS, LPG>(v[u], w, s32, mn);
                 if constexpr (BITS == 4) {
-                    // byte k of the word holds codes 2k (low nibble) and 2k + 1
-                    uint32_t ev = 0, od = 0;
-#pragma unroll
-                    for (int k = 0; k < 4; ++k) {
-                        ev = __builtin_amdgcn_cvt_pk_u8_f32(qt[2 * k], (uint32_t)k, ev);
-                        od = __builtin_amdgcn_cvt_pk_u8_f32(qt[2 * k + 1], (uint32_t)k, od);
-                    }
-                    __builtin_amdgcn_raw_buffer_store_b32(ev | (od << 4), rc[u], (int)o_c, 0, kStream);
+                    __builtin_amdgcn_raw_buffer_store_b32(w[0], rc[u], (int)o_c, 0, kStream);
                 } else {
-                    uint32_t lo = 0, hi = 0;
-#pragma unroll
-                    for (int k = 0; k < 4; ++k) {
-                        lo = __builtin_amdgcn_cvt_pk_u8_f32(qt[k], (uint32_t)k, lo);
-                        hi = __builtin_amdgcn_cvt_pk_u8_f32(qt[4 + k], (uint32_t)k, hi);
-                    }
-                    const u2 w = {lo, hi};
-                    __builtin_amdgcn_raw_buffer_store_b64(w, rc[u], (int)o_c, 0, kStream);
+                    const u2 wv = {w[0], w[1]};
+                    __builtin_amdgcn_raw_buffer_store_b64(wv, rc[u], (int)o_c, 0, kStream);
                 }
                 if (leader) {
                     if (gather) {
@@ -288,26 +213,11 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(QuantLaunch p) {
                     }
                 }
             } else {
-                float amax = 0.0f;
-#pragma unroll
-                for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[u][i]));
-                amax = group_reduce<LPG, true>(amax);
-                const float d32 = div_by_recip(amax, 127.0f, 1.0f / 127.0f);
-                const uint16_t dh = f32_to_f16(d32);
-                const float d = f16_to_f32(dh);
-                // d = 0 (an all-zero block) gives codes 0: y = 0 makes every quotient 0
-                const float y = d != 0.0f ? recip_rn16(d) : 0.0f;
-                int32_t c[8];
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const float qt = DT == DT_F32 ? (d != 0.0f ? v[u][i] / d : 0.0f) : div_by_recip(v[u][i], d, y);
-                    c[i] = rne_clamp(qt, -127, 127);
-                }
-                const u2 w = {((uint32_t)c[0] & 0xffu) | (((uint32_t)c[1] & 0xffu) << 8) |
-                                  (((uint32_t)c[2] & 0xffu) << 16) | ((uint32_t)c[3] << 24),
-                              ((uint32_t)c[4] & 0xffu) | (((uint32_t)c[5] & 0xffu) << 8) |
-                                  (((uint32_t)c[6] & 0xffu) << 16) | ((uint32_t)c[7] << 24)};
-                __builtin_amdgcn_raw_buffer_store_b64(w, rc[u], (int)o_c, 0, kStream);
+                uint32_t w[2];
+                uint16_t dh;
+                quantize_q8_0_8<DT, LPG>(v[u], w, dh);
+                const u2 wv = {w[0], w[1]};
+                __builtin_amdgcn_raw_buffer_store_b64(wv, rc[u], (int)o_c, 0, kStream);
                 if (leader) {
                     if (gather) *(uint16_t*)(s_blk[0] + o_blk + u * RPW * SROWB) = dh;
                     else __builtin_amdgcn_raw_buffer_store_b16(dh, rs[u], (int)o_s, 0, 0);

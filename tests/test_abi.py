@@ -32,7 +32,7 @@ def test_exports_every_declared_function(L):
     assert set(names) == set(_lib.EXPORTS), names
     for n in names:
         assert hasattr(L, n), n
-    assert L.qkv_abi_version() == 5
+    assert L.qkv_abi_version() == 6
 
 
 def _pack(**kw):
@@ -132,6 +132,30 @@ def test_decode_rejects(L):
     assert _decode(L, opts=opts) == _lib.QKV_EWORKSPACE
     assert "workspace" in L.qkv_last_error().decode()
     assert _decode(L, opts=_lib.QkvAttnOpts(num_splits=-1, algo=0)) == _lib.QKV_EINVAL
+
+
+def _decode_append(L, offset=63, kn=FAKE + 0x3000000, vn=FAKE + 0x3100000, strides=(256, 128, 128),
+                   q=FAKE + 0x1000000, out=FAKE + 0x2000000, kp=None, vp=None, qdt=_lib.QKV_F16):
+    kp = kp or _pack()
+    vp = vp or _pack(codes=FAKE + 0x800000, scales=FAKE + 0x900000, biases=FAKE + 0xa00000)
+    return L.qsdpa_decode_append(ctypes.c_void_p(q), qdt, 1, 4, 128, ctypes.c_void_p(kn) if kn else None,
+                                 ctypes.c_void_p(vn) if vn else None, _lib.i64_array(strides), offset,
+                                 ctypes.byref(kp), ctypes.byref(vp), 1.0, None, _lib.QKV_F32, None,
+                                 ctypes.c_void_p(out), None, 0, None, None)
+
+
+def test_decode_append_rejects(L):
+    """qsdpa_decode_append checks the append (T = 1, the query dtype) and the
+    decode over offset + 1 keys before it enqueues anything."""
+    assert _decode_append(L, offset=64) == _lib.QKV_EINVAL               # row 64 beyond L_cap
+    assert "capacity" in L.qkv_last_error().decode()
+    assert _decode_append(L, offset=-1) == _lib.QKV_EINVAL
+    assert _decode_append(L, kn=0) == _lib.QKV_EINVAL                    # null k_new
+    assert _decode_append(L, vn=FAKE + 0x3100008) == _lib.QKV_EINVAL     # v_new not 16-byte aligned
+    assert _decode_append(L, strides=(256, 128, 12)) == _lib.QKV_EINVAL  # stride not a multiple of 8
+    assert _decode_append(L, qdt=_lib.QKV_F32) == _lib.QKV_EUNSUPPORTED  # scale dtype != new-token dtype
+    assert _decode_append(L, out=FAKE + 0x100) == _lib.QKV_EINVAL        # out overlaps the K codes
+    assert _decode_append(L, q=0) == _lib.QKV_EINVAL
 
 
 def test_workspace_bytes(L):
