@@ -9,8 +9,10 @@ decode call: the attention kernel (packed K/V streamed once, dequantized in
 registers, online softmax per key split) and the split merge kernel.
 
 Other workloads (``--workload``): tiny_decode, append_decode_b8_8bit (a step
-is one qkv_update_append of a token per sequence plus the decode over the
-grown cache), q8_0_decode_gqa16 and q8_0_prefill_512 (one causal prefill).
+appends a token per sequence and decodes over the grown cache: one
+qsdpa_decode_append call, or qkv_update_append and qsdpa_decode with
+``--separate-append``), q8_0_decode_gqa16 and q8_0_prefill_512 (one causal
+prefill).
 
 Inputs are resident in HBM before the timed region.  The quantized cache is
 replicated R times (R * bytes >= twice the 256 MB Infinity Cache, at most 64
