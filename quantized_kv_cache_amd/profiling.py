@@ -27,12 +27,12 @@ KERNEL_SOURCES = {
     "attn_matrix_decode": ["qkv_attn_matrix.hip", "qkv_merge.hpp", "qkv_mfma.hpp", "qkv_device.hpp",
                            "qkv_internal.hpp"],
     "attn_decode_narrow": ["qkv_attn_narrow.hip", "qkv_merge.hpp", "qkv_mfma.hpp", "qkv_device.hpp",
-                           "qkv_internal.hpp"],
+                           "qkv_internal.hpp", "qkv_quant_math.hpp"],
     "attn_matrix_prefill": ["qkv_prefill_matrix.hip", "qkv_mfma.hpp", "qkv_device.hpp", "qkv_internal.hpp"],
     "attn_generic_kernel": ["qkv_attn_generic.hip", "qkv_device.hpp", "qkv_internal.hpp"],
     "merge_splits_kernel": ["qkv_merge.hip", "qkv_merge.hpp", "qkv_device.hpp", "qkv_internal.hpp"],
     "merge_splits_small": ["qkv_merge.hip", "qkv_merge.hpp", "qkv_device.hpp", "qkv_internal.hpp"],
-    "quantize_rows_kernel": ["qkv_quantize.hip", "qkv_device.hpp", "qkv_internal.hpp"],
+    "quantize_rows_kernel": ["qkv_quantize.hip", "qkv_device.hpp", "qkv_internal.hpp", "qkv_quant_math.hpp"],
     "unfused_scores_kernel": ["qkv_unfused.hip", "qkv_device.hpp", "qkv_internal.hpp"],
     "attn_decode_stream": ["qkv_attn_stream.hip", "qkv_mfma.hpp", "qkv_device.hpp", "qkv_internal.hpp"],
 }
