@@ -276,7 +276,8 @@ qkv_status qsdpa_decode(const void* q, int32_t q_dtype, int64_t B, int64_t Hq, i
  * launch: the wave that loads the tile holding row 'offset' quantizes the two
  * new rows first; otherwise the append kernel runs before the decode.
  * Arguments and errors as qkv_update_append (T = 1, dtype = q_dtype) and
- * qsdpa_decode (L = offset + 1); size the workspace with qsdpa_plan or
+ * qsdpa_decode (L = offset + 1), and EINVAL when k_new or v_new overlaps
+ * out, the packs or the workspace; size the workspace with qsdpa_plan or
  * qsdpa_workspace_bytes for L = offset + 1.  timing_events in opts bracket
  * the attention kernel (the fused one, or the decode after the append). */
 qkv_status qsdpa_decode_append(const void* q, int32_t q_dtype, int64_t B, int64_t Hq, int64_t D,

@@ -476,6 +476,20 @@ qkv_status attention(const char* name, const void* q, int32_t q_dtype, int64_t B
     const qkv_pack* packs[2] = {k, v};
     for (const qkv_pack* p : packs)
         if (overlaps_pack(ro, p)) return fail(QKV_EINVAL, "%s: out overlaps a pack", name);
+    // a decode with append reads the new tokens while the call writes out,
+    // the workspace and the packs' new rows
+    Range rn[2] = {{0, 0}, {0, 0}};
+    if (app) {
+        const int64_t nn[4] = {B, k->H, 1, D};
+        const int64_t ns[4] = {app->strides[0], app->strides[1], app->strides[2], 1};
+        rn[0] = strided_range(app->k_new, qe, nn, ns);
+        rn[1] = strided_range(app->v_new, qe, nn, ns);
+        for (const Range& r : rn) {
+            if (overlap(r, ro)) return fail(QKV_EINVAL, "%s: out overlaps a new token", name);
+            for (const qkv_pack* p : packs)
+                if (overlaps_pack(r, p)) return fail(QKV_EINVAL, "%s: a new token overlaps a pack", name);
+        }
+    }
     Range rm{0, 0};
     if (mask_kind == QKV_MASK_ADDITIVE) {
         const int64_t mn[4] = {B, Hq, Lq, L};
@@ -512,6 +526,8 @@ qkv_status attention(const char* name, const void* q, int32_t q_dtype, int64_t B
             if (overlaps_pack(rw, p)) return fail(QKV_EINVAL, "%s: the workspace overlaps a pack", name);
         if (mask_kind == QKV_MASK_ADDITIVE && overlap(rm, rw))
             return fail(QKV_EINVAL, "%s: the mask overlaps the workspace", name);
+        if (app && (overlap(rn[0], rw) || overlap(rn[1], rw)))
+            return fail(QKV_EINVAL, "%s: a new token overlaps the workspace", name);
     }
 
     // the dequantize-first strategy attends dense fp16 copies at the start of

@@ -156,6 +156,9 @@ def test_decode_append_rejects(L):
     assert _decode_append(L, qdt=_lib.QKV_F32) == _lib.QKV_EUNSUPPORTED  # scale dtype != new-token dtype
     assert _decode_append(L, out=FAKE + 0x100) == _lib.QKV_EINVAL        # out overlaps the K codes
     assert _decode_append(L, q=0) == _lib.QKV_EINVAL
+    assert _decode_append(L, kn=FAKE + 0x2000000) == _lib.QKV_EINVAL     # k_new is out
+    assert "new token" in L.qkv_last_error().decode()
+    assert _decode_append(L, vn=FAKE + 0x900000) == _lib.QKV_EINVAL      # v_new inside V's scales
 
 
 def test_workspace_bytes(L):
