@@ -409,7 +409,15 @@ Plan make_plan(int64_t B, int64_t Hq, int64_t Lq, int64_t D, int64_t L, const qk
                          : pl.prefill ? 64
                          : pl.narrow  ? qkv::narrow_decode_key_quantum()
                                       : qkv::decode_matrix_key_quantum();
-    chunk = (chunk + gran - 1) / gran * gran;
+    // whole granules per split: rounding the chunk up can nearly halve the
+    // splits when it is a few granules long (257 keys -> 512 with 256-key
+    // granules: the 16-row decode of 20481 keys would get 41 splits instead
+    // of 80), so it is rounded down when that keeps the split count within
+    // an eighth above the one asked for
+    const int64_t up = (chunk + gran - 1) / gran * gran;
+    const int64_t dn = std::max<int64_t>(gran, chunk / gran * gran);
+    const int64_t s_up = (L + up - 1) / up, s_dn = (L + dn - 1) / dn;
+    chunk = (s_up < S && s_dn <= std::min<int64_t>(qkv::kMaxSplits, S + S / 8)) ? dn : up;
     S = (int)((L + chunk - 1) / chunk);
     pl.S = S;
     pl.chunk = chunk;
@@ -583,13 +591,13 @@ qkv_status attention(const char* name, const void* q, int32_t q_dtype, int64_t B
         a.part_o = a.part_ml + (size_t)tiles * (size_t)pl.S * 16 * 2;
     }
     hipStream_t s = static_cast<hipStream_t>(stream);
-    // a decode with append: on the narrow decode (affine or Q8_0 codes, no
-    // additive mask) the kernel quantizes the new rows itself; otherwise the
-    // append kernel runs first
+    // a decode with append: on the narrow and the 16-row decode (affine or
+    // Q8_0 codes, no additive mask) the kernel quantizes the new rows itself;
+    // otherwise the append kernel runs first
     hipError_t e = hipSuccess;
     if (app) {
-        const bool fused = pl.narrow && !pl.unfused && mask_kind != QKV_MASK_ADDITIVE &&
-                           (k->mode == QKV_AFFINE || k->mode == QKV_Q8_0);
+        const bool fused = (pl.narrow || (pl.matrix && !pl.prefill)) && !pl.unfused && !pl.prepass &&
+                           mask_kind != QKV_MASK_ADDITIVE && (k->mode == QKV_AFFINE || k->mode == QKV_Q8_0);
         if (fused) {
             a.append = 1;
             a.k_new = app->k_new;

@@ -55,6 +55,7 @@
 #include "qkv_internal.hpp"
 #include "qkv_merge.hpp"
 #include "qkv_mfma.hpp"
+#include "qkv_quant_math.hpp"
 
 namespace qkv {
 
@@ -213,7 +214,7 @@ __device__ __forceinline__ float sum4(float x) {
     return __uint_as_float(c[0]) + __uint_as_float(c[1]);
 }
 
-template <int MODE, int BITS, int GS, int D, bool MASK, bool FOLD>
+template <int MODE, int BITS, int GS, int D, bool MASK, bool FOLD, bool APPEND = false>
 __global__ __launch_bounds__(NTHR) void attn_matrix_decode(AttnLaunch p) {
     using F = Fmt<MODE, BITS, GS, D>;
     constexpr int NG = F::NG;
@@ -447,7 +448,24 @@ __global__ __launch_bounds__(NTHR) void attn_matrix_decode(AttnLaunch p) {
     // wait for the tile)
     __builtin_amdgcn_sched_barrier(0);
     const int my_tiles = wave < ntiles ? (ntiles - wave + NWAVE - 1) / NWAVE : 0;
+    // Decode with append: the new K/V token of this (batch, kv head) is pack
+    // row L - 1, in the last tile of the last split; the wave that loads that
+    // tile first quantizes the two new rows (qm::append_rows), writes them and
+    // waits for its stores, so its load of the tile returns them.
+    auto append_here = [&](int t) { return APPEND && split == p.S - 1 && t == ntiles - 1; };
+    auto append_row = [&]() {
+        if constexpr (APPEND && (MODE == MODE_AFFINE || MODE == MODE_Q8_0)) {
+            const uint32_t row = (uint32_t)(p.L - 1);
+            const int64_t e = b * p.ns0 + kvh * p.ns1;
+            qm::append_rows<MODE, BITS, GS, D>(
+                (const uint16_t*)p.k_new + e, (const uint16_t*)p.v_new + e, (uint8_t*)kc + row * kcs,
+                (uint8_t*)vc + row * vcs, (uint8_t*)ksc + row * kss, (uint8_t*)vsc + row * vss,
+                (uint8_t*)kbi + row * kss, (uint8_t*)vbi + row * vss);
+            wait_stores();
+        }
+    };
     Tile cur;
+    if (append_here(wave)) append_row();
     load_tile(wave, cur);
     __builtin_amdgcn_sched_barrier(0);
 
@@ -714,7 +732,10 @@ __global__ __launch_bounds__(NTHR) void attn_matrix_decode(AttnLaunch p) {
         __builtin_amdgcn_sched_barrier(0);
         // no loads after the last tile: they would hold the wave (and the
         // workgroup merge behind it) until the CU's memory queue drains
-        if (i + 1 < my_tiles) load_tile(wave + (i + 1) * NWAVE, cur);
+        if (i + 1 < my_tiles) {
+            if (append_here(wave + (i + 1) * NWAVE)) append_row();
+            load_tile(wave + (i + 1) * NWAVE, cur);
+        }
         __builtin_amdgcn_sched_barrier(0);
     }
 
@@ -811,6 +832,13 @@ __global__ __launch_bounds__(NTHR) void attn_matrix_decode(AttnLaunch p) {
 template <int MODE, int BITS, int GS, int D, bool FOLD>
 hipError_t launch_m(int64_t B, const AttnLaunch& p, hipStream_t stream) {
     dim3 grid(p.S, (unsigned)p.Hk, (unsigned)B);
+    if (p.append) {
+        // the decode with append: no additive mask
+        if (p.mask_kind == MASK_ADDITIVE) return hipErrorNotSupported;
+        hipLaunchKernelGGL((attn_matrix_decode<MODE, BITS, GS, D, false, FOLD, true>), grid, dim3(NTHR), 0,
+                           stream, p);
+        return hipGetLastError();
+    }
     if (p.mask_kind == MASK_ADDITIVE)
         hipLaunchKernelGGL((attn_matrix_decode<MODE, BITS, GS, D, true, FOLD>), grid, dim3(NTHR), 0,
                            stream, p);

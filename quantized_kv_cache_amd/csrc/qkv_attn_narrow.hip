@@ -209,45 +209,18 @@ __global__ __launch_bounds__(NTH) void attn_decode_narrow(AttnLaunch p) {
     // Decode with append: the new K/V token of this (batch, kv head) is pack
     // row L - 1, in the last tile of the last split.  The wave that loads
     // that tile first quantizes the two new rows with the quantize kernel's
-    // arithmetic (lanes [0, D/8) the K row, lanes 32 + [0, D/8) the V row, 8
-    // values each), writes them into the packs and waits for its stores, so
-    // its load of the tile returns them.  No other workgroup reads the row.
+    // arithmetic (qm::append_rows), writes them into the packs and waits for
+    // its stores, so its load of the tile returns them.  No other workgroup
+    // reads the row.
     auto append_here = [&](int t) { return APPEND && split == p.S - 1 && t == ntiles - 1; };
     auto append_row = [&]() {
         if constexpr (APPEND && (MODE == MODE_AFFINE || MODE == MODE_Q8_0)) {
-            constexpr int LPR = D / 8;                                  // lanes per row
-            constexpr int LPG = (MODE == MODE_Q8_0 ? 32 : GS) / 8;      // lanes per group
-            const bool is_v = lane >= 32;
-            const int lr = lane & 31;
-            const bool on = lr < LPR;
-            const uint16_t* src = (const uint16_t*)(is_v ? p.v_new : p.k_new) + b * p.ns0 + kvh * p.ns1 + 8 * lr;
-            uint4 x = uint4{0u, 0u, 0u, 0u};
-            if (on) x = *(const uint4*)src;
-            const uint32_t xw[4] = {x.x, x.y, x.z, x.w};
-            float vals[8];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) vals[i] = f16_to_f32((uint16_t)(xw[i >> 1] >> (16 * (i & 1))));
-            uint32_t w[2];
-            float s32 = 0.0f, mn = 0.0f;
-            uint16_t dh = 0;
-            if constexpr (MODE == MODE_Q8_0) qm::quantize_q8_0_8<DT_F16, LPG>(vals, w, dh);
-            else qm::quantize_affine8<DT_F16, BITS, LPG>(vals, w, s32, mn);
             const uint32_t row = (uint32_t)(p.L - 1);
-            if (on) {
-                uint8_t* codes = (uint8_t*)(is_v ? vc : kc) + row * (is_v ? vcs : kcs) + lr * (ROWB / LPR);
-                if constexpr (BITS == 4) *(uint32_t*)codes = w[0];
-                else *(uint2*)codes = uint2{w[0], w[1]};
-                if (lr % LPG == 0) {
-                    const uint32_t so = row * (is_v ? vss : kss) + (lr / LPG) * 2;
-                    uint8_t* sc = (uint8_t*)(is_v ? vsc : ksc) + so;
-                    if constexpr (MODE == MODE_Q8_0) {
-                        *(uint16_t*)sc = dh;
-                    } else {
-                        *(uint16_t*)sc = f32_to_f16(s32);
-                        *(uint16_t*)((uint8_t*)(is_v ? vbi : kbi) + so) = f32_to_f16(mn);
-                    }
-                }
-            }
+            const int64_t e = b * p.ns0 + kvh * p.ns1;
+            qm::append_rows<MODE, BITS, GS, D>(
+                (const uint16_t*)p.k_new + e, (const uint16_t*)p.v_new + e, (uint8_t*)kc + row * kcs,
+                (uint8_t*)vc + row * vcs, (uint8_t*)ksc + row * kss, (uint8_t*)vsc + row * vss,
+                (uint8_t*)kbi + row * kss, (uint8_t*)vbi + row * vss);
             wait_stores();
         }
     };

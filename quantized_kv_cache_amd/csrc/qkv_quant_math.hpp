@@ -146,5 +146,49 @@ __device__ __forceinline__ void quantize_q8_0_8(const float v[8], uint32_t w[2],
            ((uint32_t)c[7] << 24);
 }
 
+// One new K row and one new V row (D fp16 values each, at k_new / v_new)
+// quantized by one wave into pack rows whose codes, scales and biases start at
+// the given row pointers (fp16 scales; affine or Q8_0): lanes 0 .. D/8 - 1
+// take the K row, lanes 32 .. 32 + D/8 - 1 the V row, 8 values per lane, so
+// every group lies in one DPP row of lanes.  The stores are issued, not
+// waited for.
+template <int MODE, int BITS, int GS, int D>
+__device__ __forceinline__ void append_rows(const uint16_t* k_new, const uint16_t* v_new, uint8_t* kcodes,
+                                            uint8_t* vcodes, uint8_t* kscales, uint8_t* vscales, uint8_t* kbiases,
+                                            uint8_t* vbiases) {
+    constexpr int LPR = D / 8;                                  // lanes per row
+    constexpr int LPG = (MODE == MODE_Q8_0 ? 32 : GS) / 8;      // lanes per group
+    constexpr int ROWB = D * BITS / 8;
+    static_assert(LPR <= 32 && (MODE == MODE_AFFINE || MODE == MODE_Q8_0), "one row per half wave");
+    const int lane = threadIdx.x & 63;
+    const bool is_v = lane >= 32;
+    const int lr = lane & 31;
+    const bool on = lr < LPR;
+    uint4 x = uint4{0u, 0u, 0u, 0u};
+    if (on) x = *(const uint4*)((is_v ? v_new : k_new) + 8 * lr);
+    const uint32_t xw[4] = {x.x, x.y, x.z, x.w};
+    float vals[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) vals[i] = f16_to_f32((uint16_t)(xw[i >> 1] >> (16 * (i & 1))));
+    uint32_t w[2];
+    float s32 = 0.0f, mn = 0.0f;
+    uint16_t dh = 0;
+    if constexpr (MODE == MODE_Q8_0) quantize_q8_0_8<DT_F16, LPG>(vals, w, dh);
+    else quantize_affine8<DT_F16, BITS, LPG>(vals, w, s32, mn);
+    if (!on) return;
+    uint8_t* codes = (is_v ? vcodes : kcodes) + lr * (ROWB / LPR);
+    if constexpr (BITS == 4) *(uint32_t*)codes = w[0];
+    else *(uint2*)codes = uint2{w[0], w[1]};
+    if (lr % LPG == 0) {
+        const int so = (lr / LPG) * 2;
+        if constexpr (MODE == MODE_Q8_0) {
+            *(uint16_t*)((is_v ? vscales : kscales) + so) = dh;
+        } else {
+            *(uint16_t*)((is_v ? vscales : kscales) + so) = f32_to_f16(s32);
+            *(uint16_t*)((is_v ? vbiases : kbiases) + so) = f32_to_f16(mn);
+        }
+    }
+}
+
 }  // namespace qm
 }  // namespace qkv

@@ -32,14 +32,18 @@ def _clone(p):
 
 CASES = [
     # dtype, mode, bits, gs, B, Hq, Hk, L0, D, splits, steps -- fp16 queries with a
-    # GQA factor <= 4 run on the narrow decode (one launch); the others append first
+    # GQA factor <= 16 run on the narrow or the 16-row decode (one launch); the
+    # others append first
     ("f16", "affine", 8, 64, 2, 8, 4, 1000, 128, 0, 3),      # G = 2
     ("f16", "affine", 4, 64, 1, 16, 4, 4000, 128, 0, 2),     # G = 4
     ("f16", "affine", 4, 32, 1, 4, 4, 70, 64, 0, 3),         # the new row in a wave's first tile
     ("f16", "affine", 8, 32, 2, 6, 2, 2500, 64, 7, 2),       # odd split count, 2 groups
     ("f16", "affine", 4, 128, 3, 12, 3, 777, 128, 3, 2),     # batch 3, G = 4
     ("f16", "q8_0", 8, 32, 1, 8, 2, 513, 128, 0, 3),         # Q8_0
-    ("f16", "q8_0", 8, 32, 1, 32, 2, 3000, 256, 0, 2),       # GQA 16: 16-row decode after the append
+    ("f16", "q8_0", 8, 32, 1, 32, 2, 3000, 256, 0, 2),       # GQA 16: the 16-row decode, one launch
+    ("f16", "affine", 4, 64, 1, 16, 2, 1500, 128, 5, 2),     # GQA 8: the folded 16-row decode, 5 splits
+    ("f16", "affine", 8, 64, 2, 16, 2, 100, 64, 0, 3),       # GQA 8, the new row in a wave's first tile
+    ("f16", "q8_0", 8, 32, 1, 20, 2, 260, 256, 0, 2),        # GQA 10, short cache
     ("f32", "affine", 8, 64, 1, 4, 1, 200, 64, 0, 2),        # fp32: generic kernel after the append
     ("bf16", "affine", 4, 64, 2, 8, 2, 900, 128, 0, 2),      # bf16: generic kernel after the append
 ]
