@@ -231,6 +231,20 @@ def test_plan_narrow_decode_tickets_fit_header(L):
             assert pl.num_splits == splits
 
 
+def test_plan_splits_do_not_collapse_past_a_granule(L):
+    """The 16-row decode splits the keys in whole 256-key granules: one key
+    more than 80 granules must not halve the splits (a chunk of 257 keys
+    rounded up to 512), and an exact multiple keeps its plan."""
+    for Lk, want in ((20480, 80), (20481, 81), (20700, 81)):
+        kp = _lib.QkvPack(mode=_lib.QKV_Q8_0, bits=8, group_size=32, scale_dtype=_lib.QKV_F16,
+                          B=1, H=2, L_cap=20736, D=256, codes=FAKE, scales=FAKE + 0x10000000, biases=None,
+                          stride_b=2 * 20736, stride_h=20736, stride_l=1)
+        pl = _lib.QkvAttnPlan()
+        assert L.qsdpa_plan(1, 32, 1, 256, Lk, ctypes.byref(kp), _lib.QKV_F16, None, ctypes.byref(pl)) == 0
+        assert pl.kernel == _lib.QKV_KERNEL_DECODE
+        assert pl.num_splits == want and pl.keys_per_split == 256, (Lk, pl.num_splits, pl.keys_per_split)
+
+
 @pytest.mark.parametrize("Lq,rows", [(15, 64), (16, 128), (100, 128)])
 def test_prefill_row_tile(L, Lq, rows):
     """Prefill row tiles: 64 rows below 256 GQA-packed rows per (batch, kv
