@@ -271,10 +271,10 @@ qkv_status qsdpa_decode(const void* q, int32_t q_dtype, int64_t B, int64_t Hq, i
  * fast::quantized_kv_update (kv_update) and then attends the updated cache
  * with quantized_scaled_dot_product_attention.  The cache rows written are
  * the bits qkv_update_append writes, and out is what qsdpa_decode returns on
- * the updated packs with the same options.  On the narrow matrix-core decode
- * (fp16 queries, GQA factor <= 4, affine or Q8_0 codes, no mask) it is one
- * launch: the wave that loads the tile holding row 'offset' quantizes the two
- * new rows first; otherwise the append kernel runs before the decode.
+ * the updated packs with the same options.  On the matrix-core decodes (fp16
+ * queries, GQA factor <= 16, affine 4/8-bit or Q8_0 codes, no mask) it is
+ * one launch: the wave that loads the tile holding row 'offset' quantizes the
+ * two new rows first; otherwise the append kernel runs before the decode.
  * Arguments and errors as qkv_update_append (T = 1, dtype = q_dtype) and
  * qsdpa_decode (L = offset + 1), and EINVAL when k_new or v_new overlaps
  * out, the packs or the workspace; size the workspace with qsdpa_plan or
