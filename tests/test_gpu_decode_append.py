@@ -152,3 +152,28 @@ def test_decode_append_workload_all_steps():
             assert_close(out, ref, f"decode_append step {t} (L={L})", report=True)
     assert_pack_equal(pack_numpy(kp), kr)
     assert_pack_equal(pack_numpy(vp), vr)
+
+
+@pytest.mark.parametrize("mode,bits,gs,Hq", [("affine", 4, 64, 8), ("q8_0", 8, 32, 32)])
+def test_decode_append_strided_new_tokens(mode, bits, gs, Hq):
+    """The new tokens as a view (one position of a [B, Hk, 5, D] tensor, so
+    strides 5 D per head and 5 Hk D per batch): the kernel reads them through
+    the strides; cache and output as with a contiguous copy."""
+    B, Hk, L0, D = 2, 2, 3000, 128
+    rng = np.random.default_rng(11)
+    base_k = W.draw(rng, (B, Hk, L0, D), "normal", "f16")
+    base_v = W.draw(rng, (B, Hk, L0, D), "normal", "f16")
+    kf, vf = _packs(base_k, "f16", mode, bits, gs, L0 + 1), _packs(base_v, "f16", mode, bits, gs, L0 + 1)
+    ku, vu = _clone(kf), _clone(vf)
+    big_k = W.draw(rng, (B, Hk, 5, D), "normal", "f16")
+    big_v = W.draw(rng, (B, Hk, 5, D), "normal", "f16")
+    q = W.draw(rng, (B, Hq, 1, D), "normal", "f16")
+    qd = to_dev(q, "f16")
+    kv, vv = to_dev(big_k, "f16")[:, :, 3:4], to_dev(big_v, "f16")[:, :, 3:4]
+    assert not kv.is_contiguous()
+    out_f = qkv.qsdpa_decode_append(qd, kf, vf, kv, vv, L0, 0.125)
+    qkv.qkv_update_append(ku, vu, kv.contiguous(), vv.contiguous(), L0)
+    out_u = qkv.qsdpa_decode(qd, ku, vu, L0 + 1, 0.125)
+    assert torch.equal(out_f, out_u)
+    for got, want in ((kf, ku), (vf, vu)):
+        assert_pack_equal(pack_numpy(got), pack_numpy(want))
