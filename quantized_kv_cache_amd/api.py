@@ -8,7 +8,8 @@ kernels behind the C ABI; there is no CPU path.
 The function names are those of the C ABI (include/qkv.h):
 ``qkv_quantize``, ``qkv_update_append``, ``qsdpa_workspace_bytes``,
 ``qsdpa_workspace_reset``, ``qsdpa_plan``, ``qsdpa_decode``,
-``qsdpa_decode_static``, ``qsdpa_prefill``, ``qkv_dequantize``.
+``qsdpa_decode_static``, ``qsdpa_decode_append``, ``qsdpa_prefill``,
+``qkv_dequantize``.
 """
 from __future__ import annotations
 
