@@ -37,6 +37,8 @@ Prints one JSON line:
   latency_us     single calls, each after a 512 MB write that evicts the
                  Infinity Cache: p10 / median / p90 over 50 calls
                  (``--no-extras`` skips these two, for profiled runs)
+``--graph`` times one replay of a HIP graph that captured the timed steps'
+calls instead of the calls themselves (config.launch says which).
 ``--copy-mib N`` instead runs a plain N MiB device copy ``--steps`` times (the
 known-size kernel the counter readings are scaled by).
 """
@@ -136,6 +138,9 @@ def parse():
     ap.add_argument("--separate-append", action="store_true",
                     help="append workload: qkv_update_append and qsdpa_decode as two calls per step "
                          "instead of qsdpa_decode_append")
+    ap.add_argument("--graph", action="store_true",
+                    help="time one replay of a HIP graph that captured the timed steps' calls "
+                         "(the same kernels without the per-call host path and launch gaps)")
     ap.add_argument("--read-sweep", action="store_true",
                     help="instead: the plain streaming read of the workload's K/V bytes over a "
                          "grid of load shapes (workgroups, threads, loads in flight, width)")
@@ -172,6 +177,25 @@ def time_region(torch, run, first, steps, stream):
     start.record(stream)
     for i in range(first, first + steps):
         run(i)
+    end.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps
+
+
+def graph_region(torch, run, first, steps, stream):
+    """ms per step over one replay of a graph that captured run(i) for the
+    `steps` values of i, after one untimed replay."""
+    g = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g, stream=stream):
+        for i in range(first, first + steps):
+            run(i)
+    g.replay()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    g.replay()
     end.record(stream)
     torch.cuda.synchronize()
     return start.elapsed_time(end) / steps
@@ -412,6 +436,10 @@ def main():
 
     w = W.WORKLOADS[args.workload]
     torch.cuda.set_device(0)
+    if args.graph:
+        # a graph is captured on a stream other than the legacy default one: every
+        # call below is marshalled on this one
+        torch.cuda.set_stream(torch.cuda.Stream())
     stream = torch.cuda.current_stream()
     if args.read_sweep:
         per = pack_bytes(w, w.cap)
@@ -475,7 +503,16 @@ def main():
 
     for i in range(args.warmup):
         run(i)
-    ms = time_region(torch, run, args.warmup, args.steps, stream)
+    if args.graph:
+        ms = graph_region(torch, run, args.warmup, args.steps, stream)
+        last = args.warmup + args.steps - 1
+        got = out.clone()
+        run(last)                         # the graph's last call, eagerly
+        torch.cuda.synchronize()
+        if not torch.equal(got, out):
+            sys.exit("bench: the graph replay's output differs from the eager call's")
+    else:
+        ms = time_region(torch, run, args.warmup, args.steps, stream)
 
     plan = qkv.qsdpa_plan(q0, ks[0], plan_L, args.splits, args.algo)
     kernel = plan["kernel"]
@@ -508,6 +545,7 @@ def main():
                    "cache_dtype": w.dtype, "cache_copies": R, "algo": args.algo,
                    "kernel": kernel, "num_splits": plan["num_splits"]},
     }
+    rec["config"]["launch"] = "graph replay" if args.graph else "eager calls"
     if w.steps:
         rec["config"]["append"] = "separate launch" if args.separate_append else "in the decode call"
     traffic = stored_traffic(kernel, w.name)

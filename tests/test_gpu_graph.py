@@ -1,7 +1,7 @@
 """Attention calls captured in a HIP graph (torch.cuda.CUDAGraph on ROCm) and
 replayed: the decode with the in-kernel split merge (its merge tickets must
 be back at zero after every replay), the 16-row decode followed by the split
-merge kernel, the causal prefill, qsdpa_decode_static (the entry point for
+merge kernel, the VALU decode followed by its merge kernel, the causal prefill, qsdpa_decode_static (the entry point for
 callers that cannot allocate) and qsdpa_decode_append (a decoding step).  Between replays the captured query
 tensor is rewritten and the same call runs eagerly on the same workspace;
 every replay must equal the eager call bit for bit, and the first of them
@@ -20,7 +20,9 @@ CASES = {
     "narrow_fused_merge": (1, 16, 4, 1, 9000, 128, "affine", 4, 64, False),
     "sixteen_row_merge_kernel": (1, 32, 2, 1, 6000, 256, "q8_0", 8, 32, False),
     "prefill_causal": (1, 8, 2, 40, 3000, 128, "q8_0", 8, 32, True),
+    "generic_merge_kernel": (1, 4, 1, 1, 6000, 64, "affine", 8, 64, False),
 }
+ALGO = {"generic_merge_kernel": "generic"}      # the VALU decode and its split merge kernel
 
 
 def _inputs(seed, B, Hq, Hk, Lq, L, D, mode, bits, gs):
@@ -43,7 +45,8 @@ def test_graph_replays_equal_eager_calls(name):
     with torch.cuda.stream(s):
         q = to_dev(qs[0], "f16")
         out = torch.empty_like(q)
-        call = qkv.PreparedAttention(q, kp, vp, L, scale, out, causal=causal, workspace=ws)
+        call = qkv.PreparedAttention(q, kp, vp, L, scale, out, causal=causal, workspace=ws,
+                                     algo=ALGO.get(name, "auto"))
         call()
         call()
     s.synchronize()
@@ -66,7 +69,7 @@ def test_graph_replays_equal_eager_calls(name):
                                    oracle_pack(v, "f16", mode, bits, gs), L, mode, bits, gs,
                                    scale, causal=causal)
             assert_close(got, ref, f"{name} replay {rep}")
-    plan = qkv.qsdpa_plan(q, kp, L)
+    plan = qkv.qsdpa_plan(q, kp, L, algo=ALGO.get(name, "auto"))
     assert plan["num_splits"] > 1, plan           # the split states and merge are exercised
 
 
